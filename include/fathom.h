@@ -1,0 +1,165 @@
+/*
+ * fathom.h — C ABI of the MI355X (gfx950) Fathom key scan.
+ *
+ * The method: "Fathom: Per-Query Read Depth for Sparse Decoding over
+ * Offloaded KV Caches" (papers.paperslantern.ai/papers/2609.17652, abstract
+ * and §3.2–§3.3; restated with its equations in the jaehun.me review of the
+ * same paper, "Bit-Plane K Cache", "Per-Query Read Depth" and the
+ * Appendix A walkthrough).  A decode step ranks every cached key before a
+ * top-k sparse attention step:
+ *
+ *   fathom_encode : fp16 K  -> 4 bit planes + fp16 block scales    (§3.2)
+ *   fathom_plan   : q group, channel variances, bit budget -> depths (§3.3, Eq. 4)
+ *   fathom_scan   : planes, depths, q group -> approximate scores   (§3.3, §7)
+ *   fathom_topk   : scores, k -> top-k key indices per query head   (§2)
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing, keeps no pointer after a call returns and
+ *     holds no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; no call synchronises the host
+ *     with the device.  Calls are reentrant; calls on different streams are
+ *     independent.
+ *   - All arrays are dense, row-major, with the layouts stated per call.
+ *   - d (channels per KV head) must be 128; G (query heads per KV head) must
+ *     be in [1, 8]; token counts must be positive multiples of 64 and below
+ *     2^31; "groups" is the number of KV heads in the call (KV heads x layers
+ *     x sessions, all with the same n).
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns an error status and enqueues nothing.
+ *   - Return value: FATHOM_OK (0) or a negative status below;
+ *     fathom_status_string() names it.
+ */
+#ifndef FATHOM_H_
+#define FATHOM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FATHOM_ABI_VERSION 1
+
+enum fathom_status {
+  FATHOM_OK = 0,
+  FATHOM_ERR_NULL_ARG = -1,        /* a required pointer is NULL            */
+  FATHOM_ERR_BAD_SHAPE = -2,       /* d, G, n, groups or strides invalid    */
+  FATHOM_ERR_BAD_RANGE = -3,       /* k or budget outside its range         */
+  FATHOM_ERR_WORKSPACE = -4,       /* workspace smaller than required       */
+  FATHOM_ERR_HIP = -5,             /* a HIP launch or runtime call failed   */
+  FATHOM_ERR_NO_DEVICE = -6        /* no HIP device is visible              */
+};
+
+/* Number of bit planes per channel and tokens per block (fixed by §3.2). */
+#define FATHOM_PLANES 4
+#define FATHOM_BLOCK 64
+
+/*
+ * fathom_encode — quantize fp16 keys into the channel-major bit-plane store.
+ *
+ * Defined by §3.2 "Bit-Plane K Cache" (both pages): per channel j and 64-token
+ * block b, a = max_i |k_ij| over the block, cell width s = a/8, 4-bit code
+ * c = clamp(floor(k/s) + 8, 0, 15) (code 8 is zero, the MSB is the sign;
+ * floor is fixed by the Appendix A codes).  Bit p of the codes (p = 0 is the
+ * MSB) of the 64 tokens is packed into one 64-bit word, token i of the block
+ * in bit i.  An all-zero block stores a = 0 and codes 8.
+ *
+ *   k      [groups][n][d]          fp16 bit patterns (input)
+ *   planes [groups][d][4][nb_store] uint64 (output) — for fixed (group, j) the
+ *          first t planes over all blocks are one contiguous run (§3.6)
+ *   scales [groups][d][nb_store]   fp16 bit pattern of a (output)
+ *
+ * The n/64 blocks of `k` are written to block slots
+ * [block_offset, block_offset + n/64) of a store holding nb_store blocks per
+ * channel, so a decode loop can append one block at a time.  Requires
+ * block_offset >= 0 and block_offset + n/64 <= nb_store.
+ *
+ * nonfinite_flag (nullable, device uint32): if any input element of a block is
+ * Inf or NaN the kernel ORs 1 into *nonfinite_flag; that block's output is
+ * unspecified.  The flag is never cleared by the library.
+ */
+int fathom_encode(const uint16_t* k, int64_t groups, int64_t n, int32_t d,
+                  int64_t nb_store, int64_t block_offset, uint64_t* planes,
+                  uint16_t* scales, uint32_t* nonfinite_flag, void* stream);
+
+/*
+ * fathom_plan — per query group read depths by integer reverse water-filling.
+ *
+ * Defined by §3.3 "Per-Query Read Depth" (Eq. 4) and the Appendix A
+ * walkthrough: importance g_j = (sum_h q_hj^2) * Var_j (fp64), depth
+ * t_j = clip(round(log4(g_j/theta)), 0, 4) with halves rounded up, i.e.
+ * t_j = #{m in 1..4 : g_j >= 2^(2m-1) * theta} (0 when g_j = 0).  theta is
+ * found by 30 steps of log-bisection (geometric midpoints) for the smallest
+ * theta with sum_j t_j <= budget_bits, bracket [min_{g>0} g / 256, max g];
+ * the depths at the feasible end are returned.  Special cases without
+ * bisection: budget >= 4 * #{g_j > 0} gives t_j = 4 on every g_j > 0
+ * (theta = min_{g>0} g / 256); max g = 0 or budget 0 gives all zeros
+ * (theta = max g).  The plan is shared by the G heads of the group.
+ *
+ *   q         [groups][G][d] fp32  query heads of each KV head (finite)
+ *   var       [groups][d]    fp32  per-channel key variance (>= 0, finite)
+ *   depths    [groups][d]    uint8 output, values 0..4
+ *   theta     [groups]       fp64  output water line (nullable)
+ *   bits_used [groups]       int32 output sum_j t_j (nullable)
+ *   0 <= budget_bits <= 4*d.
+ */
+int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G,
+                int32_t d, int32_t budget_bits, uint8_t* depths, double* theta,
+                int32_t* bits_used, void* stream);
+
+/*
+ * fathom_scan — approximate scores from the prefix planes the depths select.
+ *
+ * Defined by §3.2 (reading the first t planes gives c' = c >> (4-t), value
+ * (c' + 0.5 - 2^(t-1)) * a / 2^(t-1), the t-bit mid-rise quantizer) and §3.3
+ * (channels with t_j = 0 are skipped; one plan per group, read once for all
+ * G heads).  Score of token i for head h:
+ *     S_hi = sum_{j : t_j > 0} q_hj * khat_ij.
+ * Only the planes p < t_j of active channels and their scales are read.
+ *
+ * fp32 evaluation order (fixed so results are reproducible bit for bit):
+ *   o_hb  = +0; for active j ascending: o_hb = fma(e_hj, a_bj, o_hb),
+ *           e_hj = fl32(q_hj * (2^-t_j - 1));
+ *   S_hi  = o_hb; for active j ascending: S_hi = fma(w_hj, m_ij, S_hi),
+ *           w_hj = q_hj * 2^(11 - t_j), m_ij = a_bj * c'_ij * 2^-10 (both exact).
+ *
+ *   planes, scales as written by fathom_encode with nb_store blocks/channel;
+ *   blocks [0, n/64) are scanned.
+ *   depths [groups][d] uint8 (0..4), q [groups][G][d] fp32,
+ *   scores [groups][G][n] fp32 output.
+ */
+int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                const uint8_t* depths, const float* q, int64_t groups, int32_t G,
+                int32_t d, int64_t n, float* scores, void* stream);
+
+/*
+ * fathom_topk — the k highest scores of every row (per query head, §2).
+ *
+ * Order: score descending, ties broken by the lower index; -0 equals +0.
+ * Output: the selected indices of each row in ascending index order.
+ * Scores must be finite.
+ *
+ *   scores  [rows][n] fp32 (rows = groups * G for fathom_scan output)
+ *   indices [rows][k] int32 output
+ *   workspace: device scratch of at least fathom_topk_workspace_bytes(rows,
+ *   n, k) bytes, 256-byte aligned; its contents on entry do not matter.
+ *   1 <= k <= n, n < 2^31 (any n, not only multiples of 64).
+ */
+size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k);
+int fathom_topk(const float* scores, int64_t rows, int64_t n, int32_t k,
+                int32_t* indices, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* fathom_status_string(int status);
+/* FATHOM_ABI_VERSION of the loaded library. */
+int fathom_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATHOM_H_ */
