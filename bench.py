@@ -1,0 +1,217 @@
+"""Benchmark of the Fathom decode-step hot path on one MI355X.
+
+One step = the work of one decode step over a resident bit-plane store:
+encode the newest 64-token block of every KV head into its slot, plan the
+read depths for a fresh query group (importance, 30-step bisection), scan
+every key at those depths, and select the top-k of every query head.
+
+Workload (default): one Qwen3-8B-shaped layer, 8 KV heads x 4 query heads,
+d = 128, n = 1,048,576 keys per head, budget 92 code bits, k = 4096; keys,
+queries and variances from fathom_inputs (synthetic, seeded).  The store is
+held in several copies that the steps rotate through, so the index a step
+reads is not left in the 256 MB last-level cache by the previous step.
+
+Prints one JSON line: keys scanned per second for the whole step (value),
+plus the scan kernel's roofline figures (algorithmic bytes and VALU work per
+launch, over its event-timed average duration) and the CPU oracle's rate on
+a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0                    # MI355X HBM3E
+CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
+VALU_PEAK_TOPS = CUS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-instructions/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="q1m")
+    ap.add_argument("--budget", type=int, default=92)
+    ap.add_argument("--copies", type=int, default=4, help="store copies the steps rotate through")
+    ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def plan_stats(depths: np.ndarray):
+    """Per group: code bits T = sum t_j and active channels A = #{t_j > 0}."""
+    d = depths.astype(np.int64)
+    return d.sum(axis=1), (d > 0).sum(axis=1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fathom_inputs
+    import sparse_top_kv_fathom_amd as fk
+
+    w = fathom_inputs.WORKLOADS[args.workload]
+    H, G, n, d, k, B = w.groups, w.G, w.n, w.d, w.k, args.budget
+    nb = n // 64
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("[bench] generating %s: H=%d G=%d n=%d B=%d k=%d" % (w.name, H, G, n, B, k),
+          file=sys.stderr, flush=True)
+    ins = fathom_inputs.make_inputs(H, G, n, w.seed)
+    qs = np.stack([fathom_inputs.make_queries(H, G, 1000 + i, d) for i in range(args.queries)])
+
+    # Resident store copies, encoded on the GPU.
+    k_d = torch.from_numpy(ins.k).to(dev)
+    stores = []
+    for _ in range(args.copies):
+        stores.append(fk.encode(k_d))
+    newest = k_d[:, n - 64:, :].contiguous()            # the block each step re-encodes
+    del k_d
+    q_d = torch.from_numpy(qs).to(dev)
+    var_d = torch.from_numpy(ins.var).to(dev)
+    depths = torch.empty((H, d), dtype=torch.uint8, device=dev)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+    ws = fk.topk_workspace(H * G, n, k, dev)
+    torch.cuda.synchronize()
+
+    def step(s, ev=None):
+        planes, scales = stores[s % len(stores)]
+        q = q_d[s % args.queries]
+        if ev is not None:
+            ev[0].record()
+        fk.encode(newest, planes, scales, block_offset=nb - 1)
+        if ev is not None:
+            ev[1].record()
+        fk.plan(q, var_d, B, depths=depths)
+        if ev is not None:
+            ev[2].record()
+        fk.scan(planes, scales, depths, q, n, scores=scores)
+        if ev is not None:
+            ev[3].record()
+        fk.topk(scores, k, indices=idx, workspace=ws)
+        if ev is not None:
+            ev[4].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    print("[bench] warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(args.warmup + s, evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
+    stage_ms = stage.mean(axis=0)
+
+    # Algorithmic work of each timed step's scan (plans recomputed after timing).
+    Ts, As = [], []
+    for s in range(args.steps):
+        dep = fk.plan(q_d[(args.warmup + s) % args.queries], var_d, B)
+        T, A = plan_stats(dep.cpu().numpy())
+        Ts.append(T)
+        As.append(A)
+    Ts, As = np.array(Ts), np.array(As)
+    bytes_per_launch = float(np.mean((Ts * nb * 8 + As * nb * 2).sum(axis=1))) + H * G * n * 4
+    ops_per_launch = float(np.mean((Ts + G * As).sum(axis=1))) * nb * 64    # lane-ops
+    scan_s = stage_ms[2] / 1e3
+    hbm_gbps = bytes_per_launch / scan_s / 1e9
+    valu_tops = ops_per_launch / scan_s / 1e12
+    t_hbm = bytes_per_launch / (HBM_PEAK_GBPS * 1e9)
+    t_valu = ops_per_launch / (VALU_PEAK_TOPS * 1e12)
+    bound = "alu" if t_valu >= t_hbm else "hbm"
+    if bound == "alu":
+        roof = {"bound": "alu", "achieved": round(valu_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
+                "unit": "Tlane-op/s", "frac": round(valu_tops / VALU_PEAK_TOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof.update({
+        "kernel": "scan_kernel",
+        "launch_ms": round(stage_ms[2], 4),
+        "alg_bytes_per_launch": int(bytes_per_launch),
+        "alg_lane_ops_per_launch": int(ops_per_launch),
+        "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "valu_Tops": round(valu_tops, 3), "valu_frac": round(valu_tops / VALU_PEAK_TOPS, 4),
+    })
+
+    keys = H * n
+    value = keys / (ms_per_step / 1e3)
+    out = {
+        "metric": "keys scanned/sec (and HBM GB/s, % roofline) at 1M keys, 92-bit budget",
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: %s, G=%d, d=%d, B=%d code bits, k=%d" % (w.name, w.note, G, d, B, k),
+            "kv_heads": H, "G": G, "n": n, "budget_bits": B, "k": k,
+            "store_copies": args.copies, "parallelism": "single GPU",
+        },
+        "stages_ms": {"encode_block": round(stage_ms[0], 4), "plan": round(stage_ms[1], 4),
+                      "scan": round(stage_ms[2], 4), "topk": round(stage_ms[3], 4)},
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "plan": {"code_bits_mean": float(Ts.mean()), "active_channels_mean": float(As.mean()),
+                 "total_bits_per_key_mean": float((Ts + As / 4.0).mean())},
+        "roofline": roof,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = args.cpu_threads or min(H, os.cpu_count() or 1)
+        print("[bench] cpu baseline: oracle step on %d threads" % nthreads, file=sys.stderr,
+              flush=True)
+        op, os_, _ = oracle.encode(ins.k, nthreads=nthreads)           # resident store (setup)
+        qh = qs[args.warmup % args.queries]
+        kb = np.ascontiguousarray(ins.k[:, n - 64:, :])
+        t0 = time.perf_counter()
+        oracle.encode(kb, nb_store=nb, block_offset=nb - 1, planes=op, scales=os_,
+                      nthreads=nthreads)
+        od, _, _ = oracle.plan(qh, ins.var, B, nthreads=nthreads)
+        sc = oracle.scan_ref32(op, os_, od, qh, n, nthreads=nthreads)
+        oracle.topk(sc.reshape(-1, n), k, nthreads=nthreads)
+        cpu_s = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": keys / cpu_s, "unit": "keys/s", "cores": nthreads, "kind": "oracle",
+            "sample": "one full decode step of the same workload (1-block encode, plan, fp32 "
+                      "scan of all %d keys, full-sort top-k), %.1f s" % (keys, cpu_s),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,7 +127,8 @@ def channel_variance(k: np.ndarray) -> np.ndarray:
     groups, n, d = k.shape
     var = np.empty((groups, d), dtype=np.float32)
     step = 1 << 16
-    for g in range(groups):
+
+    def one(g):
         s = np.zeros(d, dtype=np.float64)
         for a in range(0, n, step):
             s += k[g, a:a + step].astype(np.float64).sum(axis=0)
@@ -137,6 +138,14 @@ def channel_variance(k: np.ndarray) -> np.ndarray:
             x = k[g, a:a + step].astype(np.float64) - mean
             ss += (x * x).sum(axis=0)
         var[g] = (ss / max(n - 1, 1)).astype(np.float32)
+
+    nt = _threads(groups)
+    if nt == 1 or groups == 1:
+        for g in range(groups):
+            one(g)
+    else:
+        with _cf.ThreadPoolExecutor(nt) as ex:
+            list(ex.map(one, range(groups)))
     return var
 
 

@@ -27,7 +27,9 @@
  *     2^31; "groups" is the number of KV heads in the call (KV heads x layers
  *     x sessions, all with the same n).
  *   - Arguments are checked on the host before any HIP call; a failed check
- *     returns an error status and enqueues nothing.
+ *     returns an error status and enqueues nothing.  Pointers must be
+ *     aligned to their element size, k to 16 bytes and the top-k workspace
+ *     to 256 bytes.  groups (and top-k rows) must be at most 65535.
  *   - Return value: FATHOM_OK (0) or a negative status below;
  *     fathom_status_string() names it.
  */
@@ -50,7 +52,8 @@ enum fathom_status {
   FATHOM_ERR_BAD_RANGE = -3,       /* k or budget outside its range         */
   FATHOM_ERR_WORKSPACE = -4,       /* workspace smaller than required       */
   FATHOM_ERR_HIP = -5,             /* a HIP launch or runtime call failed   */
-  FATHOM_ERR_NO_DEVICE = -6        /* no HIP device is visible              */
+  FATHOM_ERR_NO_DEVICE = -6,       /* no HIP device is visible              */
+  FATHOM_ERR_ALIGNMENT = -7        /* a pointer lacks its required alignment */
 };
 
 /* Number of bit planes per channel and tokens per block (fixed by §3.2). */

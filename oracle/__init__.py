@@ -53,7 +53,7 @@ def _load():
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int
-        lib.fo_encode.argtypes = [P, I64, I64, I, I64, I64, P, P]
+        lib.fo_encode.argtypes = [P, I64, I64, I, I64, I64, P, P, I]
         lib.fo_encode.restype = I64
         lib.fo_decode.argtypes = [P, P, I64, I64, I, I64, I, P]
         lib.fo_decode.restype = None
@@ -99,7 +99,8 @@ def max_threads() -> int:
 # --------------------------------------------------------------------------
 
 def encode(k_f16: np.ndarray, nb_store: int | None = None, block_offset: int = 0,
-           planes: np.ndarray | None = None, scales: np.ndarray | None = None):
+           planes: np.ndarray | None = None, scales: np.ndarray | None = None,
+           nthreads: int = 0):
     """fp16 keys [groups][n][d] -> (planes [groups][d][4][nb_store] uint64,
     scales [groups][d][nb_store] uint16 (fp16 bits of the block max a),
     number of blocks holding a non-finite value).  §3.2."""
@@ -118,7 +119,7 @@ def encode(k_f16: np.ndarray, nb_store: int | None = None, block_offset: int = 0
     if scales is None:
         scales = np.zeros((groups, d, nb_store), dtype=np.uint16)
     bad = _load().fo_encode(_ptr(k), groups, n, d, nb_store, block_offset,
-                            _ptr(planes), _ptr(scales))
+                            _ptr(planes), _ptr(scales), int(nthreads or max_threads()))
     return planes, scales, int(bad)
 
 

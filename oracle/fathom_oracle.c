@@ -77,9 +77,12 @@ static int fo_code(int64_t K, int64_t A) {
  * blocks that held a non-finite value. */
 int64_t fo_encode(const uint16_t* k, int64_t groups, int64_t n, int d,
                   int64_t nb_store, int64_t block_offset, uint64_t* planes,
-                  uint16_t* scales) {
+                  uint16_t* scales, int nthreads) {
   int64_t nb = n / FO_BLOCK;
   int64_t bad = 0;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) reduction(+ : bad) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
   for (int64_t g = 0; g < groups; ++g) {
     for (int64_t b = 0; b < nb; ++b) {
       for (int j = 0; j < d; ++j) {
@@ -107,6 +110,7 @@ int64_t fo_encode(const uint16_t* k, int64_t groups, int64_t n, int d,
       }
     }
   }
+  (void)nthreads;
   return bad;
 }
 

@@ -1,0 +1,20 @@
+"""MI355X (gfx950) Fathom key scan: encode, plan, scan and top-k behind a C ABI.
+
+The calls follow "Fathom: Per-Query Read Depth for Sparse Decoding over
+Offloaded KV Caches" (§3.2 bit-plane K store, §3.3 per-query read depth,
+§2 per-head top-k).  The work runs in hand-written HIP kernels in
+libfathom.so (include/fathom.h); this package is a thin ctypes binding that
+takes torch device tensors.  Importing a call loads the library and raises if
+it has not been built.
+"""
+_EXPORTS = ("encode", "plan", "scan", "topk", "topk_workspace_bytes", "topk_workspace",
+            "empty_store", "store_shapes", "FathomError", "lib", "STATUS", "EXPORTED")
+
+__all__ = list(_EXPORTS)
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

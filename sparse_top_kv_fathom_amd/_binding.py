@@ -1,0 +1,185 @@
+"""ctypes binding of libfathom.so: the four calls of include/fathom.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers and torch's current HIP stream are passed to
+the C ABI, and a non-zero status raises FathomError.  Every step of the path
+runs in the library's HIP kernels; there is no fallback of any kind.  Loading
+fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfathom.so")
+_lock = threading.Lock()
+_lib = None
+
+BLOCK = 64
+PLANES = 4
+D = 128
+
+STATUS = {
+    0: "FATHOM_OK",
+    -1: "FATHOM_ERR_NULL_ARG",
+    -2: "FATHOM_ERR_BAD_SHAPE",
+    -3: "FATHOM_ERR_BAD_RANGE",
+    -4: "FATHOM_ERR_WORKSPACE",
+    -5: "FATHOM_ERR_HIP",
+    -6: "FATHOM_ERR_NO_DEVICE",
+    -7: "FATHOM_ERR_ALIGNMENT",
+}
+
+EXPORTED = ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+            "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
+
+
+class FathomError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = lib().fathom_status_string(status).decode()
+        super().__init__("%s failed: %s (%d)" % (where, name, status))
+
+
+def lib():
+    """The loaded libfathom.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libfathom.so is not built (run python -m "
+                              "sparse_top_kv_fathom_amd.build); no fallback exists")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.fathom_encode.argtypes = [P, I64, I64, I32, I64, I64, P, P, P, P]
+        L.fathom_plan.argtypes = [P, P, I64, I32, I32, I32, P, P, P, P]
+        L.fathom_scan.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P]
+        L.fathom_topk.argtypes = [P, I64, I64, I32, P, P, SZ, P]
+        L.fathom_topk_workspace_bytes.argtypes = [I64, I64, I32]
+        L.fathom_topk_workspace_bytes.restype = SZ
+        L.fathom_status_string.argtypes = [ctypes.c_int]
+        L.fathom_status_string.restype = ctypes.c_char_p
+        L.fathom_abi_version.argtypes = []
+        for f in ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+                  "fathom_abi_version"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FathomError(status, where)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name, dtype, shape):
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtype, shape)
+
+
+def store_shapes(groups: int, nb_store: int, d: int = D):
+    """Shapes of the plane and scale arrays of a store of nb_store blocks."""
+    return (groups, d, PLANES, nb_store), (groups, d, nb_store)
+
+
+def empty_store(groups: int, nb_store: int, device="cuda", d: int = D):
+    ps, ss = store_shapes(groups, nb_store, d)
+    return (torch.empty(ps, dtype=torch.uint64, device=device),
+            torch.empty(ss, dtype=torch.uint16, device=device))
+
+
+def encode(k: torch.Tensor, planes: torch.Tensor | None = None, scales: torch.Tensor | None = None,
+           block_offset: int = 0, nonfinite_flag: torch.Tensor | None = None, stream=None):
+    """fathom_encode: k [groups][n][d] fp16 -> (planes, scales).  Writes block
+    slots [block_offset, block_offset + n/64) of the given store (a new store
+    of exactly n/64 blocks when planes/scales are None)."""
+    groups, n, d = k.shape
+    if planes is None:
+        planes, scales = empty_store(groups, n // BLOCK, k.device, d)
+    nb_store = planes.shape[-1]
+    ps, ss = store_shapes(groups, nb_store, d)
+    st = lib().fathom_encode(
+        _dev(k, "k", torch.float16), groups, n, d, nb_store, block_offset,
+        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+        _opt(nonfinite_flag, "nonfinite_flag", torch.int32, (1,)), _stream(stream))
+    _check(st, "fathom_encode")
+    return planes, scales
+
+
+def plan(q: torch.Tensor, var: torch.Tensor, budget_bits: int, depths: torch.Tensor | None = None,
+         theta: torch.Tensor | None = None, bits_used: torch.Tensor | None = None, stream=None):
+    """fathom_plan: q [groups][G][d] fp32, var [groups][d] fp32 -> depths uint8 [groups][d]."""
+    groups, G, d = q.shape
+    if depths is None:
+        depths = torch.empty((groups, d), dtype=torch.uint8, device=q.device)
+    st = lib().fathom_plan(
+        _dev(q, "q", torch.float32), _dev(var, "var", torch.float32, (groups, d)), groups, G, d,
+        int(budget_bits), _dev(depths, "depths", torch.uint8, (groups, d)),
+        _opt(theta, "theta", torch.float64, (groups,)),
+        _opt(bits_used, "bits_used", torch.int32, (groups,)), _stream(stream))
+    _check(st, "fathom_plan")
+    return depths
+
+
+def scan(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: torch.Tensor,
+         n: int, scores: torch.Tensor | None = None, stream=None):
+    """fathom_scan: scores [groups][G][n] fp32 of the first n keys of the store."""
+    groups, G, d = q.shape
+    nb_store = planes.shape[-1]
+    ps, ss = store_shapes(groups, nb_store, d)
+    if scores is None:
+        scores = torch.empty((groups, G, n), dtype=torch.float32, device=q.device)
+    st = lib().fathom_scan(
+        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+        nb_store, _dev(depths, "depths", torch.uint8, (groups, d)), _dev(q, "q", torch.float32),
+        groups, G, d, int(n), _dev(scores, "scores", torch.float32, (groups, G, n)),
+        _stream(stream))
+    _check(st, "fathom_scan")
+    return scores
+
+
+def topk_workspace_bytes(rows: int, n: int, k: int) -> int:
+    return int(lib().fathom_topk_workspace_bytes(rows, n, k))
+
+
+def topk_workspace(rows: int, n: int, k: int, device="cuda") -> torch.Tensor:
+    nbytes = topk_workspace_bytes(rows, n, k)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def topk(scores: torch.Tensor, k: int, indices: torch.Tensor | None = None,
+         workspace: torch.Tensor | None = None, stream=None):
+    """fathom_topk: scores [..., n] fp32 -> indices [rows][k] int32 ascending."""
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    if indices is None:
+        indices = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if workspace is None:
+        workspace = topk_workspace(rows, n, k, scores.device)
+    st = lib().fathom_topk(
+        _dev(scores, "scores", torch.float32), rows, n, int(k),
+        _dev(indices, "indices", torch.int32, (rows, k)), _dev(workspace, "workspace", torch.uint8),
+        workspace.numel(), _stream(stream))
+    _check(st, "fathom_topk")
+    return indices

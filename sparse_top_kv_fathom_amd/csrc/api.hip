@@ -1,0 +1,115 @@
+// C ABI of the gfx950 Fathom library: argument checks, then kernel launches.
+// Every check runs on the host before the first HIP call, so an invalid call
+// enqueues nothing and never touches the device.
+#include "fathom.h"
+#include "fathom_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxTokens = int64_t(1) << 31;
+constexpr int64_t kMaxGroups = 65535;
+
+int to_status(hipError_t e) {
+  if (e == hipSuccess) return FATHOM_OK;
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice || e == hipErrorInsufficientDriver)
+    return FATHOM_ERR_NO_DEVICE;
+  return FATHOM_ERR_HIP;
+}
+
+int device_ready() {
+  int count = 0;
+  const hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) return FATHOM_ERR_NO_DEVICE;
+  return FATHOM_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_tokens(int64_t n) { return n >= fathom::kBlock && n % fathom::kBlock == 0 && n < kMaxTokens; }
+
+}  // namespace
+
+extern "C" {
+
+int fathom_abi_version(void) { return FATHOM_ABI_VERSION; }
+
+const char* fathom_status_string(int status) {
+  switch (status) {
+    case FATHOM_OK: return "FATHOM_OK";
+    case FATHOM_ERR_NULL_ARG: return "FATHOM_ERR_NULL_ARG: a required pointer is NULL";
+    case FATHOM_ERR_BAD_SHAPE: return "FATHOM_ERR_BAD_SHAPE: d, G, n, groups or strides invalid";
+    case FATHOM_ERR_BAD_RANGE: return "FATHOM_ERR_BAD_RANGE: k or budget outside its range";
+    case FATHOM_ERR_WORKSPACE: return "FATHOM_ERR_WORKSPACE: workspace smaller than required";
+    case FATHOM_ERR_HIP: return "FATHOM_ERR_HIP: a HIP launch or runtime call failed";
+    case FATHOM_ERR_NO_DEVICE: return "FATHOM_ERR_NO_DEVICE: no HIP device is visible";
+    case FATHOM_ERR_ALIGNMENT: return "FATHOM_ERR_ALIGNMENT: a pointer lacks its required alignment";
+    default: return "FATHOM_ERR_UNKNOWN";
+  }
+}
+
+int fathom_encode(const uint16_t* k, int64_t groups, int64_t n, int32_t d, int64_t nb_store,
+                  int64_t block_offset, uint64_t* planes, uint16_t* scales,
+                  uint32_t* nonfinite_flag, void* stream) {
+  if (!k || !planes || !scales) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || groups < 1 || groups > kMaxGroups || !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < 1 || nb_store >= kMaxTokens / fathom::kBlock || block_offset < 0 ||
+      block_offset + n / fathom::kBlock > nb_store)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(k, 16) || !aligned(planes, 8) || !aligned(scales, 2) ||
+      !aligned(nonfinite_flag, 4))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_encode(k, groups, n, nb_store, block_offset, planes, scales,
+                                         nonfinite_flag, static_cast<hipStream_t>(stream)));
+}
+
+int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G, int32_t d,
+                int32_t budget_bits, uint8_t* depths, double* theta, int32_t* bits_used,
+                void* stream) {
+  if (!q || !var || !depths) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (budget_bits < 0 || budget_bits > fathom::kPlanes * d) return FATHOM_ERR_BAD_RANGE;
+  if (!aligned(q, 4) || !aligned(var, 4) || !aligned(theta, 8) || !aligned(bits_used, 4))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_plan(q, var, groups, G, budget_bits, depths, theta, bits_used,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                const uint8_t* depths, const float* q, int64_t groups, int32_t G, int32_t d,
+                int64_t n, float* scores, void* stream) {
+  if (!planes || !scales || !depths || !q || !scores) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups ||
+      !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < n / fathom::kBlock || nb_store >= kMaxTokens / fathom::kBlock)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(planes, 8) || !aligned(scales, 2) || !aligned(q, 4) || !aligned(scores, 4))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_scan(planes, scales, nb_store, depths, q, groups, G, n, scores,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k) {
+  if (rows < 1 || n < 1 || n >= kMaxTokens || k < 1 || k > n) return 0;
+  return fathom::topk_workspace_bytes(rows, n, k);
+}
+
+int fathom_topk(const float* scores, int64_t rows, int64_t n, int32_t k, int32_t* indices,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!scores || !indices || !workspace) return FATHOM_ERR_NULL_ARG;
+  if (rows < 1 || rows > kMaxGroups || n < 1 || n >= kMaxTokens) return FATHOM_ERR_BAD_SHAPE;
+  if (k < 1 || k > n) return FATHOM_ERR_BAD_RANGE;
+  if (workspace_bytes < fathom::topk_workspace_bytes(rows, n, k)) return FATHOM_ERR_WORKSPACE;
+  if (!aligned(scores, 4) || !aligned(indices, 4) || !aligned(workspace, 256))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_topk(scores, rows, n, k, indices, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

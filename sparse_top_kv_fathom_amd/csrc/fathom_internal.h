@@ -1,0 +1,43 @@
+// Internal declarations of the gfx950 Fathom library (kernels + launchers).
+// Not part of the public ABI; see include/fathom.h for the calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fathom {
+
+constexpr int kBlock = 64;   // tokens per block = bits per plane word = wave64 lanes
+constexpr int kPlanes = 4;   // bit planes of the 4-bit code
+constexpr int kD = 128;      // channels per KV head supported by the kernels
+
+// Launchers: enqueue on `stream`, return the hipError_t of the launch.
+hipError_t launch_encode(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
+                         int64_t block_offset, uint64_t* planes, uint16_t* scales,
+                         uint32_t* nonfinite_flag, hipStream_t stream);
+
+hipError_t launch_plan(const float* q, const float* var, int64_t groups, int G,
+                       int budget_bits, uint8_t* depths, double* theta, int32_t* bits_used,
+                       hipStream_t stream);
+
+hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                       const uint8_t* depths, const float* q, int64_t groups, int G,
+                       int64_t n, float* scores, hipStream_t stream);
+
+size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
+hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
+                       void* workspace, hipStream_t stream);
+
+// Wave-wide helpers -------------------------------------------------------
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Make the wave's earlier LDS writes visible to its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace fathom

@@ -1,0 +1,153 @@
+"""The C-ABI library loads, exports every call include/fathom.h declares, and
+rejects invalid arguments on the host before any HIP call (CPU only: fake
+non-NULL pointers are never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fathom.h")
+LIB = os.path.join(ROOT, "sparse_top_kv_fathom_amd", "libfathom.so")
+
+OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7
+P = ctypes.c_void_p
+FAKE = P(1 << 20)           # a well-aligned, never dereferenced address
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fathom_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        import sparse_top_kv_fathom_amd.build as b
+        b.build()
+    import sparse_top_kv_fathom_amd as fk
+    return fk.lib()
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_header_declares_the_calls():
+    names = declared()
+    for f in ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+              "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared():
+        assert name in exported, name
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings(L):
+    assert L.fathom_abi_version() == 1
+    for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN):
+        s = L.fathom_status_string(code).decode()
+        assert s.startswith("FATHOM_")
+    assert L.fathom_status_string(12345).decode() == "FATHOM_ERR_UNKNOWN"
+
+
+def test_encode_validation(L):
+    e = L.fathom_encode
+    assert e(None, 1, 4096, 128, 64, 0, FAKE, FAKE, None, None) == NULL_ARG
+    assert e(FAKE, 1, 4096, 128, 64, 0, None, FAKE, None, None) == NULL_ARG
+    assert e(FAKE, 1, 4096, 64, 64, 0, FAKE, FAKE, None, None) == BAD_SHAPE      # d != 128
+    assert e(FAKE, 0, 4096, 128, 64, 0, FAKE, FAKE, None, None) == BAD_SHAPE     # groups
+    assert e(FAKE, 70000, 4096, 128, 64, 0, FAKE, FAKE, None, None) == BAD_SHAPE
+    assert e(FAKE, 1, 4000, 128, 64, 0, FAKE, FAKE, None, None) == BAD_SHAPE     # n % 64
+    assert e(FAKE, 1, 0, 128, 64, 0, FAKE, FAKE, None, None) == BAD_SHAPE        # empty
+    assert e(FAKE, 1, 1 << 31, 128, 1 << 25, 0, FAKE, FAKE, None, None) == BAD_SHAPE
+    assert e(FAKE, 1, 4096, 128, 63, 0, FAKE, FAKE, None, None) == BAD_SHAPE     # capacity
+    assert e(FAKE, 1, 4096, 128, 70, 7, FAKE, FAKE, None, None) == BAD_SHAPE     # offset+nb
+    assert e(FAKE, 1, 4096, 128, 70, -1, FAKE, FAKE, None, None) == BAD_SHAPE
+    assert e(P(8), 1, 4096, 128, 64, 0, FAKE, FAKE, None, None) == ALIGN         # k 16 B
+    assert e(FAKE, 1, 4096, 128, 64, 0, P(4), FAKE, None, None) == ALIGN
+    assert e(FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, P(2), None) == ALIGN
+
+
+def test_plan_validation(L):
+    p = L.fathom_plan
+    assert p(None, FAKE, 1, 4, 128, 92, FAKE, None, None, None) == NULL_ARG
+    assert p(FAKE, FAKE, 1, 4, 128, 92, None, None, None, None) == NULL_ARG
+    assert p(FAKE, FAKE, 1, 0, 128, 92, FAKE, None, None, None) == BAD_SHAPE
+    assert p(FAKE, FAKE, 1, 9, 128, 92, FAKE, None, None, None) == BAD_SHAPE
+    assert p(FAKE, FAKE, 1, 4, 100, 92, FAKE, None, None, None) == BAD_SHAPE
+    assert p(FAKE, FAKE, 0, 4, 128, 92, FAKE, None, None, None) == BAD_SHAPE
+    assert p(FAKE, FAKE, 1, 4, 128, -1, FAKE, None, None, None) == BAD_RANGE
+    assert p(FAKE, FAKE, 1, 4, 128, 513, FAKE, None, None, None) == BAD_RANGE
+    assert p(FAKE, FAKE, 1, 4, 128, 92, FAKE, P(4), None, None) == ALIGN         # theta 8 B
+
+
+def test_scan_validation(L):
+    s = L.fathom_scan
+    args = [FAKE, FAKE, 64, FAKE, FAKE, 1, 4, 128, 4096, FAKE, None]
+    for i in (0, 1, 3, 4, 9):
+        a = list(args)
+        a[i] = None
+        assert s(*a) == NULL_ARG
+    a = list(args); a[2] = 63
+    assert s(*a) == BAD_SHAPE                                                     # nb_store < n/64
+    a = list(args); a[6] = 9
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[7] = 256
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[8] = 4095
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[8] = 0
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[5] = 0
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[0] = P(4)
+    assert s(*a) == ALIGN
+
+
+def test_topk_validation(L):
+    t = L.fathom_topk
+    need = L.fathom_topk_workspace_bytes(4, 1000, 10)
+    assert need > 0 and need % 256 == 0
+    assert t(None, 4, 1000, 10, FAKE, FAKE, need, None) == NULL_ARG
+    assert t(FAKE, 4, 1000, 10, FAKE, None, need, None) == NULL_ARG
+    assert t(FAKE, 0, 1000, 10, FAKE, FAKE, need, None) == BAD_SHAPE
+    assert t(FAKE, 4, 0, 1, FAKE, FAKE, need, None) == BAD_SHAPE
+    assert t(FAKE, 4, 1000, 0, FAKE, FAKE, need, None) == BAD_RANGE
+    assert t(FAKE, 4, 1000, 1001, FAKE, FAKE, need, None) == BAD_RANGE
+    assert t(FAKE, 4, 1000, 10, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert t(FAKE, 4, 1000, 10, FAKE, P((1 << 20) + 128), need, None) == ALIGN
+    assert L.fathom_topk_workspace_bytes(4, 1000, 1001) == 0
+    assert L.fathom_topk_workspace_bytes(8, 1 << 20, 4096) >= L.fathom_topk_workspace_bytes(4, 1 << 20, 4096)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device status; a GPU is visible")
+def test_valid_calls_report_no_device(L):
+    assert L.fathom_scan(FAKE, FAKE, 64, FAKE, FAKE, 1, 4, 128, 4096, FAKE, None) == NO_DEVICE
+    need = L.fathom_topk_workspace_bytes(4, 1000, 10)
+    assert L.fathom_topk(FAKE, 4, 1000, 10, FAKE, FAKE, need, None) == NO_DEVICE
+    assert L.fathom_plan(FAKE, FAKE, 1, 4, 128, 92, FAKE, None, None, None) == NO_DEVICE
+    assert L.fathom_encode(FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, None, None) == NO_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The binding has no fallback: a missing library raises on first use."""
+    import importlib
+    import sparse_top_kv_fathom_amd._binding as b
+    monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(ImportError):
+        b.lib()
+    importlib.reload(b)

@@ -1,0 +1,145 @@
+"""GPU parity of fathom_scan and fathom_topk against the CPU oracle.
+
+Scores: bit-exact against the oracle's fp32 evaluation order, and within
+1e-4 of the fp64 definition relative to sum_j |q_hj khat_ij|.  Top-k index
+sets: bit-exact (score descending, lower index first on ties, ascending
+output).  The end-to-end case runs the 1M-key Qwen3-shaped layer at B = 92
+with k = 4096 in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import fathom_inputs
+import oracle
+from gpu_util import first_mismatch, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def fk():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    import sparse_top_kv_fathom_amd as fk
+    fk.lib()
+    return fk
+
+
+def _scan(fk, planes, scales, depths, q, n):
+    import torch
+    s = fk.scan(to_dev(planes), to_dev(scales), to_dev(depths), to_dev(q), n)
+    torch.cuda.synchronize()
+    return to_host(s)
+
+
+def _check_scores(gpu, planes, scales, depths, q, n):
+    ref = oracle.scan_ref32(planes, scales, depths, q, n)
+    assert np.array_equal(gpu.view(np.uint32), ref.view(np.uint32)), first_mismatch(gpu, ref)
+    s64, l1 = oracle.scan_f64(planes, scales, depths, q, n)
+    err = np.abs(gpu.astype(np.float64) - s64)
+    assert np.all(err <= TOL * l1), float(np.max(err / np.maximum(l1, 1e-300)))
+
+
+def test_scan_tiny(fk):
+    w = fathom_inputs.WORKLOADS["tiny"]
+    ins = fathom_inputs.workload_inputs("tiny")
+    planes, scales, _ = oracle.encode(ins.k)
+    depths, _, _ = oracle.plan(ins.q, ins.var, 92)
+    say("scan tiny B=92")
+    _check_scores(_scan(fk, planes, scales, depths, ins.q, w.n), planes, scales, depths, ins.q, w.n)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 8])
+def test_scan_shapes_and_budgets(fk, G):
+    """Several tiles plus a ragged tail tile (n = 64 * 101), every G, budgets
+    from 0 (no active channel) to 512 (all channels at full depth)."""
+    n = 64 * 101
+    ins = fathom_inputs.make_inputs(3, G, n, seed=300 + G)
+    planes, scales, _ = oracle.encode(ins.k)
+    for B in (0, 3, 17, 92, 136, 512):
+        depths, _, _ = oracle.plan(ins.q, ins.var, B)
+        say("scan G=%d n=%d B=%d" % (G, n, B))
+        gpu = _scan(fk, planes, scales, depths, ins.q, n)
+        _check_scores(gpu, planes, scales, depths, ins.q, n)
+
+
+def test_scan_random_depths_and_store_capacity(fk):
+    """Arbitrary depth vectors (not from a plan) and a store larger than the
+    scanned range (nb_store > n/64, scanning a prefix)."""
+    rng = np.random.default_rng(31)
+    ins = fathom_inputs.make_inputs(2, 4, 64 * 70, seed=31)
+    planes, scales, _ = oracle.encode(ins.k, nb_store=90)
+    for n in (64, 64 * 33, 64 * 70):
+        depths = rng.integers(0, 5, size=(2, 128)).astype(np.uint8)
+        say("scan random depths n=%d nb_store=90" % n)
+        gpu = _scan(fk, planes, scales, depths, ins.q, n)
+        _check_scores(gpu, planes, scales, depths, ins.q, n)
+
+
+def _topk(fk, scores, k):
+    import torch
+    idx = fk.topk(to_dev(scores), k)
+    torch.cuda.synchronize()
+    return to_host(idx)
+
+
+TOPK_CASES = [
+    (4, 4096, 64), (3, 1000, 7), (2, 8192 * 3 + 17, 1000), (1, 100, 100), (5, 20000, 1),
+    (2, 70000, 4096), (1, 8192, 8192), (3, 1, 1), (2, 8193, 8000),
+]
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "const", "signed_zero"])
+def test_topk_matches_oracle(fk, kind):
+    for rows, n, k in TOPK_CASES:
+        scores = fathom_inputs.random_scores(rows, n, seed=rows * 7 + n, kind=kind)
+        say("topk kind=%s rows=%d n=%d k=%d" % (kind, rows, n, k))
+        gpu = _topk(fk, scores, k)
+        ref = oracle.topk(scores, k)
+        assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+
+
+def test_topk_repeatable(fk):
+    scores = fathom_inputs.random_scores(8, 50000, seed=41, kind="ties")
+    say("topk repeat x3")
+    a = _topk(fk, scores, 2048)
+    for _ in range(2):
+        assert np.array_equal(a, _topk(fk, scores, 2048))
+
+
+@pytest.mark.timeout(900)
+def test_end_to_end_q1m_b92(fk):
+    """1M keys x 8 KV heads, GQA 4, B = 92, k = 4096: GPU encode -> plan ->
+    scan -> top-k against the oracle, every output compared in full."""
+    import torch
+    w = fathom_inputs.WORKLOADS["q1m"]
+    ins = fathom_inputs.workload_inputs("q1m")
+    say("e2e q1m encode")
+    kd = to_dev(ins.k)
+    planes, scales = fk.encode(kd)
+    say("e2e q1m plan/scan/topk")
+    depths = fk.plan(to_dev(ins.q), to_dev(ins.var), 92)
+    scores = fk.scan(planes, scales, depths, to_dev(ins.q), w.n)
+    idx = fk.topk(scores, w.k)
+    torch.cuda.synchronize()
+    del kd
+    gp, gs, gd, gsc, gi = (to_host(planes), to_host(scales), to_host(depths), to_host(scores),
+                           to_host(idx))
+    op, os_, _ = oracle.encode(ins.k)
+    assert np.array_equal(gp, op), first_mismatch(gp, op)
+    assert np.array_equal(gs, os_), first_mismatch(gs, os_)
+    od, _, _ = oracle.plan(ins.q, ins.var, 92)
+    assert np.array_equal(gd, od), first_mismatch(gd, od)
+    ref = oracle.scan_ref32(op, os_, od, ins.q, w.n)
+    assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
+    oi = oracle.topk(ref.reshape(-1, w.n), w.k)
+    assert np.array_equal(gi, oi), first_mismatch(gi, oi)
+    # tolerance against the fp64 definition on a slice of blocks of every group
+    b0, b1 = 1000, 1064
+    sub_p = np.ascontiguousarray(op[..., b0:b1])
+    sub_s = np.ascontiguousarray(os_[..., b0:b1])
+    s64, l1 = oracle.scan_f64(sub_p, sub_s, od, ins.q, (b1 - b0) * 64)
+    got = gsc[:, :, b0 * 64:b1 * 64].astype(np.float64)
+    assert np.all(np.abs(got - s64) <= TOL * l1)
