@@ -124,13 +124,16 @@ int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G,
  * Only the planes p < t_j of active channels and their scales are read.
  *
  * fp32 evaluation order (fixed so results are reproducible bit for bit):
- *   o_hb  = +0; for active j ascending: o_hb = fma(e_hj, a_bj, o_hb),
- *           e_hj = fl32(q_hj * (2^-t_j - 1));
- *   S_hi  = o_hb; for active j ascending: S_hi = fma(w_hj, m_ij, S_hi),
- *           w_hj = q_hj * 2^(11 - t_j), m_ij = a_bj * c'_ij * 2^-10 (both exact).
+ *   U_hi = +0; for each active j: U_hi = fma(w_hj, m_ij, U_hi),
+ *          w_hj = q_hj * 2^(11 - t_j), m_ij = a_bj * c'_ij * 2^-10 (both exact);
+ *   o_hb = +0; for each active j: o_hb = fma(e_hj, a_bj, o_hb),
+ *          e_hj = fl32(q_hj * (2^-t_j - 1));
+ *   S_hi = fl32(U_hi + o_hb),
+ * where "each active j" takes the channels of depth 4 first, then 3, 2 and
+ * 1, ascending j within a depth.  Depth values above 4 read as 4.
  *
- *   planes, scales as written by fathom_encode with nb_store blocks/channel;
- *   blocks [0, n/64) are scanned.
+ *   planes, scales as written by fathom_encode with nb_store blocks/channel
+ *   (scales must be 4-byte aligned here); blocks [0, n/64) are scanned.
  *   depths [groups][d] uint8 (0..4), q [groups][G][d] fp32,
  *   scores [groups][G][n] fp32 output.
  */

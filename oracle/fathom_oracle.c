@@ -255,6 +255,9 @@ void fo_plan(const float* q, const float* var, int64_t groups, int G, int d,
 /* Scan: §3.2 prefix dequantization, §3.3 active channels                    */
 /* ------------------------------------------------------------------------ */
 
+/* Depth values above 4 read as 4 (a channel has four planes). */
+static int fo_depth_clamped(uint8_t t) { return t > FO_PLANES ? FO_PLANES : (int)t; }
+
 /* Plain definition in fp64: S_hi = sum_{j : t_j > 0} q_hj * khat_ij with the
  * prefix value of §3.2 (each product is exact in fp64).  Also returns
  * l1_hi = sum_j |q_hj * khat_ij|, the magnitude the tolerance is relative to.
@@ -273,10 +276,11 @@ void fo_scan_f64(const uint64_t* planes, const uint16_t* scales, int64_t nb_stor
         for (int h = 0; h < G; ++h) {
           double s = 0.0, m = 0.0;
           for (int j = 0; j < d; ++j) {
-            if (t[j] == 0) continue;
+            int tj = fo_depth_clamped(t[j]);
+            if (tj == 0) continue;
             int64_t gj = g * d + j;
             double kh = fo_dequant(scales[gj * nb_store + b],
-                                   fo_prefix_code(planes, nb_store, gj, b, i, t[j]), t[j]);
+                                   fo_prefix_code(planes, nb_store, gj, b, i, tj), tj);
             double prod = (double)q[(g * G + h) * d + j] * kh;
             s += prod;
             m += fabs(prod);
@@ -292,11 +296,14 @@ void fo_scan_f64(const uint64_t* planes, const uint16_t* scales, int64_t nb_stor
 /* The same scores in the fp32 order the GPU kernel uses (the pages fix no
  * fp32 order; this one is stated in fathom.h).  Splitting the §3.2 value as
  *   khat = a * (c' * 2^(1-t) + 2^-t - 1)
- * gives, per block b and head h,
- *   o  = +0;  for active j ascending: o = fmaf(e_hj, a_bj, o),
+ * gives, per block b, head h and token i of the block,
+ *   U  = +0;  for each active j: U = fmaf(w_hj, m_ij, U),
+ *             w_hj = q_hj * 2^(11-t_j), m_ij = a_bj * c'_ij * 2^-10 (both exact)
+ *   o  = +0;  for each active j: o = fmaf(e_hj, a_bj, o),
  *             e_hj = fl32(q_hj * (2^-t_j - 1))
- *   S  = o;   for active j ascending: S = fmaf(w_hj, m_ij, S),
- *             w_hj = q_hj * 2^(11-t_j), m_ij = a_bj * c'_ij * 2^-10 (exact).
+ *   S  = fl32(U + o),
+ * where "each active j" visits the channels with t_j = 4 first, then 3, 2
+ * and 1, ascending j within one depth.  Depth values above 4 read as 4.
  * Output [groups][G][n]. */
 void fo_scan_ref32(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                    const uint8_t* depths, const float* q, int64_t groups, int G,
@@ -306,31 +313,39 @@ void fo_scan_ref32(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
 #pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
 #endif
   for (int64_t g = 0; g < groups; ++g) {
-    const uint8_t* t = depths + g * d;
+    /* The visiting order: by depth 4, 3, 2, 1, then by channel index. */
+    int* order = (int*)malloc(sizeof(int) * (size_t)d);
+    int nact = 0;
+    for (int depth = FO_PLANES; depth >= 1; --depth)
+      for (int j = 0; j < d; ++j)
+        if (fo_depth_clamped(depths[g * d + j]) == depth) order[nact++] = j;
     for (int64_t b = 0; b < nb; ++b)
       for (int h = 0; h < G; ++h) {
         const float* qh = q + (g * G + h) * d;
         float o = 0.0f;
-        for (int j = 0; j < d; ++j) {
-          if (t[j] == 0) continue;
+        for (int k = 0; k < nact; ++k) {
+          int j = order[k];
+          int t = fo_depth_clamped(depths[g * d + j]);
           float a = (float)fo_f16_to_f64(scales[(g * d + j) * nb_store + b]);
-          float e = qh[j] * (ldexpf(1.0f, -t[j]) - 1.0f);
+          float e = qh[j] * (ldexpf(1.0f, -t) - 1.0f);
           o = fmaf(e, a, o);
         }
         for (int i = 0; i < FO_BLOCK; ++i) {
-          float s = o;
-          for (int j = 0; j < d; ++j) {
-            if (t[j] == 0) continue;
+          float u = 0.0f;
+          for (int k = 0; k < nact; ++k) {
+            int j = order[k];
+            int t = fo_depth_clamped(depths[g * d + j]);
             int64_t gj = g * d + j;
             float a = (float)fo_f16_to_f64(scales[gj * nb_store + b]);
-            int c = fo_prefix_code(planes, nb_store, gj, b, i, t[j]);
-            float w = ldexpf(qh[j], 11 - t[j]);
+            int c = fo_prefix_code(planes, nb_store, gj, b, i, t);
+            float w = ldexpf(qh[j], 11 - t);
             float m = ldexpf(a * (float)c, -10);
-            s = fmaf(w, m, s);
+            u = fmaf(w, m, u);
           }
-          scores[(g * G + h) * n + b * FO_BLOCK + i] = s;
+          scores[(g * G + h) * n + b * FO_BLOCK + i] = u + o;
         }
       }
+    free(order);
   }
   (void)nthreads;
 }

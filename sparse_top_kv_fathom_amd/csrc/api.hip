@@ -8,6 +8,7 @@ namespace {
 
 constexpr int64_t kMaxTokens = int64_t(1) << 31;
 constexpr int64_t kMaxGroups = 65535;
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 31) / 1024;  // grid x limit at 1024 threads
 
 int to_status(hipError_t e) {
   if (e == hipSuccess) return FATHOM_OK;
@@ -87,8 +88,9 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
     return FATHOM_ERR_BAD_SHAPE;
   if (nb_store < n / fathom::kBlock || nb_store >= kMaxTokens / fathom::kBlock)
     return FATHOM_ERR_BAD_SHAPE;
-  if (!aligned(planes, 8) || !aligned(scales, 2) || !aligned(q, 4) || !aligned(scores, 4))
+  if (!aligned(planes, 8) || !aligned(scales, 4) || !aligned(q, 4) || !aligned(scores, 4))
     return FATHOM_ERR_ALIGNMENT;
+  if (fathom::scan_max_workgroups(groups, n) > kMaxWorkgroups) return FATHOM_ERR_BAD_SHAPE;
   if (int s = device_ready()) return s;
   return to_status(fathom::launch_scan(planes, scales, nb_store, depths, q, groups, G, n, scores,
                                        static_cast<hipStream_t>(stream)));

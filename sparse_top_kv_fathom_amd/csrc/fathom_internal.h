@@ -25,6 +25,9 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t n
                        const uint8_t* depths, const float* q, int64_t groups, int G,
                        int64_t n, float* scores, hipStream_t stream);
 
+// Workgroups fathom_scan launches for `groups` groups of n keys.
+int64_t scan_max_workgroups(int64_t groups, int64_t n);
+
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* workspace, hipStream_t stream);
