@@ -5,45 +5,77 @@
 // chosen per query head.  Selection order: score descending, lower index
 // first on equal scores; the k indices of a row are returned ascending.
 //
-// Radix select on an order-preserving 32-bit key (fp32 bits with the sign
-// folded, -0 mapped to +0): three histogram passes over the row (11, 11 and
-// 10 bits) each fix one digit of the k-th largest key T and how many keys
-// equal to T are still needed.  A count pass records, per chunk of the row,
-// how many keys are > T and == T; a per-row scan turns those into output
-// offsets and per-chunk quotas of ties (the lowest indices win); a final
-// pass writes every selected index at its rank, so the output comes out in
-// index order with no sort.  Histograms are built in LDS per chunk and only
-// non-empty bins are added to the row's global histogram.
+// Scores map to order-preserving 32-bit keys (fp32 bits with the sign
+// folded, -0 mapped to +0).  Per row:
+//   sample  — an 11-bit histogram of the top key bits over every 8th chunk;
+//   guess   — a cut tau (the low edge of a histogram bin) that leaves, by the
+//             sample, comfortably more than k keys at or above it;
+//   compact — one pass over the row appends every key >= tau (key, index) to
+//             the row's candidate buffer, each chunk as one contiguous
+//             segment in index order, and records per chunk the segment and
+//             a histogram of its candidates' top digits;
+//   resolve — one workgroup per row selects exactly among the candidates:
+//             the k-th largest key T (the top digit from the chunk
+//             histograms, two more radix digits over the candidates), the
+//             keys == T still needed, and then walks the segments in chunk
+//             order, writing every key > T and the earliest keys == T, so
+//             the row comes out in index order without a sort.
+// If the guess fails (fewer than k keys >= tau, or more than the buffer
+// holds: heavy ties or adversarial rows), the resolve workgroup does the
+// same from the scores themselves: same result, many more passes.
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 8192;             // keys per workgroup chunk
-constexpr int kBins = 2048;              // widest digit (11 bits)
-constexpr int kStateWords = 16;          // per-row state: [0] prefix, [1] need
+constexpr int kWavesPerWg = kThreads / 64;
+constexpr int kPerThread = 32;                       // keys per thread in a chunk
+constexpr int kChunk = kThreads * kPerThread;        // 8192 keys per workgroup chunk
+constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
+constexpr int kBins = 2048;                          // radix digit: 11 bits
+constexpr int kSampleStride = 8;                     // every 8th chunk is sampled
+constexpr int kTopBins = 64;                         // chunk histogram: digits tau .. tau + 62, and above
+constexpr int kResolveThreads = 1024;
 
-struct RowWs {
-  uint32_t* hist;    // [kBins]
-  uint32_t* state;   // [kStateWords]
-  uint32_t* cnt;     // [nchunks][2]: keys > T, keys == T
-  uint32_t* off;     // [nchunks][2]: output base, quota of keys == T
+// Per-row workspace (32-bit words).
+enum : int {
+  kS_TAU = 0,       // candidate cut
+  kS_NCAND,         // keys >= tau seen so far (may exceed the capacity)
+  kS_NSAMPLE,       // keys in the sampled chunks
+  kS_WORDS = 16
 };
 
 __host__ __device__ inline int64_t n_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-__host__ __device__ inline size_t row_ws_words(int64_t n) {
-  return (size_t)kBins + kStateWords + (size_t)n_chunks(n) * 4;
+// Candidate buffer capacity: n / 8, between 8192 and 65536 keys.
+__host__ __device__ inline int64_t cand_cap(int64_t n) {
+  const int64_t c = n / 8;
+  return c < 8192 ? 8192 : (c > 65536 ? 65536 : c);
 }
 
+__host__ __device__ inline size_t row_words(int64_t n) {
+  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + (2 + kTopBins) * (size_t)n_chunks(n);
+}
+
+struct RowWs {
+  uint32_t* hist;    // [kBins]: sample histogram
+  uint32_t* st;      // [kS_WORDS]
+  uint32_t* cand;    // [cap][2]: key, index
+  uint32_t* seg;     // [nchunks][2]: first slot and number of the chunk's candidates
+  uint32_t* thist;   // [nchunks][kTopBins]: the chunk's candidate top digits
+  uint32_t cap;
+};
+
 __device__ inline RowWs row_ws(void* ws, int64_t n, int64_t row) {
-  uint32_t* base = reinterpret_cast<uint32_t*>(ws) + row_ws_words(n) * row;
+  uint32_t* p = reinterpret_cast<uint32_t*>(ws) + row_words(n) * row;
   RowWs r;
-  r.hist = base;
-  r.state = base + kBins;
-  r.cnt = r.state + kStateWords;
-  r.off = r.cnt + n_chunks(n) * 2;
+  r.cap = (uint32_t)cand_cap(n);
+  r.hist = p;
+  r.st = p + kBins;
+  r.cand = r.st + kS_WORDS;
+  r.seg = r.cand + 2 * (size_t)r.cap;
+  r.thist = r.seg + 2 * (size_t)n_chunks(n);
   return r;
 }
 
@@ -53,7 +85,65 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Add 1 per active lane to hist[bin] in LDS.  Lanes that share a bin
+// serialise in the LDS unit, which is cheaper than combining them first.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  if (active) atomicAdd(&hist[bin], 1u);
+}
+
+// The keys of one chunk held in registers: wave w of the workgroup owns keys
+// [w * 2048, w * 2048 + 2048) of the chunk; lane l holds, for i = 0..7, the 4
+// keys at wave offset (i * 64 + l) * 4.
+struct ChunkKeys {
+  uint32_t k[kPerThread / 4][4];
+};
+
+__device__ __forceinline__ int64_t key_index(int64_t c0, int i, int c) {
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  return c0 + (int64_t)wave * kWaveKeys + (int64_t)(i * 64 + lane) * 4 + c;
+}
+
+// FULL: the chunk lies inside the row and the row start is 16-byte aligned,
+// so every key is valid and the loads are 16-byte vectors.
+template <bool FULL>
+__device__ __forceinline__ bool valid(int64_t c0, int i, int c, int64_t n) {
+  return FULL || key_index(c0, i, c) < n;
+}
+
+__device__ __forceinline__ bool chunk_full(const float* src, int64_t n, int64_t c0) {
+  return (reinterpret_cast<uintptr_t>(src) & 15) == 0 && c0 + kChunk <= n;
+}
+
+template <bool FULL>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
+                                           ChunkKeys& K) {
+  if (FULL) {
+    float4 v[kPerThread / 4];
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i)
+      v[i] = *reinterpret_cast<const float4*>(src + key_index(c0, i, 0));
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i) {
+      K.k[i][0] = order_key(v[i].x);
+      K.k[i][1] = order_key(v[i].y);
+      K.k[i][2] = order_key(v[i].z);
+      K.k[i][3] = order_key(v[i].w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i) {
+      const int64_t e = key_index(c0, i, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) K.k[i][c] = (e + c < n) ? order_key(src[e + c]) : 0u;
+    }
+  }
+}
+
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   const int lane = lane_id();
 #pragma unroll
@@ -64,7 +154,15 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
   return v;
 }
 
-// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
+  return v;
+}
+
+// Exclusive prefix over the NT threads of a workgroup; the total through
+// `total`.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_tmp,
                                                         uint32_t& total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -73,7 +171,7 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t x = s_tmp[w];
     before += (w < wave) ? x : 0u;
     tot += x;
@@ -83,161 +181,377 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n, int k) {
-  RowWs r = row_ws(ws, n, blockIdx.x);
-  for (int i = threadIdx.x; i < kBins; i += kThreads) r.hist[i] = 0u;
-  if (threadIdx.x == 0) {
-    r.state[0] = 0u;
-    r.state[1] = (uint32_t)k;
-  }
-}
-
-// Histogram of digit (key >> SHIFT) & (2^BITS - 1) over the keys whose higher
-// digits equal the prefix fixed so far.
-template <int SHIFT, int BITS>
-__global__ __launch_bounds__(kThreads) void topk_hist(const float* __restrict__ scores,
-                                                      int64_t n, void* ws) {
-  __shared__ uint32_t s_hist[1 << BITS];
-  const int64_t row = blockIdx.y;
-  RowWs r = row_ws(ws, n, row);
-  for (int i = threadIdx.x; i < (1 << BITS); i += kThreads) s_hist[i] = 0u;
-  const uint32_t prefix = r.state[0];
-  __syncthreads();
-  const float* src = scores + row * n;
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  const int64_t c1 = min<int64_t>(n, c0 + kChunk);
-  constexpr int kHigh = SHIFT + BITS;
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += kThreads) {
-    const uint32_t key = order_key(src[i]);
-    const bool match = (kHigh >= 32) ? true : ((key >> (kHigh & 31)) == (prefix >> (kHigh & 31)));
-    if (match) atomicAdd(&s_hist[(key >> SHIFT) & ((1u << BITS) - 1u)], 1u);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < (1 << BITS); i += kThreads) {
-    const uint32_t c = s_hist[i];
-    if (c != 0u) atomicAdd(&r.hist[i], c);
-  }
-}
-
-// Pick the bin that holds the need-th largest remaining key; clear the
-// histogram for the next digit.
-template <int SHIFT, int BITS>
-__global__ __launch_bounds__(kThreads) void topk_select(int64_t n, void* ws) {
-  __shared__ uint32_t s_tmp[kThreads / 64];
-  constexpr int kPer = (1 << BITS) / kThreads;
-  RowWs r = row_ws(ws, n, blockIdx.x);
-  const uint32_t need = r.state[1];
-  uint32_t h[kPer];
+// Find, over `nb` bins held kPer per thread (highest bin last), the bin that
+// holds the need-th largest key; thread-local h[] are the thread's bins.
+// Writes (bin, need within the bin) to sel[] from the one thread that owns it.
+template <int NT, int kPer>
+__device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t need, uint32_t* s_tmp,
+                                         uint32_t* sel) {
   uint32_t mine = 0;
 #pragma unroll
-  for (int b = 0; b < kPer; ++b) {
-    h[b] = r.hist[threadIdx.x * kPer + b];
-    mine += h[b];
-  }
+  for (int b = 0; b < kPer; ++b) mine += h[b];
   uint32_t total;
-  const uint32_t before = block_exclusive_sum(mine, s_tmp, total);
-  const uint32_t above = total - before - mine;  // keys in higher bins
+  const uint32_t before = block_exclusive_sum<NT>(mine, s_tmp, total);
+  const uint32_t above = total - before - mine;   // keys in higher bins
   if (above < need && need <= above + mine) {
     uint32_t acc = above;
 #pragma unroll
     for (int b = kPer - 1; b >= 0; --b) {
       if (acc + h[b] >= need) {
-        r.state[0] |= (uint32_t)(threadIdx.x * kPer + b) << SHIFT;
-        r.state[1] = need - acc;
+        sel[0] = (uint32_t)(threadIdx.x * kPer + b);
+        sel[1] = need - acc;
         break;
       }
       acc += h[b];
     }
   }
-#pragma unroll
-  for (int b = 0; b < kPer; ++b) r.hist[threadIdx.x * kPer + b] = 0u;
 }
 
-// Per chunk: number of keys > T and == T.
-__global__ __launch_bounds__(kThreads) void topk_count(const float* __restrict__ scores,
-                                                       int64_t n, void* ws) {
-  __shared__ uint32_t s_tmp[kThreads / 64];
-  const int64_t row = blockIdx.y;
-  RowWs r = row_ws(ws, n, row);
-  const uint32_t T = r.state[0];
-  const float* src = scores + row * n;
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  const int64_t c1 = min<int64_t>(n, c0 + kChunk);
-  uint32_t gt = 0, eq = 0;
-  for (int64_t i = c0 + threadIdx.x; i < c1; i += kThreads) {
-    const uint32_t key = order_key(src[i]);
-    gt += key > T;
-    eq += key == T;
-  }
-  uint32_t tgt, teq;
-  block_exclusive_sum(gt, s_tmp, tgt);
-  block_exclusive_sum(eq, s_tmp, teq);
-  if (threadIdx.x == 0) {
-    r.cnt[blockIdx.x * 2 + 0] = tgt;
-    r.cnt[blockIdx.x * 2 + 1] = teq;
-  }
-}
+// ---------------------------------------------------------------------------
 
-// Per row: output base of every chunk and its quota of keys equal to T (the
-// earliest chunks take the ties first).
-__global__ __launch_bounds__(kThreads) void topk_offsets(int64_t n, void* ws) {
-  __shared__ uint32_t s_tmp[kThreads / 64];
+__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n) {
   RowWs r = row_ws(ws, n, blockIdx.x);
-  const uint32_t need = r.state[1];
-  const int64_t nc = n_chunks(n);
-  const int64_t per = (nc + kThreads - 1) / kThreads;
-  const int64_t a = min<int64_t>(nc, threadIdx.x * per), b = min<int64_t>(nc, a + per);
-  uint32_t gt = 0, eq = 0;
-  for (int64_t c = a; c < b; ++c) {
-    gt += r.cnt[c * 2 + 0];
-    eq += r.cnt[c * 2 + 1];
+  for (int i = threadIdx.x; i < kBins; i += kThreads) r.hist[i] = 0u;
+  if (threadIdx.x < kS_WORDS) r.st[threadIdx.x] = 0u;
+}
+
+// Histogram of the top 11 key bits of one sampled chunk (chunk
+// blockIdx.x * kSampleStride).
+template <bool F>
+__device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
+                                             uint32_t* s_hist) {
+  ChunkKeys K;
+  load_chunk<F>(src, n, c0, K);
+#pragma unroll
+  for (int i = 0; i < kPerThread / 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) hist_add(s_hist, K.k[i][c] >> 21, valid<F>(c0, i, c, n));
+}
+
+__global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict__ scores,
+                                                        int64_t n, void* ws) {
+  __shared__ uint32_t s_hist[kBins];
+  const int64_t row = blockIdx.y;
+  RowWs r = row_ws(ws, n, row);
+  for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0u;
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.x * kSampleStride * kChunk;
+  const float* src = scores + row * n;
+  if (chunk_full(src, n, c0)) sample_chunk<true>(src, n, c0, s_hist);
+  else sample_chunk<false>(src, n, c0, s_hist);
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kThreads) {
+    const uint32_t t = s_hist[b];
+    if (t != 0u) atomicAdd(&r.hist[b], t);
   }
-  uint32_t tot;
-  uint32_t cum_gt = block_exclusive_sum(gt, s_tmp, tot);
-  uint32_t cum_eq = block_exclusive_sum(eq, s_tmp, tot);
-  for (int64_t c = a; c < b; ++c) {
-    const uint32_t g = r.cnt[c * 2 + 0], e = r.cnt[c * 2 + 1];
-    const uint32_t taken_before = min(cum_eq, need);
-    const uint32_t quota = min(e, need - taken_before);
-    r.off[c * 2 + 0] = cum_gt + taken_before;
-    r.off[c * 2 + 1] = quota;
-    cum_gt += g;
-    cum_eq += e;
+  if (threadIdx.x == 0)
+    atomicAdd(&r.st[kS_NSAMPLE], (uint32_t)min<int64_t>(kChunk, n - c0));
+}
+
+// Per row: the cut tau.  With the whole row sampled the target is exactly k
+// (tau is the low edge of the bin holding the k-th largest key); otherwise
+// the sample's share of k is raised by a quarter plus 64 keys.
+__global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int k, void* ws) {
+  __shared__ uint32_t s_tmp[kWavesPerWg];
+  __shared__ uint32_t s_sel[2];
+  constexpr int kPer = kBins / kThreads;
+  RowWs r = row_ws(ws, n, blockIdx.x);
+  const uint32_t ns = r.st[kS_NSAMPLE];
+  uint32_t target = (uint32_t)k;
+  if ((int64_t)ns < n) {
+    const double share = (double)k * (double)ns / (double)n;
+    target = (uint32_t)min<double>((double)ns, share * 1.25 + 64.0);
+  }
+  uint32_t h[kPer];
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) h[b] = r.hist[threadIdx.x * kPer + b];
+  s_sel[0] = 0u;
+  __syncthreads();
+  pick_bin<kThreads, kPer>(h, target, s_tmp, s_sel);
+  __syncthreads();
+  if (threadIdx.x == 0) r.st[kS_TAU] = s_sel[0] << 21;
+}
+
+// Every key >= tau of one chunk appended to the candidate buffer as one
+// contiguous segment in index order (one atomic per workgroup reserves it;
+// same-address atomics serialise in L2), and the chunk's histogram of the
+// candidates' top digits, relative to tau's.
+template <bool F>
+__device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
+                                              const RowWs& r, uint32_t* s_cnt, uint32_t* s_th,
+                                              uint32_t& s_base) {
+  const uint32_t tau = r.st[kS_TAU];
+  const uint32_t dtau = tau >> 21;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  for (int i = threadIdx.x; i < kTopBins; i += kThreads) s_th[i] = 0u;
+  ChunkKeys K;
+  load_chunk<F>(src, n, c0, K);
+  uint32_t ncand = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread / 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ncand += (valid<F>(c0, i, c, n) && K.k[i][c] >= tau) ? 1u : 0u;
+  ncand = wave_sum(ncand);
+  if (lane == 0) s_cnt[wave] = ncand;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWg; ++w) t += s_cnt[w];
+    s_base = t ? atomicAdd(&r.st[kS_NCAND], t) : 0u;
+    r.seg[2 * blockIdx.x] = s_base;
+    r.seg[2 * blockIdx.x + 1] = t;
+  }
+  __syncthreads();
+  if (ncand != 0u) {
+    // Slots follow index order: the keys of step i are (lane, c) with index
+    // ascending in lane, then c.
+    uint32_t slot = s_base;
+    for (int w = 0; w < wave; ++w) slot += s_cnt[w];
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int i = 0; i < kPerThread / 4; ++i) {
+      bool cand[4];
+      uint64_t m[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        cand[c] = valid<F>(c0, i, c, n) && K.k[i][c] >= tau;
+        m[c] = __ballot(cand[c]);
+      }
+      if ((m[0] | m[1] | m[2] | m[3]) == 0ull) continue;
+      uint32_t sl = slot;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sl += (uint32_t)__popcll(m[c] & below);
+        slot += (uint32_t)__popcll(m[c]);
+        hist_add(s_th, min((K.k[i][c] >> 21) - dtau, (uint32_t)kTopBins - 1u), cand[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (cand[c]) {
+          if (sl < r.cap)
+            reinterpret_cast<uint2*>(r.cand)[sl] =
+                make_uint2(K.k[i][c], (uint32_t)key_index(c0, i, c));
+          ++sl;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTopBins; i += kThreads)
+    r.thist[(size_t)blockIdx.x * kTopBins + i] = s_th[i];
+}
+
+__global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict__ scores,
+                                                         int64_t n, void* ws) {
+  __shared__ uint32_t s_cnt[kWavesPerWg];
+  __shared__ uint32_t s_th[kTopBins];
+  __shared__ uint32_t s_base;
+  const int64_t row = blockIdx.y;
+  const RowWs r = row_ws(ws, n, row);
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  const float* src = scores + row * n;
+  if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, r, s_cnt, s_th, s_base);
+  else compact_chunk<false>(src, n, c0, r, s_cnt, s_th, s_base);
+}
+
+// The keys a resolve workgroup selects among: the candidate buffer, or
+// (direct mode) the row itself.
+struct ResolveSrc {
+  const uint2* cand;      // (key, index) pairs
+  const uint32_t* seg;
+  const float* scores;
+  int64_t n, nc;
+  uint32_t ncand;
+  bool direct;
+};
+
+// f(key, index) for every key, spread over the workgroup, in any order;
+// four loads in flight per thread.
+template <class F>
+__device__ __forceinline__ void for_each_key(const ResolveSrc& s, F&& f) {
+  constexpr int kU = 4;
+  if (!s.direct) {
+    for (uint32_t i0 = threadIdx.x; i0 < s.ncand; i0 += kU * kResolveThreads) {
+      uint2 e[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = i0 + u * kResolveThreads;
+        e[u] = i < s.ncand ? s.cand[i] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (i0 + u * kResolveThreads < s.ncand) f(e[u].x, e[u].y);
+    }
+  } else {
+    for (int64_t i0 = threadIdx.x; i0 < s.n; i0 += kU * kResolveThreads) {
+      float v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kResolveThreads;
+        v[u] = i < s.n ? s.scores[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t i = i0 + u * kResolveThreads;
+        if (i < s.n) f(order_key(v[u]), (uint32_t)i);
+      }
+    }
   }
 }
 
-// Ordered write: tiles of kThreads consecutive keys, one per thread.  A
-// packed (gt, eq) prefix sum ranks the selected keys of the tile.
-__global__ __launch_bounds__(kThreads) void topk_write(const float* __restrict__ scores,
-                                                       int64_t n, int k, void* ws,
-                                                       int32_t* __restrict__ out) {
-  __shared__ uint32_t s_tmp[kThreads / 64];
-  const int64_t row = blockIdx.y;
+// One wave visits the keys of chunks [cb, ce) in index order, 64 at a time:
+// g(key, index, valid) with every lane of the wave taking part.
+template <class G>
+__device__ __forceinline__ void walk_chunks(const ResolveSrc& s, int64_t cb, int64_t ce, G&& g) {
+  const int lane = lane_id();
+  for (int64_t c = cb; c < ce; ++c) {
+    if (!s.direct) {
+      const uint32_t s0 = s.seg[2 * c], cnt = s.seg[2 * c + 1];
+      for (uint32_t o = 0; o < cnt; o += 64) {
+        const bool v = o + lane < cnt;
+        const uint2 e = v ? s.cand[s0 + o + lane] : make_uint2(0u, 0u);
+        g(e.x, e.y, v);
+      }
+    } else {
+      const int64_t e = min<int64_t>(s.n, (c + 1) * kChunk);
+      for (int64_t i0 = c * kChunk; i0 < e; i0 += 64) {
+        const int64_t i = i0 + lane;
+        const bool v = i < e;
+        g(v ? order_key(s.scores[i]) : 0u, (uint32_t)i, v);
+      }
+    }
+  }
+}
+
+constexpr int kGroups = 4096;   // chunk groups of the ordered write
+
+// Per row: T (the k-th largest key), the keys == T still needed, and the
+// ordered output.
+__global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
+                                                                int64_t n, int k, void* ws,
+                                                                int32_t* __restrict__ out) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
+  __shared__ uint32_t s_tmp[kResolveThreads / 64];
+  __shared__ uint32_t s_sel[2];
+  const int64_t row = blockIdx.x;
   RowWs r = row_ws(ws, n, row);
-  const uint32_t T = r.state[0];
-  uint32_t base = r.off[blockIdx.x * 2 + 0];
-  uint32_t quota = r.off[blockIdx.x * 2 + 1];
-  const float* src = scores + row * n;
+  ResolveSrc src;
+  src.cand = reinterpret_cast<const uint2*>(r.cand);
+  src.seg = r.seg;
+  src.scores = scores + row * n;
+  src.n = n;
+  src.nc = n_chunks(n);
+  const uint32_t ncand_all = r.st[kS_NCAND];
+  src.ncand = min(ncand_all, r.cap);
+  src.direct = ncand_all < (uint32_t)k || ncand_all > r.cap;   // the guess failed
+  const uint32_t dtau = r.st[kS_TAU] >> 21;
   int32_t* dst = out + row * (int64_t)k;
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  const int64_t c1 = min<int64_t>(n, c0 + kChunk);
-  for (int64_t t0 = c0; t0 < c1; t0 += kThreads) {
-    const int64_t i = t0 + threadIdx.x;
-    uint32_t key = 0u;
-    if (i < c1) key = order_key(src[i]);
-    const bool is_gt = (i < c1) && key > T;
-    const bool is_eq = (i < c1) && key == T;
-    const uint32_t packed = ((uint32_t)is_gt << 16) | (uint32_t)is_eq;
+
+  // Top digit (bits 31..21).  Candidate mode: from the chunk histograms,
+  // unless the k-th key lies beyond their range.
+  uint32_t need = (uint32_t)k;
+  uint32_t prefix = 0;
+  bool top_done = false;
+  if (!src.direct) {
+    for (int i = threadIdx.x; i < kTopBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < src.nc * kTopBins; i += kResolveThreads) {
+      const uint32_t v = r.thist[i];
+      if (v != 0u) atomicAdd(&s_hist[i % kTopBins], v);
+    }
+    __syncthreads();
+    uint32_t h[1] = {threadIdx.x < (uint32_t)kTopBins - 1 ? s_hist[threadIdx.x] : 0u};
+    const uint32_t beyond = s_hist[kTopBins - 1];
+    __syncthreads();
+    if (beyond < need) {   // the k-th key's digit is among the first 63
+      s_sel[0] = 0u;
+      __syncthreads();
+      pick_bin<kResolveThreads, 1>(h, need - beyond, s_tmp, s_sel);
+      __syncthreads();
+      prefix = (dtau + s_sel[0]) << 21;
+      need = s_sel[1];
+      top_done = true;
+      __syncthreads();
+    }
+  }
+  for (int level = top_done ? 1 : 0; level < 3; ++level) {
+    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+    const int bits = level == 2 ? 10 : 11;
+    const int hi = shift + bits;   // bits at and above hi are fixed
+    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for_each_key(src, [&](uint32_t key, uint32_t) {
+      const bool in = hi >= 32 || (key >> (hi & 31)) == (prefix >> (hi & 31));
+      hist_add(s_hist, (key >> shift) & ((1u << bits) - 1u), in);
+    });
+    __syncthreads();
+    constexpr int kPer = kBins / kResolveThreads;   // 2
+    uint32_t h[kPer];
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+      const int bin = threadIdx.x * kPer + b;
+      h[b] = bin < (1 << bits) ? s_hist[bin] : 0u;
+    }
+    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    need = s_sel[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;   // take every key > T and the first `need` keys == T
+
+  // The row's chunks in at most kGroups groups of consecutive chunks.  Count
+  // the keys > T and == T of every group, prefix the counts over the groups,
+  // then let one wave per group write its selected indices in index order.
+  const int64_t nc = src.nc;
+  const int64_t per_group = (nc + kGroups - 1) / kGroups;
+  const int ngroups = (int)((nc + per_group - 1) / per_group);
+  for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
+  __syncthreads();
+  for_each_key(src, [&](uint32_t key, uint32_t idx) {
+    const int g = (int)((int64_t)(idx / kChunk) / per_group);
+    if (key > T) atomicAdd(&s_gt[g], 1u);
+    else if (key == T) atomicAdd(&s_eq[g], 1u);
+  });
+  __syncthreads();
+  {
+    const int gpt = (ngroups + kResolveThreads - 1) / kResolveThreads;   // groups per thread
+    const int g0 = min(ngroups, (int)threadIdx.x * gpt), g1 = min(ngroups, g0 + gpt);
+    uint32_t gt = 0, eq = 0;
+    for (int g = g0; g < g1; ++g) {
+      gt += s_gt[g];
+      eq += s_eq[g];
+    }
     uint32_t tot;
-    const uint32_t pre = block_exclusive_sum(packed, s_tmp, tot);
-    const uint32_t gt_before = pre >> 16, eq_before = pre & 0xffffu;
-    const uint32_t eq_sel_before = min(eq_before, quota);
-    const bool take = is_gt || (is_eq && eq_before < quota);
-    const uint32_t pos = base + gt_before + eq_sel_before;
-    if (take && pos < (uint32_t)k) dst[pos] = (int32_t)i;  // pos < k by construction
-    const uint32_t tot_gt = tot >> 16, tot_eq = tot & 0xffffu;
-    base += tot_gt + min(tot_eq, quota);
-    quota -= min(tot_eq, quota);
+    uint32_t gt_run = block_exclusive_sum<kResolveThreads>(gt, s_tmp, tot);
+    uint32_t eq_run = block_exclusive_sum<kResolveThreads>(eq, s_tmp, tot);
+    for (int g = g0; g < g1; ++g) {
+      const uint32_t a = s_gt[g], b = s_eq[g];
+      s_gt[g] = gt_run;
+      s_eq[g] = eq_run;
+      gt_run += a;
+      eq_run += b;
+    }
+  }
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  const uint64_t below = lanes_below();
+  for (int g = wave; g < ngroups; g += kResolveThreads / 64) {
+    uint32_t eq_seen = s_eq[g];
+    uint32_t pos = s_gt[g] + min(eq_seen, need);
+    walk_chunks(src, (int64_t)g * per_group, min<int64_t>(nc, (int64_t)(g + 1) * per_group),
+                [&](uint32_t key, uint32_t idx, bool v) {
+                  const bool gt = v && key > T, eq = v && key == T;
+                  const uint64_t eqm = __ballot(eq);
+                  const bool take = gt || (eq && eq_seen + (uint32_t)__popcll(eqm & below) < need);
+                  const uint64_t tm = __ballot(take);
+                  const uint32_t p = pos + (uint32_t)__popcll(tm & below);
+                  if (take && p < (uint32_t)k) dst[p] = (int32_t)idx;   // p < k by construction
+                  pos += (uint32_t)__popcll(tm);
+                  eq_seen += (uint32_t)__popcll(eqm);
+                });
   }
 }
 
@@ -245,24 +559,21 @@ __global__ __launch_bounds__(kThreads) void topk_write(const float* __restrict__
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
   (void)k;
-  const size_t bytes = (size_t)rows * row_ws_words(n) * sizeof(uint32_t);
+  const size_t bytes = (size_t)rows * row_words(n) * sizeof(uint32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* ws, hipStream_t stream) {
-  const unsigned nc = (unsigned)n_chunks(n);
-  const dim3 grid_rows((unsigned)rows), grid_chunks(nc, (unsigned)rows), blk(kThreads);
-  hipLaunchKernelGGL(topk_init, grid_rows, blk, 0, stream, ws, n, k);
-  hipLaunchKernelGGL((topk_hist<21, 11>), grid_chunks, blk, 0, stream, scores, n, ws);
-  hipLaunchKernelGGL((topk_select<21, 11>), grid_rows, blk, 0, stream, n, ws);
-  hipLaunchKernelGGL((topk_hist<10, 11>), grid_chunks, blk, 0, stream, scores, n, ws);
-  hipLaunchKernelGGL((topk_select<10, 11>), grid_rows, blk, 0, stream, n, ws);
-  hipLaunchKernelGGL((topk_hist<0, 10>), grid_chunks, blk, 0, stream, scores, n, ws);
-  hipLaunchKernelGGL((topk_select<0, 10>), grid_rows, blk, 0, stream, n, ws);
-  hipLaunchKernelGGL(topk_count, grid_chunks, blk, 0, stream, scores, n, ws);
-  hipLaunchKernelGGL(topk_offsets, grid_rows, blk, 0, stream, n, ws);
-  hipLaunchKernelGGL(topk_write, grid_chunks, blk, 0, stream, scores, n, k, ws, indices);
+  const int64_t nc = n_chunks(n);
+  const unsigned ns = (unsigned)((nc + kSampleStride - 1) / kSampleStride);
+  const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
+  hipLaunchKernelGGL(topk_init, grid_rows, dim3(kThreads), 0, stream, ws, n);
+  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n, ws);
+  hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, k, ws);
+  hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
+  hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, k, ws,
+                     indices);
   return hipGetLastError();
 }
 
