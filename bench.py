@@ -15,10 +15,22 @@ Prints one JSON line: keys scanned per second for the whole step (value),
 plus the scan kernel's roofline figures (algorithmic bytes and VALU work per
 launch, over its event-timed average duration) and the CPU oracle's rate on
 a bounded sample.
+
+HBM traffic of the scan comes from rocprofv3 counter runs of this same
+command (FETCH_SIZE, then WRITE_SIZE), each scaled by the factor that makes
+the counter agree with the known bytes of a plain copy (torch.neg over
+256 MiB, run here before the timed steps).  The figures are kept in
+profiles/scan_q1m_b92_traffic.txt together with the sha256 of the scan
+source they were taken on; a different source reports traffic null.
+`python bench.py --summarize DIR [DIR ...]` turns rocprofv3 csv output
+(kernel stats, counter collections) into the text kept under profiles/.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +45,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0                    # MI355X HBM3E
 CUS, LANES, CLOCK_GHZ = 256, 64, 2.4
 VALU_PEAK_TOPS = CUS * LANES * CLOCK_GHZ / 1e3   # 39.32 T lane-instructions/s
+CALIB_BYTES = 256 << 20                   # plain copy used to scale the HBM byte counters
+SCAN_SRC = os.path.join(ROOT, "sparse_top_kv_fathom_amd", "csrc", "scan.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_traffic.txt")
 
 
 def parse():
@@ -46,7 +61,57 @@ def parse():
     ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print rocprofv3 csv output under DIR as text and exit (no GPU use)")
     return ap.parse_args()
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic():
+    """Scan HBM bytes per launch from the committed counter summary, or None
+    when it is missing or was taken on another scan source."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    kv = dict(l.split(":", 1) for l in lines if ":" in l and not l.startswith(" "))
+    try:
+        if kv["scan_source_sha256"].strip() != source_sha(SCAN_SRC):
+            return None
+        return float(kv["scan_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def short_name(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return name.split("(")[0][:60]
+
+
+def summarize(dirs):
+    """rocprofv3 csv (kernel stats, counter collection) as plain text."""
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            print("## kernel stats: %s" % os.path.relpath(f, d))
+            print("%-60s %6s %12s %12s %7s" % ("kernel", "calls", "avg_us", "total_us", "pct"))
+            for r in csv.DictReader(open(f)):
+                print("%-60s %6s %12.2f %12.1f %7.2f" % (
+                    short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                    float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                                  recursive=True)):
+            print("## counters: %s" % os.path.relpath(f, d))
+            agg = {}
+            for r in csv.DictReader(open(f)):
+                key = (short_name(r["Kernel_Name"]), r["Counter_Name"])
+                agg.setdefault(key, []).append(float(r["Counter_Value"]))
+            print("%-60s %-14s %6s %14s" % ("kernel", "counter", "n", "mean"))
+            for (kname, cname), v in sorted(agg.items()):
+                print("%-60s %-14s %6d %14.1f" % (kname, cname, len(v), sum(v) / len(v)))
 
 
 def plan_stats(depths: np.ndarray):
@@ -57,6 +122,9 @@ def plan_stats(depths: np.ndarray):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -110,6 +178,13 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    # Plain copy of known size, for scaling HBM byte counters (untimed).
+    calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    for _ in range(3):
+        torch.neg(calib_src, out=calib_dst)
+    del calib_src, calib_dst
+
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
@@ -147,14 +222,17 @@ def main():
     t_hbm = bytes_per_launch / (HBM_PEAK_GBPS * 1e9)
     t_valu = ops_per_launch / (VALU_PEAK_TOPS * 1e12)
     bound = "alu" if t_valu >= t_hbm else "hbm"
+    traffic = recorded_traffic()
     if bound == "alu":
         roof = {"bound": "alu", "achieved": round(valu_tops, 3), "peak": round(VALU_PEAK_TOPS, 2),
-                "unit": "Tlane-op/s", "frac": round(valu_tops / VALU_PEAK_TOPS, 4), "traffic": None}
+                "unit": "Tlane-op/s", "frac": round(valu_tops / VALU_PEAK_TOPS, 4),
+                "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     roof.update({
-        "kernel": "scan_kernel",
+        "kernel": "scan_main",
+        "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
         "launch_ms": round(stage_ms[2], 4),
         "alg_bytes_per_launch": int(bytes_per_launch),
         "alg_lane_ops_per_launch": int(ops_per_launch),

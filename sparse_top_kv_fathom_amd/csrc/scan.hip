@@ -376,15 +376,19 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     if (t > 0) {
       const int di = kPlanes - t;
       int slot = 0, row = 0;
+      uint64_t mlo = 0, mhi = 0;   // selected without a dynamic index (no scratch)
 #pragma unroll
       for (int i = 0; i < kPlanes; ++i) {
         if (i < di) {
           slot += cnt[i];
           row += cnt[i] * (kPlanes - i);
         }
+        if (i == di) {
+          mlo = dm.lo[i];
+          mhi = dm.hi[i];
+        }
       }
-      const int rank = (j < 64) ? __popcll(dm.lo[di] & below)
-                                : __popcll(dm.lo[di]) + __popcll(dm.hi[di] & below);
+      const int rank = (j < 64) ? __popcll(mlo & below) : __popcll(mlo) + __popcll(mhi & below);
       slot += rank;
       row += rank * t;
       const float sw = __builtin_ldexpf(1.0f, 11 - t);
