@@ -10,7 +10,8 @@
 // fp16 bit patterns (positive fp16 patterns order like their values), two
 // channels per 32-bit lane word.  A workgroup of 4 waves encodes 4 consecutive
 // blocks; words and scales are staged in LDS and written as contiguous runs
-// per (channel, plane).
+// per (channel, plane).  Calls with few blocks use a column-split kernel
+// instead (below).
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -110,12 +111,57 @@ __global__ __launch_bounds__(256) void encode_kernel(
   }
 }
 
+// Few blocks (the decode-time append of one block): the channels of a block
+// are spread over 16 waves, one 16-byte column (8 channels) each, so the work
+// of a block is not one wave's serial loop.  Grid: (blocks, groups, 4); the
+// 4 waves of a workgroup take columns 4z .. 4z+3.  Words and scales are
+// written directly (8 and 2 bytes per channel).
+__global__ __launch_bounds__(256) void encode_cols_kernel(
+    const uint16_t* __restrict__ k, int64_t n, int64_t nb_store, int64_t block_offset,
+    uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag) {
+  const int lane = lane_id();
+  const int col = blockIdx.z * kWavesPerWg + (threadIdx.x >> 6);   // 0..15
+  const int64_t g = blockIdx.y;
+  const int64_t blk = blockIdx.x;
+  const uint4 v = *reinterpret_cast<const uint4*>(k + ((g * n) + blk * kBlock + lane) * kD + col * 8);
+  const uint32_t w32[4] = {v.x, v.y, v.z, v.w};
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint32_t amax2 = wave_max_u16x2(w32[u] & 0x7fff7fffu);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int64_t j = col * 8 + u * 2 + half;
+      const uint32_t kb = (w32[u] >> (16 * half)) & 0xffffu;
+      const uint32_t ab = (amax2 >> (16 * half)) & 0xffffu;
+      bad |= ab >= 0x7c00u;
+      const uint32_t code = code_of(kb, ab);
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p) {
+        const uint64_t word = __ballot((code >> (3 - p)) & 1u);
+        if (lane == p) planes[((g * kD + j) * kPlanes + p) * nb_store + block_offset + blk] = word;
+      }
+      if (lane == 4) scales[(g * kD + j) * nb_store + block_offset + blk] = (uint16_t)ab;
+    }
+  }
+  if (flag != nullptr && bad && lane == 0) atomicOr(flag, 1u);
+}
+
 }  // namespace
+
+// Below this many blocks per group the column-split kernel is used.
+constexpr int64_t kColsKernelMaxBlocks = 64;
 
 hipError_t launch_encode(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
                          int64_t block_offset, uint64_t* planes, uint16_t* scales,
                          uint32_t* nonfinite_flag, hipStream_t stream) {
   const int64_t nblk = n / kBlock;
+  if (nblk <= kColsKernelMaxBlocks) {
+    dim3 grid((unsigned)nblk, (unsigned)groups, kD / 8 / kWavesPerWg);
+    hipLaunchKernelGGL(encode_cols_kernel, grid, dim3(64 * kWavesPerWg), 0, stream, k, n,
+                       nb_store, block_offset, planes, scales, nonfinite_flag);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((nblk + kWavesPerWg - 1) / kWavesPerWg), (unsigned)groups);
   hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWavesPerWg), 0, stream, k, n, nblk,
                      nb_store, block_offset, planes, scales, nonfinite_flag);

@@ -41,7 +41,9 @@ def _gpu_encode(fk, k, nb_store=None, block_offset=0, planes=None, scales=None):
     return to_host(pd), to_host(sd), int(flag.item())
 
 
-@pytest.mark.parametrize("groups,nblk", [(1, 64), (3, 37), (2, 1), (5, 6)])
+# Up to 64 blocks per call the column-split kernel runs, above it the
+# block-per-wave kernel: both are covered.
+@pytest.mark.parametrize("groups,nblk", [(1, 64), (3, 37), (2, 1), (5, 6), (2, 65), (1, 203)])
 def test_encode_matches_oracle(fk, groups, nblk):
     n = 64 * nblk
     say("encode groups=%d n=%d" % (groups, n))
@@ -65,9 +67,11 @@ def test_encode_appends_into_store(fk):
     assert np.array_equal(gs, os_), first_mismatch(gs, os_)
 
 
-def test_encode_edge_values(fk):
-    """Zero blocks, +-a, -0, fp16 max, subnormal block maxima, exact cell edges."""
-    say("encode edge values")
+@pytest.mark.parametrize("reps", [1, 9])
+def test_encode_edge_values(fk, reps):
+    """Zero blocks, +-a, -0, fp16 max, subnormal block maxima, exact cell edges
+    (8 blocks: column-split kernel; repeated 9 times: block-per-wave kernel)."""
+    say("encode edge values x%d" % reps)
     rng = np.random.default_rng(8)
     k = np.zeros((1, 64 * 8, 128), dtype=np.float16)
     k[0, 64:128] = rng.standard_normal((64, 128)).astype(np.float16)
@@ -81,6 +85,7 @@ def test_encode_edge_values(fk):
     k[0, 320:384] = np.nextafter(blk, np.float16(np.inf))
     k[0, 384:448] = -blk
     k[0, 448:512] = rng.standard_normal((64, 128)).astype(np.float16) * np.float16(1e-3)
+    k = np.ascontiguousarray(np.tile(k, (1, reps, 1)))
     gp, gs, flag = _gpu_encode(fk, k)
     op, os_, bad = oracle.encode(k)
     assert flag == 0 and bad == 0
@@ -88,9 +93,10 @@ def test_encode_edge_values(fk):
     assert np.array_equal(gs, os_), first_mismatch(gs, os_)
 
 
-def test_encode_nonfinite_flag(fk):
-    say("encode non-finite flag")
-    k, _ = fathom_inputs.make_keys(2, 64 * 4, seed=9)
+@pytest.mark.parametrize("nblk", [4, 80])
+def test_encode_nonfinite_flag(fk, nblk):
+    say("encode non-finite flag nblk=%d" % nblk)
+    k, _ = fathom_inputs.make_keys(2, 64 * nblk, seed=9)
     _, _, flag = _gpu_encode(fk, k)
     assert flag == 0
     k[1, 130, 17] = np.float16(np.inf)
