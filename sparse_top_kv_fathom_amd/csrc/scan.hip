@@ -33,14 +33,19 @@
 // active channel once per workgroup, the scales of every active channel once
 // per round of kRoundBlocks blocks (staged with vector loads).
 //
-// Latency.  While round r is computed, the workgroup touches every plane line
-// of round r + 1 with vector loads (so the scalar loads of round r + 1 find
-// them in L2) and loads its scales.  Channels of one depth form a loop with a
-// compile-time plane count.  Scalar loads return out of order, so the only
-// usable wait is "all outstanding"; for depths 1 and 2 two register sets
-// alternate and each channel waits once, at its first instruction, before it
-// issues the next channel's loads, which then overlap its arithmetic.
-// Depths 3 and 4 (64-128 plane registers) load and compute one at a time.
+// Latency.  A workgroup first touches every plane line of its round with
+// vector loads (one 4-byte load per 128-byte line pulls the line into L2) and
+// loads the round's scales, waits for all of them, and only then computes, so
+// its scalar loads hit L2; the other workgroups resident on the CU compute
+// during that wait.  (Touching a round ahead while computing the current one
+// keeps twice the lines in flight and they are evicted from the 4 MB L2 of an
+// XCD before use; one round per workgroup measured fastest.)  Channels of one
+// depth form a loop with a compile-time plane count.  Scalar loads return out
+// of order, so the only usable wait is "all outstanding"; for depths 1 and 2
+// two register sets alternate and each channel waits once, at its first
+// instruction, before it issues the next channel's loads, which then overlap
+// its arithmetic.  Depths 3 and 4 (64-128 plane registers) load and compute
+// one at a time.
 //
 // Grid.  Main kernel: whole rounds only; workgroup ids are remapped so that
 // consecutive rounds of a group run on the same XCD (workgroups are dealt to
@@ -49,6 +54,13 @@
 // whose offsets exceed 32 bits or whose scale rows are not 16-byte aligned.
 #include "fathom_internal.h"
 
+// Compile-time tuning: SCAN_U1 = depth-1 channels per pipelined set,
+// SCAN_ROUNDS = rounds per workgroup, SCAN_TOUCHES = L2 touches per 256-byte
+// plane-row segment of a round.
+#ifndef SCAN_U1
+#define SCAN_U1 1
+#endif
+
 namespace fathom {
 namespace {
 
@@ -56,7 +68,10 @@ constexpr int kWaves = 4;                    // waves per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kNB = 8;                       // blocks per wave tile (512 tokens)
 constexpr int kRoundBlocks = kWaves * kNB;   // blocks per workgroup round
-constexpr int kRounds = 2;                   // rounds per workgroup (main kernel)
+#ifndef SCAN_ROUNDS
+#define SCAN_ROUNDS 1
+#endif
+constexpr int kRounds = SCAN_ROUNDS;         // rounds per workgroup (main kernel)
 constexpr int kXcds = 8;
 constexpr int kSlots = kD + 4;               // active slots + padding read by the pipeline
 // Byte offsets inside one group's plane array are 32-bit in the main kernel.
@@ -208,14 +223,15 @@ struct MainCtx {
 };
 
 template <int T, int G>
-__device__ __forceinline__ void main_load(const MainCtx& c, const SlotTables<G>& tb, int slot,
-                                          int j, ChanLoad<T, G>& L) {
-  const char* rp = c.planes + (uint32_t)j * (kPlanes * c.pstride);
+__device__ __forceinline__ void main_load_plane(const MainCtx& c, int j, int p, ChanLoad<T, G>& L) {
+  const char* rp = c.planes + (uint32_t)j * (kPlanes * c.pstride) + p * c.pstride;
 #pragma unroll
-  for (int p = 0; p < T; ++p)
-#pragma unroll
-    for (int b = 0; b < kNB; ++b)
-      L.pw[p][b] = *reinterpret_cast<const uint64_t*>(rp + p * c.pstride + b * 8);
+  for (int b = 0; b < kNB; ++b) L.pw[p][b] = *reinterpret_cast<const uint64_t*>(rp + b * 8);
+}
+
+template <int T, int G>
+__device__ __forceinline__ void main_load_lds(const MainCtx& c, const SlotTables<G>& tb, int slot,
+                                              ChanLoad<T, G>& L) {
   const uint16_t* sp = c.sc + slot * kRoundBlocks;
 #pragma unroll
   for (int i = 0; i < kNB / 2; ++i) L.a2[i] = reinterpret_cast<const uint32_t*>(sp)[i];
@@ -223,6 +239,14 @@ __device__ __forceinline__ void main_load(const MainCtx& c, const SlotTables<G>&
   for (int h = 0; h < G; ++h) L.w[h] = tb.w[slot][h];
   L.e = tb.e[slot][c.oh];
   L.oa = sp[c.ob];
+}
+
+template <int T, int G>
+__device__ __forceinline__ void main_load(const MainCtx& c, const SlotTables<G>& tb, int slot,
+                                          int j, ChanLoad<T, G>& L) {
+#pragma unroll
+  for (int p = 0; p < T; ++p) main_load_plane<T, G>(c, j, p, L);
+  main_load_lds<T, G>(c, tb, slot, L);
 }
 
 // The channels of depth T (mask `it`, slots [first, first + cnt)), U at a
@@ -281,9 +305,6 @@ __device__ __forceinline__ void main_depth(const MainCtx& c, const SlotTables<G>
 // plane lines into L2 ahead of the scalar loads.  Thread 4s + k loads scales
 // [8k, 8k + 8) of slot s (16 aligned bytes: the capacity is a multiple of 8
 // blocks).
-#ifndef SCAN_U1
-#define SCAN_U1 1
-#endif
 #ifndef SCAN_TOUCHES
 #define SCAN_TOUCHES 2
 #endif
