@@ -83,6 +83,14 @@ __device__ __forceinline__ uint32_t shift_in_plane(uint32_t x, uint64_t mask) {
   asm("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(x), "s"(mask) : "vcc");
   return r;
 }
+// The same as a volatile statement: it stays in program order with the other
+// volatile statements (the first instruction of a channel, which carries the
+// wait for that channel's loads).
+__device__ __forceinline__ uint32_t shift_in_plane_ordered(uint32_t x, uint64_t mask) {
+  uint32_t r;
+  asm volatile("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(x), "s"(mask) : "vcc");
+  return r;
+}
 
 // Make a value opaque to the optimizer at this point, so that work derived
 // from it is redone here instead of being hoisted (and held in registers)
@@ -153,7 +161,11 @@ __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&ac
                                              float& o, F&& issue_next) {
   constexpr uint32_t x0 = 0x3C00u >> T;
   uint32_t x[kNB];
-  x[0] = shift_in_plane(x0, L.pw[0][0]);
+  // The first instruction waits for this channel's loads; it must not move
+  // above the previous channel's arithmetic, which hides their latency (the
+  // accumulators are pinned at the end of every channel below).
+  __builtin_amdgcn_sched_barrier(0);
+  x[0] = shift_in_plane_ordered(x0, L.pw[0][0]);
   __builtin_amdgcn_sched_barrier(0);
   issue_next();
   __builtin_amdgcn_sched_barrier(0);
@@ -172,6 +184,11 @@ __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&ac
     for (int h = 0; h < G; ++h) acc[b][h] = __builtin_fmaf(L.w[h], m, acc[b][h]);
   }
   o = __builtin_fmaf(L.e, half_lo(L.oa), o);
+#pragma unroll
+  for (int b = 0; b < kNB; ++b)
+#pragma unroll
+    for (int h = 0; h < G; ++h) asm volatile("" : "+v"(acc[b][h]));
+  asm volatile("" : "+v"(o));
 }
 
 // Epilogue: S = U + o (o of block b, head h sits in lane b * G + h); blocks
