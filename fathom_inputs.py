@@ -175,13 +175,17 @@ def workload_inputs(name: str) -> Inputs:
 
 def random_scores(rows: int, n: int, seed: int, kind: str = "normal") -> np.ndarray:
     """Score rows for top-k tests: 'normal' (N(0,1) fp32), 'ties' (values on a
-    coarse grid so many keys tie), 'const' (all equal), 'signed_zero' (a mix of
-    +0 and -0 with a few larger values)."""
+    coarse grid so many keys tie), 'grid64' (N(0,1) rounded to multiples of
+    1/64: a few hundred ties per value near the top-k boundary of a 1M row),
+    'const' (all equal), 'signed_zero' (a mix of +0 and -0 with a few larger
+    values)."""
     rng = np.random.default_rng(seed)
     if kind == "normal":
         return rng.standard_normal((rows, n), dtype=np.float32)
     if kind == "ties":
         return (rng.integers(-8, 8, size=(rows, n)).astype(np.float32) * np.float32(0.25))
+    if kind == "grid64":
+        return (np.round(rng.standard_normal((rows, n)) * 64.0) / 64.0).astype(np.float32)
     if kind == "const":
         return np.full((rows, n), np.float32(1.5), dtype=np.float32)
     if kind == "signed_zero":

@@ -43,6 +43,9 @@ enum : int {
   kS_TAU = 0,       // candidate cut
   kS_NCAND,         // keys >= tau seen so far (may exceed the capacity)
   kS_NSAMPLE,       // keys in the sampled chunks
+  kS_T,             // the k-th largest key (set by the resolve)
+  kS_NEED,          // keys == T to take
+  kS_ORDER,         // 1: the ordered write is left to topk_order
   kS_WORDS = 16
 };
 
@@ -55,7 +58,7 @@ __host__ __device__ inline int64_t cand_cap(int64_t n) {
 }
 
 __host__ __device__ inline size_t row_words(int64_t n) {
-  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + (2 + kTopBins) * (size_t)n_chunks(n);
+  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + (4 + kTopBins) * (size_t)n_chunks(n);
 }
 
 struct RowWs {
@@ -64,6 +67,7 @@ struct RowWs {
   uint32_t* cand;    // [cap][2]: key, index
   uint32_t* seg;     // [nchunks][2]: first slot and number of the chunk's candidates
   uint32_t* thist;   // [nchunks][kTopBins]: the chunk's candidate top digits
+  uint32_t* ord;     // [nchunks][2]: keys > T and == T in the chunks before this one
   uint32_t cap;
 };
 
@@ -76,6 +80,7 @@ __device__ inline RowWs row_ws(void* ws, int64_t n, int64_t row) {
   r.cand = r.st + kS_WORDS;
   r.seg = r.cand + 2 * (size_t)r.cap;
   r.thist = r.seg + 2 * (size_t)n_chunks(n);
+  r.ord = r.thist + (size_t)kTopBins * n_chunks(n);
   return r;
 }
 
@@ -250,7 +255,8 @@ __global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict_
 
 // Per row: the cut tau.  With the whole row sampled the target is exactly k
 // (tau is the low edge of the bin holding the k-th largest key); otherwise
-// the sample's share of k is raised by a quarter plus 64 keys.
+// the sample's share of k is raised by a quarter plus 64 keys and tau is
+// placed inside that key's bin.
 __global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int k, void* ws) {
   __shared__ uint32_t s_tmp[kWavesPerWg];
   __shared__ uint32_t s_sel[2];
@@ -269,7 +275,19 @@ __global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int k, void* w
   __syncthreads();
   pick_bin<kThreads, kPer>(h, target, s_tmp, s_sel);
   __syncthreads();
-  if (threadIdx.x == 0) r.st[kS_TAU] = s_sel[0] << 21;
+  if (threadIdx.x == 0) {
+    const uint32_t bin = s_sel[0];
+    uint32_t tau = bin << 21;
+    if ((int64_t)ns < n) {
+      // Inside the bin, place the cut by the share of the bin's sample that
+      // is needed, doubled: densities fall towards the top of a tail bin, so
+      // the top fraction f of the keys spans more than f of the bin's range.
+      const double f = min(1.0, 2.0 * (double)s_sel[1] / (double)max(r.hist[bin], 1u));
+      const uint64_t top = ((uint64_t)bin + 1) << 21;
+      tau = (uint32_t)max<uint64_t>((uint64_t)bin << 21, top - (uint64_t)(f * (double)(1u << 21)));
+    }
+    r.st[kS_TAU] = tau;
+  }
 }
 
 // Every key >= tau of one chunk appended to the candidate buffer as one
@@ -369,7 +387,7 @@ struct ResolveSrc {
 // f(key, index) for every key, spread over the workgroup, in any order;
 // four loads in flight per thread.
 template <class F>
-__device__ __forceinline__ void for_each_key(const ResolveSrc& s, F&& f) {
+__device__ __forceinline__ void for_each_key(const ResolveSrc s, F&& f) {
   constexpr int kU = 4;
   if (!s.direct) {
     for (uint32_t i0 = threadIdx.x; i0 < s.ncand; i0 += kU * kResolveThreads) {
@@ -403,7 +421,7 @@ __device__ __forceinline__ void for_each_key(const ResolveSrc& s, F&& f) {
 // One wave visits the keys of chunks [cb, ce) in index order, 64 at a time:
 // g(key, index, valid) with every lane of the wave taking part.
 template <class G>
-__device__ __forceinline__ void walk_chunks(const ResolveSrc& s, int64_t cb, int64_t ce, G&& g) {
+__device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int64_t ce, G&& g) {
   const int lane = lane_id();
   for (int64_t c = cb; c < ce; ++c) {
     if (!s.direct) {
@@ -426,13 +444,37 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc& s, int64_t cb, int
 
 constexpr int kGroups = 4096;   // chunk groups of the ordered write
 
-// Per row: T (the k-th largest key), the keys == T still needed, and the
-// ordered output.
+// Exclusive prefix of cnt[0, m) in place, over the workgroup (m <= kGroups).
+__device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint32_t* s_tmp) {
+  const int per = (m + kResolveThreads - 1) / kResolveThreads;
+  const int g0 = min(m, (int)threadIdx.x * per), g1 = min(m, g0 + per);
+  uint32_t sum = 0;
+  for (int g = g0; g < g1; ++g) sum += cnt[g];
+  uint32_t tot;
+  uint32_t run = block_exclusive_sum<kResolveThreads>(sum, s_tmp, tot);
+  for (int g = g0; g < g1; ++g) {
+    const uint32_t v = cnt[g];
+    cnt[g] = run;
+    run += v;
+  }
+}
+
+// Candidates resolved from LDS: up to this many (key and chunk id) are
+// staged; rows with more take the global path.
+constexpr int kLdsCand = 16384;
+
+// Per row: T (the k-th largest key) and the keys == T still needed.  Rows
+// whose candidates fit in LDS (the usual case) stage them there, resolve T
+// from LDS, and leave per-chunk prefix counts for topk_order, which writes
+// the chunks in parallel.  Other rows (the guess failed, or too many
+// candidates or chunks) are resolved and written here, by one workgroup.
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
                                                                 int64_t n, int k, void* ws,
                                                                 int32_t* __restrict__ out) {
   __shared__ uint32_t s_hist[kBins];
   __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
+  __shared__ uint32_t s_key[kLdsCand];
+  __shared__ uint16_t s_cid[kLdsCand];
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
   const int64_t row = blockIdx.x;
@@ -446,8 +488,36 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   const uint32_t ncand_all = r.st[kS_NCAND];
   src.ncand = min(ncand_all, r.cap);
   src.direct = ncand_all < (uint32_t)k || ncand_all > r.cap;   // the guess failed
+  const bool lds = !src.direct && src.nc <= kGroups && src.ncand <= (uint32_t)kLdsCand;
   const uint32_t dtau = r.st[kS_TAU] >> 21;
   int32_t* dst = out + row * (int64_t)k;
+
+  if (lds) {   // stage keys and chunk ids
+    for (uint32_t i0 = threadIdx.x; i0 < src.ncand; i0 += 4 * kResolveThreads) {
+      uint2 e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * kResolveThreads;
+        e[u] = i < src.ncand ? src.cand[i] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t i = i0 + u * kResolveThreads;
+        if (i < src.ncand) {
+          s_key[i] = e[u].x;
+          s_cid[i] = (uint16_t)(e[u].y / kChunk);
+        }
+      }
+    }
+  }
+  // f(key, index or chunk) over every key the row selects among.
+  auto keys = [&](auto&& f) {
+    if (lds) {
+      for (uint32_t i = threadIdx.x; i < src.ncand; i += kResolveThreads) f(s_key[i], (uint32_t)s_cid[i]);
+    } else {
+      for_each_key(src, f);
+    }
+  };
 
   // Top digit (bits 31..21).  Candidate mode: from the chunk histograms,
   // unless the k-th key lies beyond their range.
@@ -457,9 +527,17 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   if (!src.direct) {
     for (int i = threadIdx.x; i < kTopBins; i += kResolveThreads) s_hist[i] = 0u;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < src.nc * kTopBins; i += kResolveThreads) {
-      const uint32_t v = r.thist[i];
-      if (v != 0u) atomicAdd(&s_hist[i % kTopBins], v);
+    const int64_t nth = src.nc * kTopBins;
+    for (int64_t i0 = threadIdx.x; i0 < nth; i0 += 8 * kResolveThreads) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * kResolveThreads;
+        v[u] = i < nth ? r.thist[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)   // i % kTopBins is the same for every u
+        if (v[u] != 0u) atomicAdd(&s_hist[i0 % kTopBins], v[u]);
     }
     __syncthreads();
     uint32_t h[1] = {threadIdx.x < (uint32_t)kTopBins - 1 ? s_hist[threadIdx.x] : 0u};
@@ -482,7 +560,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     const int hi = shift + bits;   // bits at and above hi are fixed
     for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
     __syncthreads();
-    for_each_key(src, [&](uint32_t key, uint32_t) {
+    keys([&](uint32_t key, uint32_t) {
       const bool in = hi >= 32 || (key >> (hi & 31)) == (prefix >> (hi & 31));
       hist_add(s_hist, (key >> shift) & ((1u << bits) - 1u), in);
     });
@@ -502,40 +580,43 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
   const uint32_t T = prefix;   // take every key > T and the first `need` keys == T
 
-  // The row's chunks in at most kGroups groups of consecutive chunks.  Count
-  // the keys > T and == T of every group, prefix the counts over the groups,
-  // then let one wave per group write its selected indices in index order.
+  // The row's chunks in at most kGroups groups of consecutive chunks: the keys
+  // > T and == T of every group, prefixed over the groups.
   const int64_t nc = src.nc;
   const int64_t per_group = (nc + kGroups - 1) / kGroups;
   const int ngroups = (int)((nc + per_group - 1) / per_group);
   for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
   __syncthreads();
-  for_each_key(src, [&](uint32_t key, uint32_t idx) {
-    const int g = (int)((int64_t)(idx / kChunk) / per_group);
-    if (key > T) atomicAdd(&s_gt[g], 1u);
-    else if (key == T) atomicAdd(&s_eq[g], 1u);
-  });
-  __syncthreads();
-  {
-    const int gpt = (ngroups + kResolveThreads - 1) / kResolveThreads;   // groups per thread
-    const int g0 = min(ngroups, (int)threadIdx.x * gpt), g1 = min(ngroups, g0 + gpt);
-    uint32_t gt = 0, eq = 0;
-    for (int g = g0; g < g1; ++g) {
-      gt += s_gt[g];
-      eq += s_eq[g];
-    }
-    uint32_t tot;
-    uint32_t gt_run = block_exclusive_sum<kResolveThreads>(gt, s_tmp, tot);
-    uint32_t eq_run = block_exclusive_sum<kResolveThreads>(eq, s_tmp, tot);
-    for (int g = g0; g < g1; ++g) {
-      const uint32_t a = s_gt[g], b = s_eq[g];
-      s_gt[g] = gt_run;
-      s_eq[g] = eq_run;
-      gt_run += a;
-      eq_run += b;
-    }
+  if (lds) {   // per_group == 1, chunk ids at hand
+    keys([&](uint32_t key, uint32_t c) {
+      if (key > T) atomicAdd(&s_gt[c], 1u);
+      if (key == T) atomicAdd(&s_eq[c], 1u);
+    });
+  } else {
+    for_each_key(src, [&](uint32_t key, uint32_t idx) {
+      const int g = (int)((int64_t)(idx / kChunk) / per_group);
+      if (key > T) atomicAdd(&s_gt[g], 1u);
+      if (key == T) atomicAdd(&s_eq[g], 1u);
+    });
   }
   __syncthreads();
+  block_prefix_inplace(s_gt, ngroups, s_tmp);
+  block_prefix_inplace(s_eq, ngroups, s_tmp);
+  __syncthreads();
+  if (lds) {   // topk_order writes the chunks
+    for (int c = threadIdx.x; c < ngroups; c += kResolveThreads) {
+      r.ord[2 * c] = s_gt[c];
+      r.ord[2 * c + 1] = s_eq[c];
+    }
+    if (threadIdx.x == 0) {
+      r.st[kS_T] = T;
+      r.st[kS_NEED] = need;
+      r.st[kS_ORDER] = 1u;
+    }
+    return;
+  }
+  if (threadIdx.x == 0) r.st[kS_ORDER] = 0u;
+  // One wave per group writes its selected indices in index order.
   const int wave = threadIdx.x >> 6;
   const uint64_t below = lanes_below();
   for (int g = wave; g < ngroups; g += kResolveThreads / 64) {
@@ -552,6 +633,35 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
                   pos += (uint32_t)__popcll(tm);
                   eq_seen += (uint32_t)__popcll(eqm);
                 });
+  }
+}
+
+// Rows resolved in LDS: one wave per (chunk, row) writes the chunk's selected
+// indices in index order at the chunk's prefix position.
+__global__ __launch_bounds__(64) void topk_order(int64_t n, int k, const void* ws,
+                                                 int32_t* __restrict__ out) {
+  const int64_t row = blockIdx.y, c = blockIdx.x;
+  const RowWs r = row_ws(const_cast<void*>(ws), n, row);
+  if (r.st[kS_ORDER] == 0u) return;
+  const uint32_t T = r.st[kS_T], need = r.st[kS_NEED];
+  const uint32_t s0 = r.seg[2 * c], cnt = r.seg[2 * c + 1];
+  uint32_t pos = r.ord[2 * c], eq_seen = r.ord[2 * c + 1];
+  pos += min(eq_seen, need);
+  const uint2* cand = reinterpret_cast<const uint2*>(r.cand);
+  int32_t* dst = out + row * (int64_t)k;
+  const int lane = lane_id();
+  const uint64_t below = lanes_below();
+  for (uint32_t o = 0; o < cnt; o += 64) {
+    const bool v = o + lane < cnt;
+    const uint2 e = v ? cand[s0 + o + lane] : make_uint2(0u, 0u);
+    const bool gt = v && e.x > T, eq = v && e.x == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = gt || (eq && eq_seen + (uint32_t)__popcll(eqm & below) < need);
+    const uint64_t tm = __ballot(take);
+    const uint32_t p = pos + (uint32_t)__popcll(tm & below);
+    if (take && p < (uint32_t)k) dst[p] = (int32_t)e.y;   // p < k by construction
+    pos += (uint32_t)__popcll(tm);
+    eq_seen += (uint32_t)__popcll(eqm);
   }
 }
 
@@ -574,6 +684,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int3
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
   hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, k, ws,
                      indices);
+  hipLaunchKernelGGL(topk_order, grid_chunks, dim3(64), 0, stream, n, k, ws, indices);
   return hipGetLastError();
 }
 

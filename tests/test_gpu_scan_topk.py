@@ -101,6 +101,18 @@ def test_topk_matches_oracle(fk, kind):
         assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
 
 
+@pytest.mark.parametrize("kind", ["normal", "grid64"])
+def test_topk_full_rows(fk, kind):
+    """Rows of 1M scores, k = 4096 (the q1m shape): the candidate path, with
+    a few hundred keys tied at the boundary for grid64."""
+    rows, n, k = 4, 1 << 20, 4096
+    scores = fathom_inputs.random_scores(rows, n, seed=77, kind=kind)
+    say("topk full rows kind=%s rows=%d n=%d k=%d" % (kind, rows, n, k))
+    gpu = _topk(fk, scores, k)
+    ref = oracle.topk(scores, k)
+    assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+
+
 def test_topk_repeatable(fk):
     scores = fathom_inputs.random_scores(8, 50000, seed=41, kind="ties")
     say("topk repeat x3")
