@@ -7,22 +7,24 @@
 //
 // Scores map to order-preserving 32-bit keys (fp32 bits with the sign
 // folded, -0 mapped to +0).  Per row:
-//   sample  — an 11-bit histogram of the top key bits over every 8th chunk;
-//   guess   — a cut tau (the low edge of a histogram bin) that leaves, by the
-//             sample, comfortably more than k keys at or above it;
-//   compact — one pass over the row appends every key >= tau (key, index) to
-//             the row's candidate buffer, each chunk as one contiguous
-//             segment in index order, and records per chunk the segment and
-//             a histogram of its candidates' top digits;
-//   resolve — one workgroup per row selects exactly among the candidates:
-//             the k-th largest key T (the top digit from the chunk
-//             histograms, two more radix digits over the candidates), the
-//             keys == T still needed, and then walks the segments in chunk
-//             order, writing every key > T and the earliest keys == T, so
-//             the row comes out in index order without a sort.
-// If the guess fails (fewer than k keys >= tau, or more than the buffer
-// holds: heavy ties or adversarial rows), the resolve workgroup does the
-// same from the scores themselves: same result, many more passes.
+//   sample  — an 11-bit histogram of the top key bits over every 8th chunk
+//             of 8192 keys;
+//   guess   — a cut tau that leaves, by the sample, comfortably more than k
+//             keys at or above it (placed inside the histogram bin);
+//   compact — one pass over the row writes every key >= tau (key, index) of
+//             a chunk, in index order, to that chunk's own region of the
+//             row's candidate buffer, and its count;
+//   resolve — one workgroup per row: stages the candidates in LDS, finds the
+//             k-th largest key T with two radix digits counted from tau,
+//             the keys == T still needed, and per chunk the number of keys
+//             > T and == T before it;
+//   order   — one wave per (chunk, row) writes the chunk's selected indices
+//             (every key > T, the earliest keys == T) at its prefix
+//             position, so the row comes out in index order without a sort.
+// If the guess fails (fewer than k keys >= tau, or a chunk with more than
+// its region holds: heavy ties or adversarial rows), or the candidates do not
+// fit in LDS, the resolve workgroup does all of it alone, from the scores or
+// the regions: same result, many more passes.
 #include "fathom_internal.h"
 
 namespace fathom {
@@ -35,13 +37,14 @@ constexpr int kChunk = kThreads * kPerThread;        // 8192 keys per workgroup 
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
 constexpr int kBins = 2048;                          // radix digit: 11 bits
 constexpr int kSampleStride = 8;                     // every 8th chunk is sampled
-constexpr int kTopBins = 64;                         // chunk histogram: digits tau .. tau + 62, and above
 constexpr int kResolveThreads = 1024;
+constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
+constexpr int kLdsCand = 16384;                      // candidates staged in LDS at most
 
 // Per-row workspace (32-bit words).
 enum : int {
   kS_TAU = 0,       // candidate cut
-  kS_NCAND,         // keys >= tau seen so far (may exceed the capacity)
+  kS_OVER,          // nonzero: a chunk had more candidates than its region
   kS_NSAMPLE,       // keys in the sampled chunks
   kS_T,             // the k-th largest key (set by the resolve)
   kS_NEED,          // keys == T to take
@@ -51,36 +54,36 @@ enum : int {
 
 __host__ __device__ inline int64_t n_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-// Candidate buffer capacity: n / 8, between 8192 and 65536 keys.
+// Candidate buffer capacity: n / 8, between 8192 and 65536 keys, shared
+// equally by the chunks (512 per chunk at n = 2^20).
 __host__ __device__ inline int64_t cand_cap(int64_t n) {
   const int64_t c = n / 8;
   return c < 8192 ? 8192 : (c > 65536 ? 65536 : c);
 }
+__host__ __device__ inline uint32_t region(int64_t n) { return (uint32_t)(cand_cap(n) / n_chunks(n)); }
 
 __host__ __device__ inline size_t row_words(int64_t n) {
-  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + (4 + kTopBins) * (size_t)n_chunks(n);
+  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n);
 }
 
 struct RowWs {
   uint32_t* hist;    // [kBins]: sample histogram
   uint32_t* st;      // [kS_WORDS]
-  uint32_t* cand;    // [cap][2]: key, index
-  uint32_t* seg;     // [nchunks][2]: first slot and number of the chunk's candidates
-  uint32_t* thist;   // [nchunks][kTopBins]: the chunk's candidate top digits
+  uint32_t* cand;    // [nchunks][region][2]: key, index
+  uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
   uint32_t* ord;     // [nchunks][2]: keys > T and == T in the chunks before this one
-  uint32_t cap;
+  uint32_t region;
 };
 
 __device__ inline RowWs row_ws(void* ws, int64_t n, int64_t row) {
   uint32_t* p = reinterpret_cast<uint32_t*>(ws) + row_words(n) * row;
   RowWs r;
-  r.cap = (uint32_t)cand_cap(n);
+  r.region = region(n);
   r.hist = p;
   r.st = p + kBins;
   r.cand = r.st + kS_WORDS;
-  r.seg = r.cand + 2 * (size_t)r.cap;
-  r.thist = r.seg + 2 * (size_t)n_chunks(n);
-  r.ord = r.thist + (size_t)kTopBins * n_chunks(n);
+  r.seg = r.cand + 2 * (size_t)cand_cap(n);
+  r.ord = r.seg + 2 * (size_t)n_chunks(n);
   return r;
 }
 
@@ -90,22 +93,24 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float whose order key is `key`; keys below that of -inf map to -inf
+// and keys above that of +inf to a NaN, so `x >= key_float(key)` is
+// `order_key(x) >= key` for every finite x.
+__device__ __forceinline__ float key_float(uint32_t key) {
+  if (key <= 0x007fffffu) return -__builtin_inff();
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Add 1 per active lane to hist[bin] in LDS.  Lanes that share a bin
-// serialise in the LDS unit, which is cheaper than combining them first.
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
-  if (active) atomicAdd(&hist[bin], 1u);
-}
-
-// The keys of one chunk held in registers: wave w of the workgroup owns keys
+// The scores of one chunk in registers: wave w of the workgroup owns keys
 // [w * 2048, w * 2048 + 2048) of the chunk; lane l holds, for i = 0..7, the 4
 // keys at wave offset (i * 64 + l) * 4.
-struct ChunkKeys {
-  uint32_t k[kPerThread / 4][4];
+struct ChunkVals {
+  float v[kPerThread / 4][4];
 };
 
 __device__ __forceinline__ int64_t key_index(int64_t c0, int i, int c) {
@@ -124,27 +129,26 @@ __device__ __forceinline__ bool chunk_full(const float* src, int64_t n, int64_t 
   return (reinterpret_cast<uintptr_t>(src) & 15) == 0 && c0 + kChunk <= n;
 }
 
+// Padding of a partial chunk reads -inf (never a candidate: see compact).
 template <bool FULL>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
-                                           ChunkKeys& K) {
+__device__ __forceinline__ void load_vals(const float* __restrict__ src, int64_t n, int64_t c0,
+                                          ChunkVals& V) {
   if (FULL) {
-    float4 v[kPerThread / 4];
-#pragma unroll
-    for (int i = 0; i < kPerThread / 4; ++i)
-      v[i] = *reinterpret_cast<const float4*>(src + key_index(c0, i, 0));
+    typedef float f4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < kPerThread / 4; ++i) {
-      K.k[i][0] = order_key(v[i].x);
-      K.k[i][1] = order_key(v[i].y);
-      K.k[i][2] = order_key(v[i].z);
-      K.k[i][3] = order_key(v[i].w);
+      const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + key_index(c0, i, 0)));
+      V.v[i][0] = x.x;
+      V.v[i][1] = x.y;
+      V.v[i][2] = x.z;
+      V.v[i][3] = x.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kPerThread / 4; ++i) {
       const int64_t e = key_index(c0, i, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) K.k[i][c] = (e + c < n) ? order_key(src[e + c]) : 0u;
+      for (int c = 0; c < 4; ++c) V.v[i][c] = (e + c < n) ? src[e + c] : -__builtin_inff();
     }
   }
 }
@@ -156,12 +160,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
     const uint32_t o = __shfl_up(v, s, 64);
     if (lane >= s) v += o;
   }
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
   return v;
 }
 
@@ -186,7 +184,23 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_
   return before + inc - v;
 }
 
-// Find, over `nb` bins held kPer per thread (highest bin last), the bin that
+// Exclusive prefix of cnt[0, m) in place, over the workgroup (m <= kGroups).
+template <int NT>
+__device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint32_t* s_tmp) {
+  const int per = (m + NT - 1) / NT;
+  const int g0 = min(m, (int)threadIdx.x * per), g1 = min(m, g0 + per);
+  uint32_t sum = 0;
+  for (int g = g0; g < g1; ++g) sum += cnt[g];
+  uint32_t tot;
+  uint32_t run = block_exclusive_sum<NT>(sum, s_tmp, tot);
+  for (int g = g0; g < g1; ++g) {
+    const uint32_t v = cnt[g];
+    cnt[g] = run;
+    run += v;
+  }
+}
+
+// Find, over bins held kPer per thread (highest bin last), the bin that
 // holds the need-th largest key; thread-local h[] are the thread's bins.
 // Writes (bin, need within the bin) to sel[] from the one thread that owns it.
 template <int NT, int kPer>
@@ -221,16 +235,18 @@ __global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n) {
 }
 
 // Histogram of the top 11 key bits of one sampled chunk (chunk
-// blockIdx.x * kSampleStride).
+// blockIdx.x * kSampleStride).  Lanes that share a bin serialise in the LDS
+// unit, which is cheaper than combining them first.
 template <bool F>
 __device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
                                              uint32_t* s_hist) {
-  ChunkKeys K;
-  load_chunk<F>(src, n, c0, K);
+  ChunkVals V;
+  load_vals<F>(src, n, c0, V);
 #pragma unroll
   for (int i = 0; i < kPerThread / 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) hist_add(s_hist, K.k[i][c] >> 21, valid<F>(c0, i, c, n));
+    for (int c = 0; c < 4; ++c)
+      if (valid<F>(c0, i, c, n)) atomicAdd(&s_hist[order_key(V.v[i][c]) >> 21], 1u);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict__ scores,
@@ -290,41 +306,40 @@ __global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int k, void* w
   }
 }
 
-// Every key >= tau of one chunk appended to the candidate buffer as one
-// contiguous segment in index order (one atomic per workgroup reserves it;
-// same-address atomics serialise in L2), and the chunk's histogram of the
-// candidates' top digits, relative to tau's.
+// Every key >= tau of one chunk written in index order to the chunk's region
+// of the candidate buffer; the count goes to the segment table (a count above
+// the region flags the row).  The test is a float compare against the cut
+// (padding reads -inf: never >= a finite cut, and a cut of -inf's key only
+// comes with whole-row sampling, where the cut is the low edge of a bin with
+// keys); order keys are formed for candidates only.
 template <bool F>
 __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
-                                              const RowWs& r, uint32_t* s_cnt, uint32_t* s_th,
-                                              uint32_t& s_base) {
-  const uint32_t tau = r.st[kS_TAU];
-  const uint32_t dtau = tau >> 21;
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  for (int i = threadIdx.x; i < kTopBins; i += kThreads) s_th[i] = 0u;
-  ChunkKeys K;
-  load_chunk<F>(src, n, c0, K);
+                                              const RowWs& r, uint32_t* s_cnt) {
+  const float tauf = key_float(r.st[kS_TAU]);
+  const int wave = threadIdx.x >> 6;
+  ChunkVals V;
+  load_vals<F>(src, n, c0, V);
   uint32_t ncand = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread / 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ncand += (valid<F>(c0, i, c, n) && K.k[i][c] >= tau) ? 1u : 0u;
-  ncand = wave_sum(ncand);
-  if (lane == 0) s_cnt[wave] = ncand;
+    for (int c = 0; c < 4; ++c)
+      ncand += (uint32_t)__popcll(__ballot(V.v[i][c] >= tauf && valid<F>(c0, i, c, n)));
+  if (lane_id() == 0) s_cnt[wave] = ncand;
   __syncthreads();
+  const uint32_t base = (uint32_t)blockIdx.x * r.region;
   if (threadIdx.x == 0) {
     uint32_t t = 0;
 #pragma unroll
     for (int w = 0; w < kWavesPerWg; ++w) t += s_cnt[w];
-    s_base = t ? atomicAdd(&r.st[kS_NCAND], t) : 0u;
-    r.seg[2 * blockIdx.x] = s_base;
+    r.seg[2 * blockIdx.x] = base;
     r.seg[2 * blockIdx.x + 1] = t;
+    if (t > r.region) atomicOr(&r.st[kS_OVER], 1u);
   }
-  __syncthreads();
   if (ncand != 0u) {
     // Slots follow index order: the keys of step i are (lane, c) with index
     // ascending in lane, then c.
-    uint32_t slot = s_base;
+    uint32_t slot = 0;
     for (int w = 0; w < wave; ++w) slot += s_cnt[w];
     const uint64_t below = lanes_below();
 #pragma unroll
@@ -333,7 +348,7 @@ __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int
       uint64_t m[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        cand[c] = valid<F>(c0, i, c, n) && K.k[i][c] >= tau;
+        cand[c] = V.v[i][c] >= tauf && valid<F>(c0, i, c, n);
         m[c] = __ballot(cand[c]);
       }
       if ((m[0] | m[1] | m[2] | m[3]) == 0ull) continue;
@@ -342,45 +357,39 @@ __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int
       for (int c = 0; c < 4; ++c) {
         sl += (uint32_t)__popcll(m[c] & below);
         slot += (uint32_t)__popcll(m[c]);
-        hist_add(s_th, min((K.k[i][c] >> 21) - dtau, (uint32_t)kTopBins - 1u), cand[c]);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (cand[c]) {
-          if (sl < r.cap)
-            reinterpret_cast<uint2*>(r.cand)[sl] =
-                make_uint2(K.k[i][c], (uint32_t)key_index(c0, i, c));
+          if (sl < r.region)
+            reinterpret_cast<uint2*>(r.cand)[base + sl] =
+                make_uint2(order_key(V.v[i][c]), (uint32_t)key_index(c0, i, c));
           ++sl;
         }
       }
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTopBins; i += kThreads)
-    r.thist[(size_t)blockIdx.x * kTopBins + i] = s_th[i];
 }
 
 __global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict__ scores,
                                                          int64_t n, void* ws) {
   __shared__ uint32_t s_cnt[kWavesPerWg];
-  __shared__ uint32_t s_th[kTopBins];
-  __shared__ uint32_t s_base;
   const int64_t row = blockIdx.y;
   const RowWs r = row_ws(ws, n, row);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   const float* src = scores + row * n;
-  if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, r, s_cnt, s_th, s_base);
-  else compact_chunk<false>(src, n, c0, r, s_cnt, s_th, s_base);
+  if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, r, s_cnt);
+  else compact_chunk<false>(src, n, c0, r, s_cnt);
 }
 
-// The keys a resolve workgroup selects among: the candidate buffer, or
+// The keys the one-workgroup path selects among: the candidate regions, or
 // (direct mode) the row itself.
 struct ResolveSrc {
-  const uint2* cand;      // (key, index) pairs
+  const uint2* cand;      // (key, index) pairs, region per chunk
   const uint32_t* seg;
   const float* scores;
   int64_t n, nc;
-  uint32_t ncand;
+  uint32_t region;
   bool direct;
 };
 
@@ -390,16 +399,20 @@ template <class F>
 __device__ __forceinline__ void for_each_key(const ResolveSrc s, F&& f) {
   constexpr int kU = 4;
   if (!s.direct) {
-    for (uint32_t i0 = threadIdx.x; i0 < s.ncand; i0 += kU * kResolveThreads) {
+    const int64_t slots = s.nc * s.region;
+    for (int64_t i0 = threadIdx.x; i0 < slots; i0 += kU * kResolveThreads) {
       uint2 e[kU];
+      bool v[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const uint32_t i = i0 + u * kResolveThreads;
-        e[u] = i < s.ncand ? s.cand[i] : make_uint2(0u, 0u);
+        const int64_t i = i0 + u * kResolveThreads;
+        const int64_t c = i / s.region;
+        v[u] = i < slots && (uint32_t)(i - c * s.region) < s.seg[2 * c + 1];
+        e[u] = v[u] ? s.cand[i] : make_uint2(0u, 0u);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u)
-        if (i0 + u * kResolveThreads < s.ncand) f(e[u].x, e[u].y);
+        if (v[u]) f(e[u].x, e[u].y);
     }
   } else {
     for (int64_t i0 = threadIdx.x; i0 < s.n; i0 += kU * kResolveThreads) {
@@ -442,27 +455,6 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
   }
 }
 
-constexpr int kGroups = 4096;   // chunk groups of the ordered write
-
-// Exclusive prefix of cnt[0, m) in place, over the workgroup (m <= kGroups).
-__device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint32_t* s_tmp) {
-  const int per = (m + kResolveThreads - 1) / kResolveThreads;
-  const int g0 = min(m, (int)threadIdx.x * per), g1 = min(m, g0 + per);
-  uint32_t sum = 0;
-  for (int g = g0; g < g1; ++g) sum += cnt[g];
-  uint32_t tot;
-  uint32_t run = block_exclusive_sum<kResolveThreads>(sum, s_tmp, tot);
-  for (int g = g0; g < g1; ++g) {
-    const uint32_t v = cnt[g];
-    cnt[g] = run;
-    run += v;
-  }
-}
-
-// Candidates resolved from LDS: up to this many (key and chunk id) are
-// staged; rows with more take the global path.
-constexpr int kLdsCand = 16384;
-
 // Per row: T (the k-th largest key) and the keys == T still needed.  Rows
 // whose candidates fit in LDS (the usual case) stage them there, resolve T
 // from LDS, and leave per-chunk prefix counts for topk_order, which writes
@@ -471,7 +463,7 @@ constexpr int kLdsCand = 16384;
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
                                                                 int64_t n, int k, void* ws,
                                                                 int32_t* __restrict__ out) {
-  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_hist[2 * kBins];
   __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
   __shared__ uint32_t s_key[kLdsCand];
   __shared__ uint16_t s_cid[kLdsCand];
@@ -485,76 +477,131 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   src.scores = scores + row * n;
   src.n = n;
   src.nc = n_chunks(n);
-  const uint32_t ncand_all = r.st[kS_NCAND];
-  src.ncand = min(ncand_all, r.cap);
-  src.direct = ncand_all < (uint32_t)k || ncand_all > r.cap;   // the guess failed
-  const bool lds = !src.direct && src.nc <= kGroups && src.ncand <= (uint32_t)kLdsCand;
-  const uint32_t dtau = r.st[kS_TAU] >> 21;
+  src.region = r.region;
+  const int64_t nc = src.nc;
   int32_t* dst = out + row * (int64_t)k;
 
-  if (lds) {   // stage keys and chunk ids
-    for (uint32_t i0 = threadIdx.x; i0 < src.ncand; i0 += 4 * kResolveThreads) {
-      uint2 e[4];
+  // Candidates of the row: the chunk counts, summed (and, when they fit,
+  // prefixed into s_gt for staging).
+  const bool small = nc <= kGroups;
+  uint32_t ncand = 0;
+  {
+    const int64_t per = (nc + kResolveThreads - 1) / kResolveThreads;
+    const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
+    uint32_t mine = 0;
+    for (int64_t c = c0; c < c1; ++c) {
+      const uint32_t t = r.seg[2 * c + 1];
+      if (small) s_gt[c] = t;
+      mine += t;
+    }
+    uint32_t tot;
+    uint32_t run = block_exclusive_sum<kResolveThreads>(mine, s_tmp, tot);
+    ncand = tot;
+    if (small)
+      for (int64_t c = c0; c < c1; ++c) {
+        const uint32_t t = s_gt[c];
+        s_gt[c] = run;   // first LDS slot of chunk c
+        run += t;
+      }
+  }
+  src.direct = ncand < (uint32_t)k || r.st[kS_OVER] != 0u;   // the guess failed
+  const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;
+  __syncthreads();
+
+  if (lds) {
+    // Stage keys and chunk ids: wave w copies chunks w, w + 16, ..., eight
+    // chunks' first 128 candidates per batch of loads, then any rest.
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
+    constexpr int kW = kResolveThreads / 64, kU = 8;
+    for (int64_t cb = wave; cb < nc; cb += kW * kU) {
+      uint2 e[kU][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * kResolveThreads;
-        e[u] = i < src.ncand ? src.cand[i] : make_uint2(0u, 0u);
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = cb + u * kW;
+        const uint32_t cnt = c < nc ? count(c) : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t o = lane + 64 * h;
+          e[u][h] = o < cnt ? src.cand[(uint32_t)c * src.region + o] : make_uint2(0u, 0u);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t i = i0 + u * kResolveThreads;
-        if (i < src.ncand) {
-          s_key[i] = e[u].x;
-          s_cid[i] = (uint16_t)(e[u].y / kChunk);
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = cb + u * kW;
+        const uint32_t cnt = c < nc ? count(c) : 0u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t o = lane + 64 * h;
+          if (o < cnt) {
+            s_key[s_gt[c] + o] = e[u][h].x;
+            s_cid[s_gt[c] + o] = (uint16_t)c;
+          }
         }
       }
     }
+    for (int64_t c = wave; c < nc; c += kW)
+      for (uint32_t o = 128 + lane; o < count(c); o += 64) {
+        const uint2 e = src.cand[(uint32_t)c * src.region + o];
+        s_key[s_gt[c] + o] = e.x;
+        s_cid[s_gt[c] + o] = (uint16_t)c;
+      }
   }
-  // f(key, index or chunk) over every key the row selects among.
+  __syncthreads();
+
+  uint32_t need = (uint32_t)k;
+  uint32_t prefix = 0;
+  bool done = false;
+  if (lds) {
+    // Candidates are keys >= tau and the cut sits just below the k-th key:
+    // bins of 4096 keys above tau (the last one open-ended), then the 4096
+    // keys of the chosen bin.
+    const uint32_t tau = r.st[kS_TAU];
+    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads)
+      atomicAdd(&s_hist[min((s_key[i] - tau) >> 12, (uint32_t)kBins - 1u)], 1u);
+    __syncthreads();
+    {
+      constexpr int kPer = kBins / kResolveThreads;
+      uint32_t h[kPer];
+#pragma unroll
+      for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+      pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+    }
+    __syncthreads();
+    const uint32_t binA = s_sel[0], needA = s_sel[1];
+    __syncthreads();
+    if (binA < (uint32_t)kBins - 1u) {
+      for (int i = threadIdx.x; i < 2 * kBins; i += kResolveThreads) s_hist[i] = 0u;
+      __syncthreads();
+      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) {
+        const uint32_t d = s_key[i] - tau;
+        if ((d >> 12) == binA) atomicAdd(&s_hist[d & 4095u], 1u);
+      }
+      __syncthreads();
+      constexpr int kPer = 2 * kBins / kResolveThreads;
+      uint32_t h[kPer];
+#pragma unroll
+      for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+      pick_bin<kResolveThreads, kPer>(h, needA, s_tmp, s_sel);
+      __syncthreads();
+      prefix = tau + (binA << 12) + s_sel[0];
+      need = s_sel[1];
+      done = true;
+      __syncthreads();
+    }
+  }
+  // f(key, index or chunk id) over every key the row selects among.
   auto keys = [&](auto&& f) {
     if (lds) {
-      for (uint32_t i = threadIdx.x; i < src.ncand; i += kResolveThreads) f(s_key[i], (uint32_t)s_cid[i]);
+      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) f(s_key[i], (uint32_t)s_cid[i]);
     } else {
       for_each_key(src, f);
     }
   };
-
-  // Top digit (bits 31..21).  Candidate mode: from the chunk histograms,
-  // unless the k-th key lies beyond their range.
-  uint32_t need = (uint32_t)k;
-  uint32_t prefix = 0;
-  bool top_done = false;
-  if (!src.direct) {
-    for (int i = threadIdx.x; i < kTopBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-    const int64_t nth = src.nc * kTopBins;
-    for (int64_t i0 = threadIdx.x; i0 < nth; i0 += 8 * kResolveThreads) {
-      uint32_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + u * kResolveThreads;
-        v[u] = i < nth ? r.thist[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)   // i % kTopBins is the same for every u
-        if (v[u] != 0u) atomicAdd(&s_hist[i0 % kTopBins], v[u]);
-    }
-    __syncthreads();
-    uint32_t h[1] = {threadIdx.x < (uint32_t)kTopBins - 1 ? s_hist[threadIdx.x] : 0u};
-    const uint32_t beyond = s_hist[kTopBins - 1];
-    __syncthreads();
-    if (beyond < need) {   // the k-th key's digit is among the first 63
-      s_sel[0] = 0u;
-      __syncthreads();
-      pick_bin<kResolveThreads, 1>(h, need - beyond, s_tmp, s_sel);
-      __syncthreads();
-      prefix = (dtau + s_sel[0]) << 21;
-      need = s_sel[1];
-      top_done = true;
-      __syncthreads();
-    }
-  }
-  for (int level = top_done ? 1 : 0; level < 3; ++level) {
+  // Three radix digits (11, 11, 10 bits), from the top.
+  for (int level = 0; level < 3 && !done; ++level) {
     const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
     const int bits = level == 2 ? 10 : 11;
     const int hi = shift + bits;   // bits at and above hi are fixed
@@ -562,7 +609,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     __syncthreads();
     keys([&](uint32_t key, uint32_t) {
       const bool in = hi >= 32 || (key >> (hi & 31)) == (prefix >> (hi & 31));
-      hist_add(s_hist, (key >> shift) & ((1u << bits) - 1u), in);
+      if (in) atomicAdd(&s_hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
     });
     __syncthreads();
     constexpr int kPer = kBins / kResolveThreads;   // 2
@@ -582,7 +629,6 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 
   // The row's chunks in at most kGroups groups of consecutive chunks: the keys
   // > T and == T of every group, prefixed over the groups.
-  const int64_t nc = src.nc;
   const int64_t per_group = (nc + kGroups - 1) / kGroups;
   const int ngroups = (int)((nc + per_group - 1) / per_group);
   for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
@@ -600,8 +646,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     });
   }
   __syncthreads();
-  block_prefix_inplace(s_gt, ngroups, s_tmp);
-  block_prefix_inplace(s_eq, ngroups, s_tmp);
+  block_prefix_inplace<kResolveThreads>(s_gt, ngroups, s_tmp);
+  block_prefix_inplace<kResolveThreads>(s_eq, ngroups, s_tmp);
   __syncthreads();
   if (lds) {   // topk_order writes the chunks
     for (int c = threadIdx.x; c < ngroups; c += kResolveThreads) {
