@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 1
+#define FATHOM_ABI_VERSION 2   /* 2: adds fathom_plan_fixed */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -112,6 +112,34 @@ int fathom_encode(const uint16_t* k, int64_t groups, int64_t n, int32_t d,
 int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G,
                 int32_t d, int32_t budget_bits, uint8_t* depths, double* theta,
                 int32_t* bits_used, void* stream);
+
+/*
+ * fathom_plan_fixed — fixed-depth plans, the pages' comparison points read
+ * through the same store and fathom_scan.
+ *
+ * The 2-bit thumbnail baseline of §2 reads every channel at two planes (288
+ * bits per token with the scales); SparQ (§2) keeps, per query, the channels
+ * with the largest |q_j|, summed over the query heads that share a KV head,
+ * here at 4 bits (r = 16 and 32 give the 68- and 136-bit scans of Table 1);
+ * Double Sparsity (§2) keeps a fixed set chosen offline from a calibration
+ * statistic.
+ *
+ *   mode FATHOM_PLAN_UNIFORM: t_j = param for every channel, 0 <= param <= 4.
+ *   mode FATHOM_PLAN_SPARQ:   s_j = sum_h |q_hj| (fp64, heads in order);
+ *                             t_j = 4 on the param channels with the largest
+ *                             s_j, 0 elsewhere, 0 <= param <= d.
+ *   mode FATHOM_PLAN_TOPSTAT: the same with s_j = stat[group][j] (fp32).
+ * Ties in s_j go to the lower channel index.
+ *
+ *   q     [groups][G][d] fp32 (read by SPARQ; finite), may be null otherwise
+ *   stat  [groups][d]    fp32 (read by TOPSTAT; finite), may be null otherwise
+ *   depths [groups][d]   uint8 output
+ */
+#define FATHOM_PLAN_UNIFORM 1
+#define FATHOM_PLAN_SPARQ 2
+#define FATHOM_PLAN_TOPSTAT 3
+int fathom_plan_fixed(const float* q, const float* stat, int64_t groups, int32_t G, int32_t d,
+                      int32_t mode, int32_t param, uint8_t* depths, void* stream);
 
 /*
  * fathom_scan — approximate scores from the prefix planes the depths select.

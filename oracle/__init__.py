@@ -204,6 +204,40 @@ def plan(q: np.ndarray, var: np.ndarray, budget: int, nthreads: int = 0):
 
 
 # --------------------------------------------------------------------------
+# Fixed-depth plans — the §2 comparison points (2-bit thumbnail, SparQ,
+# Double Sparsity's offline channel set) read through the same store
+# --------------------------------------------------------------------------
+
+def plan_fixed(mode: str, param: int, q=None, stat=None, groups=None, d: int = 128):
+    """'uniform': every channel at depth `param` (the 2-bit thumbnail reads all
+    channels at two planes).  'sparq': depth 4 on the `param` channels with the
+    largest sum over the query heads of |q_hj| (SparQ's rule under grouped
+    queries, the sum taken in fp64 head by head), 0 elsewhere.  'topstat': the
+    same ranked by a given per-channel statistic (a fixed set chosen offline).
+    Equal statistics rank by the lower channel index.  -> depths uint8
+    [groups][d]."""
+    if mode == "uniform":
+        return np.full((groups, d), param, dtype=np.uint8)
+    if mode == "sparq":
+        q = np.asarray(q, dtype=np.float32)
+        groups, G, d = q.shape
+        s = np.zeros((groups, d), dtype=np.float64)
+        for h in range(G):                      # heads in order, one rounding each
+            s = s + np.abs(q[:, h, :].astype(np.float64))
+    elif mode == "topstat":
+        s = np.asarray(stat, dtype=np.float32).astype(np.float64)
+        groups, d = s.shape
+    else:
+        raise ValueError(mode)
+    depths = np.zeros((groups, d), dtype=np.uint8)
+    j = np.arange(d)
+    for g in range(groups):
+        order = np.lexsort((j, -s[g]))          # statistic descending, then index
+        depths[g, order[:param]] = 4
+    return depths
+
+
+# --------------------------------------------------------------------------
 # Scan — §3.2 prefix dequantization over the §3.3 active channels
 # --------------------------------------------------------------------------
 

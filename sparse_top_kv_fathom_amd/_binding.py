@@ -33,7 +33,7 @@ STATUS = {
     -7: "FATHOM_ERR_ALIGNMENT",
 }
 
-EXPORTED = ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
             "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
 
 
@@ -57,6 +57,7 @@ def lib():
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.fathom_encode.argtypes = [P, I64, I64, I32, I64, I64, P, P, P, P]
         L.fathom_plan.argtypes = [P, P, I64, I32, I32, I32, P, P, P, P]
+        L.fathom_plan_fixed.argtypes = [P, P, I64, I32, I32, I32, I32, P, P]
         L.fathom_scan.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P]
         L.fathom_topk.argtypes = [P, I64, I64, I32, P, P, SZ, P]
         L.fathom_topk_workspace_bytes.argtypes = [I64, I64, I32]
@@ -64,7 +65,7 @@ def lib():
         L.fathom_status_string.argtypes = [ctypes.c_int]
         L.fathom_status_string.restype = ctypes.c_char_p
         L.fathom_abi_version.argtypes = []
-        for f in ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+        for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
                   "fathom_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -139,6 +140,35 @@ def plan(q: torch.Tensor, var: torch.Tensor, budget_bits: int, depths: torch.Ten
         _opt(theta, "theta", torch.float64, (groups,)),
         _opt(bits_used, "bits_used", torch.int32, (groups,)), _stream(stream))
     _check(st, "fathom_plan")
+    return depths
+
+
+PLAN_MODES = {"uniform": 1, "sparq": 2, "topstat": 3}
+
+
+def plan_fixed(mode: str, param: int, q: torch.Tensor | None = None,
+               stat: torch.Tensor | None = None, groups: int | None = None, G: int | None = None,
+               depths: torch.Tensor | None = None, stream=None):
+    """fathom_plan_fixed: 'uniform' (every channel at depth param), 'sparq'
+    (depth 4 on the param channels with the largest sum_h |q_hj|) or 'topstat'
+    (the same ranked by stat [groups][d]) -> depths uint8 [groups][d]."""
+    if q is not None:
+        groups, G, d = q.shape
+        device = q.device
+    elif stat is not None:
+        groups, d = stat.shape
+        G = G or 1
+        device = stat.device
+    else:
+        d = 128
+        device = depths.device if depths is not None else torch.device("cuda")
+    if depths is None:
+        depths = torch.empty((groups, d), dtype=torch.uint8, device=device)
+    st = lib().fathom_plan_fixed(
+        _opt(q, "q", torch.float32, (groups, G, d)), _opt(stat, "stat", torch.float32, (groups, d)),
+        groups, G, d, PLAN_MODES[mode], int(param),
+        _dev(depths, "depths", torch.uint8, (groups, d)), _stream(stream))
+    _check(st, "fathom_plan_fixed")
     return depths
 
 

@@ -39,7 +39,7 @@ const char* fathom_status_string(int status) {
     case FATHOM_OK: return "FATHOM_OK";
     case FATHOM_ERR_NULL_ARG: return "FATHOM_ERR_NULL_ARG: a required pointer is NULL";
     case FATHOM_ERR_BAD_SHAPE: return "FATHOM_ERR_BAD_SHAPE: d, G, n, groups or strides invalid";
-    case FATHOM_ERR_BAD_RANGE: return "FATHOM_ERR_BAD_RANGE: k or budget outside its range";
+    case FATHOM_ERR_BAD_RANGE: return "FATHOM_ERR_BAD_RANGE: k, budget or plan mode/parameter outside its range";
     case FATHOM_ERR_WORKSPACE: return "FATHOM_ERR_WORKSPACE: workspace smaller than required";
     case FATHOM_ERR_HIP: return "FATHOM_ERR_HIP: a HIP launch or runtime call failed";
     case FATHOM_ERR_NO_DEVICE: return "FATHOM_ERR_NO_DEVICE: no HIP device is visible";
@@ -77,6 +77,26 @@ int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G, int
   if (int s = device_ready()) return s;
   return to_status(fathom::launch_plan(q, var, groups, G, budget_bits, depths, theta, bits_used,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int fathom_plan_fixed(const float* q, const float* stat, int64_t groups, int32_t G, int32_t d,
+                      int32_t mode, int32_t param, uint8_t* depths, void* stream) {
+  if (!depths) return FATHOM_ERR_NULL_ARG;
+  if (mode == FATHOM_PLAN_SPARQ && !q) return FATHOM_ERR_NULL_ARG;
+  if (mode == FATHOM_PLAN_TOPSTAT && !stat) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (mode == FATHOM_PLAN_UNIFORM) {
+    if (param < 0 || param > fathom::kPlanes) return FATHOM_ERR_BAD_RANGE;
+  } else if (mode == FATHOM_PLAN_SPARQ || mode == FATHOM_PLAN_TOPSTAT) {
+    if (param < 0 || param > d) return FATHOM_ERR_BAD_RANGE;
+  } else {
+    return FATHOM_ERR_BAD_RANGE;
+  }
+  if (!aligned(q, 4) || !aligned(stat, 4)) return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_plan_fixed(q, stat, groups, G, mode, param, depths,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,

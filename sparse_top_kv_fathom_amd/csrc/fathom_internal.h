@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fathom.h"
+
 namespace fathom {
 
 constexpr int kBlock = 64;   // tokens per block = bits per plane word = wave64 lanes
@@ -21,6 +23,8 @@ hipError_t launch_plan(const float* q, const float* var, int64_t groups, int G,
                        int budget_bits, uint8_t* depths, double* theta, int32_t* bits_used,
                        hipStream_t stream);
 
+hipError_t launch_plan_fixed(const float* q, const float* stat, int64_t groups, int G, int mode,
+                             int param, uint8_t* depths, hipStream_t stream);
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                        const uint8_t* depths, const float* q, int64_t groups, int G,
                        int64_t n, float* scores, hipStream_t stream);

@@ -41,7 +41,7 @@ def _gpu_visible():
 
 def test_header_declares_the_calls():
     names = declared()
-    for f in ("fathom_encode", "fathom_plan", "fathom_scan", "fathom_topk",
+    for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
               "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
@@ -56,7 +56,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 1
+    assert L.fathom_abi_version() == 2
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
@@ -92,6 +92,26 @@ def test_plan_validation(L):
     assert p(FAKE, FAKE, 1, 4, 128, -1, FAKE, None, None, None) == BAD_RANGE
     assert p(FAKE, FAKE, 1, 4, 128, 513, FAKE, None, None, None) == BAD_RANGE
     assert p(FAKE, FAKE, 1, 4, 128, 92, FAKE, P(4), None, None) == ALIGN         # theta 8 B
+
+
+def test_plan_fixed_validation(L):
+    p = L.fathom_plan_fixed
+    L.fathom_plan_fixed.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_int32, P, P]
+    UNIFORM, SPARQ, TOPSTAT = 1, 2, 3
+    assert p(FAKE, None, 1, 4, 128, UNIFORM, 2, None, None) == NULL_ARG
+    assert p(None, FAKE, 1, 4, 128, SPARQ, 16, FAKE, None) == NULL_ARG
+    assert p(FAKE, None, 1, 4, 128, TOPSTAT, 16, FAKE, None) == NULL_ARG
+    assert p(FAKE, None, 1, 4, 100, SPARQ, 16, FAKE, None) == BAD_SHAPE
+    assert p(FAKE, None, 1, 9, 128, SPARQ, 16, FAKE, None) == BAD_SHAPE
+    assert p(FAKE, None, 0, 4, 128, SPARQ, 16, FAKE, None) == BAD_SHAPE
+    assert p(None, None, 1, 4, 128, UNIFORM, 5, FAKE, None) == BAD_RANGE
+    assert p(None, None, 1, 4, 128, UNIFORM, -1, FAKE, None) == BAD_RANGE
+    assert p(FAKE, None, 1, 4, 128, SPARQ, 129, FAKE, None) == BAD_RANGE
+    assert p(FAKE, None, 1, 4, 128, 7, 1, FAKE, None) == BAD_RANGE
+    assert p(P(2), None, 1, 4, 128, SPARQ, 16, FAKE, None) == ALIGN
+    assert p(None, None, 1, 4, 128, UNIFORM, 2, FAKE, None) == NO_DEVICE
+    assert p(FAKE, None, 1, 4, 128, SPARQ, 16, FAKE, None) == NO_DEVICE
 
 
 def test_scan_validation(L):

@@ -162,3 +162,30 @@ def test_plan_q1m_queries(fk):
         dep, theta, bits = _gpu_plan(fk, ins.q, ins.var, B)
         od, ot, ob = oracle.plan(ins.q, ins.var, B)
         assert np.array_equal(dep, od) and np.array_equal(theta, ot) and np.array_equal(bits, ob)
+
+
+# --------------------------------------------------------------------------
+# Fixed-depth plans
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_plan_fixed_matches_oracle(fk, G):
+    import torch
+    rng = np.random.default_rng(60 + G)
+    groups = 9
+    q = rng.standard_normal((groups, G, 128)).astype(np.float32)
+    q[1] = np.round(q[1])                      # many equal |q| sums
+    q[2] = 1.0                                 # all equal
+    stat = rng.integers(0, 5, size=(groups, 128)).astype(np.float32)
+    say("plan_fixed G=%d" % G)
+    for t in range(5):
+        got = to_host(fk.plan_fixed("uniform", t, groups=groups, G=G))
+        torch.cuda.synchronize()
+        assert np.array_equal(got, oracle.plan_fixed("uniform", t, groups=groups))
+    for r in (0, 1, 16, 32, 127, 128):
+        got = to_host(fk.plan_fixed("sparq", r, q=to_dev(q)))
+        ref = oracle.plan_fixed("sparq", r, q=q)
+        assert np.array_equal(got, ref), (r, first_mismatch(got, ref))
+        got = to_host(fk.plan_fixed("topstat", r, stat=to_dev(stat), G=G))
+        ref = oracle.plan_fixed("topstat", r, stat=stat)
+        assert np.array_equal(got, ref), (r, first_mismatch(got, ref))

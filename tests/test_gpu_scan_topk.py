@@ -155,3 +155,28 @@ def test_end_to_end_q1m_b92(fk):
     s64, l1 = oracle.scan_f64(sub_p, sub_s, od, ins.q, (b1 - b0) * 64)
     got = gsc[:, :, b0 * 64:b1 * 64].astype(np.float64)
     assert np.all(np.abs(got - s64) <= TOL * l1)
+
+
+@pytest.mark.parametrize("mode,param", [("uniform", 2), ("uniform", 4), ("sparq", 16), ("sparq", 32)])
+def test_fixed_plans_through_the_scan(fk, mode, param):
+    """The comparison plans (2-bit thumbnail, full 4-bit, SparQ at 68 and 136
+    bits) read through the same store, scan and top-k as the water-filled plan."""
+    groups, G, n, k = 2, 4, 1 << 16, 256
+    ins = fathom_inputs.make_inputs(groups, G, n, seed=81)
+    say("fixed plan %s %d" % (mode, param))
+    planes, scales = fk.encode(to_dev(ins.k))
+    if mode == "uniform":
+        depths = fk.plan_fixed(mode, param, groups=groups, G=G)
+        od = oracle.plan_fixed(mode, param, groups=groups)
+    else:
+        depths = fk.plan_fixed(mode, param, q=to_dev(ins.q))
+        od = oracle.plan_fixed(mode, param, q=ins.q)
+    scores = fk.scan(planes, scales, depths, to_dev(ins.q), n)
+    idx = fk.topk(scores, k)
+    gd, gsc, gi = to_host(depths), to_host(scores), to_host(idx)
+    assert np.array_equal(gd, od), first_mismatch(gd, od)
+    op, os_, _ = oracle.encode(ins.k)
+    ref = oracle.scan_ref32(op, os_, od, ins.q, n)
+    assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
+    oi = oracle.topk(ref.reshape(-1, n), k)
+    assert np.array_equal(gi, oi), first_mismatch(gi, oi)

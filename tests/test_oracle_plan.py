@@ -187,3 +187,57 @@ def test_active_channels_at_48_bits_soft_check():
     active = (depths > 0).sum(axis=1).mean()
     assert np.all(bits <= 48)
     assert 20 <= active <= 40, active
+
+
+# --------------------------------------------------------------------------
+# Fixed-depth plans (§2 comparison points)
+# --------------------------------------------------------------------------
+
+def test_thumbnail_reads_288_bits_per_token():
+    """The 2-bit thumbnail reads all 128 channels at two planes: 256 code bits
+    plus the 16-bit scale per 64 tokens of each channel = 288 bits (§2)."""
+    t = oracle.plan_fixed("uniform", 2, groups=3)
+    assert t.shape == (3, 128) and (t == 2).all()
+    code = int(t[0].astype(int).sum())
+    assert code + 128 * 16 // 64 == 288
+
+
+@pytest.mark.parametrize("r,total", [(16, 68), (32, 136)])
+def test_sparq_budgets_are_the_pages_68_and_136_bits(r, total):
+    """r channels at 4 bits plus their scales: 68 and 136 bits per token, the
+    scan widths of the pages' Table 1 comparison."""
+    q = np.random.default_rng(r).standard_normal((2, 4, 128)).astype(np.float32)
+    t = oracle.plan_fixed("sparq", r, q=q)
+    assert ((t == 4).sum(axis=1) == r).all() and ((t == 0) | (t == 4)).all()
+    assert 4 * r + r * 16 // 64 == total
+
+
+def test_sparq_selects_largest_head_sums():
+    """|q_hj| grows with j in every head, so the top r are the last r channels."""
+    G, d = 4, 128
+    base = np.arange(1, d + 1, dtype=np.float32)
+    q = np.stack([base * (h + 1) * (-1) ** h for h in range(G)])[None]
+    t = oracle.plan_fixed("sparq", 10, q=q)
+    assert (np.nonzero(t[0])[0] == np.arange(d - 10, d)).all()
+
+
+def test_sparq_ties_take_lower_channels():
+    q = np.ones((1, 4, 128), dtype=np.float32)
+    q[0, :, 64:] = -1.0                     # |q| equal everywhere
+    t = oracle.plan_fixed("sparq", 7, q=q)
+    assert (np.nonzero(t[0])[0] == np.arange(7)).all()
+
+
+def test_topstat_brute_force_small():
+    """Against the best r-subset found by enumeration (d = 8): the largest sum,
+    and among equal sums the lexicographically smallest index set."""
+    import itertools
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        d = 8
+        stat = rng.integers(0, 4, size=(1, d)).astype(np.float32)   # many ties
+        for r in range(d + 1):
+            t = oracle.plan_fixed("topstat", r, stat=stat, d=d)
+            best = max(itertools.combinations(range(d), r),
+                       key=lambda c: (sum(stat[0, list(c)]), [-i for i in c]))
+            assert sorted(np.nonzero(t[0])[0].tolist()) == sorted(best), (trial, r)
