@@ -3,7 +3,9 @@
 One step = the work of one decode step over a resident bit-plane store:
 encode the newest 64-token block of every KV head into its slot, plan the
 read depths for a fresh query group (importance, 30-step bisection), scan
-every key at those depths, and select the top-k of every query head.
+every key at those depths, and select the top-k of every query head.  The
+fused call fathom_scan_topk (the scan takes the top-k candidates itself) is
+timed on the same inputs after the steps and reported beside them.
 
 Workload (default): one Qwen3-8B-shaped layer, 8 KV heads x 4 query heads,
 d = 128, n = 1,048,576 keys per head, budget 92 code bits, k = 4096; keys,
@@ -184,7 +186,10 @@ def main():
     ws = fk.topk_workspace(H * G, n, k, dev)
     torch.cuda.synchronize()
 
+    fws = fk.scan_topk_workspace(H, G, n, k, dev)
+
     def step(s, ev=None):
+        """One decode step: append the newest block, plan, scan, select."""
         planes, scales = stores[s % len(stores)]
         q = q_d[s % args.queries]
         if ev is not None:
@@ -201,6 +206,15 @@ def main():
         fk.topk(scores, k, indices=idx, workspace=ws)
         if ev is not None:
             ev[4].record()
+
+    def fused(s, ev):
+        """The scan and selection as the one call fathom_scan_topk."""
+        planes, scales = stores[s % len(stores)]
+        q = q_d[s % args.queries]
+        fk.plan(q, var_d, B, depths=depths)
+        ev[0].record()
+        fk.scan_topk(planes, scales, depths, q, n, k, scores=scores, indices=idx, workspace=fws)
+        ev[1].record()
 
     # Plain copy of known size, for scaling HBM byte counters (untimed).
     calib_src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
@@ -229,6 +243,16 @@ def main():
     ms_per_step = total_ms / args.steps
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
     stage_ms = stage.mean(axis=0)
+
+    # The fused call on the same inputs, timed after the steps.
+    for s in range(args.warmup):
+        fused(s, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        fused(args.warmup + s, fev[s])
+    torch.cuda.synchronize()
+    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
 
     # Algorithmic work of each timed step's scan (plans recomputed after timing).
     Ts, As = [], []
@@ -292,6 +316,7 @@ def main():
         },
         "stages_ms": {"encode_block": round(stage_ms[0], 4), "plan": round(stage_ms[1], 4),
                       "scan": round(stage_ms[2], 4), "topk": round(stage_ms[3], 4)},
+        "fused_scan_topk_ms": round(fused_ms, 4),
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "plan": {"code_bits_mean": float(Ts.mean()), "active_channels_mean": float(As.mean()),
                  "total_bits_per_key_mean": float((Ts + As / 4.0).mean())},

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 2   /* 2: adds fathom_plan_fixed */
+#define FATHOM_ABI_VERSION 3   /* 2: adds fathom_plan_fixed; 3: adds fathom_scan_topk */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -186,6 +186,33 @@ size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k);
 int fathom_topk(const float* scores, int64_t rows, int64_t n, int32_t k,
                 int32_t* indices, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * fathom_scan_topk — fathom_scan followed by fathom_topk on its scores, with
+ * the top-k candidates taken by the scan itself instead of by a second pass
+ * over the scores.
+ *
+ * Results are those of the two calls, bit for bit: scores as fathom_scan
+ * writes them, indices as fathom_topk selects them (§2 order, ascending).
+ * When n is a multiple of 65536 and the store takes the fast scan path
+ * (nb_store a multiple of 8 blocks, scales 16-byte aligned), the rounds of
+ * 2048 keys that fathom_topk samples are scanned first, the cut is set from
+ * their scores, and the other rounds write every score at or above the cut
+ * to a per-round candidate region as they are scanned; only the sampled
+ * rounds are read back.  Otherwise the two calls run as they are.
+ *
+ *   planes, scales, nb_store, depths, q, groups, G, d, n: as fathom_scan
+ *   scores  [groups][G][n] fp32 output (always written)
+ *   indices [groups * G][k] int32 output
+ *   workspace: device scratch of at least fathom_scan_topk_workspace_bytes(
+ *   groups, G, n, k) bytes, 256-byte aligned; contents on entry do not matter.
+ *   1 <= k <= n.
+ */
+size_t fathom_scan_topk_workspace_bytes(int64_t groups, int32_t G, int64_t n, int32_t k);
+int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                     const uint8_t* depths, const float* q, int64_t groups, int32_t G, int32_t d,
+                     int64_t n, int32_t k, float* scores, int32_t* indices, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* fathom_status_string(int status);

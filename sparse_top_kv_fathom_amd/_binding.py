@@ -34,6 +34,7 @@ STATUS = {
 }
 
 EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+            "fathom_scan_topk", "fathom_scan_topk_workspace_bytes",
             "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
 
 
@@ -61,11 +62,15 @@ def lib():
         L.fathom_scan.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P]
         L.fathom_topk.argtypes = [P, I64, I64, I32, P, P, SZ, P]
         L.fathom_topk_workspace_bytes.argtypes = [I64, I64, I32]
+        L.fathom_scan_topk.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, I32, P, P, P, SZ, P]
+        L.fathom_scan_topk_workspace_bytes.argtypes = [I64, I32, I64, I32]
+        L.fathom_scan_topk_workspace_bytes.restype = SZ
         L.fathom_topk_workspace_bytes.restype = SZ
         L.fathom_status_string.argtypes = [ctypes.c_int]
         L.fathom_status_string.restype = ctypes.c_char_p
         L.fathom_abi_version.argtypes = []
         for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+                  "fathom_scan_topk",
                   "fathom_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -187,6 +192,35 @@ def scan(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: to
         _stream(stream))
     _check(st, "fathom_scan")
     return scores
+
+
+def scan_topk_workspace(groups: int, G: int, n: int, k: int, device="cuda") -> torch.Tensor:
+    nbytes = int(lib().fathom_scan_topk_workspace_bytes(groups, G, n, k))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def scan_topk(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: torch.Tensor,
+              n: int, k: int, scores: torch.Tensor | None = None,
+              indices: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+              stream=None):
+    """fathom_scan_topk: (scores [groups][G][n] fp32, indices [groups*G][k] int32)."""
+    groups, G, d = q.shape
+    nb_store = planes.shape[-1]
+    ps, ss = store_shapes(groups, nb_store, d)
+    if scores is None:
+        scores = torch.empty((groups, G, n), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((groups * G, k), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = scan_topk_workspace(groups, G, n, k, q.device)
+    st = lib().fathom_scan_topk(
+        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+        nb_store, _dev(depths, "depths", torch.uint8, (groups, d)), _dev(q, "q", torch.float32),
+        groups, G, d, int(n), int(k), _dev(scores, "scores", torch.float32, (groups, G, n)),
+        _dev(indices, "indices", torch.int32, (groups * G, k)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, "fathom_scan_topk")
+    return scores, indices
 
 
 def topk_workspace_bytes(rows: int, n: int, k: int) -> int:

@@ -116,6 +116,36 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
                                        static_cast<hipStream_t>(stream)));
 }
 
+size_t fathom_scan_topk_workspace_bytes(int64_t groups, int32_t G, int64_t n, int32_t k) {
+  if (groups < 1 || groups > kMaxGroups || G < 1 || G > 8 || !valid_tokens(n) || k < 1 || k > n)
+    return 0;
+  return fathom::scan_topk_workspace_bytes(groups, G, n, k);
+}
+
+int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                     const uint8_t* depths, const float* q, int64_t groups, int32_t G, int32_t d,
+                     int64_t n, int32_t k, float* scores, int32_t* indices, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!planes || !scales || !depths || !q || !scores || !indices || !workspace)
+    return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups ||
+      !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < n / fathom::kBlock || nb_store >= kMaxTokens / fathom::kBlock)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (fathom::scan_max_workgroups(groups, n) > kMaxWorkgroups) return FATHOM_ERR_BAD_SHAPE;
+  if (k < 1 || k > n) return FATHOM_ERR_BAD_RANGE;
+  if (!aligned(planes, 8) || !aligned(scales, 4) || !aligned(q, 4) || !aligned(scores, 4) ||
+      !aligned(indices, 4) || !aligned(workspace, 256))
+    return FATHOM_ERR_ALIGNMENT;
+  if (workspace_bytes < fathom::scan_topk_workspace_bytes(groups, G, n, k))
+    return FATHOM_ERR_WORKSPACE;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_scan_topk(planes, scales, nb_store, depths, q, groups, G, n, k,
+                                            scores, indices, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k) {
   if (rows < 1 || n < 1 || n >= kMaxTokens || k < 1 || k > n) return 0;
   return fathom::topk_workspace_bytes(rows, n, k);

@@ -53,6 +53,7 @@
 // small tail kernel with per-block clamped loads, which also serves stores
 // whose offsets exceed 32 bits or whose scale rows are not 16-byte aligned.
 #include "fathom_internal.h"
+#include "topk_layout.h"
 
 // Compile-time tuning: SCAN_U1 = depth-1 channels per pipelined set,
 // SCAN_ROUNDS = rounds per workgroup, SCAN_TOUCHES = L2 touches per 256-byte
@@ -206,6 +207,78 @@ __device__ __forceinline__ void store_tile(const float (&acc)[kNB][G], float o, 
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
         __builtin_nontemporal_store(acc[b][h] + obh, out + h * n + b * kBlock + lane);
       }
+    }
+  }
+}
+
+// Scan with top-k candidate emission.  The row's rounds (kRoundBlocks blocks
+// = 2048 keys each) come in runs of 32; the first 4 of every run (one chunk
+// of 8192 keys in 8) are scanned first, their scores alone set the cut tau of
+// every row, and the other rounds then also write each score >= tau, as
+// (order key, index) in index order, to the round's region of the row's
+// candidate buffer (a round with more than its region holds flags the row).
+constexpr int kRunRounds = 32, kSampledRounds = 4;
+
+struct EmitCtx {
+  void* tws;        // top-k workspace, one row per (group, head)
+  int64_t n;
+  int64_t round;    // the workgroup's round in its row
+};
+
+// Candidates of a wave tile: 8 blocks x G heads; `tf` the cuts as floats.
+template <int G>
+__device__ __forceinline__ void emit_tile(const float (&acc)[kNB][G], float o, const float (&tf)[G],
+                                          int64_t grp, int64_t blk0, const EmitCtx& ec,
+                                          uint32_t (*s_emit)[8]) {
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t cnt[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) cnt[h] = 0u;
+#pragma unroll
+  for (int b = 0; b < kNB; ++b)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float obh = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
+      cnt[h] += (uint32_t)__popcll(__ballot(acc[b][h] + obh >= tf[h]));
+    }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_emit[wave][h] = cnt[h];
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    uint32_t slot = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = s_emit[w][h];
+      slot += w < wave ? c : 0u;
+      total += c;
+    }
+    const topk::RowWs rw = topk::row_ws(ec.tws, ec.n, kRoundBlocks * kBlock, grp * G + h);
+    const uint32_t base = (uint32_t)ec.round * rw.region;
+    if (wave == 0 && lane == 0) {
+      rw.seg[2 * ec.round] = base;
+      rw.seg[2 * ec.round + 1] = total;
+      if (total > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
+    }
+    if (cnt[h] == 0u) continue;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      const float obh = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
+      const float sc = acc[b][h] + obh;
+      const bool cand = sc >= tf[h];
+      const uint64_t m = __ballot(cand);
+      if (cand) {
+        const uint32_t sl = slot + (uint32_t)__popcll(m & below);
+        if (sl < rw.region)
+          reinterpret_cast<uint2*>(rw.cand)[base + sl] =
+              make_uint2(topk::order_key(sc), (uint32_t)((blk0 + b) * kBlock + lane));
+      }
+      slot += (uint32_t)__popcll(m);
     }
   }
 }
@@ -373,13 +446,18 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const S
   }
 }
 
-template <int G>
+// MODE 0: every round; 1: the sampled rounds of the candidate emission
+// (first kSampledRounds of every kRunRounds); 2: the other rounds, which also
+// emit candidates.  Modes 1 and 2 need kRounds == 1 and whole runs.
+template <int G, int MODE = 0>
 __global__ __launch_bounds__(kThreads) void scan_main(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t nrounds, int64_t n,
-    int64_t wgs_per_group, float* __restrict__ scores) {
+    int64_t wgs_per_group, float* __restrict__ scores, void* tws) {
   static_assert(kNB * G <= 64, "one lane per (block, head) in the offset fold");
+  static_assert(MODE == 0 || kRounds == 1, "candidate emission runs one round per workgroup");
   __shared__ MainShared<G> sh;
+  __shared__ uint32_t s_emit[kWaves][8];
 
   // XCD-aware remap of the workgroup id (bijective on [0, gridDim.x)).
   const uint32_t nwg = gridDim.x;
@@ -387,8 +465,20 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   uint32_t id = blockIdx.x;
   if (id < per_xcd * kXcds) id = (id % kXcds) * per_xcd + id / kXcds;
   const int64_t grp = id / wgs_per_group;
-  const int64_t round0 = (id % wgs_per_group) * kRounds;
-  const int nr = (int)min<int64_t>(kRounds, nrounds - round0);
+  int64_t round0 = (id % wgs_per_group) * kRounds;
+  if (MODE == 1)
+    round0 = (round0 / kSampledRounds) * kRunRounds + round0 % kSampledRounds;
+  else if (MODE == 2)
+    round0 = (round0 / (kRunRounds - kSampledRounds)) * kRunRounds + kSampledRounds +
+             round0 % (kRunRounds - kSampledRounds);
+  const int nr = kRounds > 1 ? (int)min<int64_t>(kRounds, nrounds - round0) : 1;
+  float tf[G];   // MODE 2: the rows' cuts as floats
+  if (MODE == 2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      tf[h] = topk::key_float(
+          topk::row_ws(tws, n, kRoundBlocks * kBlock, grp * G + h).st[topk::kS_TAU]);
+  }
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -482,6 +572,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
     store_tile<G>(acc, o, kNB - 1, n, scores_g + blk0 * kBlock);
+    if (MODE == 2) emit_tile<G>(acc, o, tf, grp, blk0, EmitCtx{tws, n, round0}, s_emit);
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
@@ -577,8 +668,9 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
   const int64_t nrounds = fast ? nblk / kRoundBlocks : 0;
   if (nrounds > 0) {
     const int64_t wgs = (nrounds + kRounds - 1) / kRounds;
-    hipLaunchKernelGGL(scan_main<G>, dim3((unsigned)(wgs * groups)), dim3(kThreads), 0, stream,
-                       planes, scales, nb_store, depths, q, nrounds, n, wgs, scores);
+    hipLaunchKernelGGL((scan_main<G, 0>), dim3((unsigned)(wgs * groups)), dim3(kThreads), 0,
+                       stream, planes, scales, nb_store, depths, q, nrounds, n, wgs, scores,
+                       (void*)nullptr);
   }
   const int64_t first = nrounds * kRoundBlocks;
   if (first < nblk) {
@@ -589,6 +681,32 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
 }
 
 }  // namespace
+
+template <int G>
+hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                              const uint8_t* depths, const float* q, int64_t groups, int64_t n,
+                              int k, float* scores, int32_t* indices, void* ws,
+                              hipStream_t stream) {
+  const int64_t rows = groups * G, R = (int64_t)kRoundBlocks * kBlock;
+  const int64_t nrounds = n / R;
+  const bool fused = kRounds == 1 && n % (R * kRunRounds) == 0 && nb_store <= kMaxFastBlocks &&
+                     nb_store % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  if (!fused) {   // the two calls one after the other
+    launch_scan_g<G>(planes, scales, nb_store, depths, q, groups, n, scores, stream);
+    return launch_topk(scores, rows, n, k, indices, ws, stream);
+  }
+  const int64_t nsampled = nrounds / kRunRounds * kSampledRounds;
+  hipLaunchKernelGGL((scan_main<G, 1>), dim3((unsigned)(nsampled * groups)), dim3(kThreads), 0,
+                     stream, planes, scales, nb_store, depths, q, nrounds, n, nsampled, scores, ws);
+  hipError_t e = launch_topk_rounds_cut(scores, rows, n, R, k, ws, stream);
+  if (e != hipSuccess) return e;
+  const int64_t nemit = nrounds - nsampled;
+  hipLaunchKernelGGL((scan_main<G, 2>), dim3((unsigned)(nemit * groups)), dim3(kThreads), 0,
+                     stream, planes, scales, nb_store, depths, q, nrounds, n, nemit, scores, ws);
+  return launch_topk_rounds_finish(scores, rows, n, R, kRunRounds, kSampledRounds, k, indices,
+                                   ws, stream);
+}
 
 int64_t scan_max_workgroups(int64_t groups, int64_t n) {
   const int64_t nblk = n / kBlock;
@@ -610,6 +728,35 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t n
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+size_t scan_topk_workspace_bytes(int64_t groups, int G, int64_t n, int k) {
+  const int64_t rows = groups * G;
+  const size_t a = topk_rounds_workspace_bytes(rows, n, (int64_t)kRoundBlocks * kBlock);
+  const size_t b = topk_workspace_bytes(rows, n, k);
+  return a > b ? a : b;
+}
+
+hipError_t launch_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                            const uint8_t* depths, const float* q, int64_t groups, int G,
+                            int64_t n, int k, float* scores, int32_t* indices, void* ws,
+                            hipStream_t stream) {
+  switch (G) {
+#define FATHOM_SCAN_TOPK_CASE(g)                                                                 \
+  case g:                                                                                        \
+    return launch_scan_topk_g<g>(planes, scales, nb_store, depths, q, groups, n, k, scores,     \
+                                 indices, ws, stream);
+    FATHOM_SCAN_TOPK_CASE(1)
+    FATHOM_SCAN_TOPK_CASE(2)
+    FATHOM_SCAN_TOPK_CASE(3)
+    FATHOM_SCAN_TOPK_CASE(4)
+    FATHOM_SCAN_TOPK_CASE(5)
+    FATHOM_SCAN_TOPK_CASE(6)
+    FATHOM_SCAN_TOPK_CASE(7)
+    FATHOM_SCAN_TOPK_CASE(8)
+#undef FATHOM_SCAN_TOPK_CASE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fathom

@@ -26,80 +26,22 @@
 // fit in LDS, the resolve workgroup does all of it alone, from the scores or
 // the regions: same result, many more passes.
 #include "fathom_internal.h"
+#include "topk_layout.h"
 
 namespace fathom {
 namespace {
+
+using namespace topk;
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerWg = kThreads / 64;
 constexpr int kPerThread = 32;                       // keys per thread in a chunk
 constexpr int kChunk = kThreads * kPerThread;        // 8192 keys per workgroup chunk
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
-constexpr int kBins = 2048;                          // radix digit: 11 bits
 constexpr int kSampleStride = 8;                     // every 8th chunk is sampled
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
 constexpr int kLdsCand = 16384;                      // candidates staged in LDS at most
-
-// Per-row workspace (32-bit words).
-enum : int {
-  kS_TAU = 0,       // candidate cut
-  kS_OVER,          // nonzero: a chunk had more candidates than its region
-  kS_NSAMPLE,       // keys in the sampled chunks
-  kS_T,             // the k-th largest key (set by the resolve)
-  kS_NEED,          // keys == T to take
-  kS_ORDER,         // 1: the ordered write is left to topk_order
-  kS_WORDS = 16
-};
-
-__host__ __device__ inline int64_t n_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
-
-// Candidate buffer capacity: n / 8, between 8192 and 65536 keys, shared
-// equally by the chunks (512 per chunk at n = 2^20).
-__host__ __device__ inline int64_t cand_cap(int64_t n) {
-  const int64_t c = n / 8;
-  return c < 8192 ? 8192 : (c > 65536 ? 65536 : c);
-}
-__host__ __device__ inline uint32_t region(int64_t n) { return (uint32_t)(cand_cap(n) / n_chunks(n)); }
-
-__host__ __device__ inline size_t row_words(int64_t n) {
-  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n);
-}
-
-struct RowWs {
-  uint32_t* hist;    // [kBins]: sample histogram
-  uint32_t* st;      // [kS_WORDS]
-  uint32_t* cand;    // [nchunks][region][2]: key, index
-  uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
-  uint32_t* ord;     // [nchunks][2]: keys > T and == T in the chunks before this one
-  uint32_t region;
-};
-
-__device__ inline RowWs row_ws(void* ws, int64_t n, int64_t row) {
-  uint32_t* p = reinterpret_cast<uint32_t*>(ws) + row_words(n) * row;
-  RowWs r;
-  r.region = region(n);
-  r.hist = p;
-  r.st = p + kBins;
-  r.cand = r.st + kS_WORDS;
-  r.seg = r.cand + 2 * (size_t)cand_cap(n);
-  r.ord = r.seg + 2 * (size_t)n_chunks(n);
-  return r;
-}
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// The float whose order key is `key`; keys below that of -inf map to -inf
-// and keys above that of +inf to a NaN, so `x >= key_float(key)` is
-// `order_key(x) >= key` for every finite x.
-__device__ __forceinline__ float key_float(uint32_t key) {
-  if (key <= 0x007fffffu) return -__builtin_inff();
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
 
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
@@ -228,8 +170,8 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t nee
 
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n) {
-  RowWs r = row_ws(ws, n, blockIdx.x);
+__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n, int64_t R) {
+  RowWs r = row_ws(ws, n, R, blockIdx.x);
   for (int i = threadIdx.x; i < kBins; i += kThreads) r.hist[i] = 0u;
   if (threadIdx.x < kS_WORDS) r.st[threadIdx.x] = 0u;
 }
@@ -249,35 +191,39 @@ __device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int6
       if (valid<F>(c0, i, c, n)) atomicAdd(&s_hist[order_key(V.v[i][c]) >> 21], 1u);
 }
 
+// Sampled keys: chunk blockIdx.x * stride of a row of `len` keys at
+// src + row * pitch (the score rows themselves, stride kSampleStride; or the
+// scan's sampled rounds, gathered, stride 1).
 __global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict__ scores,
-                                                        int64_t n, void* ws) {
+                                                        int64_t pitch, int64_t len, int stride,
+                                                        int64_t n, int64_t R, void* ws) {
   __shared__ uint32_t s_hist[kBins];
   const int64_t row = blockIdx.y;
-  RowWs r = row_ws(ws, n, row);
+  RowWs r = row_ws(ws, n, R, row);
   for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0u;
   __syncthreads();
-  const int64_t c0 = (int64_t)blockIdx.x * kSampleStride * kChunk;
-  const float* src = scores + row * n;
-  if (chunk_full(src, n, c0)) sample_chunk<true>(src, n, c0, s_hist);
-  else sample_chunk<false>(src, n, c0, s_hist);
+  const int64_t c0 = (int64_t)blockIdx.x * stride * kChunk;
+  const float* src = scores + row * pitch;
+  if (chunk_full(src, len, c0)) sample_chunk<true>(src, len, c0, s_hist);
+  else sample_chunk<false>(src, len, c0, s_hist);
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kThreads) {
     const uint32_t t = s_hist[b];
     if (t != 0u) atomicAdd(&r.hist[b], t);
   }
   if (threadIdx.x == 0)
-    atomicAdd(&r.st[kS_NSAMPLE], (uint32_t)min<int64_t>(kChunk, n - c0));
+    atomicAdd(&r.st[kS_NSAMPLE], (uint32_t)min<int64_t>(kChunk, len - c0));
 }
 
 // Per row: the cut tau.  With the whole row sampled the target is exactly k
 // (tau is the low edge of the bin holding the k-th largest key); otherwise
 // the sample's share of k is raised by a quarter plus 64 keys and tau is
 // placed inside that key's bin.
-__global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int k, void* ws) {
+__global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int64_t R, int k, void* ws) {
   __shared__ uint32_t s_tmp[kWavesPerWg];
   __shared__ uint32_t s_sel[2];
   constexpr int kPer = kBins / kThreads;
-  RowWs r = row_ws(ws, n, blockIdx.x);
+  RowWs r = row_ws(ws, n, R, blockIdx.x);
   const uint32_t ns = r.st[kS_NSAMPLE];
   uint32_t target = (uint32_t)k;
   if ((int64_t)ns < n) {
@@ -375,11 +321,77 @@ __global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict
                                                          int64_t n, void* ws) {
   __shared__ uint32_t s_cnt[kWavesPerWg];
   const int64_t row = blockIdx.y;
-  const RowWs r = row_ws(ws, n, row);
+  const RowWs r = row_ws(ws, n, kChunk, row);
   const int64_t c0 = (int64_t)blockIdx.x * kChunk;
   const float* src = scores + row * n;
   if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, r, s_cnt);
   else compact_chunk<false>(src, n, c0, r, s_cnt);
+}
+
+// The scan's sampled rounds (R keys each: the first `sampled` of every `run`
+// rounds of a row) read back from the scores: every key >= tau, in index
+// order, to that round's region, as compact_chunk does for a chunk.
+// Workgroup = one sampled round of one row; R / 256 keys per thread.
+template <int kPer>
+__global__ __launch_bounds__(kThreads) void topk_compact_rounds(const float* __restrict__ scores,
+                                                                int run, int sampled, int64_t n,
+                                                                int64_t R, void* ws) {
+  __shared__ uint32_t s_cnt[kWavesPerWg];
+  const int64_t row = blockIdx.y, j = blockIdx.x;
+  const int64_t rd = (j / sampled) * run + j % sampled;   // the round's index in the row
+  const RowWs r = row_ws(ws, n, R, row);
+  const float tauf = key_float(r.st[kS_TAU]);
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const float* src = scores + row * n + rd * R + wave * (64 * kPer);
+  float v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer / 4; ++i) {
+    const float4 x = *reinterpret_cast<const float4*>(src + (i * 64 + lane) * 4);
+    v[4 * i] = x.x;
+    v[4 * i + 1] = x.y;
+    v[4 * i + 2] = x.z;
+    v[4 * i + 3] = x.w;
+  }
+  uint32_t nw = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) nw += (uint32_t)__popcll(__ballot(v[e] >= tauf));
+  if (lane == 0) s_cnt[wave] = nw;
+  __syncthreads();
+  const uint32_t base = (uint32_t)rd * r.region;
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerWg; ++w) t += s_cnt[w];
+    r.seg[2 * rd] = base;
+    r.seg[2 * rd + 1] = t;
+    if (t > r.region) atomicOr(&r.st[kS_OVER], 1u);
+  }
+  if (nw != 0u) {
+    uint32_t slot = 0;
+    for (int w = 0; w < wave; ++w) slot += s_cnt[w];
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+      uint64_t m[4];
+      uint32_t sl = slot;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        m[c] = __ballot(v[4 * i + c] >= tauf);
+        sl += (uint32_t)__popcll(m[c] & below);
+        slot += (uint32_t)__popcll(m[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (v[4 * i + c] >= tauf) {
+          if (sl < r.region)
+            reinterpret_cast<uint2*>(r.cand)[base + sl] = make_uint2(
+                order_key(v[4 * i + c]),
+                (uint32_t)(rd * R + wave * (64 * kPer) + (i * 64 + lane) * 4 + c));
+          ++sl;
+        }
+      }
+    }
+  }
 }
 
 // The keys the one-workgroup path selects among: the candidate regions, or
@@ -388,7 +400,7 @@ struct ResolveSrc {
   const uint2* cand;      // (key, index) pairs, region per chunk
   const uint32_t* seg;
   const float* scores;
-  int64_t n, nc;
+  int64_t n, nc, R;       // keys, regions and keys per region of the row
   uint32_t region;
   bool direct;
 };
@@ -445,8 +457,8 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
         g(e.x, e.y, v);
       }
     } else {
-      const int64_t e = min<int64_t>(s.n, (c + 1) * kChunk);
-      for (int64_t i0 = c * kChunk; i0 < e; i0 += 64) {
+      const int64_t e = min<int64_t>(s.n, (c + 1) * s.R);
+      for (int64_t i0 = c * s.R; i0 < e; i0 += 64) {
         const int64_t i = i0 + lane;
         const bool v = i < e;
         g(v ? order_key(s.scores[i]) : 0u, (uint32_t)i, v);
@@ -461,7 +473,8 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
 // the chunks in parallel.  Other rows (the guess failed, or too many
 // candidates or chunks) are resolved and written here, by one workgroup.
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
-                                                                int64_t n, int k, void* ws,
+                                                                int64_t n, int64_t R, int k,
+                                                                void* ws,
                                                                 int32_t* __restrict__ out) {
   __shared__ uint32_t s_hist[2 * kBins];
   __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
@@ -470,13 +483,14 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
   const int64_t row = blockIdx.x;
-  RowWs r = row_ws(ws, n, row);
+  RowWs r = row_ws(ws, n, R, row);
   ResolveSrc src;
   src.cand = reinterpret_cast<const uint2*>(r.cand);
   src.seg = r.seg;
   src.scores = scores + row * n;
   src.n = n;
-  src.nc = n_chunks(n);
+  src.nc = n_chunks(n, R);
+  src.R = R;
   src.region = r.region;
   const int64_t nc = src.nc;
   int32_t* dst = out + row * (int64_t)k;
@@ -640,7 +654,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     });
   } else {
     for_each_key(src, [&](uint32_t key, uint32_t idx) {
-      const int g = (int)((int64_t)(idx / kChunk) / per_group);
+      const int g = (int)((int64_t)(idx / R) / per_group);
       if (key > T) atomicAdd(&s_gt[g], 1u);
       if (key == T) atomicAdd(&s_eq[g], 1u);
     });
@@ -684,10 +698,10 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 
 // Rows resolved in LDS: one wave per (chunk, row) writes the chunk's selected
 // indices in index order at the chunk's prefix position.
-__global__ __launch_bounds__(64) void topk_order(int64_t n, int k, const void* ws,
+__global__ __launch_bounds__(64) void topk_order(int64_t n, int64_t R, int k, const void* ws,
                                                  int32_t* __restrict__ out) {
   const int64_t row = blockIdx.y, c = blockIdx.x;
-  const RowWs r = row_ws(const_cast<void*>(ws), n, row);
+  const RowWs r = row_ws(const_cast<void*>(ws), n, R, row);
   if (r.st[kS_ORDER] == 0u) return;
   const uint32_t T = r.st[kS_T], need = r.st[kS_NEED];
   const uint32_t s0 = r.seg[2 * c], cnt = r.seg[2 * c + 1];
@@ -715,22 +729,57 @@ __global__ __launch_bounds__(64) void topk_order(int64_t n, int k, const void* w
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
   (void)k;
-  const size_t bytes = (size_t)rows * row_words(n) * sizeof(uint32_t);
+  const size_t bytes = (size_t)rows * row_words(n, kChunk) * sizeof(uint32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* ws, hipStream_t stream) {
-  const int64_t nc = n_chunks(n);
+  const int64_t R = kChunk, nc = n_chunks(n, R);
   const unsigned ns = (unsigned)((nc + kSampleStride - 1) / kSampleStride);
   const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
-  hipLaunchKernelGGL(topk_init, grid_rows, dim3(kThreads), 0, stream, ws, n);
-  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n, ws);
-  hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, k, ws);
+  hipLaunchKernelGGL(topk_init, grid_rows, dim3(kThreads), 0, stream, ws, n, R);
+  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
+                     n, kSampleStride, n, R, ws);
+  hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
-  hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, k, ws,
-                     indices);
-  hipLaunchKernelGGL(topk_order, grid_chunks, dim3(64), 0, stream, n, k, ws, indices);
+  hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
+                     ws, indices);
+  hipLaunchKernelGGL(topk_order, grid_chunks, dim3(64), 0, stream, n, R, k, ws, indices);
+  return hipGetLastError();
+}
+
+// Pieces of the selection for candidates the scan emits itself, per region
+// of R = 2048 keys (one scan round); the first `sampled` of every `run` rounds
+// are scanned first (the chunks of 8192 keys that the sample reads).
+size_t topk_rounds_workspace_bytes(int64_t rows, int64_t n, int64_t R) {
+  const size_t bytes = (size_t)rows * row_words(n, R) * sizeof(uint32_t);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+hipError_t launch_topk_rounds_cut(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
+                                  void* ws, hipStream_t stream) {
+  const int64_t nc = n_chunks(n, kChunk);
+  const unsigned ns = (unsigned)((nc + kSampleStride - 1) / kSampleStride);
+  hipLaunchKernelGGL(topk_init, dim3((unsigned)rows), dim3(kThreads), 0, stream, ws, n, R);
+  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
+                     n, kSampleStride, n, R, ws);
+  hipLaunchKernelGGL(topk_guess, dim3((unsigned)rows), dim3(kThreads), 0, stream, n, R, k, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rounds_finish(const float* scores, int64_t rows, int64_t n, int64_t R,
+                                     int run, int sampled, int k, int32_t* indices, void* ws,
+                                     hipStream_t stream) {
+  const int64_t nr = n / R;
+  if (R != 8 * kThreads || kChunk != sampled * R || run != kSampleStride * sampled)
+    return hipErrorInvalidValue;   // the sampled rounds are the sampled chunks
+  hipLaunchKernelGGL(topk_compact_rounds<8>, dim3((unsigned)(nr / run * sampled), (unsigned)rows),
+                     dim3(kThreads), 0, stream, scores, run, sampled, n, R, ws);
+  hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
+                     n, R, k, ws, indices);
+  hipLaunchKernelGGL(topk_order, dim3((unsigned)nr, (unsigned)rows), dim3(64), 0, stream, n, R, k,
+                     ws, indices);
   return hipGetLastError();
 }
 

@@ -1,0 +1,77 @@
+// Per-row workspace of the top-k selection, shared by the top-k kernels and
+// by the scan when it emits candidates itself.  Not part of the public ABI.
+#pragma once
+
+#include "fathom_internal.h"
+
+namespace fathom {
+namespace topk {
+
+constexpr int kBins = 2048;   // radix digit: 11 bits
+
+// Per-row workspace (32-bit words).
+enum : int {
+  kS_TAU = 0,       // candidate cut
+  kS_OVER,          // nonzero: a chunk had more candidates than its region
+  kS_NSAMPLE,       // keys in the sampled chunks
+  kS_T,             // the k-th largest key (set by the resolve)
+  kS_NEED,          // keys == T to take
+  kS_ORDER,         // 1: the ordered write is left to topk_order
+  kS_WORDS = 16
+};
+
+// Candidates are kept per region of R consecutive keys of a row: R = kChunk
+// when compacting from scores, the scan's round when the scan emits them.
+__host__ __device__ inline int64_t n_chunks(int64_t n, int64_t R) { return (n + R - 1) / R; }
+
+// Candidate buffer capacity: n / 8, between 8192 and 65536 keys, shared
+// equally by the chunks (512 per chunk at n = 2^20).
+__host__ __device__ inline int64_t cand_cap(int64_t n) {
+  const int64_t c = n / 8;
+  return c < 8192 ? 8192 : (c > 65536 ? 65536 : c);
+}
+__host__ __device__ inline uint32_t region(int64_t n, int64_t R) {
+  return (uint32_t)(cand_cap(n) / n_chunks(n, R));
+}
+
+__host__ __device__ inline size_t row_words(int64_t n, int64_t R) {
+  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n, R);
+}
+
+struct RowWs {
+  uint32_t* hist;    // [kBins]: sample histogram
+  uint32_t* st;      // [kS_WORDS]
+  uint32_t* cand;    // [nchunks][region][2]: key, index
+  uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
+  uint32_t* ord;     // [nchunks][2]: keys > T and == T in the chunks before this one
+  uint32_t region;
+};
+
+__device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t row) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(ws) + row_words(n, R) * row;
+  RowWs r;
+  r.region = region(n, R);
+  r.hist = p;
+  r.st = p + kBins;
+  r.cand = r.st + kS_WORDS;
+  r.seg = r.cand + 2 * (size_t)cand_cap(n);
+  r.ord = r.seg + 2 * (size_t)n_chunks(n, R);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The float whose order key is `key`; keys below that of -inf map to -inf
+// and keys above that of +inf to a NaN, so `x >= key_float(key)` is
+// `order_key(x) >= key` for every finite x.
+__device__ __forceinline__ float key_float(uint32_t key) {
+  if (key <= 0x007fffffu) return -__builtin_inff();
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+}  // namespace topk
+}  // namespace fathom

@@ -42,6 +42,7 @@ def _gpu_visible():
 def test_header_declares_the_calls():
     names = declared()
     for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+              "fathom_scan_topk", "fathom_scan_topk_workspace_bytes",
               "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
@@ -56,7 +57,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 2
+    assert L.fathom_abi_version() == 3
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
@@ -112,6 +113,39 @@ def test_plan_fixed_validation(L):
     assert p(P(2), None, 1, 4, 128, SPARQ, 16, FAKE, None) == ALIGN
     assert p(None, None, 1, 4, 128, UNIFORM, 2, FAKE, None) == NO_DEVICE
     assert p(FAKE, None, 1, 4, 128, SPARQ, 16, FAKE, None) == NO_DEVICE
+
+
+def test_scan_topk_validation(L):
+    L.fathom_scan_topk.argtypes = [P, P, ctypes.c_int64, P, P, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, P,
+                                   ctypes.c_size_t, P]
+    L.fathom_scan_topk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64,
+                                                   ctypes.c_int32]
+    L.fathom_scan_topk_workspace_bytes.restype = ctypes.c_size_t
+    need = L.fathom_scan_topk_workspace_bytes(2, 4, 1 << 17, 256)
+    assert need >= L.fathom_topk_workspace_bytes(8, 1 << 17, 256) > 0
+    assert L.fathom_scan_topk_workspace_bytes(2, 4, 1 << 17, 0) == 0
+    assert L.fathom_scan_topk_workspace_bytes(2, 9, 1 << 17, 1) == 0
+    f = L.fathom_scan_topk
+    args = [FAKE, FAKE, 2048, FAKE, FAKE, 2, 4, 128, 1 << 17, 256, FAKE, FAKE, FAKE, need, None]
+    for i in (0, 1, 3, 4, 10, 11, 12):
+        a = list(args)
+        a[i] = None
+        assert f(*a) == NULL_ARG, i
+    for i, v in ((6, 9), (7, 64), (8, 1000), (2, 100)):
+        a = list(args)
+        a[i] = v
+        assert f(*a) == BAD_SHAPE, (i, v)
+    a = list(args)
+    a[9] = 0
+    assert f(*a) == BAD_RANGE
+    a = list(args)
+    a[12] = P((1 << 20) + 64)
+    assert f(*a) == ALIGN
+    a = list(args)
+    a[13] = need - 1
+    assert f(*a) == WORKSPACE
+    assert f(*args) == NO_DEVICE
 
 
 def test_scan_validation(L):

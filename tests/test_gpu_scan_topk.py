@@ -180,3 +180,40 @@ def test_fixed_plans_through_the_scan(fk, mode, param):
     assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
     oi = oracle.topk(ref.reshape(-1, n), k)
     assert np.array_equal(gi, oi), first_mismatch(gi, oi)
+
+
+def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None):
+    """fathom_scan_topk against the oracle's scan and top-k."""
+    ins = fathom_inputs.make_inputs(groups, 4, n, seed=seed)
+    planes, scales = fk.encode(to_dev(ins.k))
+    if depths is None:
+        dd = fk.plan(to_dev(ins.q), to_dev(ins.var), budget)
+        od, _, _ = oracle.plan(ins.q, ins.var, budget)
+    else:
+        dd = to_dev(depths)
+        od = depths
+    scores, idx = fk.scan_topk(planes, scales, dd, to_dev(ins.q), n, k)
+    gsc, gi = to_host(scores), to_host(idx)
+    op, os_, _ = oracle.encode(ins.k)
+    ref = oracle.scan_ref32(op, os_, od, ins.q, n)
+    assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
+    oi = oracle.topk(ref.reshape(-1, n), k)
+    assert np.array_equal(gi, oi), first_mismatch(gi, oi)
+
+
+@pytest.mark.parametrize("groups,n,k", [(2, 1 << 17, 512), (3, 1 << 16, 64), (1, 1 << 18, 4096),
+                                        (2, 3 * 4096, 100), (1, 65536 + 2048, 300)])
+def test_scan_topk_matches_scan_then_topk(fk, groups, n, k):
+    """Fused (n a multiple of 65536) and unfused (other n) paths."""
+    say("scan_topk groups=%d n=%d k=%d" % (groups, n, k))
+    _scan_topk_case(fk, groups, n, k, 92, seed=90 + groups)
+
+
+def test_scan_topk_heavy_ties_fall_back(fk):
+    """One active channel at depth 1: every score takes one of two values per
+    block, so the candidate regions overflow and rows take the direct path."""
+    n, k = 1 << 17, 1000
+    depths = np.zeros((2, 128), dtype=np.uint8)
+    depths[:, 5] = 1
+    say("scan_topk heavy ties")
+    _scan_topk_case(fk, 2, n, k, 0, seed=97, depths=depths)
