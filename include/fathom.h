@@ -43,17 +43,18 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 3   /* 2: adds fathom_plan_fixed; 3: adds fathom_scan_topk */
+#define FATHOM_ABI_VERSION 4   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather */
 
 enum fathom_status {
   FATHOM_OK = 0,
   FATHOM_ERR_NULL_ARG = -1,        /* a required pointer is NULL            */
   FATHOM_ERR_BAD_SHAPE = -2,       /* d, G, n, groups or strides invalid    */
-  FATHOM_ERR_BAD_RANGE = -3,       /* k or budget outside its range         */
+  FATHOM_ERR_BAD_RANGE = -3,       /* k, budget or plan parameter invalid   */
   FATHOM_ERR_WORKSPACE = -4,       /* workspace smaller than required       */
   FATHOM_ERR_HIP = -5,             /* a HIP launch or runtime call failed   */
   FATHOM_ERR_NO_DEVICE = -6,       /* no HIP device is visible              */
-  FATHOM_ERR_ALIGNMENT = -7        /* a pointer lacks its required alignment */
+  FATHOM_ERR_ALIGNMENT = -7,       /* a pointer lacks its required alignment */
+  FATHOM_ERR_NOT_PINNED = -8       /* host memory the device cannot address  */
 };
 
 /* Number of bit planes per channel and tokens per block (fixed by §3.2). */
@@ -213,6 +214,28 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_
                      const uint8_t* depths, const float* q, int64_t groups, int32_t G, int32_t d,
                      int64_t n, int32_t k, float* scores, int32_t* indices, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * fathom_gather — copy the runs a plan reads from a host-resident store into
+ * the device store (§3.6: the first t_j planes of channel j are one run of
+ * t_j * n / 8 bytes; Fig. 10: contiguous copies run at the link rate).
+ *
+ * For every group and channel with t_j > 0: planes p < t_j and the scale row,
+ * blocks [0, n/64), from host_planes / host_scales to planes / scales at the
+ * same positions.  Nothing else of the device store is written (the scan
+ * never reads it).  The depths stay in device memory: no host round trip.
+ *
+ *   host_planes, host_scales: store layout of fathom_encode, in pinned host
+ *     memory the device can address (hipHostMalloc; torch pin_memory)
+ *   planes, scales: device store of the same nb_store
+ *   depths [groups][d] uint8 (device)
+ *   nb_store a multiple of 8 blocks; all four store pointers 16-byte aligned.
+ *   FATHOM_ERR_NOT_PINNED if the host store is not memory the device can
+ *   address.
+ */
+int fathom_gather(const uint64_t* host_planes, const uint16_t* host_scales, int64_t nb_store,
+                  const uint8_t* depths, int64_t groups, int32_t d, int64_t n, uint64_t* planes,
+                  uint16_t* scales, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* fathom_status_string(int status);

@@ -7,7 +7,7 @@ libfathom.so (include/fathom.h); this package is a thin ctypes binding that
 takes torch device tensors.  Importing a call loads the library and raises if
 it has not been built.
 """
-_EXPORTS = ("encode", "plan", "plan_fixed", "PLAN_MODES", "scan", "scan_topk", "scan_topk_workspace", "topk", "topk_workspace_bytes", "topk_workspace",
+_EXPORTS = ("encode", "plan", "plan_fixed", "PLAN_MODES", "scan", "scan_topk", "scan_topk_workspace", "gather", "topk", "topk_workspace_bytes", "topk_workspace",
             "empty_store", "store_shapes", "FathomError", "lib", "STATUS", "EXPORTED")
 
 __all__ = list(_EXPORTS)

@@ -34,7 +34,7 @@ STATUS = {
 }
 
 EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
-            "fathom_scan_topk", "fathom_scan_topk_workspace_bytes",
+            "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
             "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
 
 
@@ -65,12 +65,13 @@ def lib():
         L.fathom_scan_topk.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, I32, P, P, P, SZ, P]
         L.fathom_scan_topk_workspace_bytes.argtypes = [I64, I32, I64, I32]
         L.fathom_scan_topk_workspace_bytes.restype = SZ
+        L.fathom_gather.argtypes = [P, P, I64, P, I64, I32, I64, P, P, P]
         L.fathom_topk_workspace_bytes.restype = SZ
         L.fathom_status_string.argtypes = [ctypes.c_int]
         L.fathom_status_string.restype = ctypes.c_char_p
         L.fathom_abi_version.argtypes = []
         for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
-                  "fathom_scan_topk",
+                  "fathom_scan_topk", "fathom_gather",
                   "fathom_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -192,6 +193,26 @@ def scan(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: to
         _stream(stream))
     _check(st, "fathom_scan")
     return scores
+
+
+def gather(host_planes: torch.Tensor, host_scales: torch.Tensor, depths: torch.Tensor, n: int,
+           planes: torch.Tensor, scales: torch.Tensor, stream=None):
+    """fathom_gather: the runs `depths` reads, blocks [0, n/64), from a pinned
+    host store into the device store (same layout)."""
+    groups, d, _, nb_store = planes.shape
+    ps, ss = store_shapes(groups, nb_store, d)
+    for t, name in ((host_planes, "host_planes"), (host_scales, "host_scales")):
+        if t.is_cuda or not t.is_pinned() or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous pinned host tensor" % name)
+    if tuple(host_planes.shape) != ps or tuple(host_scales.shape) != ss:
+        raise ValueError("host store shapes must match the device store")
+    st = lib().fathom_gather(
+        ctypes.c_void_p(host_planes.data_ptr()), ctypes.c_void_p(host_scales.data_ptr()), nb_store,
+        _dev(depths, "depths", torch.uint8, (groups, d)), groups, d, int(n),
+        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+        _stream(stream))
+    _check(st, "fathom_gather")
+    return planes, scales
 
 
 def scan_topk_workspace(groups: int, G: int, n: int, k: int, device="cuda") -> torch.Tensor:

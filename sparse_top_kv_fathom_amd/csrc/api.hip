@@ -44,6 +44,7 @@ const char* fathom_status_string(int status) {
     case FATHOM_ERR_HIP: return "FATHOM_ERR_HIP: a HIP launch or runtime call failed";
     case FATHOM_ERR_NO_DEVICE: return "FATHOM_ERR_NO_DEVICE: no HIP device is visible";
     case FATHOM_ERR_ALIGNMENT: return "FATHOM_ERR_ALIGNMENT: a pointer lacks its required alignment";
+    case FATHOM_ERR_NOT_PINNED: return "FATHOM_ERR_NOT_PINNED: host memory is not pinned for the device";
     default: return "FATHOM_ERR_UNKNOWN";
   }
 }
@@ -114,6 +115,37 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
   if (int s = device_ready()) return s;
   return to_status(fathom::launch_scan(planes, scales, nb_store, depths, q, groups, G, n, scores,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int fathom_gather(const uint64_t* host_planes, const uint16_t* host_scales, int64_t nb_store,
+                  const uint8_t* depths, int64_t groups, int32_t d, int64_t n, uint64_t* planes,
+                  uint16_t* scales, void* stream) {
+  if (!host_planes || !host_scales || !depths || !planes || !scales) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || groups < 1 || groups > kMaxGroups || !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < n / fathom::kBlock || nb_store >= kMaxTokens / fathom::kBlock || nb_store % 8 != 0)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(host_planes, 16) || !aligned(host_scales, 16) || !aligned(planes, 16) ||
+      !aligned(scales, 16))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  // The host store must be pinned memory the device can address; its device
+  // addresses are used.
+  const void* dev_src[2] = {nullptr, nullptr};
+  const void* host_src[2] = {host_planes, host_scales};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, host_src[i]);
+    if (e != hipSuccess || attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) {
+      (void)hipGetLastError();
+      return FATHOM_ERR_NOT_PINNED;
+    }
+    dev_src[i] = attr.devicePointer;
+  }
+  return to_status(fathom::launch_gather(static_cast<const uint64_t*>(dev_src[0]),
+                                         static_cast<const uint16_t*>(dev_src[1]), nb_store,
+                                         depths, groups, n, planes, scales,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 size_t fathom_scan_topk_workspace_bytes(int64_t groups, int32_t G, int64_t n, int32_t k) {

@@ -44,6 +44,9 @@ hipError_t launch_scan_topk(const uint64_t* planes, const uint16_t* scales, int6
                             const uint8_t* depths, const float* q, int64_t groups, int G,
                             int64_t n, int k, float* scores, int32_t* indices, void* ws,
                             hipStream_t stream);
+hipError_t launch_gather(const uint64_t* hplanes, const uint16_t* hscales, int64_t nb_store,
+                         const uint8_t* depths, int64_t groups, int64_t n, uint64_t* planes,
+                         uint16_t* scales, hipStream_t stream);
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* workspace, hipStream_t stream);
 

@@ -42,7 +42,7 @@ def _gpu_visible():
 def test_header_declares_the_calls():
     names = declared()
     for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
-              "fathom_scan_topk", "fathom_scan_topk_workspace_bytes",
+              "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
               "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
@@ -57,8 +57,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 3
-    for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN):
+    assert L.fathom_abi_version() == 4
+    for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
     assert L.fathom_status_string(12345).decode() == "FATHOM_ERR_UNKNOWN"
@@ -146,6 +146,25 @@ def test_scan_topk_validation(L):
     a[13] = need - 1
     assert f(*a) == WORKSPACE
     assert f(*args) == NO_DEVICE
+
+
+def test_gather_validation(L):
+    L.fathom_gather.argtypes = [P, P, ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32,
+                                ctypes.c_int64, P, P, P]
+    g = L.fathom_gather
+    args = [FAKE, FAKE, 64, FAKE, 2, 128, 4096, FAKE, FAKE, None]
+    for i in (0, 1, 3, 7, 8):
+        a = list(args)
+        a[i] = None
+        assert g(*a) == NULL_ARG, i
+    for i, v in ((2, 60), (2, 63), (5, 64), (4, 0), (6, 100)):
+        a = list(args)
+        a[i] = v
+        assert g(*a) == BAD_SHAPE, (i, v)
+    a = list(args)
+    a[0] = P((1 << 20) + 8)
+    assert g(*a) == ALIGN
+    assert g(*args) == NO_DEVICE
 
 
 def test_scan_validation(L):
