@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip timing fathom_gather from a pinned host store")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print rocprofv3 csv output under DIR as text and exit (no GPU use)")
     return ap.parse_args()
@@ -254,6 +256,49 @@ def main():
     torch.cuda.synchronize()
     fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
 
+    # fathom_gather: the runs each step's plan reads, copied from a pinned host
+    # copy of the store into a device store (outside the step: the store the
+    # step scans is resident).
+    gather = None
+    if not args.no_gather:
+        hp = stores[0][0].view(torch.int64).cpu().pin_memory().view(torch.uint64)
+        hs = stores[0][1].view(torch.int16).cpu().pin_memory().view(torch.uint16)
+        gp, gs = fk.empty_store(H, nb, dev)
+        gdep = [fk.plan(q_d[i % args.queries], var_d, B) for i in range(args.steps)]
+        for i in range(2):
+            fk.gather(hp, hs, gdep[i], n, gp, gs)
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            gev[i][0].record()
+            fk.gather(hp, hs, gdep[i], n, gp, gs)
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
+        g_bytes = float(np.mean([(lambda T, A: (T * nb * 8 + A * nb * 2).sum())(
+            *plan_stats(x.cpu().numpy())) for x in gdep]))
+        # The host link's own rate: one contiguous pinned-to-device copy of
+        # the same byte count.
+        nbytes = int(g_bytes) // 8 * 8
+        src = hp.view(torch.int64).view(-1)[: nbytes // 8]
+        dst = gp.view(torch.int64).view(-1)[: nbytes // 8]
+        dst.copy_(src, non_blocking=True)
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        cev[0].record()
+        for _ in range(args.steps):
+            dst.copy_(src, non_blocking=True)
+        cev[1].record()
+        torch.cuda.synchronize()
+        c_ms = cev[0].elapsed_time(cev[1]) / args.steps
+        gather = {"ms": round(g_ms, 4), "bytes_per_call": int(g_bytes),
+                  "host_GBps": round(g_bytes / (g_ms / 1e3) / 1e9, 2),
+                  "contiguous_copy_GBps": round(nbytes / (c_ms / 1e3) / 1e9, 2),
+                  "source": "pinned host store, all %d groups" % H}
+        del src, dst
+        del hp, hs, gp, gs
+
     # Algorithmic work of each timed step's scan (plans recomputed after timing).
     Ts, As = [], []
     for s in range(args.steps):
@@ -317,6 +362,7 @@ def main():
         "stages_ms": {"encode_block": round(stage_ms[0], 4), "plan": round(stage_ms[1], 4),
                       "scan": round(stage_ms[2], 4), "topk": round(stage_ms[3], 4)},
         "fused_scan_topk_ms": round(fused_ms, 4),
+        "gather_from_host": gather,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "plan": {"code_bits_mean": float(Ts.mean()), "active_channels_mean": float(As.mean()),
                  "total_bits_per_key_mean": float((Ts + As / 4.0).mean())},

@@ -13,10 +13,16 @@
  *   fathom_scan   : planes, depths, q group -> approximate scores   (§3.3, §7)
  *   fathom_topk   : scores, k -> top-k key indices per query head   (§2)
  *
+ * and around them: fathom_plan_fixed (the fixed-depth reads the pages
+ * compare against, §2 and §5), fathom_scan_topk (scan and selection in one
+ * call) and fathom_gather (the runs a plan reads, from a host-resident store,
+ * §3.6).
+ *
  * Conventions shared by every call
- *   - Every data pointer is a DEVICE pointer owned by the caller.  The
- *     library allocates nothing, keeps no pointer after a call returns and
- *     holds no state between calls.
+ *   - Every data pointer is a DEVICE pointer owned by the caller, except the
+ *     host store of fathom_gather (pinned host memory).  The library
+ *     allocates nothing, keeps no pointer after a call returns and holds no
+ *     state between calls.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; no call synchronises the host
  *     with the device.  Calls are reentrant; calls on different streams are
