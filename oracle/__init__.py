@@ -5,8 +5,10 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 its Python binding) never imports, links or calls anything here, and this
 package never imports the product.
 
-The arithmetic lives in ``fathom_oracle.c`` (plain C, fp64 except for the one
-fp32 evaluation order reproduced on purpose).  This module compiles it with
+The arithmetic lives in ``fathom_oracle.c`` (plain C, fp64 except for the
+fp32 evaluation orders reproduced on purpose: the scan's, and the rotation
+folds of the KLT-rotated store) and, for the KLT fit, in numpy fp64 with its
+symmetric eigensolver.  This module compiles it with
 gcc on first use and wraps it for numpy arrays.  Each wrapper names the
 passage of "Fathom: Per-Query Read Depth for Sparse Decoding over Offloaded KV
 Caches" (papers.paperslantern.ai/papers/2609.17652 and the jaehun.me review)
@@ -79,6 +81,10 @@ def _load():
         lib.fo_scan_ref32.restype = None
         lib.fo_topk.argtypes = [P, I64, I64, I, P, I]
         lib.fo_topk.restype = None
+        lib.fo_klt_rotate.argtypes = [P, P, P, I64, I64, I, P, I]
+        lib.fo_klt_rotate.restype = None
+        lib.fo_klt_rotate_q.argtypes = [P, P, I64, I, I, P]
+        lib.fo_klt_rotate_q.restype = None
         lib.fo_max_threads.argtypes = []
         lib.fo_max_threads.restype = I
         _lib = lib
@@ -281,3 +287,78 @@ def topk(scores: np.ndarray, k: int, nthreads: int = 0) -> np.ndarray:
     idx = np.zeros((rows, k), dtype=np.int32)
     _load().fo_topk(_ptr(s2), rows, n, int(k), _ptr(idx), int(nthreads or max_threads()))
     return idx
+
+
+# ---------------------------------------------------------------------------
+# KLT-rotated store (§3.5 "rotated variant"; Appendix D's calibration-free fit)
+# ---------------------------------------------------------------------------
+
+def klt_order_and_sign(lam: np.ndarray, V: np.ndarray):
+    """Canonical eigenbasis: columns by eigenvalue descending (equal values
+    keep their incoming order); in each column the first component of
+    magnitude at least 1/(2 sqrt(d)) made positive (a unit vector always has
+    one; a threshold well below the largest magnitude keeps the choice stable
+    when several components are nearly equal); eigenvalues below 0, which a
+    covariance cannot have, read as 0."""
+    order = np.argsort(-lam, kind="stable")
+    lam = np.maximum(lam[order], 0.0)
+    V = V[:, order].copy()
+    thr = 0.5 / np.sqrt(V.shape[0])
+    for j in range(V.shape[1]):
+        r = int(np.argmax(np.abs(V[:, j]) >= thr))
+        if V[r, j] < 0:
+            V[:, j] = -V[:, j]
+    return lam, V
+
+
+def klt_fit(k_f16: np.ndarray):
+    """Per group: mean mu, covariance C = (k - mu)^T (k - mu) / (n - 1) of the
+    binary16 keys, in fp64, and its eigenpairs (numpy's symmetric
+    eigensolver), canonically ordered and signed.  The pages build the
+    rotated store from the eigenbasis of the keys' covariance with its
+    eigenvalues as the channel variances (§3.5), fitted once on calibration
+    keys or, in the calibration-free variant, on the session's own keys
+    (Appendix D).  Returns (mu [groups][d], V [groups][d][d] with eigenvector
+    j in column j, lam [groups][d]), all fp64."""
+    k = np.asarray(k_f16, dtype=np.float16)
+    groups, n, d = k.shape
+    mu = np.empty((groups, d))
+    V = np.empty((groups, d, d))
+    lam = np.empty((groups, d))
+    for g in range(groups):
+        x = k[g].astype(np.float64)
+        mu[g] = x.sum(axis=0) / n
+        xc = x - mu[g]
+        C = (xc.T @ xc) / (n - 1)
+        w, E = np.linalg.eigh(C)
+        lam[g], V[g] = klt_order_and_sign(w, E)
+    return mu, V, lam
+
+
+def klt_rotate_keys(k_f16: np.ndarray, mu32: np.ndarray, V32: np.ndarray, nthreads: int = 0,
+                    raw: bool = False):
+    """Rotated keys (k - mu) V (§3.5), the fp32 fold of fo_klt_rotate rounded
+    to binary16 nearest-even: the input of encode in the rotated variant.
+    raw=True returns the fp32 fold before rounding."""
+    k = np.ascontiguousarray(np.asarray(k_f16, dtype=np.float16))
+    groups, n, d = k.shape
+    mu = np.ascontiguousarray(mu32, dtype=np.float32)
+    V = np.ascontiguousarray(V32, dtype=np.float32)
+    assert mu.shape == (groups, d) and V.shape == (groups, d, d)
+    out = np.empty((groups, n, d), dtype=np.float32)
+    _load().fo_klt_rotate(_ptr(k.view(np.uint16)), _ptr(mu), _ptr(V), groups, n, d, _ptr(out),
+                          nthreads or max_threads())
+    return out if raw else out.astype(np.float16)
+
+
+def klt_rotate_queries(q: np.ndarray, V32: np.ndarray):
+    """Rotated queries q V (§3.5: the importance becomes sum_h ((q_h V)_j)^2
+    lambda_j, i.e. the plan of the rotated queries with lambda as the
+    variances), the fp32 fold of fo_klt_rotate_q."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    groups, G, d = q.shape
+    V = np.ascontiguousarray(V32, dtype=np.float32)
+    assert V.shape == (groups, d, d)
+    out = np.empty_like(q)
+    _load().fo_klt_rotate_q(_ptr(q), _ptr(V), groups, G, d, _ptr(out))
+    return out

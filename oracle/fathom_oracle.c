@@ -389,6 +389,57 @@ void fo_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* idx,
   (void)nthreads;
 }
 
+/* ------------------------------------------------------------------------ */
+/* KLT-rotated store (§3.5; calibration-free fit in Appendix D)              */
+/* ------------------------------------------------------------------------ */
+
+/* Rotated key coordinates, the store's input in the rotated variant: the
+ * planes hold codes of (k - mu) V instead of k.  For each token i and output
+ * coordinate j, in fp32:
+ *   d_c  = fl32(k_ic - mu_c)                      (k_ic binary16, exact in fp32)
+ *   acc  = +0;  for c = 0 .. d-1 ascending: acc = fmaf(d_c, V[c][j], acc)
+ * k [groups][n][d] binary16 bits, mu [groups][d], V [groups][d][d] (row c,
+ * column j), out [groups][n][d] fp32 (the caller rounds it to binary16,
+ * nearest-even). */
+void fo_klt_rotate(const uint16_t* k, const float* mu, const float* V, int64_t groups,
+                   int64_t n, int d, float* out, int nthreads) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+#endif
+  for (int64_t gi = 0; gi < groups * n; ++gi) {
+    int64_t g = gi / n;
+    const uint16_t* row = k + gi * d;
+    const float* m = mu + g * d;
+    const float* Vg = V + g * (int64_t)d * d;
+    float* dst = out + gi * d;
+    float* dc = (float*)malloc(sizeof(float) * (size_t)d);
+    for (int c = 0; c < d; ++c) dc[c] = (float)fo_f16_to_f64(row[c]) - m[c];
+    for (int j = 0; j < d; ++j) {
+      float acc = 0.0f;
+      for (int c = 0; c < d; ++c) acc = fmaf(dc[c], Vg[(int64_t)c * d + j], acc);
+      dst[j] = acc;
+    }
+    free(dc);
+  }
+  (void)nthreads;
+}
+
+/* Rotated queries q V, the same fold without a mean:
+ *   acc = +0;  for c ascending: acc = fmaf(q_hc, V[c][j], acc).
+ * q [groups][G][d] fp32 -> out [groups][G][d] fp32. */
+void fo_klt_rotate_q(const float* q, const float* V, int64_t groups, int G, int d, float* out) {
+  for (int64_t g = 0; g < groups; ++g)
+    for (int h = 0; h < G; ++h) {
+      const float* qh = q + (g * G + h) * d;
+      const float* Vg = V + g * (int64_t)d * d;
+      for (int j = 0; j < d; ++j) {
+        float acc = 0.0f;
+        for (int c = 0; c < d; ++c) acc = fmaf(qh[c], Vg[(int64_t)c * d + j], acc);
+        out[(g * G + h) * d + j] = acc;
+      }
+    }
+}
+
 int fo_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
