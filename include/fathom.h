@@ -15,8 +15,8 @@
  *
  * and around them: fathom_plan_fixed (the fixed-depth reads the pages
  * compare against, §2 and §5), fathom_scan_topk (scan and selection in one
- * call) and fathom_gather (the runs a plan reads, from a host-resident store,
- * §3.6).
+ * call), fathom_gather (the runs a plan reads, from a host-resident store,
+ * §3.6) and fathom_klt_* (the rotated store of §3.5).
  *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer owned by the caller, except the
@@ -49,7 +49,8 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 4   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather */
+#define FATHOM_ABI_VERSION 5   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
+                                  5: fathom_klt_* */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -242,6 +243,50 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_
 int fathom_gather(const uint64_t* host_planes, const uint16_t* host_scales, int64_t nb_store,
                   const uint8_t* depths, int64_t groups, int32_t d, int64_t n, uint64_t* planes,
                   uint16_t* scales, void* stream);
+
+/*
+ * The KLT-rotated store (§3.5 "rotated variant"; the calibration-free fit of
+ * Appendix D).  For keys whose variance is not concentrated in few raw
+ * channels the store holds the planes of (k - mu) V, V the eigenbasis of the
+ * keys' covariance, and the plan uses g_j = sum_h ((q_h V)_j)^2 lambda_j.
+ * With these calls the rotated variant is
+ *   fathom_klt_fit -> fathom_klt_rotate_keys -> fathom_encode     (store)
+ *   fathom_klt_rotate_queries -> fathom_plan(q V, lambda) -> fathom_scan(q V)
+ * and its scores are q . (k - mu) up to the quantisation: the per-row
+ * constant q . mu is left out (it moves no key across the top-k boundary).
+ *
+ * fathom_klt_fit — per group: mu_c = mean of the n binary16 keys of channel
+ * c; C = (k - mu)^T (k - mu) / (n - 1), all in fp64 (sum order unspecified);
+ * its eigenpairs by cyclic Jacobi (fp64 covariance, fp32 accumulated
+ * rotation), eigenvalues descending (equal values: lower Jacobi index
+ * first), each eigenvector signed so its first component of magnitude at
+ * least 1/(2 sqrt(d)) is positive; eigenvalues below 0 read as 0.
+ *   k      [groups][n][d] binary16 (16-byte aligned), n >= 64, n % 64 == 0
+ *   mu     [groups][d]    fp32 output
+ *   basis  [groups][d][d] fp32 output, eigenvector j in column j (row c =
+ *          raw channel c)
+ *   lambda [groups][d]    fp32 output (the rotated channels' variances)
+ *   workspace: device scratch of fathom_klt_fit_workspace_bytes(groups, n, d)
+ *          bytes, 256-byte aligned (0 from the query for invalid shapes).
+ *
+ * fathom_klt_rotate_keys — k_rot[g][i][j] = binary16 (nearest-even) of the
+ * fp32 fold over c = 0 .. d-1 ascending, from +0, of
+ * fma(fl32(k_ic - mu_c), basis[c][j], acc).  k, k_rot 16-byte aligned,
+ * basis 16-byte aligned.  |k_rot| beyond the binary16 range gives Inf, which
+ * fathom_encode then flags.
+ *
+ * fathom_klt_rotate_queries — q_rot[g][h][j] = the fp32 fold over c
+ * ascending, from +0, of fma(q_hc, basis[c][j], acc).  q, q_rot
+ * [groups][G][d] fp32.
+ */
+size_t fathom_klt_fit_workspace_bytes(int64_t groups, int64_t n, int32_t d);
+int fathom_klt_fit(const uint16_t* k, int64_t groups, int64_t n, int32_t d, float* mu,
+                   float* basis, float* lambda, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int fathom_klt_rotate_keys(const uint16_t* k, const float* mu, const float* basis,
+                           int64_t groups, int64_t n, int32_t d, uint16_t* k_rot, void* stream);
+int fathom_klt_rotate_queries(const float* q, const float* basis, int64_t groups, int32_t G,
+                              int32_t d, float* q_rot, void* stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* fathom_status_string(int status);

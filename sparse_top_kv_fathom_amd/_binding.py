@@ -1,4 +1,4 @@
-"""ctypes binding of libfathom.so: the four calls of include/fathom.h.
+"""ctypes binding of libfathom.so: the calls of include/fathom.h.
 
 Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity, their data pointers and torch's current HIP stream are passed to
@@ -31,10 +31,13 @@ STATUS = {
     -5: "FATHOM_ERR_HIP",
     -6: "FATHOM_ERR_NO_DEVICE",
     -7: "FATHOM_ERR_ALIGNMENT",
+    -8: "FATHOM_ERR_NOT_PINNED",
 }
 
 EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
             "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
+            "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
+            "fathom_klt_rotate_queries",
             "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
 
 
@@ -66,13 +69,18 @@ def lib():
         L.fathom_scan_topk_workspace_bytes.argtypes = [I64, I32, I64, I32]
         L.fathom_scan_topk_workspace_bytes.restype = SZ
         L.fathom_gather.argtypes = [P, P, I64, P, I64, I32, I64, P, P, P]
+        L.fathom_klt_fit_workspace_bytes.argtypes = [I64, I64, I32]
+        L.fathom_klt_fit_workspace_bytes.restype = SZ
+        L.fathom_klt_fit.argtypes = [P, I64, I64, I32, P, P, P, P, SZ, P]
+        L.fathom_klt_rotate_keys.argtypes = [P, P, P, I64, I64, I32, P, P]
+        L.fathom_klt_rotate_queries.argtypes = [P, P, I64, I32, I32, P, P]
         L.fathom_topk_workspace_bytes.restype = SZ
         L.fathom_status_string.argtypes = [ctypes.c_int]
         L.fathom_status_string.restype = ctypes.c_char_p
         L.fathom_abi_version.argtypes = []
         for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
-                  "fathom_scan_topk", "fathom_gather",
-                  "fathom_abi_version"):
+                  "fathom_scan_topk", "fathom_gather", "fathom_klt_fit",
+                  "fathom_klt_rotate_keys", "fathom_klt_rotate_queries", "fathom_abi_version"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
         return L
@@ -268,3 +276,54 @@ def topk(scores: torch.Tensor, k: int, indices: torch.Tensor | None = None,
         workspace.numel(), _stream(stream))
     _check(st, "fathom_topk")
     return indices
+
+
+def klt_fit_workspace(groups: int, n: int, device="cuda") -> torch.Tensor:
+    nbytes = int(lib().fathom_klt_fit_workspace_bytes(groups, n, D))
+    if nbytes == 0:
+        raise ValueError("invalid shape for fathom_klt_fit (groups=%d, n=%d)" % (groups, n))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def klt_fit(k: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+    """fathom_klt_fit: k [groups][n][d] fp16 -> (mu [groups][d], basis
+    [groups][d][d], lam [groups][d]), fp32."""
+    groups, n, d = k.shape
+    mu = torch.empty((groups, d), dtype=torch.float32, device=k.device)
+    basis = torch.empty((groups, d, d), dtype=torch.float32, device=k.device)
+    lam = torch.empty((groups, d), dtype=torch.float32, device=k.device)
+    if workspace is None:
+        workspace = klt_fit_workspace(groups, n, k.device)
+    st = lib().fathom_klt_fit(_dev(k, "k", torch.float16), groups, n, d, _dev(mu, "mu", torch.float32),
+                              _dev(basis, "basis", torch.float32), _dev(lam, "lam", torch.float32),
+                              _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                              _stream(stream))
+    _check(st, "fathom_klt_fit")
+    return mu, basis, lam
+
+
+def klt_rotate_keys(k: torch.Tensor, mu: torch.Tensor, basis: torch.Tensor,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """fathom_klt_rotate_keys: (k - mu) basis, binary16 [groups][n][d]."""
+    groups, n, d = k.shape
+    if out is None:
+        out = torch.empty_like(k)
+    st = lib().fathom_klt_rotate_keys(
+        _dev(k, "k", torch.float16), _dev(mu, "mu", torch.float32, (groups, d)),
+        _dev(basis, "basis", torch.float32, (groups, d, d)), groups, n, d,
+        _dev(out, "out", torch.float16, (groups, n, d)), _stream(stream))
+    _check(st, "fathom_klt_rotate_keys")
+    return out
+
+
+def klt_rotate_queries(q: torch.Tensor, basis: torch.Tensor, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """fathom_klt_rotate_queries: q basis, fp32 [groups][G][d]."""
+    groups, G, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().fathom_klt_rotate_queries(
+        _dev(q, "q", torch.float32), _dev(basis, "basis", torch.float32, (groups, d, d)), groups,
+        G, d, _dev(out, "out", torch.float32, (groups, G, d)), _stream(stream))
+    _check(st, "fathom_klt_rotate_queries")
+    return out

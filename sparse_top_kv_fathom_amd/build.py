@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfathom.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
-SOURCES = ["api.hip", "encode.hip", "plan.hip", "scan.hip", "topk.hip", "gather.hip"]
+SOURCES = ["api.hip", "encode.hip", "plan.hip", "scan.hip", "topk.hip", "gather.hip", "klt.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

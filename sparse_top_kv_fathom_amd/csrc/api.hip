@@ -178,6 +178,49 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_
                                             static_cast<hipStream_t>(stream)));
 }
 
+size_t fathom_klt_fit_workspace_bytes(int64_t groups, int64_t n, int32_t d) {
+  if (d != fathom::kD || groups < 1 || groups > kMaxGroups || !valid_tokens(n)) return 0;
+  return fathom::klt_fit_workspace_bytes(groups, n);
+}
+
+int fathom_klt_fit(const uint16_t* k, int64_t groups, int64_t n, int32_t d, float* mu,
+                   float* basis, float* lambda, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!k || !mu || !basis || !lambda || !workspace) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || groups < 1 || groups > kMaxGroups || !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(k, 16) || !aligned(mu, 4) || !aligned(basis, 4) || !aligned(lambda, 4) ||
+      !aligned(workspace, 256))
+    return FATHOM_ERR_ALIGNMENT;
+  if (workspace_bytes < fathom::klt_fit_workspace_bytes(groups, n)) return FATHOM_ERR_WORKSPACE;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_klt_fit(k, groups, n, mu, basis, lambda, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fathom_klt_rotate_keys(const uint16_t* k, const float* mu, const float* basis,
+                           int64_t groups, int64_t n, int32_t d, uint16_t* k_rot, void* stream) {
+  if (!k || !mu || !basis || !k_rot) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || groups < 1 || groups > kMaxGroups || !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(k, 16) || !aligned(k_rot, 16) || !aligned(mu, 4) || !aligned(basis, 16))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_klt_rotate_keys(k, mu, basis, groups, n, k_rot,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int fathom_klt_rotate_queries(const float* q, const float* basis, int64_t groups, int32_t G,
+                              int32_t d, float* q_rot, void* stream) {
+  if (!q || !basis || !q_rot) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(q, 4) || !aligned(basis, 4) || !aligned(q_rot, 4)) return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_klt_rotate_queries(q, basis, groups, G, q_rot,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k) {
   if (rows < 1 || n < 1 || n >= kMaxTokens || k < 1 || k > n) return 0;
   return fathom::topk_workspace_bytes(rows, n, k);

@@ -50,6 +50,14 @@ hipError_t launch_gather(const uint64_t* hplanes, const uint16_t* hscales, int64
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* workspace, hipStream_t stream);
 
+size_t klt_fit_workspace_bytes(int64_t groups, int64_t n);
+hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* mu, float* basis,
+                          float* lambda, void* ws, hipStream_t stream);
+hipError_t launch_klt_rotate_keys(const uint16_t* k, const float* mu, const float* basis,
+                                  int64_t groups, int64_t n, uint16_t* out, hipStream_t stream);
+hipError_t launch_klt_rotate_queries(const float* q, const float* basis, int64_t groups, int G,
+                                     float* out, hipStream_t stream);
+
 // Wave-wide helpers -------------------------------------------------------
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }

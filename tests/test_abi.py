@@ -43,6 +43,8 @@ def test_header_declares_the_calls():
     names = declared()
     for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
               "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
+              "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
+              "fathom_klt_rotate_queries",
               "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
@@ -57,7 +59,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 4
+    assert L.fathom_abi_version() == 5
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
@@ -165,6 +167,59 @@ def test_gather_validation(L):
     a[0] = P((1 << 20) + 8)
     assert g(*a) == ALIGN
     assert g(*args) == NO_DEVICE
+
+
+def test_klt_validation(L):
+    assert L.fathom_klt_fit_workspace_bytes(8, 1 << 20, 128) == 8 * 32 * (128 + 128 * 128) * 8
+    assert L.fathom_klt_fit_workspace_bytes(128, 1 << 17, 128) == 128 * 4 * (128 + 128 * 128) * 8
+    assert L.fathom_klt_fit_workspace_bytes(1, 64, 128) == 1 * 1 * (128 + 128 * 128) * 8
+    assert L.fathom_klt_fit_workspace_bytes(1, 100, 128) == 0
+    need = L.fathom_klt_fit_workspace_bytes(2, 4096, 128)
+    f = L.fathom_klt_fit
+    args = [FAKE, 2, 4096, 128, FAKE, FAKE, FAKE, FAKE, need, None]
+    for i in (0, 4, 5, 6, 7):
+        a = list(args)
+        a[i] = None
+        assert f(*a) == NULL_ARG, i
+    for i, v in ((1, 0), (2, 100), (2, 0), (3, 64)):
+        a = list(args)
+        a[i] = v
+        assert f(*a) == BAD_SHAPE, (i, v)
+    a = list(args)
+    a[7] = P((1 << 20) + 16)
+    assert f(*a) == ALIGN
+    a = list(args)
+    a[8] = need - 1
+    assert f(*a) == WORKSPACE
+    assert f(*args) == NO_DEVICE
+
+    r = L.fathom_klt_rotate_keys
+    args = [FAKE, FAKE, FAKE, 2, 4096, 128, FAKE, None]
+    for i in (0, 1, 2, 6):
+        a = list(args)
+        a[i] = None
+        assert r(*a) == NULL_ARG, i
+    for i, v in ((3, 0), (4, 96), (5, 127)):
+        a = list(args)
+        a[i] = v
+        assert r(*a) == BAD_SHAPE, (i, v)
+    for i in (0, 2, 6):
+        a = list(args)
+        a[i] = P((1 << 20) + 4)
+        assert r(*a) == ALIGN, i
+    assert r(*args) == NO_DEVICE
+
+    rq = L.fathom_klt_rotate_queries
+    args = [FAKE, FAKE, 2, 4, 128, FAKE, None]
+    for i in (0, 1, 5):
+        a = list(args)
+        a[i] = None
+        assert rq(*a) == NULL_ARG, i
+    for i, v in ((2, 0), (3, 0), (3, 9), (4, 64)):
+        a = list(args)
+        a[i] = v
+        assert rq(*a) == BAD_SHAPE, (i, v)
+    assert rq(*args) == NO_DEVICE
 
 
 def test_scan_validation(L):
