@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--store", choices=("raw", "klt"), default="raw",
+                    help="raw channel planes, or planes of the KLT-rotated keys")
+    ap.add_argument("--no-klt", action="store_true",
+                    help="skip timing the KLT fit and rotations (raw store only)")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip timing fathom_gather from a pinned host store")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -173,15 +177,53 @@ def main():
     ins = fathom_inputs.make_inputs(H, G, n, w.seed)
     qs = np.stack([fathom_inputs.make_queries(H, G, 1000 + i, d) for i in range(args.queries)])
 
-    # Resident store copies, encoded on the GPU.
     k_d = torch.from_numpy(ins.k).to(dev)
-    stores = []
-    for _ in range(args.copies):
-        stores.append(fk.encode(k_d))
-    newest = k_d[:, n - 64:, :].contiguous()            # the block each step re-encodes
-    del k_d
     q_d = torch.from_numpy(qs).to(dev)
     var_d = torch.from_numpy(ins.var).to(dev)
+
+    # KLT-rotated store: the fit on the keys themselves, the key rotation and
+    # one query rotation, each timed with events (one-time costs, outside
+    # the step).
+    klt, basis_k, src = None, None, k_d
+    if args.store == "klt" or not args.no_klt:
+        kws = fk.klt_fit_workspace(H, n, dev)
+        mu_k, basis_k, lam_k = fk.klt_fit(k_d, kws)
+        kr = fk.klt_rotate_keys(k_d, mu_k, basis_k)
+        qr = fk.klt_rotate_queries(q_d[0], basis_k)
+        ts = {}
+        for name, fn, reps in (("fit_ms", lambda: fk.klt_fit(k_d, kws), 3),
+                               ("rotate_keys_ms", lambda: fk.klt_rotate_keys(k_d, mu_k, basis_k,
+                                                                             out=kr), 3),
+                               ("rotate_queries_ms", lambda: fk.klt_rotate_queries(
+                                   q_d[0], basis_k, out=qr), 10)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts[name] = round(e0.elapsed_time(e1) / reps, 4)
+        klt = dict(ts, keys=H * n, groups=H)
+        if args.store == "klt":
+            src, var_d = kr, lam_k
+        else:
+            del kr, basis_k
+            basis_k = None
+        del kws
+
+    # Resident store copies, encoded on the GPU.
+    stores = []
+    for _ in range(args.copies):
+        stores.append(fk.encode(src))
+    newest = src[:, n - 64:, :].contiguous()            # the block each step re-encodes
+    del k_d, src
+    qrot = torch.empty((H, G, d), dtype=torch.float32, device=dev)
+
+    def query(i):
+        """Query group i as the plan and scan take it (rotated for the KLT store)."""
+        q = q_d[i % args.queries]
+        return q if basis_k is None else fk.klt_rotate_queries(q, basis_k, out=qrot)
     depths = torch.empty((H, d), dtype=torch.uint8, device=dev)
     scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
     idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
@@ -193,12 +235,12 @@ def main():
     def step(s, ev=None):
         """One decode step: append the newest block, plan, scan, select."""
         planes, scales = stores[s % len(stores)]
-        q = q_d[s % args.queries]
         if ev is not None:
             ev[0].record()
         fk.encode(newest, planes, scales, block_offset=nb - 1)
         if ev is not None:
             ev[1].record()
+        q = query(s)
         fk.plan(q, var_d, B, depths=depths)
         if ev is not None:
             ev[2].record()
@@ -212,7 +254,7 @@ def main():
     def fused(s, ev):
         """The scan and selection as the one call fathom_scan_topk."""
         planes, scales = stores[s % len(stores)]
-        q = q_d[s % args.queries]
+        q = query(s)
         fk.plan(q, var_d, B, depths=depths)
         ev[0].record()
         fk.scan_topk(planes, scales, depths, q, n, k, scores=scores, indices=idx, workspace=fws)
@@ -264,7 +306,7 @@ def main():
         hp = stores[0][0].view(torch.int64).cpu().pin_memory().view(torch.uint64)
         hs = stores[0][1].view(torch.int16).cpu().pin_memory().view(torch.uint16)
         gp, gs = fk.empty_store(H, nb, dev)
-        gdep = [fk.plan(q_d[i % args.queries], var_d, B) for i in range(args.steps)]
+        gdep = [fk.plan(query(i), var_d, B) for i in range(args.steps)]
         for i in range(2):
             fk.gather(hp, hs, gdep[i], n, gp, gs)
         gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -302,7 +344,7 @@ def main():
     # Algorithmic work of each timed step's scan (plans recomputed after timing).
     Ts, As = [], []
     for s in range(args.steps):
-        dep = fk.plan(q_d[(args.warmup + s) % args.queries], var_d, B)
+        dep = fk.plan(query(args.warmup + s), var_d, B)
         T, A = plan_stats(dep.cpu().numpy())
         Ts.append(T)
         As.append(A)
@@ -355,7 +397,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": "%s: %s, G=%d, d=%d, B=%d code bits, k=%d" % (w.name, w.note, G, d, B, k),
+            "workload": "%s: %s, G=%d, d=%d, B=%d code bits, k=%d%s" % (
+                w.name, w.note, G, d, B, k,
+                ", KLT-rotated store" if args.store == "klt" else ""),
+            "store": args.store,
             "kv_heads": H, "G": G, "n": n, "budget_bits": B, "k": k,
             "store_copies": args.copies, "parallelism": "single GPU",
         },
@@ -363,13 +408,14 @@ def main():
                       "scan": round(stage_ms[2], 4), "topk": round(stage_ms[3], 4)},
         "fused_scan_topk_ms": round(fused_ms, 4),
         "gather_from_host": gather,
+        "klt_store": klt,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "plan": {"code_bits_mean": float(Ts.mean()), "active_channels_mean": float(As.mean()),
                  "total_bits_per_key_mean": float((Ts + As / 4.0).mean())},
         "roofline": roof,
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.store == "raw":
         import oracle
         nthreads = args.cpu_threads or min(H, os.cpu_count() or 1)
         print("[bench] cpu baseline: oracle step on %d threads" % nthreads, file=sys.stderr,

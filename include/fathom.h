@@ -277,7 +277,7 @@ int fathom_gather(const uint64_t* host_planes, const uint16_t* host_scales, int6
  *
  * fathom_klt_rotate_queries — q_rot[g][h][j] = the fp32 fold over c
  * ascending, from +0, of fma(q_hc, basis[c][j], acc).  q, q_rot
- * [groups][G][d] fp32.
+ * [groups][G][d] fp32; basis 16-byte aligned.
  */
 size_t fathom_klt_fit_workspace_bytes(int64_t groups, int64_t n, int32_t d);
 int fathom_klt_fit(const uint16_t* k, int64_t groups, int64_t n, int32_t d, float* mu,

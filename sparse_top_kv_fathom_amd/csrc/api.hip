@@ -215,7 +215,7 @@ int fathom_klt_rotate_queries(const float* q, const float* basis, int64_t groups
   if (!q || !basis || !q_rot) return FATHOM_ERR_NULL_ARG;
   if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups)
     return FATHOM_ERR_BAD_SHAPE;
-  if (!aligned(q, 4) || !aligned(basis, 4) || !aligned(q_rot, 4)) return FATHOM_ERR_ALIGNMENT;
+  if (!aligned(q, 4) || !aligned(basis, 16) || !aligned(q_rot, 4)) return FATHOM_ERR_ALIGNMENT;
   if (int s = device_ready()) return s;
   return to_status(fathom::launch_klt_rotate_queries(q, basis, groups, G, q_rot,
                                                      static_cast<hipStream_t>(stream)));

@@ -11,10 +11,14 @@
 //
 // Fit (fp64):
 //   klt_mean  — per (chunk of tokens, group): fp64 column sums;
-//   klt_cov   — per (chunk, group): the 128 x 128 sums of centred products,
-//               one 8 x 8 tile per thread, tokens staged in LDS as fp64;
-//   klt_eig   — per group, one 1024-thread workgroup: sums the chunks in a
-//               fixed order, then cyclic Jacobi on the covariance (upper
+//   klt_cov   — per (chunk, group): the upper triangle of the 128 x 128 sums
+//               of centred products, one 8 x 8 tile per thread and half of
+//               the chunk's tokens (272 threads: 136 tiles x 2 halves),
+//               tokens staged in LDS as fp64;
+//   klt_reduce— per (element block, group): the partial sums added in a
+//               fixed order, divided by n - 1;
+//   klt_eig   — per group, one 1024-thread workgroup: cyclic Jacobi on the
+//               covariance (upper
 //               triangle packed in LDS, fp64; the accumulated rotation in
 //               LDS, fp32), 64 disjoint rotations per step in round-robin
 //               order, sweeps until the off-diagonal mass falls below 1e-28
@@ -29,15 +33,17 @@
 namespace fathom {
 namespace {
 
-constexpr int kCovThreads = 256;
+constexpr int kCovThreads = 272;    // 136 upper-triangle 8 x 8 tiles x 2 token halves
+constexpr int kCovTiles = 136;
 constexpr int kCovTok = 32;          // tokens staged per step of klt_cov
 constexpr int kEigThreads = 1024;
 constexpr int kPairs = kD / 2;       // disjoint rotations per Jacobi step
 constexpr int kPacked = kD * (kD + 1) / 2;
 constexpr int kMaxSweeps = 24;
 constexpr int kRotThreads = 256;
-constexpr int kRotTiles = 16;        // 64-token tiles per rotation workgroup
-constexpr int kXPitch = kBlock + 4;  // floats per channel row of the staged tile
+constexpr int kRotTok = 128;         // tokens per rotation tile
+constexpr int kRotTiles = 8;         // tiles per rotation workgroup
+constexpr int kXPitch = kRotTok + 4; // floats per channel row of the staged tile
 
 __device__ __forceinline__ double f16_to_f64(uint16_t h) {
   return (double)__builtin_bit_cast(_Float16, h);
@@ -57,45 +63,71 @@ __device__ __forceinline__ int tri(int a, int b) {
 }
 
 struct FitLayout {
-  double* mean;   // [groups][P][d]
-  double* cov;    // [groups][P][d][d]
+  double* mean;   // [groups][P][d]       column sums per chunk
+  double* cov;    // [groups][2P][d][d]   centred product sums per chunk half (r <= c)
+  double* csum;   // [groups][d][d]       the covariance (r <= c)
 };
 
 __host__ __device__ inline FitLayout fit_layout(void* ws, int64_t groups, int64_t P) {
   FitLayout L;
   L.mean = static_cast<double*>(ws);
   L.cov = L.mean + groups * P * kD;
+  L.csum = L.cov + groups * 2 * P * kD * kD;
   return L;
 }
 
 // Column sums of chunk blockIdx.x of group blockIdx.y.  Thread t sums
-// channels 2(t % 64) and 2(t % 64) + 1 over every 4th token of the chunk.
-__global__ __launch_bounds__(kCovThreads) void klt_mean(const uint16_t* __restrict__ k, int64_t n,
-                                                        int64_t per, int64_t P, void* ws,
-                                                        int64_t groups) {
-  __shared__ double s_part[4][kD];
+// channels 8(t % 16) .. +7 over tokens t / 16, t / 16 + 16, ... of the chunk
+// (16-byte loads, four rows in flight per thread).
+__global__ __launch_bounds__(256) void klt_mean(const uint16_t* __restrict__ k, int64_t n,
+                                                int64_t per, int64_t P, void* ws, int64_t groups) {
+  __shared__ double s_part[16][kD];
   const int64_t g = blockIdx.y, p = blockIdx.x;
   const int64_t t0 = p * per, t1 = min(n, t0 + per);
-  const int cp = threadIdx.x & 63, r = threadIdx.x >> 6;
-  double s0 = 0.0, s1 = 0.0;
-  const uint32_t* rows = reinterpret_cast<const uint32_t*>(k + g * n * kD);
-  for (int64_t t = t0 + r; t < t1; t += 4) {
-    const uint32_t w = rows[t * (kD / 2) + cp];
-    s0 += f16_to_f64((uint16_t)(w & 0xffffu));
-    s1 += f16_to_f64((uint16_t)(w >> 16));
+  const int c8 = threadIdx.x & 15, r = threadIdx.x >> 4;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  const uint4* rows = reinterpret_cast<const uint4*>(k + g * n * kD);
+  int64_t t = t0 + r;
+  for (; t + 48 < t1; t += 64) {
+    uint4 w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = rows[(t + 16 * u) * (kD / 8) + c8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += f16_to_f64((uint16_t)(x[e] & 0xffffu));
+        acc[2 * e + 1] += f16_to_f64((uint16_t)(x[e] >> 16));
+      }
+    }
   }
-  s_part[r][2 * cp] = s0;
-  s_part[r][2 * cp + 1] = s1;
+  for (; t < t1; t += 16) {
+    const uint4 w = rows[t * (kD / 8) + c8];
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += f16_to_f64((uint16_t)(x[e] & 0xffffu));
+      acc[2 * e + 1] += f16_to_f64((uint16_t)(x[e] >> 16));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_part[r][8 * c8 + e] = acc[e];
   __syncthreads();
   if (threadIdx.x < kD) {
     const int c = threadIdx.x;
-    const double s = ((s_part[0][c] + s_part[1][c]) + s_part[2][c]) + s_part[3][c];
+    double s = 0.0;
+    for (int i = 0; i < 16; ++i) s += s_part[i][c];
     fit_layout(ws, groups, P).mean[(g * P + p) * kD + c] = s;
   }
 }
 
-// Sums of centred products of chunk blockIdx.x of group blockIdx.y: thread t
-// owns rows 8(t / 16) .. +7 and columns 8(t % 16) .. +7 of the 128 x 128 sum.
+// Sums of centred products of chunk blockIdx.x of group blockIdx.y.  Thread
+// t owns tile t % 136 of the upper triangle (8 x 8 tiles (ti, tj), ti <= tj,
+// row by row) over the staged tokens u with u % 2 == t / 136, and writes them
+// as partial 2 * chunk + t / 136.
 __global__ __launch_bounds__(kCovThreads) void klt_cov(const uint16_t* __restrict__ k, int64_t n,
                                                        int64_t per, int64_t P, void* ws,
                                                        int64_t groups) {
@@ -109,18 +141,24 @@ __global__ __launch_bounds__(kCovThreads) void klt_cov(const uint16_t* __restric
     for (int64_t i = 0; i < P; ++i) s += L.mean[(g * P + i) * kD + threadIdx.x];
     s_mu[threadIdx.x] = s / (double)n;
   }
-  const int ti = threadIdx.x >> 4, tj = threadIdx.x & 15;
+  const int half = threadIdx.x / kCovTiles;
+  int ti = 0, rest = threadIdx.x % kCovTiles;
+  while (rest >= 16 - ti) {
+    rest -= 16 - ti;
+    ++ti;
+  }
+  const int tj = ti + rest;
   double acc[8][8];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
-  // Staging: thread t loads token t / 8 of the step, channels 16 (t % 8) .. +15.
+  // Staging (threads < 256): token t / 8 of the step, channels 16 (t % 8) .. +15.
   const int lt = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 16;
   for (int64_t s0 = t0; s0 < t1; s0 += kCovTok) {
     __syncthreads();
     const int64_t tok = s0 + lt;
-    if (tok < t1) {
+    if (threadIdx.x < 256 && tok < t1) {
       const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok) * kD + lc);
       const uint4 w0 = src[0], w1 = src[1];
       const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -129,12 +167,13 @@ __global__ __launch_bounds__(kCovThreads) void klt_cov(const uint16_t* __restric
         s_x[lt][lc + 2 * e] = f16_to_f64((uint16_t)(w[e] & 0xffffu)) - s_mu[lc + 2 * e];
         s_x[lt][lc + 2 * e + 1] = f16_to_f64((uint16_t)(w[e] >> 16)) - s_mu[lc + 2 * e + 1];
       }
-    } else {
+    } else if (threadIdx.x < 256) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_x[lt][lc + e] = 0.0;
     }
     __syncthreads();
-    for (int u = 0; u < kCovTok; ++u) {
+#pragma unroll 2
+    for (int u = half; u < kCovTok; u += 2) {
       double ra[8], cb[8];
 #pragma unroll
       for (int a = 0; a < 8; ++a) ra[a] = s_x[u][8 * ti + a];
@@ -146,11 +185,25 @@ __global__ __launch_bounds__(kCovThreads) void klt_cov(const uint16_t* __restric
         for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fma(ra[a], cb[b], acc[a][b]);
     }
   }
-  double* dst = L.cov + (g * P + p) * kD * kD;
+  double* dst = L.cov + (g * 2 * P + 2 * p + half) * kD * kD;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) dst[(8 * ti + a) * kD + 8 * tj + b] = acc[a][b];
+}
+
+// The covariance: element e = blockIdx.x * 256 + t of group blockIdx.y (row
+// e / 128, column e % 128, upper triangle only) summed over the 2P partials
+// in index order, times 1 / (n - 1).
+__global__ __launch_bounds__(256) void klt_reduce(int64_t n, int64_t P, void* ws, int64_t groups) {
+  const int64_t g = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e / kD > e % kD) return;
+  const FitLayout L = fit_layout(ws, groups, P);
+  const double* src = L.cov + g * 2 * P * kD * kD + e;
+  double s = 0.0;
+  for (int64_t i = 0; i < 2 * P; ++i) s += src[i * kD * kD];
+  L.csum[g * kD * kD + e] = s * (1.0 / (double)(n - 1));
 }
 
 // Sum over the workgroup in a fixed order (per-wave shuffles, then the waves
@@ -185,14 +238,9 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
     for (int64_t i = 0; i < P; ++i) s += L.mean[(g * P + i) * kD + tid];
     mu[g * kD + tid] = (float)(s / (double)n);
   }
-  const double inv = 1.0 / (double)(n - 1);
   for (int e = tid; e < kD * kD; e += kEigThreads) {
     const int r = e / kD, c = e % kD;
-    if (r <= c) {
-      double s = 0.0;
-      for (int64_t i = 0; i < P; ++i) s += L.cov[(g * P + i) * kD * kD + e];
-      s_a[tri(r, c)] = s * inv;
-    }
+    if (r <= c) s_a[tri(r, c)] = L.csum[g * kD * kD + e];
     s_v[r][c] = r == c ? 1.0f : 0.0f;
   }
   __syncthreads();
@@ -243,9 +291,15 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
         s_t[tid] = t;
       }
       __syncthreads();
-      // A <- J^T A J, one 2 x 2 block (pair i, pair k), i <= k, per item.
-      for (int e = tid; e < kPairs * kPairs; e += kEigThreads) {
-        const int i = e / kPairs, kk = e % kPairs;
+      // A <- J^T A J, one 2 x 2 block (pair i, pair k), i <= k, per item;
+      // item e = tid + 1024 m has k = tid % 64 (fixed per thread) and
+      // i = tid / 64 + 16 m.
+      const int kk = tid & (kPairs - 1);
+      const int p2 = s_p[kk], q2 = s_q[kk];
+      const double ck = s_c[kk], sk = s_s[kk];
+#pragma unroll
+      for (int m = 0; m < kPairs * kPairs / kEigThreads; ++m) {
+        const int i = (tid >> 6) + 16 * m;
         if (i > kk) continue;
         const int p = s_p[i], q = s_q[i];
         if (i == kk) {
@@ -255,8 +309,7 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
           s_a[tri(p, q)] = 0.0;
           continue;
         }
-        const int p2 = s_p[kk], q2 = s_q[kk];
-        const double ci = s_c[i], si = s_s[i], ck = s_c[kk], sk = s_s[kk];
+        const double ci = s_c[i], si = s_s[i];
         const int i00 = tri(p, p2), i01 = tri(p, q2), i10 = tri(q, p2), i11 = tri(q, q2);
         const double x00 = s_a[i00], x01 = s_a[i01], x10 = s_a[i10], x11 = s_a[i11];
         const double y00 = ci * x00 - si * x10, y01 = ci * x01 - si * x11;
@@ -266,14 +319,16 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
         s_a[i10] = y10 * ck - y11 * sk;
         s_a[i11] = y10 * sk + y11 * ck;
       }
-      // V <- V J: row r, pair i per item.
-      for (int e = tid; e < kD * kPairs; e += kEigThreads) {
-        const int r = e / kPairs, i = e % kPairs;
-        const int p = s_p[i], q = s_q[i];
-        const float c = (float)s_c[i], s = (float)s_s[i];
-        const float vp = s_v[r][p], vq = s_v[r][q];
-        s_v[r][p] = c * vp - s * vq;
-        s_v[r][q] = s * vp + c * vq;
+      // V <- V J: item e = tid + 1024 m is row tid / 64 + 16 m of pair tid % 64.
+      {
+        const float c = (float)ck, sn = (float)sk;
+#pragma unroll
+        for (int m = 0; m < kD * kPairs / kEigThreads; ++m) {
+          const int r = (tid >> 6) + 16 * m;
+          const float vp = s_v[r][p2], vq = s_v[r][q2];
+          s_v[r][p2] = c * vp - sn * vq;
+          s_v[r][q2] = sn * vp + c * vq;
+        }
       }
       __syncthreads();
     }
@@ -303,8 +358,10 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
   }
 }
 
-// Rotated keys of kRotTiles 64-token tiles of group blockIdx.y.  Thread t owns
-// tokens 4 (t % 16) .. +3 and outputs 8 (t / 16) .. +7 of a tile.
+// Rotated keys of kRotTiles 128-token tiles of group blockIdx.y.  Thread t
+// owns tokens 8 (t % 16) .. +7 and outputs 8 (t / 16) .. +7 of a tile; per
+// channel c it reads 8 centred values and 8 basis entries from LDS for 64
+// fused multiply-adds.
 __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __restrict__ k,
                                                           const float* __restrict__ mu,
                                                           const float* __restrict__ basis,
@@ -318,65 +375,79 @@ __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __rest
   for (int e = tid; e < kD * kD / 4; e += kRotThreads)
     reinterpret_cast<float4*>(&s_v[0][0])[e] = vsrc[e];
   if (tid < kD) s_mu[tid] = mu[g * kD + tid];
-  const int tq = tid & 15, jo = tid >> 4;
-  const int lt = tid >> 2, lc = (tid & 3) * 32;       // staging: token, first channel
-  const int64_t nb = n / kBlock;
+  const int to = tid & 15, jo = tid >> 4;
+  const int lt = tid >> 1, lc = (tid & 1) * 64;      // staging: token, first channel
+  const int64_t ntile = (n + kRotTok - 1) / kRotTok;
   for (int64_t tile = (int64_t)blockIdx.x * kRotTiles;
-       tile < min<int64_t>(nb, ((int64_t)blockIdx.x + 1) * kRotTiles); ++tile) {
+       tile < min<int64_t>(ntile, ((int64_t)blockIdx.x + 1) * kRotTiles); ++tile) {
+    const int64_t tok0 = tile * kRotTok;
     __syncthreads();
-    const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tile * kBlock + lt) * kD + lc);
+    if (tok0 + lt < n) {
+      const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok0 + lt) * kD + lc);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint4 w = src[v];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int v = 0; v < 8; ++v) {
+        const uint4 w = src[v];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = lc + 8 * v + 2 * e;
-        s_x[c][lt] = f16_to_f32((uint16_t)(ws[e] & 0xffffu)) - s_mu[c];
-        s_x[c + 1][lt] = f16_to_f32((uint16_t)(ws[e] >> 16)) - s_mu[c + 1];
+        for (int e = 0; e < 4; ++e) {
+          const int c = lc + 8 * v + 2 * e;
+          s_x[c][lt] = f16_to_f32((uint16_t)(ws[e] & 0xffffu)) - s_mu[c];
+          s_x[c + 1][lt] = f16_to_f32((uint16_t)(ws[e] >> 16)) - s_mu[c + 1];
+        }
       }
     }
     __syncthreads();
-    float acc[4][8];
+    float acc[8][8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
       for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
+#pragma unroll 4
     for (int c = 0; c < kD; ++c) {
-      const float4 x = *reinterpret_cast<const float4*>(&s_x[c][4 * tq]);
+      const float4 x0 = *reinterpret_cast<const float4*>(&s_x[c][8 * to]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&s_x[c][8 * to + 4]);
       const float4 v0 = *reinterpret_cast<const float4*>(&s_v[c][8 * jo]);
       const float4 v1 = *reinterpret_cast<const float4*>(&s_v[c][8 * jo + 4]);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fmaf(xs[a], vs[b], acc[a][b]);
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 8; ++a) {
+      const int64_t tok = tok0 + 8 * to + a;
+      if (tok >= n) break;
       uint32_t h[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         h[b] = (uint32_t)f32_to_f16_rne(acc[a][2 * b]) |
                ((uint32_t)f32_to_f16_rne(acc[a][2 * b + 1]) << 16);
-      *reinterpret_cast<uint4*>(out + (g * n + tile * kBlock + 4 * tq + a) * kD + 8 * jo) =
+      *reinterpret_cast<uint4*>(out + (g * n + tok) * kD + 8 * jo) =
           make_uint4(h[0], h[1], h[2], h[3]);
     }
   }
 }
 
-// Rotated queries: thread j of group blockIdx.x folds coordinate j of every head.
-__global__ __launch_bounds__(kD) void klt_rotate_q(const float* __restrict__ q,
-                                                   const float* __restrict__ basis, int G,
-                                                   float* __restrict__ out) {
+// Rotated queries of group blockIdx.x: the basis and the G query heads are
+// staged in LDS with 16-byte loads, then thread t folds coordinate t % 128 of
+// heads t / 128, t / 128 + 2, ...
+__global__ __launch_bounds__(256) void klt_rotate_q(const float* __restrict__ q,
+                                                    const float* __restrict__ basis, int G,
+                                                    float* __restrict__ out) {
+  __shared__ float s_v[kD][kD];
+  __shared__ float s_q[8][kD];
   const int64_t g = blockIdx.x;
-  const int j = threadIdx.x;
-  const float* V = basis + g * kD * kD;
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + (g * G + h) * kD;
+  const float4* vsrc = reinterpret_cast<const float4*>(basis + g * kD * kD);
+  for (int e = threadIdx.x; e < kD * kD / 4; e += 256)
+    reinterpret_cast<float4*>(&s_v[0][0])[e] = vsrc[e];
+  for (int e = threadIdx.x; e < G * kD; e += 256) s_q[e / kD][e % kD] = q[g * G * kD + e];
+  __syncthreads();
+  const int j = threadIdx.x % kD;
+  for (int h = threadIdx.x / kD; h < G; h += 2) {
     float acc = 0.0f;
-    for (int c = 0; c < kD; ++c) acc = __builtin_fmaf(qh[c], V[c * kD + j], acc);
+    for (int c = 0; c < kD; ++c) acc = __builtin_fmaf(s_q[h][c], s_v[c][j], acc);
     out[(g * G + h) * kD + j] = acc;
   }
 }
@@ -384,7 +455,7 @@ __global__ __launch_bounds__(kD) void klt_rotate_q(const float* __restrict__ q,
 int64_t fit_chunks(int64_t groups, int64_t n) {
   const int64_t nb = n / kBlock;
   int64_t p = (512 + groups - 1) / groups;
-  p = p < 32 ? p : 32;
+  p = p < 64 ? p : 64;
   p = p < nb ? p : nb;
   return p > 1 ? p : 1;
 }
@@ -393,7 +464,7 @@ int64_t fit_chunks(int64_t groups, int64_t n) {
 
 size_t klt_fit_workspace_bytes(int64_t groups, int64_t n) {
   const int64_t P = fit_chunks(groups, n);
-  return (size_t)(groups * P * (kD + kD * kD)) * sizeof(double);
+  return (size_t)(groups * (P * kD + 2 * P * kD * kD + kD * kD)) * sizeof(double);
 }
 
 hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* mu, float* basis,
@@ -402,8 +473,10 @@ hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* m
   const int64_t nb = n / kBlock;
   const int64_t per = (nb + P - 1) / P * kBlock;
   const dim3 grid((unsigned)P, (unsigned)groups);
-  hipLaunchKernelGGL(klt_mean, grid, dim3(kCovThreads), 0, stream, k, n, per, P, ws, groups);
+  hipLaunchKernelGGL(klt_mean, grid, dim3(256), 0, stream, k, n, per, P, ws, groups);
   hipLaunchKernelGGL(klt_cov, grid, dim3(kCovThreads), 0, stream, k, n, per, P, ws, groups);
+  hipLaunchKernelGGL(klt_reduce, dim3(kD * kD / 256, (unsigned)groups), dim3(256), 0, stream, n,
+                     P, ws, groups);
   hipLaunchKernelGGL(klt_eig, dim3((unsigned)groups), dim3(kEigThreads), 0, stream, n, P,
                      (const void*)ws, groups, mu, basis, lambda);
   return hipGetLastError();
@@ -411,15 +484,15 @@ hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* m
 
 hipError_t launch_klt_rotate_keys(const uint16_t* k, const float* mu, const float* basis,
                                   int64_t groups, int64_t n, uint16_t* out, hipStream_t stream) {
-  const int64_t nb = n / kBlock;
-  const dim3 grid((unsigned)((nb + kRotTiles - 1) / kRotTiles), (unsigned)groups);
+  const int64_t ntile = (n + kRotTok - 1) / kRotTok;
+  const dim3 grid((unsigned)((ntile + kRotTiles - 1) / kRotTiles), (unsigned)groups);
   hipLaunchKernelGGL(klt_rotate, grid, dim3(kRotThreads), 0, stream, k, mu, basis, n, out);
   return hipGetLastError();
 }
 
 hipError_t launch_klt_rotate_queries(const float* q, const float* basis, int64_t groups, int G,
                                      float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(klt_rotate_q, dim3((unsigned)groups), dim3(kD), 0, stream, q, basis, G, out);
+  hipLaunchKernelGGL(klt_rotate_q, dim3((unsigned)groups), dim3(256), 0, stream, q, basis, G, out);
   return hipGetLastError();
 }
 
