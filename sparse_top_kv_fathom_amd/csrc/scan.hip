@@ -689,7 +689,9 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
                               hipStream_t stream) {
   const int64_t rows = groups * G, R = (int64_t)kRoundBlocks * kBlock;
   const int64_t nrounds = n / R;
-  const bool fused = kRounds == 1 && n % (R * kRunRounds) == 0 && nb_store <= kMaxFastBlocks &&
+  const bool fused = kRounds == 1 && n % (R * kRunRounds) == 0 &&
+                     topk::sample_stride(n) * kSampledRounds * R == kRunRounds * R &&
+                     nb_store <= kMaxFastBlocks &&
                      nb_store % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   if (!fused) {   // the two calls one after the other

@@ -7,16 +7,19 @@
 //
 // Scores map to order-preserving 32-bit keys (fp32 bits with the sign
 // folded, -0 mapped to +0).  Per row:
-//   sample  — an 11-bit histogram of the top key bits over every 8th chunk
-//             of 8192 keys;
-//   guess   — a cut tau that leaves, by the sample, comfortably more than k
-//             keys at or above it (placed inside the histogram bin);
+//   sample  — per sampled chunk of 8192 keys (every 8th, at most 64 per
+//             row), an 11-bit histogram of the top key bits, in its own slot
+//             (nothing to clear beforehand);
+//   guess   — sums the slots; a cut tau that leaves, by the sample,
+//             comfortably more than k keys at or above it (placed inside the
+//             histogram bin); clears the row's overflow flag;
 //   compact — one pass over the row writes every key >= tau (key, index) of
 //             a chunk, in index order, to that chunk's own region of the
 //             row's candidate buffer, and its count;
-//   resolve — one workgroup per row: stages the candidates in LDS, finds the
-//             k-th largest key T with two radix digits counted from tau,
-//             the keys == T still needed, and per chunk the number of keys
+//   resolve — one workgroup per row: stages the candidates' keys in LDS,
+//             finds the k-th largest key T with two radix digits counted
+//             from tau, the keys == T still needed, and per chunk (counted
+//             by one wave over the chunk's staged range) the number of keys
 //             > T and == T before it;
 //   order   — one wave per (chunk, row) writes the chunk's selected indices
 //             (every key > T, the earliest keys == T) at its prefix
@@ -37,8 +40,8 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerWg = kThreads / 64;
 constexpr int kPerThread = 32;                       // keys per thread in a chunk
 constexpr int kChunk = kThreads * kPerThread;        // 8192 keys per workgroup chunk
+static_assert(kChunk == kSampleChunk, "the sample reads whole compaction chunks");
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
-constexpr int kSampleStride = 8;                     // every 8th chunk is sampled
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
 constexpr int kLdsCand = 16384;                      // candidates staged in LDS at most
@@ -170,14 +173,7 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t nee
 
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void topk_init(void* ws, int64_t n, int64_t R) {
-  RowWs r = row_ws(ws, n, R, blockIdx.x);
-  for (int i = threadIdx.x; i < kBins; i += kThreads) r.hist[i] = 0u;
-  if (threadIdx.x < kS_WORDS) r.st[threadIdx.x] = 0u;
-}
-
-// Histogram of the top 11 key bits of one sampled chunk (chunk
-// blockIdx.x * kSampleStride).  Lanes that share a bin serialise in the LDS
+// Histogram of the top 11 key bits of one sampled chunk.  Lanes that share a bin serialise in the LDS
 // unit, which is cheaper than combining them first.
 template <bool F>
 __device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
@@ -191,28 +187,23 @@ __device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int6
       if (valid<F>(c0, i, c, n)) atomicAdd(&s_hist[order_key(V.v[i][c]) >> 21], 1u);
 }
 
-// Sampled keys: chunk blockIdx.x * stride of a row of `len` keys at
-// src + row * pitch (the score rows themselves, stride kSampleStride; or the
-// scan's sampled rounds, gathered, stride 1).
+// Sample blockIdx.x of row blockIdx.y: chunk blockIdx.x * sample_stride(n)
+// of the row's n keys at scores + row * n, its histogram to slot blockIdx.x.
 __global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict__ scores,
-                                                        int64_t pitch, int64_t len, int stride,
                                                         int64_t n, int64_t R, void* ws) {
   __shared__ uint32_t s_hist[kBins];
   const int64_t row = blockIdx.y;
   RowWs r = row_ws(ws, n, R, row);
   for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0u;
   __syncthreads();
-  const int64_t c0 = (int64_t)blockIdx.x * stride * kChunk;
-  const float* src = scores + row * pitch;
-  if (chunk_full(src, len, c0)) sample_chunk<true>(src, len, c0, s_hist);
-  else sample_chunk<false>(src, len, c0, s_hist);
+  const int64_t c0 = (int64_t)blockIdx.x * sample_stride(n) * kChunk;
+  const float* src = scores + row * n;
+  if (chunk_full(src, n, c0)) sample_chunk<true>(src, n, c0, s_hist);
+  else sample_chunk<false>(src, n, c0, s_hist);
   __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += kThreads) {
-    const uint32_t t = s_hist[b];
-    if (t != 0u) atomicAdd(&r.hist[b], t);
-  }
-  if (threadIdx.x == 0)
-    atomicAdd(&r.st[kS_NSAMPLE], (uint32_t)min<int64_t>(kChunk, len - c0));
+  uint4* dst = reinterpret_cast<uint4*>(r.hist + (int64_t)blockIdx.x * kBins);
+  for (int i = threadIdx.x; i < kBins / 4; i += kThreads)
+    dst[i] = *reinterpret_cast<const uint4*>(&s_hist[4 * i]);
 }
 
 // Per row: the cut tau.  With the whole row sampled the target is exactly k
@@ -222,17 +213,39 @@ __global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict_
 __global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int64_t R, int k, void* ws) {
   __shared__ uint32_t s_tmp[kWavesPerWg];
   __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_h[kBins];
   constexpr int kPer = kBins / kThreads;
+  static_assert(kPer == 8, "two 16-byte loads per slot and thread");
   RowWs r = row_ws(ws, n, R, blockIdx.x);
-  const uint32_t ns = r.st[kS_NSAMPLE];
+  const int64_t nsl = n_samples(n), stride = sample_stride(n);
+  int64_t ns = 0;   // keys sampled
+  for (int64_t sl = 0; sl < nsl; ++sl) ns += min<int64_t>(kChunk, n - sl * stride * kChunk);
+  uint32_t h[kPer];
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) h[b] = 0u;
+  // Eight slots' loads in flight at a time, added in slot order.
+  for (int64_t s0 = 0; s0 < nsl; s0 += 8) {
+    uint4 a[8], c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t sl = s0 + u;
+      const uint4* src = reinterpret_cast<const uint4*>(r.hist + sl * kBins + threadIdx.x * kPer);
+      a[u] = sl < nsl ? src[0] : make_uint4(0u, 0u, 0u, 0u);
+      c[u] = sl < nsl ? src[1] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      h[0] += a[u].x; h[1] += a[u].y; h[2] += a[u].z; h[3] += a[u].w;
+      h[4] += c[u].x; h[5] += c[u].y; h[6] += c[u].z; h[7] += c[u].w;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < kPer; ++b) s_h[threadIdx.x * kPer + b] = h[b];
   uint32_t target = (uint32_t)k;
-  if ((int64_t)ns < n) {
+  if (ns < n) {
     const double share = (double)k * (double)ns / (double)n;
     target = (uint32_t)min<double>((double)ns, share * 1.25 + 64.0);
   }
-  uint32_t h[kPer];
-#pragma unroll
-  for (int b = 0; b < kPer; ++b) h[b] = r.hist[threadIdx.x * kPer + b];
   s_sel[0] = 0u;
   __syncthreads();
   pick_bin<kThreads, kPer>(h, target, s_tmp, s_sel);
@@ -240,15 +253,16 @@ __global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int64_t R, int
   if (threadIdx.x == 0) {
     const uint32_t bin = s_sel[0];
     uint32_t tau = bin << 21;
-    if ((int64_t)ns < n) {
+    if (ns < n) {
       // Inside the bin, place the cut by the share of the bin's sample that
       // is needed, doubled: densities fall towards the top of a tail bin, so
       // the top fraction f of the keys spans more than f of the bin's range.
-      const double f = min(1.0, 2.0 * (double)s_sel[1] / (double)max(r.hist[bin], 1u));
+      const double f = min(1.0, 2.0 * (double)s_sel[1] / (double)max(s_h[bin], 1u));
       const uint64_t top = ((uint64_t)bin + 1) << 21;
       tau = (uint32_t)max<uint64_t>((uint64_t)bin << 21, top - (uint64_t)(f * (double)(1u << 21)));
     }
     r.st[kS_TAU] = tau;
+    r.st[kS_OVER] = 0u;
   }
 }
 
@@ -479,7 +493,6 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   __shared__ uint32_t s_hist[2 * kBins];
   __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
   __shared__ uint32_t s_key[kLdsCand];
-  __shared__ uint16_t s_cid[kLdsCand];
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
   const int64_t row = blockIdx.x;
@@ -494,6 +507,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   src.region = r.region;
   const int64_t nc = src.nc;
   int32_t* dst = out + row * (int64_t)k;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  constexpr int kW = kResolveThreads / 64, kU = 8;
 
   // Candidates of the row: the chunk counts, summed (and, when they fit,
   // prefixed into s_gt for staging).
@@ -523,11 +538,10 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   __syncthreads();
 
   if (lds) {
-    // Stage keys and chunk ids: wave w copies chunks w, w + 16, ..., eight
-    // chunks' first 128 candidates per batch of loads, then any rest.
-    const int wave = threadIdx.x >> 6, lane = lane_id();
+    // Stage the keys, chunk after chunk in index order: chunk c at
+    // [s_gt[c], s_gt[c] + count(c)).  Wave w copies chunks w, w + 16, ...,
+    // eight chunks' first 128 candidates per batch of loads, then any rest.
     auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
-    constexpr int kW = kResolveThreads / 64, kU = 8;
     for (int64_t cb = wave; cb < nc; cb += kW * kU) {
       uint2 e[kU][2];
 #pragma unroll
@@ -547,19 +561,13 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const uint32_t o = lane + 64 * h;
-          if (o < cnt) {
-            s_key[s_gt[c] + o] = e[u][h].x;
-            s_cid[s_gt[c] + o] = (uint16_t)c;
-          }
+          if (o < cnt) s_key[s_gt[c] + o] = e[u][h].x;
         }
       }
     }
     for (int64_t c = wave; c < nc; c += kW)
-      for (uint32_t o = 128 + lane; o < count(c); o += 64) {
-        const uint2 e = src.cand[(uint32_t)c * src.region + o];
-        s_key[s_gt[c] + o] = e.x;
-        s_cid[s_gt[c] + o] = (uint16_t)c;
-      }
+      for (uint32_t o = 128 + lane; o < count(c); o += 64)
+        s_key[s_gt[c] + o] = src.cand[(uint32_t)c * src.region + o].x;
   }
   __syncthreads();
 
@@ -606,10 +614,11 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
       __syncthreads();
     }
   }
-  // f(key, index or chunk id) over every key the row selects among.
+  // f(key, index) over every key the row selects among (LDS: the index is
+  // not needed, 0 is passed).
   auto keys = [&](auto&& f) {
     if (lds) {
-      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) f(s_key[i], (uint32_t)s_cid[i]);
+      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) f(s_key[i], 0u);
     } else {
       for_each_key(src, f);
     }
@@ -645,14 +654,26 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   // > T and == T of every group, prefixed over the groups.
   const int64_t per_group = (nc + kGroups - 1) / kGroups;
   const int ngroups = (int)((nc + per_group - 1) / per_group);
-  for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
-  __syncthreads();
-  if (lds) {   // per_group == 1, chunk ids at hand
-    keys([&](uint32_t key, uint32_t c) {
-      if (key > T) atomicAdd(&s_gt[c], 1u);
-      if (key == T) atomicAdd(&s_eq[c], 1u);
-    });
+  if (lds) {   // per_group == 1: chunk c's keys are s_key[s_gt[c] .. s_gt[c + 1])
+    for (int64_t c = wave; c < nc; c += kW) {
+      const uint32_t o0 = s_gt[c], o1 = c + 1 < nc ? s_gt[c + 1] : ncand;
+      uint32_t gt = 0, eq = 0;
+      for (uint32_t o = o0; o < o1; o += 64) {
+        const bool v = o + lane < o1;
+        const uint32_t key = v ? s_key[o + lane] : 0u;
+        gt += (uint32_t)__popcll(__ballot(v && key > T));
+        eq += (uint32_t)__popcll(__ballot(v && key == T));
+      }
+      if (lane == 0) {
+        s_hist[c] = gt;
+        s_eq[c] = eq;
+      }
+    }
+    __syncthreads();
+    for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_hist[g];
   } else {
+    for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
+    __syncthreads();
     for_each_key(src, [&](uint32_t key, uint32_t idx) {
       const int g = (int)((int64_t)(idx / R) / per_group);
       if (key > T) atomicAdd(&s_gt[g], 1u);
@@ -676,9 +697,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     return;
   }
   if (threadIdx.x == 0) r.st[kS_ORDER] = 0u;
-  // One wave per group writes its selected indices in index order.
-  const int wave = threadIdx.x >> 6;
   const uint64_t below = lanes_below();
+  // One wave per group writes its selected indices in index order.
   for (int g = wave; g < ngroups; g += kResolveThreads / 64) {
     uint32_t eq_seen = s_eq[g];
     uint32_t pos = s_gt[g] + min(eq_seen, need);
@@ -736,11 +756,10 @@ size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* ws, hipStream_t stream) {
   const int64_t R = kChunk, nc = n_chunks(n, R);
-  const unsigned ns = (unsigned)((nc + kSampleStride - 1) / kSampleStride);
+  const unsigned ns = (unsigned)n_samples(n);
   const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
-  hipLaunchKernelGGL(topk_init, grid_rows, dim3(kThreads), 0, stream, ws, n, R);
   hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
-                     n, kSampleStride, n, R, ws);
+                     R, ws);
   hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
   hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
@@ -759,11 +778,9 @@ size_t topk_rounds_workspace_bytes(int64_t rows, int64_t n, int64_t R) {
 
 hipError_t launch_topk_rounds_cut(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                   void* ws, hipStream_t stream) {
-  const int64_t nc = n_chunks(n, kChunk);
-  const unsigned ns = (unsigned)((nc + kSampleStride - 1) / kSampleStride);
-  hipLaunchKernelGGL(topk_init, dim3((unsigned)rows), dim3(kThreads), 0, stream, ws, n, R);
+  const unsigned ns = (unsigned)n_samples(n);
   hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
-                     n, kSampleStride, n, R, ws);
+                     R, ws);
   hipLaunchKernelGGL(topk_guess, dim3((unsigned)rows), dim3(kThreads), 0, stream, n, R, k, ws);
   return hipGetLastError();
 }
@@ -772,7 +789,7 @@ hipError_t launch_topk_rounds_finish(const float* scores, int64_t rows, int64_t 
                                      int run, int sampled, int k, int32_t* indices, void* ws,
                                      hipStream_t stream) {
   const int64_t nr = n / R;
-  if (R != 8 * kThreads || kChunk != sampled * R || run != kSampleStride * sampled)
+  if (R != 8 * kThreads || kChunk != sampled * R || run != sample_stride(n) * sampled)
     return hipErrorInvalidValue;   // the sampled rounds are the sampled chunks
   hipLaunchKernelGGL(topk_compact_rounds<8>, dim3((unsigned)(nr / run * sampled), (unsigned)rows),
                      dim3(kThreads), 0, stream, scores, run, sampled, n, R, ws);

@@ -7,13 +7,14 @@
 namespace fathom {
 namespace topk {
 
-constexpr int kBins = 2048;   // radix digit: 11 bits
+constexpr int kBins = 2048;          // radix digit: 11 bits
+constexpr int kSampleChunk = 8192;   // keys per sampled chunk
+constexpr int kMaxSamples = 64;      // sampled chunks per row at most
 
 // Per-row workspace (32-bit words).
 enum : int {
   kS_TAU = 0,       // candidate cut
   kS_OVER,          // nonzero: a chunk had more candidates than its region
-  kS_NSAMPLE,       // keys in the sampled chunks
   kS_T,             // the k-th largest key (set by the resolve)
   kS_NEED,          // keys == T to take
   kS_ORDER,         // 1: the ordered write is left to topk_order
@@ -34,12 +35,24 @@ __host__ __device__ inline uint32_t region(int64_t n, int64_t R) {
   return (uint32_t)(cand_cap(n) / n_chunks(n, R));
 }
 
+// The sample: every stride-th chunk of 8192 keys, stride 8, raised so that
+// at most 64 chunks are sampled; each sampled chunk has its own histogram.
+__host__ __device__ inline int64_t sample_stride(int64_t n) {
+  const int64_t nc = n_chunks(n, kSampleChunk);
+  const int64_t s = (nc + kMaxSamples - 1) / kMaxSamples;
+  return s < 8 ? 8 : s;
+}
+__host__ __device__ inline int64_t n_samples(int64_t n) {
+  return (n_chunks(n, kSampleChunk) + sample_stride(n) - 1) / sample_stride(n);
+}
+
 __host__ __device__ inline size_t row_words(int64_t n, int64_t R) {
-  return (size_t)kBins + kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n, R);
+  return (size_t)kBins * n_samples(n) + kS_WORDS + 2 * (size_t)cand_cap(n) +
+         4 * (size_t)n_chunks(n, R);
 }
 
 struct RowWs {
-  uint32_t* hist;    // [kBins]: sample histogram
+  uint32_t* hist;    // [n_samples][kBins]: one histogram per sampled chunk
   uint32_t* st;      // [kS_WORDS]
   uint32_t* cand;    // [nchunks][region][2]: key, index
   uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
@@ -52,7 +65,7 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   RowWs r;
   r.region = region(n, R);
   r.hist = p;
-  r.st = p + kBins;
+  r.st = p + kBins * n_samples(n);
   r.cand = r.st + kS_WORDS;
   r.seg = r.cand + 2 * (size_t)cand_cap(n);
   r.ord = r.seg + 2 * (size_t)n_chunks(n, R);
