@@ -73,6 +73,11 @@ def parse():
                     help="skip timing the KLT fit and rotations (raw store only)")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip timing fathom_gather from a pinned host store")
+    ap.add_argument("--sweep", action="store_true",
+                    help="budget sweep over layers of the 1M-key shape with planted needles: "
+                         "recall against exact scores and scan rate per budget (one JSON object)")
+    ap.add_argument("--layers", default="0,17,35",
+                    help="sweep layers: comma-separated indices or 'all' (36)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print rocprofv3 csv output under DIR as text and exit (no GPU use)")
     return ap.parse_args()
@@ -152,10 +157,112 @@ def plan_stats(depths: np.ndarray):
     return d.sum(axis=1), (d > 0).sum(axis=1)
 
 
+def exact_topk(s: np.ndarray, k: int) -> np.ndarray:
+    """The k largest of s, ties to the lower index (the selection's order),
+    as sorted indices."""
+    part = np.argpartition(-s, k - 1)[:k]
+    kth = s[part].min()
+    above = np.flatnonzero(s > kth)
+    eq = np.flatnonzero(s == kth)
+    return np.sort(np.concatenate([above, eq[:k - len(above)]]))
+
+
+def run_sweep(args):
+    """Budgets 32..256 over layers of the 1M-key shape with needles: per
+    budget, recall of the top-k against the top-k of exact fp64 scores over
+    the fp16 keys, needle recall, plan sizes and the scan's event time."""
+    import torch
+
+    import fathom_inputs
+    import sparse_top_kv_fathom_amd as fk
+
+    layers = (list(range(fathom_inputs.SWEEP_LAYERS)) if args.layers == "all"
+              else [int(x) for x in args.layers.split(",")])
+    budgets = fathom_inputs.SWEEP_BUDGETS
+    w = fathom_inputs.WORKLOADS["q1m"]
+    H, G, n, d, k = w.groups, w.G, w.n, w.d, fathom_inputs.SWEEP_K
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ws = fk.topk_workspace(H * G, n, k, dev)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+    depths = torch.empty((H, d), dtype=torch.uint8, device=dev)
+    acc = {B: {"recall": [], "needle_own": [], "needle_all": [], "scan_ms": [], "topk_ms": [],
+               "T": [], "A": []} for B in budgets}
+    for L in layers:
+        t0 = time.perf_counter()
+        ins = fathom_inputs.sweep_inputs(L)
+        pos = ins.extra["needles"]
+        kd = torch.from_numpy(ins.k).to(dev)
+        planes, scales = fk.encode(kd)
+        del kd
+        q_d, var_d = torch.from_numpy(ins.q).to(dev), torch.from_numpy(ins.var).to(dev)
+        exact = []
+        for g in range(H):
+            s = ins.q[g].astype(np.float64) @ ins.k[g].astype(np.float64).T
+            exact.extend(exact_topk(s[h], k) for h in range(G))
+        for B in budgets:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            for rep in range(3):   # the last repetition is timed
+                fk.plan(q_d, var_d, B, depths=depths)
+                ev[0].record()
+                fk.scan(planes, scales, depths, q_d, n, scores=scores)
+                ev[1].record()
+                fk.topk(scores, k, indices=idx, workspace=ws)
+                ev[2].record()
+            torch.cuda.synchronize()
+            got = idx.cpu().numpy()
+            T, A = plan_stats(depths.cpu().numpy())
+            a = acc[B]
+            a["scan_ms"].append(ev[0].elapsed_time(ev[1]))
+            a["topk_ms"].append(ev[1].elapsed_time(ev[2]))
+            a["T"].extend(T.tolist())
+            a["A"].extend(A.tolist())
+            for r in range(H * G):
+                g, h = divmod(r, G)
+                sel = got[r]
+                a["recall"].append(np.intersect1d(sel, exact[r], assume_unique=True).size / k)
+                own = pos[g][h::G]
+                a["needle_own"].append(np.isin(own, sel).mean())
+                a["needle_all"].append(np.isin(pos[g], sel).mean())
+        del planes, scales
+        print("[sweep] layer %d done in %.1f s" % (L, time.perf_counter() - t0), file=sys.stderr,
+              flush=True)
+    rows = []
+    for B in budgets:
+        a = acc[B]
+        scan_ms = float(np.mean(a["scan_ms"]))
+        rows.append({
+            "budget_bits": B,
+            "code_bits_mean": float(np.mean(a["T"])),
+            "total_bits_mean": float(np.mean(np.array(a["T"]) + np.array(a["A"]) / 4.0)),
+            "active_channels_mean": float(np.mean(a["A"])),
+            "recall_mean": float(np.mean(a["recall"])),
+            "recall_min": float(np.min(a["recall"])),
+            "needle_recall_own_head": float(np.mean(a["needle_own"])),
+            "needle_recall_all": float(np.mean(a["needle_all"])),
+            "scan_ms": round(scan_ms, 4),
+            "topk_ms": round(float(np.mean(a["topk_ms"])), 4),
+            "keys_per_s": H * n / (scan_ms / 1e3),
+        })
+    print(json.dumps({
+        "sweep": "budget sweep, 1M keys x 8 KV heads per layer, G=%d, k=%d, %d needles per KV "
+                 "head (cosine %.1f); recall against the top-k of exact fp64 scores over the "
+                 "fp16 keys" % (G, k, fathom_inputs.SWEEP_NEEDLES, fathom_inputs.SWEEP_COSINE),
+        "layers": layers, "data": "synthetic", "rows": rows}))
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize)
+        return
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
+                  file=sys.stderr)
+            sys.exit(2)
+        run_sweep(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

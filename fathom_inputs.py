@@ -18,6 +18,9 @@ contexts on synthetic KV):
 * channel variance Var_j = the fp64 sample variance (ddof = 1) of the fp16
   column over all n keys of the group, cast to fp32.  (Appendix A's 0.127 for
   its channel 2 is the ddof = 1 variance of that channel's six values.)
+* budget sweep: 36 layers of the 1M-key shape, seed 5 + layer, with 32
+  needle keys per KV head aligned with the query heads in turn (cosine 0.6,
+  norm |sigma|_2), for recall against exact scores.
 
 Generator: numpy PCG64 via ``default_rng``; each group draws from its own
 child of ``SeedSequence(seed)`` so groups can be generated in parallel.
@@ -166,6 +169,56 @@ def make_inputs(groups: int, G: int, n: int, seed: int, d: int = D,
     q = make_queries(groups, G, seed if query_seed is None else query_seed, d)
     var = channel_variance(k)
     return Inputs(k=k, q=q, var=var, sigma=sigma)
+
+
+# The budget sweep: 36 layers of the 1M-key layer shape (seed 5 + layer),
+# budgets 32..256 code bits in steps of 16, k = 4096, 32 planted needles per
+# KV head.
+SWEEP_LAYERS = 36
+SWEEP_BUDGETS = tuple(range(32, 257, 16))
+SWEEP_K = 4096
+SWEEP_NEEDLES = 32
+SWEEP_COSINE = 0.6
+
+
+def sweep_seed(layer: int) -> int:
+    return 5 + layer
+
+
+def plant_needles(ins: Inputs, seed: int, count: int = SWEEP_NEEDLES,
+                  cosine: float = SWEEP_COSINE) -> np.ndarray:
+    """Overwrite `count` keys per group, at distinct uniformly drawn
+    positions, with needles aligned to the group's query heads in turn
+    (needle i to head i % G): k = |sigma|_2 (c qhat_h + sqrt(1 - c^2) w), w a
+    random unit vector orthogonal to qhat_h, built in fp64 and rounded to
+    fp16.  The channel variances are then recomputed over the keys that hold
+    the needles.  Returns the positions, [groups][count] int64."""
+    groups, n, d = ins.k.shape
+    G = ins.q.shape[1]
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x6e656564]))
+    pos = np.empty((groups, count), dtype=np.int64)
+    s = np.sqrt(1.0 - cosine * cosine)
+    for g in range(groups):
+        pos[g] = rng.choice(n, size=count, replace=False)
+        norm = float(np.sqrt(np.sum(ins.sigma[g].astype(np.float64) ** 2)))
+        for i in range(count):
+            qh = ins.q[g, i % G].astype(np.float64)
+            qh /= np.linalg.norm(qh)
+            w = rng.standard_normal(d)
+            w -= (w @ qh) * qh
+            w /= np.linalg.norm(w)
+            ins.k[g, pos[g, i]] = (norm * (cosine * qh + s * w)).astype(np.float16)
+    ins.var[...] = channel_variance(ins.k)
+    ins.extra["needles"] = pos
+    return pos
+
+
+def sweep_inputs(layer: int) -> Inputs:
+    """One layer of the budget sweep: the 1M-key layer shape with needles."""
+    w = WORKLOADS["q1m"]
+    ins = make_inputs(w.groups, w.G, w.n, sweep_seed(layer), w.d)
+    plant_needles(ins, sweep_seed(layer))
+    return ins
 
 
 def workload_inputs(name: str) -> Inputs:
