@@ -18,13 +18,12 @@
 //   klt_reduce— per (element block, group): the partial sums added in a
 //               fixed order, divided by n - 1;
 //   klt_eig   — per group, one 1024-thread workgroup: cyclic Jacobi on the
-//               covariance (upper
-//               triangle packed in LDS, fp64; the accumulated rotation in
-//               LDS, fp32), 64 disjoint rotations per step in round-robin
-//               order, sweeps until the off-diagonal mass falls below 1e-28
-//               of the total; eigenvalues descending, each eigenvector
-//               signed so that its first component of magnitude at least
-//               1/(2 sqrt(d)) is positive.
+//               covariance (upper triangle packed in LDS, fp64; the
+//               accumulated rotation in LDS, fp32), 64 disjoint rotations
+//               per step in round-robin order, sweeps until the off-diagonal
+//               mass falls below 1e-28 of the total (at most 24); eigenvalues
+//               descending, each eigenvector signed so that its first
+//               component of magnitude at least 1/(2 sqrt(d)) is positive.
 // Rotation (fp32, order fixed):
 //   k'_ij = fold over c ascending from +0 of fma(fl32(k_ic - mu_c), V_cj, .),
 //   rounded to binary16 nearest-even;  q'_hj = the same fold of q_hc.
