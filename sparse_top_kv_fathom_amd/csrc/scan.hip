@@ -21,17 +21,20 @@
 // words of one (channel, plane) are one 64-byte scalar load, and a word is
 // used directly as the per-lane carry-in of v_addc_co_u32, so plane p of a
 // block costs one VALU instruction:  x <- 2x + bit_p.  Starting from
-// 0x3C00 >> t, t steps leave x = 0x3C00 + c', the fp16 pattern of
-// 1 + c' * 2^-10, and one v_fma_mix_f32 (fp16 a, fp16 x, -a) gives m exactly.
-// Each head then costs one fp32 FMA: t + 1 + G VALU instructions per channel
-// and block.  The block offsets o fold on 8 * G lanes (lane = block * G +
+// 0x3F800000 >> t, t steps leave x = 0x3F800000 + c', the fp32 pattern of
+// 1 + c' * 2^-23, and one fp32 FMA with the block scale staged as
+// A = a * 2^13 gives m = A * x - A = a * c' * 2^-10 exactly (all operands in
+// vector registers, which issue faster than the mixed-precision form).  Each head
+// then costs one fp32 FMA: t + 1 + G VALU instructions per channel and
+// block.  The block offsets o fold on 8 * G lanes (lane = block * G +
 // head), one instruction per channel, and are added in the epilogue.
 //
 // Resources.  The scalar-load path of gfx950 moves only a few bytes per clock
 // per CU, so it carries nothing but plane words (the bytes the method reads).
 // Weights, offset coefficients and block scales come from LDS: w and e per
 // active channel once per workgroup, the scales of every active channel once
-// per round of kRoundBlocks blocks (staged with vector loads).
+// per round of kRoundBlocks blocks (staged with vector loads, stored in LDS
+// as fp32 A = a * 2^13).
 //
 // Latency.  A workgroup first touches every plane line of its round with
 // vector loads (one 4-byte load per 128-byte line pulls the line into L2) and
@@ -79,9 +82,13 @@ constexpr int kSlots = kD + 4;               // active slots + padding read by t
 constexpr int64_t kMaxFastBlocks = (int64_t(1) << 32) / (kD * kPlanes * 8) - 1;
 
 // x <- 2x + (bit lane of mask): the plane word is the carry-in lane mask.
+// The carry-out (always 0 here: x < 2^31) goes to a scratch scalar pair, not
+// to VCC: a stream of these adds interleaved with fp32 FMAs issues about a
+// third faster when they do not write VCC.
 __device__ __forceinline__ uint32_t shift_in_plane(uint32_t x, uint64_t mask) {
   uint32_t r;
-  asm("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(x), "s"(mask) : "vcc");
+  uint64_t co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=&s"(co) : "v"(x), "s"(mask));
   return r;
 }
 // The same as a volatile statement: it stays in program order with the other
@@ -89,7 +96,8 @@ __device__ __forceinline__ uint32_t shift_in_plane(uint32_t x, uint64_t mask) {
 // wait for that channel's loads).
 __device__ __forceinline__ uint32_t shift_in_plane_ordered(uint32_t x, uint64_t mask) {
   uint32_t r;
-  asm volatile("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(x), "s"(mask) : "vcc");
+  uint64_t co;
+  asm volatile("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=&s"(co) : "v"(x), "s"(mask));
   return r;
 }
 
@@ -146,10 +154,10 @@ struct ChanIter {
 template <int T, int G>
 struct ChanLoad {
   uint64_t pw[T][kNB];    // plane words (wave-uniform)
-  uint32_t a2[kNB / 2];   // fp16 scales of the blocks, two per dword (same in every lane)
+  float A[kNB];           // block scales as a * 2^13 (same in every lane)
   float w[G];             // per-head weights (same in every lane)
   float e;                // offset coefficient of this lane's head
-  uint32_t oa;            // fp16 scale of this lane's block (offset fold)
+  float oa;               // a * 2^13 of this lane's block (offset fold)
 };
 
 // Channel of depth T for the wave tile.  `issue_next` runs right after the
@@ -160,7 +168,7 @@ struct ChanLoad {
 template <int T, int G, class F>
 __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&acc)[kNB][G],
                                              float& o, F&& issue_next) {
-  constexpr uint32_t x0 = 0x3C00u >> T;
+  constexpr uint32_t x0 = 0x3F800000u >> T;
   uint32_t x[kNB];
   // The first instruction waits for this channel's loads; it must not move
   // above the previous channel's arithmetic, which hides their latency (the
@@ -178,13 +186,11 @@ __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&ac
     for (int b = 0; b < kNB; ++b) x[b] = shift_in_plane(x[b], L.pw[p][b]);
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
-    const uint32_t ab = (b & 1) ? (L.a2[b >> 1] >> 16) : L.a2[b >> 1];
-    const float a = half_lo(ab);
-    const float m = __builtin_fmaf(a, half_lo(x[b]), -a);
+    const float m = __builtin_fmaf(L.A[b], __builtin_bit_cast(float, x[b]), -L.A[b]);
 #pragma unroll
     for (int h = 0; h < G; ++h) acc[b][h] = __builtin_fmaf(L.w[h], m, acc[b][h]);
   }
-  o = __builtin_fmaf(L.e, half_lo(L.oa), o);
+  o = __builtin_fmaf(L.e, __builtin_ldexpf(L.oa, -13), o);
 #pragma unroll
   for (int b = 0; b < kNB; ++b)
 #pragma unroll
@@ -300,7 +306,7 @@ constexpr int kScalePasses = kD * kRoundBlocks / 8 / kThreads;                  
 template <int G>
 struct MainShared {
   SlotTables<G> tb;
-  alignas(16) uint16_t sc[kSlots][kRoundBlocks];   // this round's block scales
+  alignas(16) float sc[kSlots][kRoundBlocks];      // this round's block scales as a * 2^13
   uint32_t prow[kD * kPlanes];                     // byte offset of every active plane row
   uint8_t sj[kSlots];                              // channel of every active slot
 };
@@ -308,7 +314,7 @@ struct MainShared {
 struct MainCtx {
   const char* planes;   // the group's plane rows at the tile's first block
   uint32_t pstride;     // bytes between two planes of a channel (nb_store * 8)
-  const uint16_t* sc;   // this round's staged scales at the wave's first block
+  const float* sc;      // this round's staged scales at the wave's first block
   int ob, oh;           // this lane's block and head in the offset fold
 };
 
@@ -322,9 +328,9 @@ __device__ __forceinline__ void main_load_plane(const MainCtx& c, int j, int p, 
 template <int T, int G>
 __device__ __forceinline__ void main_load_lds(const MainCtx& c, const SlotTables<G>& tb, int slot,
                                               ChanLoad<T, G>& L) {
-  const uint16_t* sp = c.sc + slot * kRoundBlocks;
+  const float* sp = c.sc + slot * kRoundBlocks;
 #pragma unroll
-  for (int i = 0; i < kNB / 2; ++i) L.a2[i] = reinterpret_cast<const uint32_t*>(sp)[i];
+  for (int i = 0; i < kNB; ++i) L.A[i] = sp[i];
 #pragma unroll
   for (int h = 0; h < G; ++h) L.w[h] = tb.w[slot][h];
   L.e = tb.e[slot][c.oh];
@@ -430,8 +436,9 @@ __device__ __forceinline__ void round_issue(const MainShared<G>& sh, int nact, i
   }
 }
 
-// Write a round's scales to LDS and retire its L2 touches (their values are
-// folded into `sink`, which only keeps the loads alive).
+// Write a round's scales to LDS as a * 2^13 (exact) and retire its L2
+// touches (their values are folded into `sink`, which only keeps the loads
+// alive).
 template <int G>
 __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S,
                                             uint32_t& sink) {
@@ -442,7 +449,18 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const S
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
     const int slot = k >> 2, part = k & 3;
-    if (slot < nact) *reinterpret_cast<uint4*>(&sh.sc[slot][part * 8]) = S.st[i];
+    if (slot < nact) {
+      const uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
+      float f[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        f[2 * u] = __builtin_ldexpf(half_lo(wd[u]), 13);
+        f[2 * u + 1] = __builtin_ldexpf(half_lo(wd[u] >> 16), 13);
+      }
+      float4* dst = reinterpret_cast<float4*>(&sh.sc[slot][part * 8]);
+      dst[0] = make_float4(f[0], f[1], f[2], f[3]);
+      dst[1] = make_float4(f[4], f[5], f[6], f[7]);
+    }
   }
 }
 
@@ -612,12 +630,11 @@ __device__ __forceinline__ void tail_depth(const TailCtx& c, ChanIter it, int cn
       for (int b = 0; b < kNB; ++b) L.pw[p][b] = rp[p * c.nb_store + min(b, c.last)];
     const uint16_t* sp = c.scales + j * c.nb_store + c.blk0;
 #pragma unroll
-    for (int i2 = 0; i2 < kNB / 2; ++i2)
-      L.a2[i2] = (uint32_t)sp[min(2 * i2, c.last)] | ((uint32_t)sp[min(2 * i2 + 1, c.last)] << 16);
+    for (int b = 0; b < kNB; ++b) L.A[b] = __builtin_ldexpf(half_lo(sp[min(b, c.last)]), 13);
 #pragma unroll
     for (int h = 0; h < G; ++h) L.w[h] = c.q[h * kD + j] * sw;
     L.e = c.q[c.oh * kD + j] * se;
-    L.oa = sp[c.ob_c];
+    L.oa = __builtin_ldexpf(half_lo(sp[c.ob_c]), 13);
     compute_chan<T, G>(L, acc, o, [] {});
   }
 }
