@@ -98,13 +98,17 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ src, int64_t
   }
 }
 
+// Inclusive prefix sum over the wave with DPP moves: shifts by 1, 2, 4 and 8
+// lanes inside each row of 16 (lanes shifted in from outside the row read 0),
+// then the last lane of row 0 added to row 1 and of row 2 to row 3
+// (row_bcast:15), then lane 31 added to rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const uint32_t o = __shfl_up(v, s, 64);
-    if (lane >= s) v += o;
-  }
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -511,15 +515,35 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   constexpr int kW = kResolveThreads / 64, kU = 8;
 
   // Candidates of the row: the chunk counts, summed (and, when they fit,
-  // prefixed into s_gt for staging).
+  // prefixed into s_gt for staging).  With at most 128 chunks, the first 128
+  // candidate slots of the wave's chunks (w, w + 16, ...) are loaded at the
+  // same time as the counts and the overflow flag, before either is known,
+  // so staging them costs no second round trip to memory; slots past a
+  // chunk's count are never used.
   const bool small = nc <= kGroups;
+  const bool pre = nc <= kW * kU;
   uint32_t ncand = 0;
+  const int64_t per = (nc + kResolveThreads - 1) / kResolveThreads;
+  const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
+  const uint32_t first_count = c0 < c1 ? r.seg[2 * c0 + 1] : 0u;
+  const uint32_t over = r.st[kS_OVER];
+  uint2 e[kU][2];
+  if (pre) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t c = wave + u * kW;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t o = lane + 64 * h;
+        e[u][h] = (c < nc && o < src.region) ? src.cand[(uint32_t)c * src.region + o]
+                                             : make_uint2(0u, 0u);
+      }
+    }
+  }
   {
-    const int64_t per = (nc + kResolveThreads - 1) / kResolveThreads;
-    const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
     uint32_t mine = 0;
     for (int64_t c = c0; c < c1; ++c) {
-      const uint32_t t = r.seg[2 * c + 1];
+      const uint32_t t = c == c0 ? first_count : r.seg[2 * c + 1];
       if (small) s_gt[c] = t;
       mine += t;
     }
@@ -533,16 +557,30 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         run += t;
       }
   }
-  src.direct = ncand < (uint32_t)k || r.st[kS_OVER] != 0u;   // the guess failed
+  src.direct = ncand < (uint32_t)k || over != 0u;   // the guess failed
   const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;
   __syncthreads();
 
+  if (lds && pre) {
+    auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t c = wave + u * kW;
+      const uint32_t cnt = c < nc ? count(c) : 0u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t o = lane + 64 * h;
+        if (o < cnt) s_key[s_gt[c] + o] = e[u][h].x;
+      }
+    }
+  }
   if (lds) {
     // Stage the keys, chunk after chunk in index order: chunk c at
     // [s_gt[c], s_gt[c] + count(c)).  Wave w copies chunks w, w + 16, ...,
-    // eight chunks' first 128 candidates per batch of loads, then any rest.
+    // eight chunks' first 128 candidates per batch of loads (already loaded
+    // above when the row has at most 128 chunks), then any rest.
     auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
-    for (int64_t cb = wave; cb < nc; cb += kW * kU) {
+    for (int64_t cb = pre ? nc : wave; cb < nc; cb += kW * kU) {
       uint2 e[kU][2];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -655,6 +693,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   const int64_t per_group = (nc + kGroups - 1) / kGroups;
   const int ngroups = (int)((nc + per_group - 1) / per_group);
   if (lds) {   // per_group == 1: chunk c's keys are s_key[s_gt[c] .. s_gt[c + 1])
+    // Keys > T and == T per chunk, packed as gt | eq << 16 (both totals are
+    // at most kLdsCand < 2^16), prefixed in one pass; topk_order writes.
     for (int64_t c = wave; c < nc; c += kW) {
       const uint32_t o0 = s_gt[c], o1 = c + 1 < nc ? s_gt[c + 1] : ncand;
       uint32_t gt = 0, eq = 0;
@@ -664,13 +704,21 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         gt += (uint32_t)__popcll(__ballot(v && key > T));
         eq += (uint32_t)__popcll(__ballot(v && key == T));
       }
-      if (lane == 0) {
-        s_hist[c] = gt;
-        s_eq[c] = eq;
-      }
+      if (lane == 0) s_hist[c] = gt | (eq << 16);
     }
     __syncthreads();
-    for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_hist[g];
+    block_prefix_inplace<kResolveThreads>(s_hist, (int)nc, s_tmp);
+    __syncthreads();
+    for (int c = threadIdx.x; c < (int)nc; c += kResolveThreads) {
+      r.ord[2 * c] = s_hist[c] & 0xffffu;
+      r.ord[2 * c + 1] = s_hist[c] >> 16;
+    }
+    if (threadIdx.x == 0) {
+      r.st[kS_T] = T;
+      r.st[kS_NEED] = need;
+      r.st[kS_ORDER] = 1u;
+    }
+    return;
   } else {
     for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
     __syncthreads();
@@ -684,18 +732,6 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   block_prefix_inplace<kResolveThreads>(s_gt, ngroups, s_tmp);
   block_prefix_inplace<kResolveThreads>(s_eq, ngroups, s_tmp);
   __syncthreads();
-  if (lds) {   // topk_order writes the chunks
-    for (int c = threadIdx.x; c < ngroups; c += kResolveThreads) {
-      r.ord[2 * c] = s_gt[c];
-      r.ord[2 * c + 1] = s_eq[c];
-    }
-    if (threadIdx.x == 0) {
-      r.st[kS_T] = T;
-      r.st[kS_NEED] = need;
-      r.st[kS_ORDER] = 1u;
-    }
-    return;
-  }
   if (threadIdx.x == 0) r.st[kS_ORDER] = 0u;
   const uint64_t below = lanes_below();
   // One wave per group writes its selected indices in index order.
