@@ -411,40 +411,46 @@ struct Stage {
   uint32_t tv[kTouchPerThread > 0 ? kTouchPerThread : 1];
 };
 
+// Retire a round's L2 touches: their values are folded into `sink`, which
+// only keeps the loads alive.
+__device__ __forceinline__ void retire_touches(const Stage& S, uint32_t& sink) {
+#pragma unroll
+  for (int i = 0; i < kTouchPerThread; ++i) sink ^= S.tv[i];
+}
+
 template <int G>
 __device__ __forceinline__ void round_issue(const MainShared<G>& sh, int nact, int nrows,
                                             const char* planes_g, const char* scales_g,
                                             int64_t nb_store, int64_t r0, Stage& S) {
   int tid = threadIdx.x;
   opaque_v(tid);
+  // Every load is issued unconditionally (threads without a slot or row read
+  // channel 0's scales or plane row, and ignore them), so the compiler can
+  // count them exactly and the scale wait need not cover the touches.
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
     const int slot = k >> 2, part = k & 3;
-    S.st[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (slot < nact)
-      S.st[i] = *reinterpret_cast<const uint4*>(
-          scales_g + ((int64_t)sh.sj[slot] * nb_store + r0) * 2 + part * 16);
+    const int64_t ch = slot < nact ? (int64_t)sh.sj[slot] : 0;
+    S.st[i] = *reinterpret_cast<const uint4*>(scales_g + (ch * nb_store + r0) * 2 + part * 16);
   }
 #pragma unroll
   for (int i = 0; i < kTouchPerThread; ++i) {
     const int k = tid + i * kThreads;
-    S.tv[i] = 0u;
-    if (k / kTouches < nrows)
-      S.tv[i] = *reinterpret_cast<const uint32_t*>(planes_g + sh.prow[k / kTouches] + r0 * 8 +
-                                                   (k % kTouches) * (kRoundBlocks * 8 / kTouches));
+    const int row = k / kTouches;
+    const uint32_t off = row < nrows ? sh.prow[row] : 0u;
+    S.tv[i] = *reinterpret_cast<const uint32_t*>(planes_g + off + r0 * 8 +
+                                                 (k % kTouches) * (kRoundBlocks * 8 / kTouches));
   }
 }
 
-// Write a round's scales to LDS as a * 2^13 (exact) and retire its L2
-// touches (their values are folded into `sink`, which only keeps the loads
-// alive).
+// Write a round's scales to LDS as a * 2^13 (exact).  The scale loads were
+// issued before the L2 touches and vector loads complete in order, so this
+// waits for the scales only: the touches stay in flight while the first
+// channels are computed.
 template <int G>
-__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S,
-                                            uint32_t& sink) {
+__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kTouchPerThread; ++i) sink ^= S.tv[i];
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
@@ -554,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   uint32_t sink = 0u;
   Stage S;
   round_issue<G>(sh, nact, nrows, planes_g, scales_g, nb_store, round0 * kRoundBlocks, S);
-  round_stage<G>(sh, nact, S, sink);
+  round_stage<G>(sh, nact, S);
   __syncthreads();
 
   const bool olane = lane < kNB * G;
@@ -565,7 +571,10 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
   for (int r = 0; r < nr; ++r) {
     const int64_t r0 = (round0 + r) * kRoundBlocks;
-    if (r + 1 < nr) round_issue<G>(sh, nact, nrows, planes_g, scales_g, nb_store, r0 + kRoundBlocks, S);
+    if (r + 1 < nr) {
+      retire_touches(S, sink);
+      round_issue<G>(sh, nact, nrows, planes_g, scales_g, nb_store, r0 + kRoundBlocks, S);
+    }
 
     DepthMasks rm = dm;   // per-round copy: nothing derived from it is hoisted
 #pragma unroll
@@ -594,10 +603,11 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
-      round_stage<G>(sh, nact, S, sink);
+      round_stage<G>(sh, nact, S);
       __syncthreads();
     }
   }
+  retire_touches(S, sink);
   asm volatile("" ::"v"(sink));   // keeps the L2 touches alive
 }
 
