@@ -117,6 +117,7 @@ __device__ __forceinline__ float half_lo(uint32_t bits) {
 struct DepthMasks {
   uint64_t lo[kPlanes], hi[kPlanes];   // index 0: depth 4, ... 3: depth 1
   int count[kPlanes];
+  int tlo, thi;                        // depths of channels lane and 64 + lane
 };
 
 __device__ __forceinline__ DepthMasks depth_masks(const uint8_t* __restrict__ drow) {
@@ -124,6 +125,8 @@ __device__ __forceinline__ DepthMasks depth_masks(const uint8_t* __restrict__ dr
   const int tlo = min((int)drow[lane], kPlanes);        // depths above 4 read as 4
   const int thi = min((int)drow[64 + lane], kPlanes);
   DepthMasks m;
+  m.tlo = tlo;
+  m.thi = thi;
 #pragma unroll
   for (int i = 0; i < kPlanes; ++i) {
     m.lo[i] = __ballot(tlo == kPlanes - i);
@@ -309,6 +312,7 @@ struct MainShared {
   alignas(16) float sc[kSlots][kRoundBlocks];      // this round's block scales as a * 2^13
   uint32_t prow[kD * kPlanes];                     // byte offset of every active plane row
   uint8_t sj[kSlots];                              // channel of every active slot
+  uint8_t slot_of[kD];                             // slot of every channel (0xFF: inactive)
 };
 
 struct MainCtx {
@@ -418,22 +422,29 @@ __device__ __forceinline__ void retire_touches(const Stage& S, uint32_t& sink) {
   for (int i = 0; i < kTouchPerThread; ++i) sink ^= S.tv[i];
 }
 
-template <int G>
-__device__ __forceinline__ void round_issue(const MainShared<G>& sh, int nact, int nrows,
-                                            const char* planes_g, const char* scales_g,
-                                            int64_t nb_store, int64_t r0, Stage& S) {
+// The round's block scales of every channel (active or not: they are
+// requested before the plan is read, so the two loads share one round trip to
+// memory); thread 4c + k loads scales [8k, 8k + 8) of channel c.
+__device__ __forceinline__ void issue_scales(const char* scales_g, int64_t nb_store, int64_t r0,
+                                             Stage& S) {
   int tid = threadIdx.x;
   opaque_v(tid);
-  // Every load is issued unconditionally (threads without a slot or row read
-  // channel 0's scales or plane row, and ignore them), so the compiler can
-  // count them exactly and the scale wait need not cover the touches.
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int slot = k >> 2, part = k & 3;
-    const int64_t ch = slot < nact ? (int64_t)sh.sj[slot] : 0;
-    S.st[i] = *reinterpret_cast<const uint4*>(scales_g + (ch * nb_store + r0) * 2 + part * 16);
+    const int64_t ch = k >> 2;
+    S.st[i] = *reinterpret_cast<const uint4*>(scales_g + (ch * nb_store + r0) * 2 + (k & 3) * 16);
   }
+}
+
+// The round's L2 touches.  Every load is issued unconditionally (threads
+// without a row touch channel 0's first plane row and ignore it), so the
+// compiler can count them exactly and the scale wait need not cover them.
+template <int G>
+__device__ __forceinline__ void issue_touches(const MainShared<G>& sh, int nrows,
+                                              const char* planes_g, int64_t r0, Stage& S) {
+  int tid = threadIdx.x;
+  opaque_v(tid);
 #pragma unroll
   for (int i = 0; i < kTouchPerThread; ++i) {
     const int k = tid + i * kThreads;
@@ -449,13 +460,13 @@ __device__ __forceinline__ void round_issue(const MainShared<G>& sh, int nact, i
 // waits for the scales only: the touches stay in flight while the first
 // channels are computed.
 template <int G>
-__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S) {
+__device__ __forceinline__ void round_stage(MainShared<G>& sh, const Stage& S) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int slot = k >> 2, part = k & 3;
-    if (slot < nact) {
+    const int slot = sh.slot_of[k >> 2], part = k & 3;
+    if (slot != 0xFF) {
       const uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
       float f[8];
 #pragma unroll
@@ -513,6 +524,10 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   const char* scales_g = reinterpret_cast<const char*>(scales + grp * kD * nb_store);
   float* scores_g = scores + grp * G * n;
 
+  // The round's scales are requested before the plan is read, so the two
+  // loads share one round trip to memory.
+  Stage S;
+  issue_scales(scales_g, nb_store, round0 * kRoundBlocks, S);
   const DepthMasks dm = depth_masks(depths + grp * kD);
   int cnt[kPlanes];
 #pragma unroll
@@ -523,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   // Slot tables: waves 0 and 1 own channels 0..127 (thread j, channel j).
   if (tid < 2 * 64) {
     const int j = tid;
-    const int t = min((int)depths[grp * kD + j], kPlanes);
+    const int t = j < 64 ? dm.tlo : dm.thi;   // depth of channel j, as depth_masks read it
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     if (t > 0) {
       const int di = kPlanes - t;
@@ -552,15 +567,17 @@ __global__ __launch_bounds__(kThreads) void scan_main(
         sh.tb.e[slot][h] = qv * se;
       }
       sh.sj[slot] = (uint8_t)j;
+      sh.slot_of[j] = (uint8_t)slot;
       for (int p = 0; p < t; ++p) sh.prow[row + p] = ((uint32_t)j * kPlanes + p) * pstride;
+    } else {
+      sh.slot_of[j] = 0xFF;
     }
   }
   __syncthreads();
 
   uint32_t sink = 0u;
-  Stage S;
-  round_issue<G>(sh, nact, nrows, planes_g, scales_g, nb_store, round0 * kRoundBlocks, S);
-  round_stage<G>(sh, nact, S);
+  issue_touches<G>(sh, nrows, planes_g, round0 * kRoundBlocks, S);
+  round_stage<G>(sh, S);
   __syncthreads();
 
   const bool olane = lane < kNB * G;
@@ -573,7 +590,8 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     const int64_t r0 = (round0 + r) * kRoundBlocks;
     if (r + 1 < nr) {
       retire_touches(S, sink);
-      round_issue<G>(sh, nact, nrows, planes_g, scales_g, nb_store, r0 + kRoundBlocks, S);
+      issue_scales(scales_g, nb_store, r0 + kRoundBlocks, S);
+      issue_touches<G>(sh, nrows, planes_g, r0 + kRoundBlocks, S);
     }
 
     DepthMasks rm = dm;   // per-round copy: nothing derived from it is hoisted
@@ -603,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
-      round_stage<G>(sh, nact, S);
+      round_stage<G>(sh, S);
       __syncthreads();
     }
   }
