@@ -36,11 +36,11 @@
 // per round of kRoundBlocks blocks (staged with vector loads, stored in LDS
 // as fp32 A = a * 2^13).
 //
-// Latency.  A workgroup loads its round's scales and then touches every plane
-// line of the round with vector loads (one 4-byte load per 128-byte line pulls
-// the line into L2); it waits for the scales only and computes while the
-// touches are in flight, so its scalar loads hit L2 or a fill already on its
-// way.  (Touching a round ahead while computing the current one keeps twice
+// Latency.  A workgroup requests its round's scales (of all channels) before
+// it reads the plan, then touches every plane line of the round with vector
+// loads (one 4-byte load per 128-byte line pulls the line into L2); it waits
+// for the scales only and computes while the touches are in flight, so its
+// scalar loads hit L2 or a fill already on its way.  (Touching a round ahead while computing the current one keeps twice
 // the lines in flight and they are evicted from the 4 MB L2 of an XCD before
 // use; one round per workgroup measured fastest.)  Channels of one
 // depth form a loop with a compile-time plane count.  Scalar loads return out
