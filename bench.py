@@ -54,6 +54,7 @@ INT_PEAK_TOPS = CUS * 64 * CLOCK_GHZ / 1e3       # 39.32 T lane-ops/s
 CALIB_BYTES = 256 << 20                   # plain copy used to scale the HBM byte counters
 SCAN_SRC = os.path.join(ROOT, "sparse_top_kv_fathom_amd", "csrc", "scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_traffic.txt")
+INSTR_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_instructions.txt")
 
 
 def parse():
@@ -88,20 +89,30 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic():
-    """Scan HBM bytes per launch from the committed counter summary, or None
-    when it is missing or was taken on another scan source."""
+def recorded_counter(path, key):
+    """A per-launch scan figure from a committed counter summary, or None when
+    it is missing or was taken on another scan source."""
     try:
-        lines = open(TRAFFIC_FILE).read().splitlines()
+        lines = open(path).read().splitlines()
     except OSError:
         return None
-    kv = dict(l.split(":", 1) for l in lines if ":" in l and not l.startswith(" "))
+    kv = dict(l.split(":", 1) for l in lines if ":" in l and not l.startswith((" ", "#")))
     try:
         if kv["scan_source_sha256"].strip() != source_sha(SCAN_SRC):
             return None
-        return float(kv["scan_hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """Scan HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)."""
+    return recorded_counter(TRAFFIC_FILE, "scan_hbm_bytes_per_launch")
+
+
+def recorded_valu():
+    """Scan VALU instructions (wave64) per launch (SQ_INSTS_VALU)."""
+    return recorded_counter(INSTR_FILE, "scan_valu_instructions_per_launch")
 
 
 def short_name(name):
@@ -131,6 +142,11 @@ def summarize(dirs):
             for (kname, cname), v in sorted(agg.items()):
                 print("%-60s %-14s %6d %14.1f" % (kname, cname, len(v), sum(v) / len(v)))
                 means[(kname, cname)] = sum(v) / len(v)
+    valu = [v for (kname, cname), v in means.items()
+            if kname.startswith("fathom::scan_main<") and kname.endswith(", 0>") and cname == "SQ_INSTS_VALU"]
+    if valu:
+        print("scan_valu_instructions_per_launch: %.0f" % valu[0])
+        print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
     # HBM traffic of the scan: each byte counter (KiB per dispatch) scaled by
     # the factor that makes it read the known bytes of the plain copy.
     calib = [k for k in means if "neg" in k[0]]
@@ -502,6 +518,14 @@ def main():
         "alu_bound_ms": round(t_alu * 1e3, 4),
         "hbm_bound_ms": round(t_hbm * 1e3, 4),
         "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+    })
+    # VALU issue: wave64 VALU instructions per launch (SQ_INSTS_VALU, from the
+    # committed counter summary) over one issue per CU per clock.
+    valu = recorded_valu()
+    roof.update({
+        "valu_instructions_per_launch": valu,
+        "valu_issue_frac": (None if valu is None else
+                            round(valu / (scan_s * CUS * CLOCK_GHZ * 1e9), 4)),
     })
 
     keys = H * n
