@@ -202,20 +202,22 @@ __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&ac
 }
 
 // Epilogue: S = U + o (o of block b, head h sits in lane b * G + h); blocks
-// [0, store_to] of the tile are stored.
+// [0, store_to] of the tile are stored.  The offsets pass through the wave's
+// own kNB * G floats of LDS (`s_o`) and come back as broadcast reads, so the
+// adds take vector operands (dual issue) instead of one lane read and one
+// scalar-operand add per (block, head).
 template <int G>
 __device__ __forceinline__ void store_tile(const float (&acc)[kNB][G], float o, int store_to,
-                                           int64_t n, float* __restrict__ out) {
+                                           int64_t n, float* __restrict__ out, float* s_o) {
   const int lane = lane_id();
+  if (lane < kNB * G) s_o[lane] = o;
+  wave_lds_sync();
 #pragma unroll
   for (int b = 0; b < kNB; ++b) {
     if (b <= store_to) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float obh = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
-        __builtin_nontemporal_store(acc[b][h] + obh, out + h * n + b * kBlock + lane);
-      }
+      for (int h = 0; h < G; ++h)
+        __builtin_nontemporal_store(acc[b][h] + s_o[b * G + h], out + h * n + b * kBlock + lane);
     }
   }
 }
@@ -493,6 +495,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   static_assert(MODE == 0 || kRounds == 1, "candidate emission runs one round per workgroup");
   __shared__ MainShared<G> sh;
   __shared__ uint32_t s_emit[kWaves][8];
+  __shared__ float s_o[kWaves][kNB * G];
 
   // XCD-aware remap of the workgroup id (bijective on [0, gridDim.x)).
   const uint32_t nwg = gridDim.x;
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     main_depth<2, G, true>(c, sh.tb, rc[0] + rc[1], rc[2], ChanIter{rm.lo[2], rm.hi[2]}, acc, o);
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
-    store_tile<G>(acc, o, kNB - 1, n, scores_g + blk0 * kBlock);
+    store_tile<G>(acc, o, kNB - 1, n, scores_g + blk0 * kBlock, s_o[wave]);
     if (MODE == 2) emit_tile<G>(acc, o, tf, grp, blk0, EmitCtx{tws, n, round0}, s_emit);
 
     if (r + 1 < nr) {
@@ -672,6 +675,7 @@ __global__ __launch_bounds__(kThreads) void scan_tail(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t first_blk,
     int64_t nblk, int64_t n, int64_t wgs_per_group, float* __restrict__ scores) {
+  __shared__ float s_o[kWaves][kNB * G];
   const int64_t grp = blockIdx.x / wgs_per_group;
   const int64_t wg = blockIdx.x % wgs_per_group;
   const int lane = lane_id();
@@ -699,7 +703,7 @@ __global__ __launch_bounds__(kThreads) void scan_tail(
   tail_depth<3, G>(c, ChanIter{dm.lo[1], dm.hi[1]}, dm.count[1], acc, o);
   tail_depth<2, G>(c, ChanIter{dm.lo[2], dm.hi[2]}, dm.count[2], acc, o);
   tail_depth<1, G>(c, ChanIter{dm.lo[3], dm.hi[3]}, dm.count[3], acc, o);
-  store_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock);
+  store_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock, s_o[wave]);
 }
 
 template <int G>
