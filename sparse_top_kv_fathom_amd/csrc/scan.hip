@@ -36,11 +36,11 @@
 // per round of kRoundBlocks blocks (staged with vector loads, stored in LDS
 // as fp32 A = a * 2^13).
 //
-// Latency.  A workgroup requests its round's scales (of all channels) before
-// it reads the plan, then touches every plane line of the round with vector
-// loads (one 4-byte load per 128-byte line pulls the line into L2); it waits
-// for the scales only and computes while the touches are in flight, so its
-// scalar loads hit L2 or a fill already on its way.  (Touching a round ahead while computing the current one keeps twice
+// Latency.  A workgroup reads the plan and the queries in one round trip,
+// then loads its round's scales and touches every plane line of the round with
+// vector loads (one 4-byte load per 128-byte line pulls the line into L2); it
+// waits for the scales only and computes while the touches are in flight, so
+// its scalar loads hit L2 or a fill already on its way.  (Touching a round ahead while computing the current one keeps twice
 // the lines in flight and they are evicted from the 4 MB L2 of an XCD before
 // use; one round per workgroup measured fastest.)  Channels of one
 // depth form a loop with a compile-time plane count.  Scalar loads return out
@@ -120,10 +120,9 @@ struct DepthMasks {
   int tlo, thi;                        // depths of channels lane and 64 + lane
 };
 
-__device__ __forceinline__ DepthMasks depth_masks(const uint8_t* __restrict__ drow) {
-  const int lane = lane_id();
-  const int tlo = min((int)drow[lane], kPlanes);        // depths above 4 read as 4
-  const int thi = min((int)drow[64 + lane], kPlanes);
+__device__ __forceinline__ DepthMasks depth_masks(int dlo, int dhi) {
+  const int tlo = min(dlo, kPlanes);   // depths above 4 read as 4
+  const int thi = min(dhi, kPlanes);
   DepthMasks m;
   m.tlo = tlo;
   m.thi = thi;
@@ -314,7 +313,7 @@ struct MainShared {
   alignas(16) float sc[kSlots][kRoundBlocks];      // this round's block scales as a * 2^13
   uint32_t prow[kD * kPlanes];                     // byte offset of every active plane row
   uint8_t sj[kSlots];                              // channel of every active slot
-  uint8_t slot_of[kD];                             // slot of every channel (0xFF: inactive)
+  float qraw[kD][G];                               // the group's queries, by channel
 };
 
 struct MainCtx {
@@ -424,17 +423,20 @@ __device__ __forceinline__ void retire_touches(const Stage& S, uint32_t& sink) {
   for (int i = 0; i < kTouchPerThread; ++i) sink ^= S.tv[i];
 }
 
-// The round's block scales of every channel (active or not: they are
-// requested before the plan is read, so the two loads share one round trip to
-// memory); thread 4c + k loads scales [8k, 8k + 8) of channel c.
-__device__ __forceinline__ void issue_scales(const char* scales_g, int64_t nb_store, int64_t r0,
+// The round's block scales of every active slot: thread 4s + k loads scales
+// [8k, 8k + 8) of slot s (threads past the active slots load channel 0's and
+// ignore them, so every load is issued unconditionally).
+template <int G>
+__device__ __forceinline__ void issue_scales(const MainShared<G>& sh, int nact,
+                                             const char* scales_g, int64_t nb_store, int64_t r0,
                                              Stage& S) {
   int tid = threadIdx.x;
   opaque_v(tid);
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int64_t ch = k >> 2;
+    const int slot = k >> 2;
+    const int64_t ch = slot < nact ? (int64_t)sh.sj[slot] : 0;
     S.st[i] = *reinterpret_cast<const uint4*>(scales_g + (ch * nb_store + r0) * 2 + (k & 3) * 16);
   }
 }
@@ -462,13 +464,13 @@ __device__ __forceinline__ void issue_touches(const MainShared<G>& sh, int nrows
 // waits for the scales only: the touches stay in flight while the first
 // channels are computed.
 template <int G>
-__device__ __forceinline__ void round_stage(MainShared<G>& sh, const Stage& S) {
+__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int slot = sh.slot_of[k >> 2], part = k & 3;
-    if (slot != 0xFF) {
+    const int slot = k >> 2, part = k & 3;
+    if (slot < nact) {
       const uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
       float f[8];
 #pragma unroll
@@ -527,11 +529,15 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   const char* scales_g = reinterpret_cast<const char*>(scales + grp * kD * nb_store);
   float* scores_g = scores + grp * G * n;
 
-  // The round's scales are requested before the plan is read, so the two
-  // loads share one round trip to memory.
-  Stage S;
-  issue_scales(scales_g, nb_store, round0 * kRoundBlocks, S);
-  const DepthMasks dm = depth_masks(depths + grp * kD);
+  // The plan's depths and the group's queries are requested together, so they
+  // share one round trip to memory (the queries go straight to LDS: held in
+  // registers, their loads would be issued only where the plan is known).
+  const int dlo = depths[grp * kD + lane_id()], dhi = depths[grp * kD + 64 + lane_id()];
+  if (threadIdx.x < kD) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) sh.qraw[threadIdx.x][h] = q[(grp * G + h) * kD + threadIdx.x];
+  }
+  const DepthMasks dm = depth_masks(dlo, dhi);
   int cnt[kPlanes];
 #pragma unroll
   for (int i = 0; i < kPlanes; ++i) cnt[i] = dm.count[i];
@@ -565,22 +571,21 @@ __global__ __launch_bounds__(kThreads) void scan_main(
       const float se = __builtin_ldexpf(1.0f, -t) - 1.0f;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float qv = q[(grp * G + h) * kD + j];
+        const float qv = sh.qraw[j][h];   // written by this thread
         sh.tb.w[slot][h] = qv * sw;
         sh.tb.e[slot][h] = qv * se;
       }
       sh.sj[slot] = (uint8_t)j;
-      sh.slot_of[j] = (uint8_t)slot;
       for (int p = 0; p < t; ++p) sh.prow[row + p] = ((uint32_t)j * kPlanes + p) * pstride;
-    } else {
-      sh.slot_of[j] = 0xFF;
     }
   }
   __syncthreads();
 
   uint32_t sink = 0u;
+  Stage S;
+  issue_scales<G>(sh, nact, scales_g, nb_store, round0 * kRoundBlocks, S);
   issue_touches<G>(sh, nrows, planes_g, round0 * kRoundBlocks, S);
-  round_stage<G>(sh, S);
+  round_stage<G>(sh, nact, S);
   __syncthreads();
 
   const bool olane = lane < kNB * G;
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     const int64_t r0 = (round0 + r) * kRoundBlocks;
     if (r + 1 < nr) {
       retire_touches(S, sink);
-      issue_scales(scales_g, nb_store, r0 + kRoundBlocks, S);
+      issue_scales<G>(sh, nact, scales_g, nb_store, r0 + kRoundBlocks, S);
       issue_touches<G>(sh, nrows, planes_g, r0 + kRoundBlocks, S);
     }
 
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
-      round_stage<G>(sh, S);
+      round_stage<G>(sh, nact, S);
       __syncthreads();
     }
   }
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void scan_tail(
   const bool olane = lane < kNB * G;
   c.ob_c = min(olane ? lane / G : 0, c.last);
   c.oh = olane ? lane % G : 0;
-  const DepthMasks dm = depth_masks(depths + grp * kD);
+  const DepthMasks dm = depth_masks(depths[grp * kD + lane], depths[grp * kD + 64 + lane]);
 
   float acc[kNB][G];
 #pragma unroll
