@@ -19,16 +19,30 @@ namespace {
 
 constexpr int kWavesPerWg = 4;
 
-// Lane-wise max of two packed 16-bit magnitudes across the wave.
+// Max of two packed 16-bit lanes.
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Max of two packed 16-bit magnitudes across the wave, returned to every
+// lane: DPP moves take the max within quads (lanes xor 1, xor 2), within rows
+// of 16 (half mirror, mirror), then rows 0 and 2 into rows 1 and 3 (row
+// broadcast of lane 15) and lanes 0-31 into rows 2 and 3 (broadcast of lane
+// 31); lane 63 then holds the wave's max.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
 __device__ __forceinline__ uint32_t wave_max_u16x2(uint32_t v) {
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    uint32_t o = __shfl_xor(v, s, 64);
-    uint32_t lo = max(v & 0xffffu, o & 0xffffu);
-    uint32_t hi = max(v >> 16, o >> 16);
-    v = lo | (hi << 16);
-  }
-  return v;
+  v = max_u16x2(v, dpp<0xB1, 0xf>(v));    // quad_perm [1, 0, 3, 2]
+  v = max_u16x2(v, dpp<0x4E, 0xf>(v));    // quad_perm [2, 3, 0, 1]
+  v = max_u16x2(v, dpp<0x141, 0xf>(v));   // row_half_mirror
+  v = max_u16x2(v, dpp<0x140, 0xf>(v));   // row_mirror
+  v = max_u16x2(v, dpp<0x142, 0xa>(v));   // row_bcast:15 into rows 1 and 3
+  v = max_u16x2(v, dpp<0x143, 0xc>(v));   // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
