@@ -113,6 +113,26 @@ def test_topk_full_rows(fk, kind):
     assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
 
 
+def test_topk_crowded_chunks(fk):
+    """Rows of 1M scores with 300 and 200 large scores planted in two chunks
+    of 8192 keys that the cut's sample does not read (chunks 3 and 77): those
+    chunks hold more candidates than the 128 per chunk the resolve stages
+    straight from the loads it issues with the chunk counts, and fewer than a
+    chunk's region holds, so the rest of them are staged afterwards."""
+    rows, n, k = 2, 1 << 20, 4096
+    scores = fathom_inputs.random_scores(rows, n, seed=79, kind="normal")
+    rng = np.random.default_rng(80)
+    sd = float(scores.std())
+    for r in range(rows):
+        for chunk, count in ((3, 300), (77, 200)):
+            pos = chunk * 8192 + rng.choice(8192, count, replace=False)
+            scores[r, pos] = (sd * rng.uniform(3.0, 5.0, count)).astype(np.float32)
+    say("topk crowded chunks rows=%d n=%d k=%d" % (rows, n, k))
+    gpu = _topk(fk, scores, k)
+    ref = oracle.topk(scores, k)
+    assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+
+
 def test_topk_repeatable(fk):
     scores = fathom_inputs.random_scores(8, 50000, seed=41, kind="ties")
     say("topk repeat x3")
