@@ -156,11 +156,49 @@ struct ChanIter {
 template <int T, int G>
 struct ChanLoad {
   uint64_t pw[T][kNB];    // plane words (wave-uniform)
-  float A[kNB];           // block scales as a * 2^13 (same in every lane)
+  float A[kNB];           // block scales as a * 2^13; a * 2^-10 at depth 1 (same in every lane)
   float w[G];             // per-head weights (same in every lane)
   float e;                // offset coefficient of this lane's head
-  float oa;               // a * 2^13 of this lane's block (offset fold)
+  float oa;               // the scale of this lane's block as in A (offset fold)
 };
+
+// acc[h] = fma(w[h], m, acc[h]) for NH heads, in the lanes whose bit is set
+// in `mask` only (EXEC is narrowed to the mask and restored inside the one
+// asm statement, so no other instruction runs under it).
+template <int NH>
+__device__ __forceinline__ void masked_fmac(uint64_t mask, float* acc, const float* w, float m) {
+  uint64_t save;
+  if constexpr (NH == 1) {
+    asm volatile("s_and_saveexec_b64 %0, %2\n\tv_fmac_f32 %1, %3, %4\n\ts_mov_b64 exec, %0"
+                 : "=&s"(save), "+v"(acc[0]) : "s"(mask), "v"(w[0]), "v"(m) : "scc");
+  } else if constexpr (NH == 2) {
+    asm volatile("s_and_saveexec_b64 %0, %3\n\tv_fmac_f32 %1, %4, %6\n\tv_fmac_f32 %2, %5, %6\n\t"
+                 "s_mov_b64 exec, %0"
+                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1])
+                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(m) : "scc");
+  } else if constexpr (NH == 3) {
+    asm volatile("s_and_saveexec_b64 %0, %4\n\tv_fmac_f32 %1, %5, %8\n\tv_fmac_f32 %2, %6, %8\n\t"
+                 "v_fmac_f32 %3, %7, %8\n\ts_mov_b64 exec, %0"
+                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])
+                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(m) : "scc");
+  } else {
+    static_assert(NH == 4, "one to four heads per masked statement");
+    asm volatile("s_and_saveexec_b64 %0, %5\n\tv_fmac_f32 %1, %6, %10\n\tv_fmac_f32 %2, %7, %10\n\t"
+                 "v_fmac_f32 %3, %8, %10\n\tv_fmac_f32 %4, %9, %10\n\ts_mov_b64 exec, %0"
+                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
+                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(m) : "scc");
+  }
+}
+
+template <int G, int H0 = 0>
+__device__ __forceinline__ void masked_heads(uint64_t mask, float (&acc)[G], const float (&w)[G],
+                                             float m) {
+  if constexpr (H0 < G) {
+    constexpr int NH = G - H0 < 4 ? G - H0 : 4;
+    masked_fmac<NH>(mask, acc + H0, w + H0, m);
+    masked_heads<G, H0 + NH>(mask, acc, w, m);
+  }
+}
 
 // Channel of depth T for the wave tile.  `issue_next` runs right after the
 // first instruction that reads this channel's registers (which carries the
@@ -170,6 +208,23 @@ struct ChanLoad {
 template <int T, int G, class F>
 __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&acc)[kNB][G],
                                              float& o, F&& issue_next) {
+  if constexpr (T == 1) {
+    // Depth 1: c' is the plane bit, so m = a * c' * 2^-10 is either 0, which
+    // leaves every accumulator unchanged (fma(w, 0, U) = U, U never -0), or
+    // a * 2^-10, staged as A for depth-1 channels.  The head FMAs run in the
+    // lanes whose bit is set, with the plane word as the execution mask: the
+    // same results as the general form without its two per-block steps.
+    __builtin_amdgcn_sched_barrier(0);
+    masked_heads<G>(L.pw[0][0], acc[0], L.w, L.A[0]);   // waits for this channel's loads
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 1; b < kNB; ++b) masked_heads<G>(L.pw[0][b], acc[b], L.w, L.A[b]);
+    o = __builtin_fmaf(L.e, __builtin_ldexpf(L.oa, 10), o);
+    asm volatile("" : "+v"(o));
+    return;
+  }
   constexpr uint32_t x0 = 0x3F800000u >> T;
   uint32_t x[kNB];
   // The first instruction waits for this channel's loads; it must not move
@@ -464,7 +519,8 @@ __device__ __forceinline__ void issue_touches(const MainShared<G>& sh, int nrows
 // waits for the scales only: the touches stay in flight while the first
 // channels are computed.
 template <int G>
-__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const Stage& S) {
+__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int first1,
+                                            const Stage& S) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
@@ -472,11 +528,12 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, const S
     const int slot = k >> 2, part = k & 3;
     if (slot < nact) {
       const uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
+      const int ex = slot >= first1 ? -10 : 13;   // depth-1 slots hold a * 2^-10
       float f[8];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        f[2 * u] = __builtin_ldexpf(half_lo(wd[u]), 13);
-        f[2 * u + 1] = __builtin_ldexpf(half_lo(wd[u] >> 16), 13);
+        f[2 * u] = __builtin_ldexpf(half_lo(wd[u]), ex);
+        f[2 * u + 1] = __builtin_ldexpf(half_lo(wd[u] >> 16), ex);
       }
       float4* dst = reinterpret_cast<float4*>(&sh.sc[slot][part * 8]);
       dst[0] = make_float4(f[0], f[1], f[2], f[3]);
@@ -585,7 +642,8 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   Stage S;
   issue_scales<G>(sh, nact, scales_g, nb_store, round0 * kRoundBlocks, S);
   issue_touches<G>(sh, nrows, planes_g, round0 * kRoundBlocks, S);
-  round_stage<G>(sh, nact, S);
+  const int first1 = cnt[0] + cnt[1] + cnt[2];   // first depth-1 slot
+  round_stage<G>(sh, nact, first1, S);
   __syncthreads();
 
   const bool olane = lane < kNB * G;
@@ -629,7 +687,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
-      round_stage<G>(sh, nact, S);
+      round_stage<G>(sh, nact, first1, S);
       __syncthreads();
     }
   }
@@ -665,12 +723,13 @@ __device__ __forceinline__ void tail_depth(const TailCtx& c, ChanIter it, int cn
 #pragma unroll
       for (int b = 0; b < kNB; ++b) L.pw[p][b] = rp[p * c.nb_store + min(b, c.last)];
     const uint16_t* sp = c.scales + j * c.nb_store + c.blk0;
+    constexpr int ex = T == 1 ? -10 : 13;   // depth 1 takes a * 2^-10, as staged
 #pragma unroll
-    for (int b = 0; b < kNB; ++b) L.A[b] = __builtin_ldexpf(half_lo(sp[min(b, c.last)]), 13);
+    for (int b = 0; b < kNB; ++b) L.A[b] = __builtin_ldexpf(half_lo(sp[min(b, c.last)]), ex);
 #pragma unroll
     for (int h = 0; h < G; ++h) L.w[h] = c.q[h * kD + j] * sw;
     L.e = c.q[c.oh * kD + j] * se;
-    L.oa = __builtin_ldexpf(half_lo(sp[c.ob_c]), 13);
+    L.oa = __builtin_ldexpf(half_lo(sp[c.ob_c]), ex);
     compute_chan<T, G>(L, acc, o, [] {});
   }
 }
