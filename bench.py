@@ -30,6 +30,7 @@ source they were taken on; a different source reports traffic null.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import csv
 import glob
 import hashlib
@@ -55,6 +56,62 @@ CALIB_BYTES = 256 << 20                   # plain copy used to scale the HBM byt
 SCAN_SRC = os.path.join(ROOT, "sparse_top_kv_fathom_amd", "csrc", "scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_traffic.txt")
 INSTR_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_instructions.txt")
+
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP timing event recorded on torch's current stream (the stream the
+    library launches on), created with hipEventDisableSystemFence.
+
+    Recording a default event ends with a system-scope release: a cache
+    writeback and invalidation that leaves the GPU idle for several
+    microseconds around every record and slows the work after it.  These
+    events only take timestamps; they are read after a device synchronize.
+    Same interface as torch.cuda.Event: record(), elapsed_time(other) in ms.
+    """
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        if cls._lib is None:
+            # The HIP runtime torch has loaded (one runtime per process).
+            path = next(line.split()[-1] for line in open("/proc/self/maps")
+                        if "libamdhip64" in line)
+            lib = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [P, P]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+            lib.hipEventDestroy.argtypes = [P]
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        rc = self._hip().hipEventCreateWithFlags(ctypes.byref(self.h),
+                                                 HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed: %d" % rc)
+
+    def record(self):
+        import torch
+        rc = self._hip().hipEventRecord(self.h, ctypes.c_void_p(
+            torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed: %d" % rc)
+
+    def elapsed_time(self, other) -> float:
+        ms = ctypes.c_float()
+        rc = self._hip().hipEventElapsedTime(ctypes.byref(ms), self.h, other.h)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed: %d" % rc)
+        return ms.value
+
+    def __del__(self):
+        if self.h and TimingEvent._lib is not None:
+            TimingEvent._lib.hipEventDestroy(self.h)
 
 
 def parse():
@@ -401,9 +458,9 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
 
-    # The timed steps: events around the scan only (its launch time for the
-    # roofline); nothing else between the calls.
-    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # The timed steps: fence-free timing events around the scan only (its
+    # launch time for the roofline); nothing else between the calls.
+    sevs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -419,7 +476,7 @@ def main():
     scan_ms_timed = float(np.mean([e[0].elapsed_time(e[1]) for e in sevs]))
 
     # The same steps again with events between all stages, for the breakdown.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
         step(args.warmup + s, evs[s])
@@ -429,8 +486,8 @@ def main():
 
     # The fused call on the same inputs, timed after the steps.
     for s in range(args.warmup):
-        fused(s, [torch.cuda.Event(enable_timing=True) for _ in range(2)])
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        fused(s, [TimingEvent() for _ in range(2)])
+    fev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
         fused(args.warmup + s, fev[s])
