@@ -178,6 +178,21 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
                 int32_t d, int64_t n, float* scores, void* stream);
 
 /*
+ * fathom_scan_timed — fathom_scan, the same work and results, with the time
+ * its kernels take recorded in two caller-created HIP events (hipEvent_t
+ * passed as void*, both non-null): start_event takes the start timestamp of
+ * the scan's first kernel and stop_event the end timestamp of its last, from
+ * the kernels' own dispatches, so no marker packet is added to the stream
+ * between the scan and the work around it.  hipEventElapsedTime(start,
+ * stop) then gives the scan's duration once stop_event has completed.  For
+ * callers that time the scan inside a pipeline (the benchmark's roofline).
+ */
+int fathom_scan_timed(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                      const uint8_t* depths, const float* q, int64_t groups, int32_t G,
+                      int32_t d, int64_t n, float* scores, void* start_event, void* stop_event,
+                      void* stream);
+
+/*
  * fathom_topk — the k highest scores of every row (per query head, §2).
  *
  * Order: score descending, ties broken by the lower index; -0 equals +0.

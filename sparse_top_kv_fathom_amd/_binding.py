@@ -34,7 +34,8 @@ STATUS = {
     -8: "FATHOM_ERR_NOT_PINNED",
 }
 
-EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+            "fathom_scan_timed", "fathom_topk",
             "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
             "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
             "fathom_klt_rotate_queries",
@@ -63,6 +64,7 @@ def lib():
         L.fathom_plan.argtypes = [P, P, I64, I32, I32, I32, P, P, P, P]
         L.fathom_plan_fixed.argtypes = [P, P, I64, I32, I32, I32, I32, P, P]
         L.fathom_scan.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P]
+        L.fathom_scan_timed.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P, P, P]
         L.fathom_topk.argtypes = [P, I64, I64, I32, P, P, SZ, P]
         L.fathom_topk_workspace_bytes.argtypes = [I64, I64, I32]
         L.fathom_scan_topk.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, I32, P, P, P, SZ, P]
@@ -78,7 +80,8 @@ def lib():
         L.fathom_status_string.argtypes = [ctypes.c_int]
         L.fathom_status_string.restype = ctypes.c_char_p
         L.fathom_abi_version.argtypes = []
-        for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+        for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+                  "fathom_scan_timed", "fathom_topk",
                   "fathom_scan_topk", "fathom_gather", "fathom_klt_fit",
                   "fathom_klt_rotate_keys", "fathom_klt_rotate_queries", "fathom_abi_version"):
             getattr(L, f).restype = ctypes.c_int
@@ -187,19 +190,28 @@ def plan_fixed(mode: str, param: int, q: torch.Tensor | None = None,
 
 
 def scan(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: torch.Tensor,
-         n: int, scores: torch.Tensor | None = None, stream=None):
-    """fathom_scan: scores [groups][G][n] fp32 of the first n keys of the store."""
+         n: int, scores: torch.Tensor | None = None, stream=None, events=None):
+    """fathom_scan: scores [groups][G][n] fp32 of the first n keys of the store.
+
+    events: None, or (start, stop) raw hipEvent_t handles (ints or
+    ctypes.c_void_p) that fathom_scan_timed records from the scan kernels' own
+    start and end timestamps."""
     groups, G, d = q.shape
     nb_store = planes.shape[-1]
     ps, ss = store_shapes(groups, nb_store, d)
     if scores is None:
         scores = torch.empty((groups, G, n), dtype=torch.float32, device=q.device)
-    st = lib().fathom_scan(
-        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
-        nb_store, _dev(depths, "depths", torch.uint8, (groups, d)), _dev(q, "q", torch.float32),
-        groups, G, d, int(n), _dev(scores, "scores", torch.float32, (groups, G, n)),
-        _stream(stream))
-    _check(st, "fathom_scan")
+    args = (_dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+            nb_store, _dev(depths, "depths", torch.uint8, (groups, d)),
+            _dev(q, "q", torch.float32), groups, G, d, int(n),
+            _dev(scores, "scores", torch.float32, (groups, G, n)))
+    if events is None:
+        st = lib().fathom_scan(*args, _stream(stream))
+        _check(st, "fathom_scan")
+    else:
+        e0, e1 = (e if isinstance(e, ctypes.c_void_p) else ctypes.c_void_p(e) for e in events)
+        st = lib().fathom_scan_timed(*args, e0, e1, _stream(stream))
+        _check(st, "fathom_scan_timed")
     return scores
 
 

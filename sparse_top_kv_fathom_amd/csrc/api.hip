@@ -117,6 +117,27 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
                                        static_cast<hipStream_t>(stream)));
 }
 
+int fathom_scan_timed(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
+                      const uint8_t* depths, const float* q, int64_t groups, int32_t G,
+                      int32_t d, int64_t n, float* scores, void* start_event, void* stop_event,
+                      void* stream) {
+  if (!start_event || !stop_event) return FATHOM_ERR_NULL_ARG;
+  if (!planes || !scales || !depths || !q || !scores) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups ||
+      !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < n / fathom::kBlock || nb_store >= kMaxTokens / fathom::kBlock)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (!aligned(planes, 8) || !aligned(scales, 4) || !aligned(q, 4) || !aligned(scores, 4))
+    return FATHOM_ERR_ALIGNMENT;
+  if (fathom::scan_max_workgroups(groups, n) > kMaxWorkgroups) return FATHOM_ERR_BAD_SHAPE;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_scan(planes, scales, nb_store, depths, q, groups, G, n, scores,
+                                       static_cast<hipStream_t>(stream),
+                                       static_cast<hipEvent_t>(start_event),
+                                       static_cast<hipEvent_t>(stop_event)));
+}
+
 int fathom_gather(const uint64_t* host_planes, const uint16_t* host_scales, int64_t nb_store,
                   const uint8_t* depths, int64_t groups, int32_t d, int64_t n, uint64_t* planes,
                   uint16_t* scales, void* stream) {

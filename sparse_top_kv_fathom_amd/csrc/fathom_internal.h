@@ -25,9 +25,12 @@ hipError_t launch_plan(const float* q, const float* var, int64_t groups, int G,
 
 hipError_t launch_plan_fixed(const float* q, const float* stat, int64_t groups, int G, int mode,
                              int param, uint8_t* depths, hipStream_t stream);
+// ev_start / ev_stop (may be null): recorded from the first and the last
+// kernel's own start and end timestamps.
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                        const uint8_t* depths, const float* q, int64_t groups, int G,
-                       int64_t n, float* scores, hipStream_t stream);
+                       int64_t n, float* scores, hipStream_t stream,
+                       hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 // Workgroups fathom_scan launches for `groups` groups of n keys.
 int64_t scan_max_workgroups(int64_t groups, int64_t n);

@@ -55,6 +55,8 @@
 // the 8 XCDs round-robin).  The blocks after the last whole round go to a
 // small tail kernel with per-block clamped loads, which also serves stores
 // whose offsets exceed 32 bits or whose scale rows are not 16-byte aligned.
+#include <hip/hip_ext.h>
+
 #include "fathom_internal.h"
 #include "topk_layout.h"
 
@@ -778,26 +780,41 @@ __global__ __launch_bounds__(kThreads) void scan_tail(
   store_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock, s_o[wave]);
 }
 
+// With timing events, the first launch records ev_start and the last one
+// ev_stop from the kernels' own dispatch timestamps (no marker packets).
 template <int G>
 void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                    const uint8_t* depths, const float* q, int64_t groups, int64_t n,
-                   float* scores, hipStream_t stream) {
+                   float* scores, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                   hipEvent_t ev_stop = nullptr) {
   const int64_t nblk = n / kBlock;
   // Main kernel: 32-bit offsets and 16-byte aligned scale rows.
   const bool fast = nb_store <= kMaxFastBlocks && nb_store % 8 == 0 &&
                     (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
   const int64_t nrounds = fast ? nblk / kRoundBlocks : 0;
+  const int64_t first = nrounds * kRoundBlocks;
+  const bool timed = ev_start != nullptr || ev_stop != nullptr;
   if (nrounds > 0) {
     const int64_t wgs = (nrounds + kRounds - 1) / kRounds;
-    hipLaunchKernelGGL((scan_main<G, 0>), dim3((unsigned)(wgs * groups)), dim3(kThreads), 0,
-                       stream, planes, scales, nb_store, depths, q, nrounds, n, wgs, scores,
-                       (void*)nullptr);
+    const dim3 grid((unsigned)(wgs * groups)), block(kThreads);
+    if (timed)
+      hipExtLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, ev_start,
+                            first < nblk ? nullptr : ev_stop, 0u, planes, scales, nb_store,
+                            depths, q, nrounds, n, wgs, scores, (void*)nullptr);
+    else
+      hipLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, planes, scales, nb_store,
+                         depths, q, nrounds, n, wgs, scores, (void*)nullptr);
   }
-  const int64_t first = nrounds * kRoundBlocks;
   if (first < nblk) {
     const int64_t wgs = (nblk - first + kRoundBlocks - 1) / kRoundBlocks;
-    hipLaunchKernelGGL(scan_tail<G>, dim3((unsigned)(wgs * groups)), dim3(kThreads), 0, stream,
-                       planes, scales, nb_store, depths, q, first, nblk, n, wgs, scores);
+    const dim3 grid((unsigned)(wgs * groups)), block(kThreads);
+    if (timed)
+      hipExtLaunchKernelGGL(scan_tail<G>, grid, block, 0, stream,
+                            nrounds > 0 ? nullptr : ev_start, ev_stop, 0u, planes, scales,
+                            nb_store, depths, q, first, nblk, n, wgs, scores);
+    else
+      hipLaunchKernelGGL(scan_tail<G>, grid, block, 0, stream, planes, scales, nb_store, depths,
+                         q, first, nblk, n, wgs, scores);
   }
 }
 
@@ -838,16 +855,41 @@ int64_t scan_max_workgroups(int64_t groups, int64_t n) {
 
 hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                        const uint8_t* depths, const float* q, int64_t groups, int G, int64_t n,
-                       float* scores, hipStream_t stream) {
+                       float* scores, hipStream_t stream, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
   switch (G) {
-    case 1: launch_scan_g<1>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 2: launch_scan_g<2>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 3: launch_scan_g<3>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 4: launch_scan_g<4>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 5: launch_scan_g<5>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 6: launch_scan_g<6>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 7: launch_scan_g<7>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
-    case 8: launch_scan_g<8>(planes, scales, nb_store, depths, q, groups, n, scores, stream); break;
+    case 1:
+      launch_scan_g<1>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 2:
+      launch_scan_g<2>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 3:
+      launch_scan_g<3>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 4:
+      launch_scan_g<4>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 5:
+      launch_scan_g<5>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 6:
+      launch_scan_g<6>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 7:
+      launch_scan_g<7>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
+    case 8:
+      launch_scan_g<8>(planes, scales, nb_store, depths, q, groups, n, scores, stream, ev_start,
+                        ev_stop);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -38,3 +38,38 @@ def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
         return "equal"
     i = tuple(bad[0])
     return "%d mismatches, first at %s: %r vs %r" % (len(bad), i, a[i], b[i])
+
+
+class HipEvent:
+    """A raw hipEvent_t from the HIP runtime torch has loaded (for the timed
+    scan entry point): handle in .h, elapsed_ms(other) after a synchronize."""
+    _lib = None
+
+    @classmethod
+    def _hip(cls):
+        import ctypes
+        if cls._lib is None:
+            path = next(line.split()[-1] for line in open("/proc/self/maps")
+                        if "libamdhip64" in line)
+            lib = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            lib.hipEventCreate.argtypes = [ctypes.POINTER(P)]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+            lib.hipEventDestroy.argtypes = [P]
+            cls._lib = lib
+        return cls._lib
+
+    def __init__(self):
+        import ctypes
+        self.h = ctypes.c_void_p()
+        assert self._hip().hipEventCreate(ctypes.byref(self.h)) == 0
+
+    def elapsed_ms(self, other) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        assert self._hip().hipEventElapsedTime(ctypes.byref(ms), self.h, other.h) == 0
+        return ms.value
+
+    def __del__(self):
+        if self.h and HipEvent._lib is not None:
+            HipEvent._lib.hipEventDestroy(self.h)

@@ -41,7 +41,8 @@ def _gpu_visible():
 
 def test_header_declares_the_calls():
     names = declared()
-    for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan", "fathom_topk",
+    for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+              "fathom_scan_timed", "fathom_topk",
               "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
               "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
               "fathom_klt_rotate_queries",
@@ -242,6 +243,23 @@ def test_scan_validation(L):
     a = list(args); a[8] = 0
     assert s(*a) == BAD_SHAPE
     a = list(args); a[5] = 0
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[0] = P(4)
+    assert s(*a) == ALIGN
+
+
+def test_scan_timed_validation(L):
+    s = L.fathom_scan_timed
+    args = [FAKE, FAKE, 64, FAKE, FAKE, 1, 4, 128, 4096, FAKE, FAKE, FAKE, None]
+    for i in (0, 1, 3, 4, 9, 10, 11):
+        a = list(args)
+        a[i] = None
+        assert s(*a) == NULL_ARG
+    a = list(args); a[2] = 63
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[6] = 0
+    assert s(*a) == BAD_SHAPE
+    a = list(args); a[8] = 4095
     assert s(*a) == BAD_SHAPE
     a = list(args); a[0] = P(4)
     assert s(*a) == ALIGN

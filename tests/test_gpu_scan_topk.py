@@ -11,7 +11,7 @@ import pytest
 
 import fathom_inputs
 import oracle
-from gpu_util import first_mismatch, say, to_dev, to_host
+from gpu_util import HipEvent, first_mismatch, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -76,6 +76,26 @@ def test_scan_random_depths_and_store_capacity(fk):
         say("scan random depths n=%d nb_store=90" % n)
         gpu = _scan(fk, planes, scales, depths, ins.q, n)
         _check_scores(gpu, planes, scales, depths, ins.q, n)
+
+
+def test_scan_timed_same_scores(fk):
+    """fathom_scan_timed: the same scores bit for bit, and a positive kernel
+    time in its events, with the main kernel only (n = 64 * 64), the main
+    and the tail kernel (64 * 101) and the tail kernel only (64 * 5)."""
+    import torch
+    ins = fathom_inputs.make_inputs(2, 4, 64 * 101, seed=41)
+    planes, scales, _ = oracle.encode(ins.k)
+    depths, _, _ = oracle.plan(ins.q, ins.var, 92)
+    dp, ds, dd, dq = to_dev(planes), to_dev(scales), to_dev(depths), to_dev(ins.q)
+    for n in (64 * 64, 64 * 101, 64 * 5):
+        say("scan timed n=%d" % n)
+        e0, e1 = HipEvent(), HipEvent()
+        s = fk.scan(dp, ds, dd, dq, n, events=(e0.h, e1.h))
+        torch.cuda.synchronize()
+        gpu = to_host(s)
+        ref = oracle.scan_ref32(planes, scales, depths, ins.q, n)
+        assert np.array_equal(gpu.view(np.uint32), ref.view(np.uint32)), first_mismatch(gpu, ref)
+        assert e0.elapsed_ms(e1) > 0.0
 
 
 def _topk(fk, scores, k):
