@@ -26,15 +26,17 @@
 // A = a * 2^13 gives m = A * x - A = a * c' * 2^-10 exactly (all operands in
 // vector registers, which issue faster than the mixed-precision form).  Each head
 // then costs one fp32 FMA: t + 1 + G VALU instructions per channel and
-// block.  The block offsets o fold on 8 * G lanes (lane = block * G +
-// head), one instruction per channel, and are added in the epilogue.
+// block.  At depth 1, m is 0 or a * 2^-10 (staged as such), so the G head
+// FMAs run with the plane word as the execution mask: G instructions.  The
+// block offsets o fold on 8 * G lanes (lane = block * G + head), one
+// instruction per channel, and are added in the epilogue.
 //
 // Resources.  The scalar-load path of gfx950 moves only a few bytes per clock
 // per CU, so it carries nothing but plane words (the bytes the method reads).
 // Weights, offset coefficients and block scales come from LDS: w and e per
 // active channel once per workgroup, the scales of every active channel once
 // per round of kRoundBlocks blocks (staged with vector loads, stored in LDS
-// as fp32 A = a * 2^13).
+// as fp32 A = a * 2^13, or a * 2^-10 for depth-1 channels).
 //
 // Latency.  A workgroup reads the plan and the queries in one round trip,
 // then loads its round's scales and touches every plane line of the round with
@@ -367,7 +369,8 @@ constexpr int kScalePasses = kD * kRoundBlocks / 8 / kThreads;                  
 template <int G>
 struct MainShared {
   SlotTables<G> tb;
-  alignas(16) float sc[kSlots][kRoundBlocks];      // this round's block scales as a * 2^13
+  alignas(16) float sc[kSlots][kRoundBlocks];      // this round's block scales (a * 2^13;
+                                                   // a * 2^-10 in depth-1 slots)
   uint32_t prow[kD * kPlanes];                     // byte offset of every active plane row
   uint8_t sj[kSlots];                              // channel of every active slot
   float qraw[kD][G];                               // the group's queries, by channel
@@ -516,7 +519,8 @@ __device__ __forceinline__ void issue_touches(const MainShared<G>& sh, int nrows
   }
 }
 
-// Write a round's scales to LDS as a * 2^13 (exact).  The scale loads were
+// Write a round's scales to LDS as a * 2^13, a * 2^-10 in the depth-1 slots
+// from first1 on (both exact).  The scale loads were
 // issued before the L2 touches and vector loads complete in order, so this
 // waits for the scales only: the touches stay in flight while the first
 // channels are computed.
