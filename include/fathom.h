@@ -49,8 +49,8 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 5   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
-                                  5: fathom_klt_* */
+#define FATHOM_ABI_VERSION 6   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
+                                  5: fathom_klt_*; 6: fathom_scan_timed */
 
 enum fathom_status {
   FATHOM_OK = 0,

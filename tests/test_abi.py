@@ -60,7 +60,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 5
+    assert L.fathom_abi_version() == 6
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
