@@ -98,6 +98,65 @@ def test_scan_timed_same_scores(fk):
         assert e0.elapsed_ms(e1) > 0.0
 
 
+def test_scan_random_shapes_sweep(fk):
+    """24 seeded random cases: groups 1-3, G 1-8, n up to 25,600 keys, store
+    capacities with and without the main kernel's alignment (nb_store a
+    multiple of 8 or not), depth vectors from all-zero to all-four, half of
+    them through fathom_scan_timed; scores equal the oracle's bit for bit."""
+    import torch
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        groups, G = int(rng.integers(1, 4)), int(rng.integers(1, 9))
+        n = 64 * int(rng.integers(1, 401))
+        nb_store = n // 64 + int(rng.integers(0, 40))
+        kind = case % 4
+        if kind == 0:
+            depths = rng.integers(0, 5, size=(groups, 128))
+        elif kind == 1:
+            depths = np.where(rng.random((groups, 128)) < 0.6, 0, rng.integers(1, 5, (groups, 128)))
+        elif kind == 2:
+            depths = np.full((groups, 128), int(rng.integers(0, 5)))
+        else:
+            depths = np.where(rng.random((groups, 128)) < 0.5, 1, 4)
+        depths = depths.astype(np.uint8)
+        ins = fathom_inputs.make_inputs(groups, G, n, seed=5000 + case)
+        planes, scales, _ = oracle.encode(ins.k, nb_store=nb_store)
+        say("scan sweep case %d: groups=%d G=%d n=%d nb_store=%d kind=%d"
+            % (case, groups, G, n, nb_store, kind))
+        args = (to_dev(planes), to_dev(scales), to_dev(depths), to_dev(ins.q), n)
+        if case % 2:
+            e0, e1 = HipEvent(), HipEvent()
+            s = fk.scan(*args, events=(e0.h, e1.h))
+        else:
+            s = fk.scan(*args)
+        torch.cuda.synchronize()
+        gpu = to_host(s)
+        ref = oracle.scan_ref32(planes, scales, depths, ins.q, n)
+        assert np.array_equal(gpu.view(np.uint32), ref.view(np.uint32)), first_mismatch(gpu, ref)
+
+
+def test_topk_random_shapes_sweep(fk):
+    """20 seeded random cases: rows 1-6, n from 1 to 60,000 (any n), k from 1
+    to n, scores normal, heavy-tailed or rounded to few values (many ties);
+    indices equal the oracle's."""
+    rng = np.random.default_rng(77)
+    for case in range(20):
+        rows = int(rng.integers(1, 7))
+        n = int(rng.integers(1, 60001))
+        k = int(rng.integers(1, n + 1)) if case % 3 else int(rng.integers(1, min(n, 64) + 1))
+        kind = case % 3
+        if kind == 0:
+            sc = rng.standard_normal((rows, n)).astype(np.float32)
+        elif kind == 1:
+            sc = rng.standard_t(2, (rows, n)).astype(np.float32)
+        else:
+            sc = np.round(rng.standard_normal((rows, n)) * 4).astype(np.float32)
+        say("topk sweep case %d: rows=%d n=%d k=%d kind=%d" % (case, rows, n, k, kind))
+        got = _topk(fk, sc, k)
+        ref = oracle.topk(sc, k)
+        assert np.array_equal(got, ref), first_mismatch(got, ref)
+
+
 def _topk(fk, scores, k):
     import torch
     idx = fk.topk(to_dev(scores), k)
