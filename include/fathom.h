@@ -183,9 +183,12 @@ int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store
  * passed as void*, both non-null): start_event takes the start timestamp of
  * the scan's first kernel and stop_event the end timestamp of its last, from
  * the kernels' own dispatches, so no marker packet is added to the stream
- * between the scan and the work around it.  hipEventElapsedTime(start,
- * stop) then gives the scan's duration once stop_event has completed.  For
- * callers that time the scan inside a pipeline (the benchmark's roofline).
+ * between the scan and the work around it (the HIP runtime still ends a
+ * timed dispatch with a system-scope release, a few microseconds of idle
+ * GPU around the scan).  hipEventElapsedTime(start, stop) then gives the
+ * scan's duration once stop_event has completed.  For callers that time the
+ * scan inside a pipeline (the benchmark's roofline).  Errors as fathom_scan;
+ * a null event is FATHOM_ERR_NULL_ARG.
  */
 int fathom_scan_timed(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                       const uint8_t* depths, const float* q, int64_t groups, int32_t G,
