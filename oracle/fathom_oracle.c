@@ -261,7 +261,9 @@ static int fo_depth_clamped(uint8_t t) { return t > FO_PLANES ? FO_PLANES : (int
 /* Plain definition in fp64: S_hi = sum_{j : t_j > 0} q_hj * khat_ij with the
  * prefix value of §3.2 (each product is exact in fp64).  Also returns
  * l1_hi = sum_j |q_hj * khat_ij|, the magnitude the tolerance is relative to.
- * Output [groups][G][n]. */
+ * Per token the prefix values of the active channels are read back first, then
+ * each head's sum runs over them by ascending channel.  Threads split the
+ * (group, block) pairs, which are independent.  Output [groups][G][n]. */
 void fo_scan_f64(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                  const uint8_t* depths, const float* q, int64_t groups, int G,
                  int d, int64_t n, double* scores, double* l1, int nthreads) {
@@ -269,26 +271,32 @@ void fo_scan_f64(const uint64_t* planes, const uint16_t* scales, int64_t nb_stor
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
 #endif
-  for (int64_t g = 0; g < groups; ++g) {
+  for (int64_t gb = 0; gb < groups * nb; ++gb) {
+    int64_t g = gb / nb, b = gb % nb;
     const uint8_t* t = depths + g * d;
-    for (int64_t b = 0; b < nb; ++b)
-      for (int i = 0; i < FO_BLOCK; ++i)
-        for (int h = 0; h < G; ++h) {
-          double s = 0.0, m = 0.0;
-          for (int j = 0; j < d; ++j) {
-            int tj = fo_depth_clamped(t[j]);
-            if (tj == 0) continue;
-            int64_t gj = g * d + j;
-            double kh = fo_dequant(scales[gj * nb_store + b],
-                                   fo_prefix_code(planes, nb_store, gj, b, i, tj), tj);
-            double prod = (double)q[(g * G + h) * d + j] * kh;
-            s += prod;
-            m += fabs(prod);
-          }
-          int64_t o = (g * G + h) * n + b * FO_BLOCK + i;
-          scores[o] = s;
-          if (l1) l1[o] = m;
+    double* kh = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int i = 0; i < FO_BLOCK; ++i) {
+      for (int j = 0; j < d; ++j) {
+        int tj = fo_depth_clamped(t[j]);
+        int64_t gj = g * d + j;
+        kh[j] = tj == 0 ? 0.0
+                        : fo_dequant(scales[gj * nb_store + b],
+                                     fo_prefix_code(planes, nb_store, gj, b, i, tj), tj);
+      }
+      for (int h = 0; h < G; ++h) {
+        double s = 0.0, m = 0.0;
+        for (int j = 0; j < d; ++j) {
+          if (fo_depth_clamped(t[j]) == 0) continue;
+          double prod = (double)q[(g * G + h) * d + j] * kh[j];
+          s += prod;
+          m += fabs(prod);
         }
+        int64_t o = (g * G + h) * n + b * FO_BLOCK + i;
+        scores[o] = s;
+        if (l1) l1[o] = m;
+      }
+    }
+    free(kh);
   }
   (void)nthreads;
 }
@@ -304,49 +312,54 @@ void fo_scan_f64(const uint64_t* planes, const uint16_t* scales, int64_t nb_stor
  *   S  = fl32(U + o),
  * where "each active j" visits the channels with t_j = 4 first, then 3, 2
  * and 1, ascending j within one depth.  Depth values above 4 read as 4.
- * Output [groups][G][n]. */
+ * Threads split the (group, block) pairs.  Output [groups][G][n]. */
 void fo_scan_ref32(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                    const uint8_t* depths, const float* q, int64_t groups, int G,
                    int d, int64_t n, float* scores, int nthreads) {
   int64_t nb = n / FO_BLOCK;
+  /* The visiting order of every group: by depth 4, 3, 2, 1, then by channel. */
+  int* order = (int*)malloc(sizeof(int) * (size_t)(groups * d));
+  int* nact = (int*)malloc(sizeof(int) * (size_t)groups);
+  for (int64_t g = 0; g < groups; ++g) {
+    nact[g] = 0;
+    for (int depth = FO_PLANES; depth >= 1; --depth)
+      for (int j = 0; j < d; ++j)
+        if (fo_depth_clamped(depths[g * d + j]) == depth) order[g * d + nact[g]++] = j;
+  }
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
 #endif
-  for (int64_t g = 0; g < groups; ++g) {
-    /* The visiting order: by depth 4, 3, 2, 1, then by channel index. */
-    int* order = (int*)malloc(sizeof(int) * (size_t)d);
-    int nact = 0;
-    for (int depth = FO_PLANES; depth >= 1; --depth)
-      for (int j = 0; j < d; ++j)
-        if (fo_depth_clamped(depths[g * d + j]) == depth) order[nact++] = j;
-    for (int64_t b = 0; b < nb; ++b)
-      for (int h = 0; h < G; ++h) {
-        const float* qh = q + (g * G + h) * d;
-        float o = 0.0f;
-        for (int k = 0; k < nact; ++k) {
-          int j = order[k];
-          int t = fo_depth_clamped(depths[g * d + j]);
-          float a = (float)fo_f16_to_f64(scales[(g * d + j) * nb_store + b]);
-          float e = qh[j] * (ldexpf(1.0f, -t) - 1.0f);
-          o = fmaf(e, a, o);
-        }
-        for (int i = 0; i < FO_BLOCK; ++i) {
-          float u = 0.0f;
-          for (int k = 0; k < nact; ++k) {
-            int j = order[k];
-            int t = fo_depth_clamped(depths[g * d + j]);
-            int64_t gj = g * d + j;
-            float a = (float)fo_f16_to_f64(scales[gj * nb_store + b]);
-            int c = fo_prefix_code(planes, nb_store, gj, b, i, t);
-            float w = ldexpf(qh[j], 11 - t);
-            float m = ldexpf(a * (float)c, -10);
-            u = fmaf(w, m, u);
-          }
-          scores[(g * G + h) * n + b * FO_BLOCK + i] = u + o;
-        }
+  for (int64_t gb = 0; gb < groups * nb; ++gb) {
+    int64_t g = gb / nb, b = gb % nb;
+    const int* og = order + g * d;
+    for (int h = 0; h < G; ++h) {
+      const float* qh = q + (g * G + h) * d;
+      float o = 0.0f;
+      for (int k = 0; k < nact[g]; ++k) {
+        int j = og[k];
+        int t = fo_depth_clamped(depths[g * d + j]);
+        float a = (float)fo_f16_to_f64(scales[(g * d + j) * nb_store + b]);
+        float e = qh[j] * (ldexpf(1.0f, -t) - 1.0f);
+        o = fmaf(e, a, o);
       }
-    free(order);
+      for (int i = 0; i < FO_BLOCK; ++i) {
+        float u = 0.0f;
+        for (int k = 0; k < nact[g]; ++k) {
+          int j = og[k];
+          int t = fo_depth_clamped(depths[g * d + j]);
+          int64_t gj = g * d + j;
+          float a = (float)fo_f16_to_f64(scales[gj * nb_store + b]);
+          int c = fo_prefix_code(planes, nb_store, gj, b, i, t);
+          float w = ldexpf(qh[j], 11 - t);
+          float m = ldexpf(a * (float)c, -10);
+          u = fmaf(w, m, u);
+        }
+        scores[(g * G + h) * n + b * FO_BLOCK + i] = u + o;
+      }
+    }
   }
+  free(order);
+  free(nact);
   (void)nthreads;
 }
 

@@ -16,6 +16,7 @@ import pytest
 import fathom_inputs
 import oracle
 from gpu_util import first_mismatch, say, to_dev, to_host
+from topk_check import assert_scores_within_band, assert_topk_valid
 from klt_cases import D, expected_basis, planted
 
 pytestmark = pytest.mark.gpu
@@ -121,4 +122,8 @@ def test_rotated_store_end_to_end(fk):
     ref = oracle.scan_ref32(planes, scales, depths, qr, n)
     sc = to_host(sc_d)
     assert np.array_equal(sc.view(np.uint32), ref.view(np.uint32)), first_mismatch(sc, ref)
-    assert np.array_equal(to_host(idx_d), oracle.topk(ref.reshape(groups * G, n), k))
+    gi = to_host(idx_d)
+    assert np.array_equal(gi, oracle.topk(ref.reshape(groups * G, n), k))
+    s64, l1 = oracle.scan_f64(planes, scales, depths, qr, n)
+    assert_scores_within_band(sc, s64, l1)
+    assert_topk_valid(gi, s64, l1, k)

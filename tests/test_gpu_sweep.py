@@ -1,8 +1,10 @@
 """GPU parity on the budget sweep's layers (the 1M-key layer shape with 32
 planted needles per KV head), sampled at layers 0, 17 and 35 and every
-budget from 32 to 256 code bits: plans bit-exact, scores of a slice of
-blocks of every group bit-exact, and top-k index sets bit-exact against the
-oracle's selection over the same scores.
+budget from 32 to 256 code bits: the encoding bit-exact in full, plans
+bit-exact, scores of a slice of blocks of every group bit-exact, top-k index
+sets bit-exact against the oracle's selection over the same scores; every
+score within the 1e-4 band of the fp64 definition and every set a valid
+top-k of the fp64 scores up to that band.
 """
 import numpy as np
 import pytest
@@ -10,6 +12,7 @@ import pytest
 import fathom_inputs
 import oracle
 from gpu_util import first_mismatch, say, to_dev, to_host
+from topk_check import assert_scores_within_band, assert_topk_valid
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +39,11 @@ def test_sweep_layer_every_budget(fk, layer):
     b0, b1 = 7000, 7040                       # a slice of blocks of every group
     torch.cuda.synchronize()
     gp, gs = to_host(planes), to_host(scales)
-    sub_p = np.ascontiguousarray(gp[..., b0:b1])
-    sub_s = np.ascontiguousarray(gs[..., b0:b1])
-    op, os_, _ = oracle.encode(np.ascontiguousarray(ins.k[:, b0 * 64:b1 * 64]))
-    assert np.array_equal(sub_p, op) and np.array_equal(sub_s, os_)
+    say("sweep layer %d oracle encode" % layer)
+    fp, fs, _ = oracle.encode(ins.k)
+    assert np.array_equal(gp, fp) and np.array_equal(gs, fs)
+    op = np.ascontiguousarray(fp[..., b0:b1])
+    os_ = np.ascontiguousarray(fs[..., b0:b1])
     for B in fathom_inputs.SWEEP_BUDGETS:
         say("sweep layer %d B=%d" % (layer, B))
         depths = fk.plan(q_d, var_d, B)
@@ -54,3 +58,6 @@ def test_sweep_layer_every_budget(fk, layer):
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), first_mismatch(got, ref)
         oi = oracle.topk(gsc.reshape(-1, n), k)
         assert np.array_equal(gi, oi), first_mismatch(gi, oi)
+        s64, l1 = oracle.scan_f64(fp, fs, od, ins.q, n)
+        assert_scores_within_band(gsc, s64, l1)
+        assert_topk_valid(gi, s64, l1, k)

@@ -4,7 +4,9 @@ through the fused call, and the 16-session case (128 groups of 131,072 keys)
 with every output of a spread of groups compared.
 
 Everything is bit-exact against the oracle: encodings, plans, scores (the
-fixed fp32 order) and top-k index sets.
+fixed fp32 order) and top-k index sets.  Every compared score is also within
+the 1e-4 band of the fp64 definition and every compared set a valid top-k of
+the fp64 scores up to that band.
 """
 import numpy as np
 import pytest
@@ -12,6 +14,7 @@ import pytest
 import fathom_inputs
 import oracle
 from gpu_util import first_mismatch, say, to_dev, to_host
+from topk_check import assert_scores_within_band, assert_topk_valid
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +46,9 @@ def _check_layer(fk, ins, n, k, budgets, planes, scales, op, os_, fused=False):
         assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
         oi = oracle.topk(ref.reshape(-1, n), k)
         assert np.array_equal(gi, oi), first_mismatch(gi, oi)
+        s64, l1 = oracle.scan_f64(op, os_, od, ins.q, n)
+        assert_scores_within_band(gsc, s64, l1)
+        assert_topk_valid(gi, s64, l1, k)
         if fused:
             assert np.array_equal(to_host(fs).view(np.uint32), ref.view(np.uint32))
             assert np.array_equal(to_host(fi), oi)
@@ -105,3 +111,6 @@ def test_sixteen_sessions(fk):
         assert np.array_equal(gsc[g:g + 1].view(np.uint32), ref.view(np.uint32)), g
         oi = oracle.topk(ref.reshape(-1, w.n), w.k)
         assert np.array_equal(gi[g * G:(g + 1) * G], oi), g
+        s64, l1 = oracle.scan_f64(op, os_, od[g:g + 1], ins.q[g:g + 1], w.n)
+        assert_scores_within_band(gsc[g:g + 1], s64, l1)
+        assert_topk_valid(gi[g * G:(g + 1) * G], s64, l1, w.k)

@@ -133,3 +133,110 @@ def test_store_capacity_is_respected(small):
     a = oracle.scan_ref32(planes, scales, depths, ins.q, n)
     b = oracle.scan_ref32(big_p, big_s, depths, ins.q, n)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# The fp32 evaluation order of scan_ref32, pinned by exact rational arithmetic
+# ---------------------------------------------------------------------------
+# The pages fix the score (§3.2 prefix value, §3.3 active channels) but no
+# fp32 order; the library states one (fathom.h: U over fma(w, m) and o over
+# fma(e, a), each folded from +0 over the active channels deepest first and
+# by ascending index within a depth, then S = fl32(U + o)).  Here that order
+# is re-derived with Python Fractions, every fp32 step rounded to nearest-even
+# by hand below, so the oracle's bits are checked by a route that shares no
+# floating-point arithmetic with it.  Cases are chosen where other orders (one
+# ascending-index fold, or U and o in one accumulator) round differently, so
+# a change of order fails here.
+
+def _r32(x: Fraction) -> Fraction:
+    """x rounded to the nearest binary32 value, ties to even (normal and
+    subnormal range; the cases here stay far from overflow)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * ulp
+    assert r < Fraction(2) ** 128
+    return sign * r
+
+
+def _fma32(a: Fraction, b: Fraction, c: Fraction) -> Fraction:
+    return _r32(a * b + c)
+
+
+def _f16(bits: int) -> Fraction:
+    """binary16 bit pattern -> exact rational (finite values only)."""
+    e, m = (bits >> 10) & 0x1F, bits & 0x3FF
+    assert e != 0x1F
+    v = Fraction(m, 1 << 24) if e == 0 else Fraction(m | 0x400, 1 << 10) * Fraction(2) ** (e - 15)
+    return -v if bits & 0x8000 else v
+
+
+def _prefix(planes, g, j, b, i, t):
+    c = 0
+    for p in range(t):
+        c = 2 * c + int((int(planes[g, j, p, b]) >> i) & 1)
+    return c
+
+
+def _scores_by_order(planes, scales, depths, q, n, order_kind):
+    """Scores of token range [0, n) with the U/o split, folds in the given
+    channel order: 'stated' (depth 4, 3, 2, 1; ascending within a depth),
+    'ascending' (one ascending-index fold), or 'one_acc' (the stated order
+    with U and o in one accumulator started at o)."""
+    groups, G, d = q.shape
+    out = np.zeros((groups, G, n), dtype=np.float64)
+    for g in range(groups):
+        t = [min(int(x), 4) for x in depths[g]]
+        if order_kind == "ascending":
+            order = [j for j in range(d) if t[j] > 0]
+        else:
+            order = [j for dep in (4, 3, 2, 1) for j in range(d) if t[j] == dep]
+        for b in range(n // 64):
+            for h in range(G):
+                qh = [Fraction(float(x)) for x in q[g, h]]
+                o = Fraction(0)
+                for j in order:
+                    e = _r32(qh[j] * (Fraction(1, 2 ** t[j]) - 1))
+                    o = _fma32(e, _f16(int(scales[g, j, b])), o)
+                for i in range(64):
+                    u = o if order_kind == "one_acc" else Fraction(0)
+                    for j in order:
+                        w = qh[j] * Fraction(2) ** (11 - t[j])
+                        m = _f16(int(scales[g, j, b])) * _prefix(planes, g, j, b, i, t[j]) \
+                            * Fraction(1, 1024)
+                        u = _fma32(w, m, u)
+                    s = u if order_kind == "one_acc" else _r32(u + o)
+                    out[g, h, b * 64 + i] = float(s)
+    return out
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_ref32_order_pinned_by_exact_arithmetic(seed):
+    rng = np.random.default_rng(400 + seed)
+    G, n = 2, 128
+    ins = fathom_inputs.make_inputs(1, G, n, seed=410 + seed)
+    planes, scales, _ = oracle.encode(ins.k)
+    depths = np.zeros((1, 128), dtype=np.uint8)
+    chans = rng.choice(128, 12, replace=False)
+    depths[0, chans] = rng.permutation([4, 4, 3, 3, 3, 2, 2, 2, 1, 1, 1, 1])
+    depths[0, rng.choice(np.setdiff1d(np.arange(128), chans), 1)] = 7   # reads as 4
+    got = oracle.scan_ref32(planes, scales, depths, ins.q, n).astype(np.float64)
+    want = _scores_by_order(planes, scales, depths, ins.q, n, "stated")
+    assert np.array_equal(got, want)
+    # the test can tell the stated order from the others
+    for other in ("ascending", "one_acc"):
+        alt = _scores_by_order(planes, scales, depths, ins.q, n, other)
+        assert np.count_nonzero(alt != want) > 0, other

@@ -66,3 +66,31 @@ def test_duplicate_scores_across_blocks():
     assert list(idx[0]) == [5, 6, 700, 1400, 3000, 4095]
     idx = oracle.topk(s, 3)
     assert list(idx[0]) == [5, 700, 1400]
+
+
+def test_validity_check_accepts_exact_and_rejects_swaps():
+    """The fp64 validity check used by the GPU parity tests: the oracle's own
+    top-k of fp64-close scores passes; swapping one selected index for a
+    clearly lower-scoring key fails; a duplicate or unsorted set fails."""
+    import pytest
+    from topk_check import assert_topk_valid
+    rng = np.random.default_rng(5)
+    rows, n, k = 3, 5000, 100
+    s64 = rng.standard_normal((rows, n))
+    l1 = np.abs(s64) + 1.0
+    s32 = s64.astype(np.float32)
+    idx = oracle.topk(s32, k)
+    assert_topk_valid(idx, s64, l1, k)
+    bad = idx.copy()
+    worst = int(np.argmin(s64[0]))
+    bad[0, 0] = worst
+    bad[0] = np.sort(bad[0])
+    with pytest.raises(AssertionError):
+        assert_topk_valid(bad, s64, l1, k)
+    dup = idx.copy()
+    dup[1, 1] = dup[1, 0]
+    with pytest.raises(AssertionError):
+        assert_topk_valid(dup, s64, l1, k)
+    rev = idx[:, ::-1].copy()
+    with pytest.raises(AssertionError):
+        assert_topk_valid(rev, s64, l1, k)
