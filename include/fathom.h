@@ -22,7 +22,8 @@
  *   - Every data pointer is a DEVICE pointer owned by the caller, except the
  *     host store of fathom_gather (pinned host memory).  The library
  *     allocates nothing, keeps no pointer after a call returns and holds no
- *     state between calls.
+ *     state between calls, apart from the fixed per-GPU scratch of
+ *     fathom_topk_noalloc (and its looked-up device address).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; no call synchronises the host
  *     with the device.  Calls are reentrant; calls on different streams are
@@ -49,8 +50,9 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 6   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
-                                  5: fathom_klt_*; 6: fathom_scan_timed */
+#define FATHOM_ABI_VERSION 7   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
+                                  5: fathom_klt_*; 6: fathom_scan_timed;
+                                  7: fathom_topk_noalloc */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -61,7 +63,8 @@ enum fathom_status {
   FATHOM_ERR_HIP = -5,             /* a HIP launch or runtime call failed   */
   FATHOM_ERR_NO_DEVICE = -6,       /* no HIP device is visible              */
   FATHOM_ERR_ALIGNMENT = -7,       /* a pointer lacks its required alignment */
-  FATHOM_ERR_NOT_PINNED = -8       /* host memory the device cannot address  */
+  FATHOM_ERR_NOT_PINNED = -8,      /* host memory the device cannot address  */
+  FATHOM_ERR_TOO_LARGE = -9        /* beyond the fixed no-allocation scratch */
 };
 
 /* Number of bit planes per channel and tokens per block (fixed by §3.2). */
@@ -212,6 +215,31 @@ size_t fathom_topk_workspace_bytes(int64_t rows, int64_t n, int32_t k);
 int fathom_topk(const float* scores, int64_t rows, int64_t n, int32_t k,
                 int32_t* indices, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * fathom_topk_noalloc — fathom_topk for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same selection, bit for bit, with the workspace
+ * taken from a fixed scratch array the library holds in device memory, one
+ * per GPU it runs on, until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ *
+ *   scores, rows, n, k, indices, stream: as fathom_topk.
+ *   The scratch is fathom_topk_noalloc_max_bytes() bytes (64 MiB); a call
+ *   whose fathom_topk_workspace_bytes(rows, n, k) exceeds it returns
+ *   FATHOM_ERR_TOO_LARGE and enqueues nothing (32 rows of 2^20 keys need
+ *   about 21 MB).
+ *   The scratch of a GPU is shared by every call on that GPU and keeps the
+ *   last call's contents (the selection writes everything it reads, so
+ *   nothing has to start cleared): calls that overlap on one GPU (two
+ *   streams, two host threads) race and must be serialised by the caller.
+ *   The scratch's device address is looked up once per GPU, on the first
+ *   call that runs there (the device of `stream`, or the current device for
+ *   the null stream).
+ */
+size_t fathom_topk_noalloc_max_bytes(void);
+int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
+                        int32_t* indices, void* stream);
 
 /*
  * fathom_scan_topk — fathom_scan followed by fathom_topk on its scores, with

@@ -32,6 +32,7 @@ STATUS = {
     -6: "FATHOM_ERR_NO_DEVICE",
     -7: "FATHOM_ERR_ALIGNMENT",
     -8: "FATHOM_ERR_NOT_PINNED",
+    -9: "FATHOM_ERR_TOO_LARGE",
 }
 
 EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
@@ -39,7 +40,8 @@ EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
             "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
             "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
             "fathom_klt_rotate_queries",
-            "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version")
+            "fathom_topk_workspace_bytes", "fathom_topk_noalloc", "fathom_topk_noalloc_max_bytes",
+            "fathom_status_string", "fathom_abi_version")
 
 
 class FathomError(RuntimeError):
@@ -67,6 +69,9 @@ def lib():
         L.fathom_scan_timed.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P, P, P]
         L.fathom_topk.argtypes = [P, I64, I64, I32, P, P, SZ, P]
         L.fathom_topk_workspace_bytes.argtypes = [I64, I64, I32]
+        L.fathom_topk_noalloc.argtypes = [P, I64, I64, I32, P, P]
+        L.fathom_topk_noalloc_max_bytes.argtypes = []
+        L.fathom_topk_noalloc_max_bytes.restype = SZ
         L.fathom_scan_topk.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, I32, P, P, P, SZ, P]
         L.fathom_scan_topk_workspace_bytes.argtypes = [I64, I32, I64, I32]
         L.fathom_scan_topk_workspace_bytes.restype = SZ
@@ -287,6 +292,19 @@ def topk(scores: torch.Tensor, k: int, indices: torch.Tensor | None = None,
         _dev(indices, "indices", torch.int32, (rows, k)), _dev(workspace, "workspace", torch.uint8),
         workspace.numel(), _stream(stream))
     _check(st, "fathom_topk")
+    return indices
+
+
+def topk_noalloc(scores: torch.Tensor, k: int, indices: torch.Tensor, stream=None):
+    """fathom_topk_noalloc: fathom_topk with the library's fixed scratch as
+    its workspace (the call allocates nothing; `indices` [rows][k] int32 is
+    the caller's)."""
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    st = lib().fathom_topk_noalloc(
+        _dev(scores, "scores", torch.float32), rows, n, int(k),
+        _dev(indices, "indices", torch.int32, (rows, k)), _stream(stream))
+    _check(st, "fathom_topk_noalloc")
     return indices
 
 

@@ -45,6 +45,7 @@ const char* fathom_status_string(int status) {
     case FATHOM_ERR_NO_DEVICE: return "FATHOM_ERR_NO_DEVICE: no HIP device is visible";
     case FATHOM_ERR_ALIGNMENT: return "FATHOM_ERR_ALIGNMENT: a pointer lacks its required alignment";
     case FATHOM_ERR_NOT_PINNED: return "FATHOM_ERR_NOT_PINNED: host memory is not pinned for the device";
+    case FATHOM_ERR_TOO_LARGE: return "FATHOM_ERR_TOO_LARGE: the call needs more scratch than the fixed no-allocation scratch holds";
     default: return "FATHOM_ERR_UNKNOWN";
   }
 }
@@ -258,6 +259,21 @@ int fathom_topk(const float* scores, int64_t rows, int64_t n, int32_t k, int32_t
   if (int s = device_ready()) return s;
   return to_status(fathom::launch_topk(scores, rows, n, k, indices, workspace,
                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t fathom_topk_noalloc_max_bytes(void) { return fathom::kNoAllocScratchBytes; }
+
+int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k, int32_t* indices,
+                        void* stream) {
+  if (!scores || !indices) return FATHOM_ERR_NULL_ARG;
+  if (rows < 1 || rows > kMaxGroups || n < 1 || n >= kMaxTokens) return FATHOM_ERR_BAD_SHAPE;
+  if (k < 1 || k > n) return FATHOM_ERR_BAD_RANGE;
+  if (!aligned(scores, 4) || !aligned(indices, 4)) return FATHOM_ERR_ALIGNMENT;
+  if (fathom::topk_workspace_bytes(rows, n, k) > fathom::kNoAllocScratchBytes)
+    return FATHOM_ERR_TOO_LARGE;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_topk_noalloc(scores, rows, n, k, indices,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -52,6 +52,11 @@ hipError_t launch_gather(const uint64_t* hplanes, const uint16_t* hscales, int64
                          uint16_t* scales, hipStream_t stream);
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* workspace, hipStream_t stream);
+// fathom_topk with the library's fixed per-device scratch as its workspace
+// (no allocation); hipErrorInvalidValue if the workspace would exceed it.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t launch_topk_noalloc(const float* scores, int64_t rows, int64_t n, int k,
+                               int32_t* indices, hipStream_t stream);
 
 size_t klt_fit_workspace_bytes(int64_t groups, int64_t n);
 hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* mu, float* basis,

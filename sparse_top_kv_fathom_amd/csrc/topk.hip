@@ -28,10 +28,20 @@
 // its region holds: heavy ties or adversarial rows), or the candidates do not
 // fit in LDS, the resolve workgroup does all of it alone, from the scores or
 // the regions: same result, many more passes.
+#include <mutex>
+
 #include "fathom_internal.h"
 #include "topk_layout.h"
 
 namespace fathom {
+
+// Fixed scratch of fathom_topk_noalloc: the selection's workspace for callers
+// that cannot allocate.  One copy per GPU the library runs on, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace {
 
 using namespace topk;
@@ -802,6 +812,52 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int3
                      ws, indices);
   hipLaunchKernelGGL(topk_order, grid_chunks, dim3(64), 0, stream, n, R, k, ws, indices);
   return hipGetLastError();
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev`, looked up on the first call
+// for that device with it current (the caller's current device is restored).
+hipError_t scratch_ptr(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_topk_noalloc(const float* scores, int64_t rows, int64_t n, int k,
+                               int32_t* indices, hipStream_t stream) {
+  if (topk_workspace_bytes(rows, n, k) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  void* ws = nullptr;
+  if ((e = scratch_ptr(dev, &ws)) != hipSuccess) return e;
+  // Every kernel of the selection writes what it later reads (per-chunk
+  // histograms in their own slots, the cut and flags set by the guess), so
+  // nothing of the previous call's contents needs clearing.
+  return launch_topk(scores, rows, n, k, indices, ws, stream);
 }
 
 // Pieces of the selection for candidates the scan emits itself, per region

@@ -46,7 +46,8 @@ def test_header_declares_the_calls():
               "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
               "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
               "fathom_klt_rotate_queries",
-              "fathom_topk_workspace_bytes", "fathom_status_string", "fathom_abi_version"):
+              "fathom_topk_workspace_bytes", "fathom_topk_noalloc", "fathom_topk_noalloc_max_bytes",
+              "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
 
@@ -60,8 +61,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 6
-    for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8):
+    assert L.fathom_abi_version() == 7
+    for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8, -9):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
     assert L.fathom_status_string(12345).decode() == "FATHOM_ERR_UNKNOWN"
@@ -281,11 +282,29 @@ def test_topk_validation(L):
     assert L.fathom_topk_workspace_bytes(8, 1 << 20, 4096) >= L.fathom_topk_workspace_bytes(4, 1 << 20, 4096)
 
 
+def test_topk_noalloc_validation(L):
+    """The no-allocation top-k checks its arguments like fathom_topk and
+    rejects calls whose workspace would exceed its fixed scratch."""
+    t = L.fathom_topk_noalloc
+    cap = L.fathom_topk_noalloc_max_bytes()
+    assert cap == 64 << 20
+    assert t(None, 4, 1000, 10, FAKE, None) == NULL_ARG
+    assert t(FAKE, 4, 1000, 10, None, None) == NULL_ARG
+    assert t(FAKE, 0, 1000, 10, FAKE, None) == BAD_SHAPE
+    assert t(FAKE, 4, 1000, 0, FAKE, None) == BAD_RANGE
+    assert t(FAKE, 4, 1000, 10, P((1 << 20) + 2), None) == ALIGN
+    # 32 rows of 2^20 keys fit; 512 rows of 131,072 keys (76 MB) do not
+    assert L.fathom_topk_workspace_bytes(32, 1 << 20, 4096) <= cap
+    assert L.fathom_topk_workspace_bytes(512, 131072, 1024) > cap
+    assert t(FAKE, 512, 131072, 1024, FAKE, None) == -9
+
+
 @pytest.mark.skipif(_gpu_visible(), reason="checks the no-device status; a GPU is visible")
 def test_valid_calls_report_no_device(L):
     assert L.fathom_scan(FAKE, FAKE, 64, FAKE, FAKE, 1, 4, 128, 4096, FAKE, None) == NO_DEVICE
     need = L.fathom_topk_workspace_bytes(4, 1000, 10)
     assert L.fathom_topk(FAKE, 4, 1000, 10, FAKE, FAKE, need, None) == NO_DEVICE
+    assert L.fathom_topk_noalloc(FAKE, 4, 1000, 10, FAKE, None) == NO_DEVICE
     assert L.fathom_plan(FAKE, FAKE, 1, 4, 128, 92, FAKE, None, None, None) == NO_DEVICE
     assert L.fathom_encode(FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, None, None) == NO_DEVICE
 
