@@ -3,9 +3,7 @@
 One step = the work of one decode step over a resident bit-plane store:
 encode the newest 64-token block of every KV head into its slot, plan the
 read depths for a fresh query group (importance, 30-step bisection), scan
-every key at those depths, and select the top-k of every query head.  The
-fused call fathom_scan_topk (the scan takes the top-k candidates itself) is
-timed on the same inputs after the steps and reported beside them.
+every key at those depths, and select the top-k of every query head.
 
 Workload (default): one Qwen3-8B-shaped layer, 8 KV heads x 4 query heads,
 d = 128, n = 1,048,576 keys per head, budget 92 code bits, k = 4096; keys,
@@ -13,19 +11,29 @@ queries and variances from fathom_inputs (synthetic, seeded).  The store is
 held in several copies that the steps rotate through, so the index a step
 reads is not left in the 256 MB last-level cache by the previous step.
 
-Prints one JSON line: keys scanned per second for the whole step (value),
-plus the scan kernel's roofline figures (algorithmic bytes and VALU work per
-launch, over its event-timed average duration) and the CPU oracle's rate on
-a bounded sample.
+Passes over the same inputs, each K steps after W warm-up steps:
+  * the headline pass: plain calls, timed as a whole (value, ms_per_step);
+  * a scan pass: every scan through fathom_scan_timed, whose events take the
+    scan kernels' own start and end timestamps (scan median, p10, p90; the
+    roofline figures);
+  * a stage pass: events between the stages (per-stage and per-step
+    medians, p10, p90);
+  * the fused call fathom_scan_topk.
+Then, unless switched off: the other workloads and budgets (scan and top-k
+times, roofline fractions), the fixed-depth plans the pages compare against
+read through the same scan (scan time and recall against exact top-k), the
+host-resident gather against run size, and the CPU oracle's rate on a
+bounded sample (one thread and all host threads).
 
-HBM traffic of the scan comes from rocprofv3 counter runs of this same
-command (FETCH_SIZE, then WRITE_SIZE), each scaled by the factor that makes
-the counter agree with the known bytes of a plain copy (torch.neg over
-256 MiB, run here before the timed steps).  The figures are kept in
-profiles/scan_q1m_b92_traffic.txt together with the sha256 of the scan
-source they were taken on; a different source reports traffic null.
-`python bench.py --summarize DIR [DIR ...]` turns rocprofv3 csv output
-(kernel stats, counter collections) into the text kept under profiles/.
+Prints one JSON line.  HBM traffic of the scan comes from rocprofv3 counter
+runs of this command (read requests by size, TCC_EA0_RDREQ_32B/64B/128B, and
+write requests, TCC_EA0_WRREQ and TCC_EA0_WRREQ_64B), each scaled by the
+factor that makes the counters read the known bytes of a plain copy
+(torch.neg over 256 MiB, run here before the timed steps).  The figures are
+kept in profiles/scan_q1m_b92_traffic.txt with the sha256 of the scan source
+they were taken on; a different source reports traffic null.
+`python bench.py --summarize DIR [DIR ...]` turns rocprofv3 csv output into
+the text kept under profiles/.
 """
 from __future__ import annotations
 
@@ -56,7 +64,7 @@ CALIB_BYTES = 256 << 20                   # plain copy used to scale the HBM byt
 SCAN_SRC = os.path.join(ROOT, "sparse_top_kv_fathom_amd", "csrc", "scan.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_traffic.txt")
 INSTR_FILE = os.path.join(ROOT, "profiles", "scan_q1m_b92_instructions.txt")
-
+METRIC = "keys scanned/sec (and HBM GB/s, % roofline) at 1M keys, 92-bit budget"
 
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
@@ -124,13 +132,16 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="store copies the steps rotate through")
     ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--store", choices=("raw", "klt"), default="raw",
                     help="raw channel planes, or planes of the KLT-rotated keys")
     ap.add_argument("--no-klt", action="store_true",
                     help="skip timing the KLT fit and rotations (raw store only)")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip timing fathom_gather from a pinned host store")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads and budgets")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the fixed-depth plans read through the same scan")
     ap.add_argument("--sweep", action="store_true",
                     help="budget sweep over layers of the 1M-key shape with planted needles: "
                          "recall against exact scores and scan rate per budget (one JSON object)")
@@ -162,16 +173,6 @@ def recorded_counter(path, key):
         return None
 
 
-def recorded_traffic():
-    """Scan HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)."""
-    return recorded_counter(TRAFFIC_FILE, "scan_hbm_bytes_per_launch")
-
-
-def recorded_valu():
-    """Scan VALU instructions (wave64) per launch (SQ_INSTS_VALU)."""
-    return recorded_counter(INSTR_FILE, "scan_valu_instructions_per_launch")
-
-
 def short_name(name):
     name = name.replace("void ", "").replace("(anonymous namespace)::", "")
     return name.split("(")[0][:60]
@@ -195,39 +196,62 @@ def summarize(dirs):
             for r in csv.DictReader(open(f)):
                 key = (short_name(r["Kernel_Name"]), r["Counter_Name"])
                 agg.setdefault(key, []).append(float(r["Counter_Value"]))
-            print("%-60s %-14s %6s %14s" % ("kernel", "counter", "n", "mean"))
+            print("%-60s %-24s %6s %14s" % ("kernel", "counter", "n", "mean"))
             for (kname, cname), v in sorted(agg.items()):
-                print("%-60s %-14s %6d %14.1f" % (kname, cname, len(v), sum(v) / len(v)))
+                print("%-60s %-24s %6d %14.1f" % (kname, cname, len(v), sum(v) / len(v)))
                 means[(kname, cname)] = sum(v) / len(v)
-    valu = [v for (kname, cname), v in means.items()
-            if kname.startswith("fathom::scan_main<") and kname.endswith(", 0>") and cname == "SQ_INSTS_VALU"]
+
+    def scan_key(k):
+        return k[0].startswith("fathom::scan_main<") and k[0].endswith(", 0>")
+    valu = [v for k, v in means.items() if scan_key(k) and k[1] == "SQ_INSTS_VALU"]
     if valu:
         print("scan_valu_instructions_per_launch: %.0f" % valu[0])
         print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
-    # HBM traffic of the scan: each byte counter (KiB per dispatch) scaled by
-    # the factor that makes it read the known bytes of the plain copy.
-    calib = [k for k in means if "neg" in k[0]]
-    scan = [k for k in means if "scan_main" in k[0]]
-    if calib and scan:
-        total = 0.0
-        print("## scan traffic (counters scaled by the plain-copy factor)")
-        for cname, known_kib in (("FETCH_SIZE", CALIB_BYTES / 1024), ("WRITE_SIZE", CALIB_BYTES / 1024)):
-            c = [means[k] for k in calib if k[1] == cname]
-            sc = [means[k] for k in scan if k[1] == cname]
-            if not c or not sc:
-                return
-            factor = known_kib / c[0]
-            print("    %s: copy of %d KiB reads %.1f KiB -> factor %.4f; scan %.1f KiB -> %.0f bytes"
-                  % (cname, known_kib, c[0], factor, sc[0], sc[0] * factor * 1024))
-            total += sc[0] * factor * 1024
-        print("scan_hbm_bytes_per_launch: %.0f" % total)
-        print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
+    # HBM traffic: read requests by size and write requests, in bytes per
+    # dispatch, scaled by the factor that makes them read the plain copy's
+    # known bytes (reads 256 MiB, writes 256 MiB).
+    def get(kfilter, cname):
+        v = [val for k, val in means.items() if kfilter(k) and k[1].startswith(cname)
+             and (k[1] == cname or k[1] == cname + "_sum")]
+        return v[0] if v else None
+    is_copy = lambda k: "neg" in k[0]
+    rd = ("TCC_EA0_RDREQ_32B", "TCC_EA0_RDREQ_64B", "TCC_EA0_RDREQ_128B")
+    if all(get(scan_key, c) is not None for c in rd) and all(get(is_copy, c) is not None for c in rd):
+        def rbytes(f):
+            return 32 * get(f, rd[0]) + 64 * get(f, rd[1]) + 128 * get(f, rd[2])
+        rfac = CALIB_BYTES / rbytes(is_copy)
+        scan_r = rbytes(scan_key) * rfac
+        print("## scan traffic (request counts by size, scaled by the plain-copy factor)")
+        print("    reads: copy of %d bytes counts %.0f -> factor %.4f; scan %.0f bytes"
+              % (CALIB_BYTES, rbytes(is_copy), rfac, scan_r))
+        total = scan_r
+        wr, wr64 = "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B"
+        if all(get(f, c) is not None for f in (scan_key, is_copy) for c in (wr, wr64)):
+            def wbytes(f):
+                return 32 * (get(f, wr) - get(f, wr64)) + 64 * get(f, wr64)
+            wfac = CALIB_BYTES / wbytes(is_copy)
+            scan_w = wbytes(scan_key) * wfac
+            print("    writes: copy of %d bytes counts %.0f -> factor %.4f; scan %.0f bytes"
+                  % (CALIB_BYTES, wbytes(is_copy), wfac, scan_w))
+            total += scan_w
+            print("scan_hbm_read_bytes_per_launch: %.0f" % scan_r)
+            print("scan_hbm_write_bytes_per_launch: %.0f" % scan_w)
+            print("scan_hbm_bytes_per_launch: %.0f" % total)
+            print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
 
 
 def plan_stats(depths: np.ndarray):
     """Per group: code bits T = sum t_j and active channels A = #{t_j > 0}."""
     d = depths.astype(np.int64)
     return d.sum(axis=1), (d > 0).sum(axis=1)
+
+
+def stats(xs):
+    """median, p10, p90, mean of a list of times (ms), rounded."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4),
+            "n": int(a.size)}
 
 
 def exact_topk(s: np.ndarray, k: int) -> np.ndarray:
@@ -238,6 +262,74 @@ def exact_topk(s: np.ndarray, k: int) -> np.ndarray:
     above = np.flatnonzero(s > kth)
     eq = np.flatnonzero(s == kth)
     return np.sort(np.concatenate([above, eq[:k - len(above)]]))
+
+
+def exact_topk_rows(k16: np.ndarray, q: np.ndarray, k: int):
+    """Top-k of the exact fp64 scores q . k over the fp16 keys, per query
+    head: k16 [groups][n][d] fp16, q [groups][G][d] -> list of index arrays
+    (row r = group * G + head)."""
+    groups, n, _ = k16.shape
+    out = []
+    step = 1 << 17
+    for g in range(groups):
+        qg = q[g].astype(np.float64)
+        s = np.empty((qg.shape[0], n))
+        for a in range(0, n, step):
+            s[:, a:a + step] = qg @ k16[g, a:a + step].astype(np.float64).T
+        out.extend(exact_topk(s[h], k) for h in range(qg.shape[0]))
+    return out
+
+
+def roofline_of(T, A, G, n, scan_ms):
+    """Algorithmic bytes and ALU work of one scan launch over the plans' code
+    bits T and active channels A (arrays over groups), against its time."""
+    nb = n // 64
+    bytes_per_launch = float((T * nb * 8 + A * nb * 2).sum()) + T.size * G * n * 4
+    # one integer op per plane bit and token, one fp32 multiply-add per
+    # active channel, token and query head
+    int_ops = float(T.sum()) * nb * 64
+    fma_ops = float((G * A).sum()) * nb * 64
+    s = scan_ms / 1e3
+    t_hbm = bytes_per_launch / (HBM_PEAK_GBPS * 1e9)
+    t_alu = int_ops / (INT_PEAK_TOPS * 1e12) + fma_ops / (FMA_PEAK_TOPS * 1e12)
+    return {
+        "bytes": bytes_per_launch, "int_ops": int_ops, "fma_ops": fma_ops,
+        "t_hbm_ms": t_hbm * 1e3, "t_alu_ms": t_alu * 1e3,
+        "alu_peak": (int_ops + fma_ops) / t_alu / 1e12,
+        "alu_tops": (int_ops + fma_ops) / s / 1e12,
+        "alu_frac": t_alu / s, "hbm_gbps": bytes_per_launch / s / 1e9,
+        "hbm_frac": t_hbm / s, "bound": "alu" if t_alu >= t_hbm else "hbm",
+    }
+
+
+def host_info():
+    """What the host offers the CPU baseline: logical CPUs, the ones this
+    process may run on, model name and sockets (from /proc/cpuinfo)."""
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity_cpus"] = os.cpu_count()
+    model, sockets, cores = None, set(), {}
+    try:
+        phys = None
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                continue
+            key, val = (x.strip() for x in line.split(":", 1))
+            if key == "model name" and model is None:
+                model = val
+            elif key == "physical id":
+                phys = val
+                sockets.add(val)
+            elif key == "cpu cores" and phys is not None:
+                cores[phys] = int(val)
+    except OSError:
+        pass
+    info["cpu_model"] = model
+    info["sockets"] = len(sockets) or None
+    info["physical_cores"] = sum(cores.values()) or None
+    return info
 
 
 def run_sweep(args):
@@ -270,10 +362,7 @@ def run_sweep(args):
         planes, scales = fk.encode(kd)
         del kd
         q_d, var_d = torch.from_numpy(ins.q).to(dev), torch.from_numpy(ins.var).to(dev)
-        exact = []
-        for g in range(H):
-            s = ins.q[g].astype(np.float64) @ ins.k[g].astype(np.float64).T
-            exact.extend(exact_topk(s[h], k) for h in range(G))
+        exact = exact_topk_rows(ins.k, ins.q, k)
         for B in budgets:
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             for rep in range(3):   # the last repetition is timed
@@ -325,22 +414,253 @@ def run_sweep(args):
         "layers": layers, "data": "synthetic", "rows": rows}))
 
 
+def timed_scans(fk, stores, depths_of, q_of, n, reps, scores):
+    """Scan event times (ms) over `reps` launches rotating through the store
+    copies, each through fathom_scan_timed (the kernels' own timestamps)."""
+    import torch
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        p, s = stores[i % len(stores)]
+        fk.scan(p, s, depths_of(i), q_of(i), n, scores=scores, events=(evs[i][0].h, evs[i][1].h))
+    torch.cuda.synchronize()
+    return [e[0].elapsed_time(e[1]) for e in evs]
+
+
+def run_configs(fk, args, main_ctx):
+    """The other workloads and budgets: scan (event-timed) and top-k medians,
+    roofline fractions and keys/s, per (workload, budget)."""
+    import torch
+
+    import fathom_inputs
+    out = []
+    reps = max(10, args.steps)
+    dev = torch.device("cuda:0")
+    todo = [("q256k", (68, 92, 136)), ("q1m", (68, 136)), ("s16", (92,))]
+    for name, budgets in todo:
+        w = fathom_inputs.WORKLOADS[name]
+        H, G, n, d, k = w.groups, w.G, w.n, w.d, w.k
+        t0 = time.perf_counter()
+        if name == args.workload and main_ctx is not None:
+            stores, qs_d, var_d = main_ctx["stores"], main_ctx["q_d"], main_ctx["var_d"]
+        else:
+            ins = fathom_inputs.make_inputs(H, G, n, w.seed)
+            qs = np.stack([fathom_inputs.make_queries(H, G, 1000 + i, d) for i in range(4)])
+            kd = torch.from_numpy(ins.k).to(dev)
+            del ins.k
+            ncop = max(1, min(4, int(2.2e9 // (H * n * 68)) + 1))
+            stores = [fk.encode(kd) for _ in range(ncop)]
+            del kd
+            qs_d = torch.from_numpy(qs).to(dev)
+            var_d = torch.from_numpy(ins.var).to(dev)
+        nq = qs_d.shape[0]
+        scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+        idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+        ws = fk.topk_workspace(H * G, n, k, dev)
+        for B in budgets:
+            deps = [fk.plan(qs_d[i], var_d, B) for i in range(nq)]
+            timed_scans(fk, stores, lambda i: deps[i % nq], lambda i: qs_d[i % nq], n, 3, scores)
+            sc = timed_scans(fk, stores, lambda i: deps[i % nq], lambda i: qs_d[i % nq], n, reps,
+                             scores)
+            tev = [[TimingEvent() for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                tev[i][0].record()
+                fk.topk(scores, k, indices=idx, workspace=ws)
+                tev[i][1].record()
+            torch.cuda.synchronize()
+            tk = [e[0].elapsed_time(e[1]) for e in tev]
+            TA = [plan_stats(x.cpu().numpy()) for x in deps]
+            T = np.mean([x[0] for x in TA], axis=0)
+            A = np.mean([x[1] for x in TA], axis=0)
+            med = float(np.median(sc))
+            rf = roofline_of(T, A, G, n, med)
+            out.append({
+                "workload": name, "budget_bits": B, "kv_heads": H, "G": G, "n": n, "k": k,
+                "scan_ms": stats(sc), "topk_ms": stats(tk),
+                "scan_keys_per_s": H * n / (med / 1e3),
+                "code_bits_mean": float(T.mean()), "active_channels_mean": float(A.mean()),
+                "roofline_bound": rf["bound"], "alu_frac": round(rf["alu_frac"], 4),
+                "hbm_frac": round(rf["hbm_frac"], 4), "hbm_GBps": round(rf["hbm_gbps"], 1),
+            })
+        del stores, scores, ws
+        torch.cuda.empty_cache()
+        print("[bench] configs %s done in %.1f s" % (name, time.perf_counter() - t0),
+              file=sys.stderr, flush=True)
+    return out
+
+
+def run_compare(fk, args, ctx, ins):
+    """The pages' comparison reads through the same store, scan and top-k at
+    the main workload: Fathom at several budgets, SparQ's top-r channels at
+    r = 16 and 32 (68 and 136 bits with scales), the 2-bit thumbnail and the
+    full 4-bit read; scan time and recall against the exact top-k."""
+    import torch
+    stores, q_d, var_d, n, k = ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["k"]
+    H, G = q_d.shape[1], q_d.shape[2]
+    nq = q_d.shape[0]
+    reps = max(10, args.steps)
+    dev = q_d.device
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+    ws = fk.topk_workspace(H * G, n, k, dev)
+    exact = exact_topk_rows(ins.k, ctx["qs"][0], k)
+    plans = [("fathom", B, lambda i, B=B: fk.plan(q_d[i], var_d, B)) for B in (48, 68, 92, 136)]
+    plans += [("sparq", r, lambda i, r=r: fk.plan_fixed("sparq", r, q=q_d[i])) for r in (16, 32)]
+    plans += [("thumbnail_2bit", 2, lambda i: fk.plan_fixed("uniform", 2, groups=H, G=G)),
+              ("full_4bit", 4, lambda i: fk.plan_fixed("uniform", 4, groups=H, G=G))]
+    rows = []
+    for name, param, mk in plans:
+        deps = [mk(i) for i in range(nq)]
+        timed_scans(fk, stores, lambda i: deps[i % nq], lambda i: q_d[i % nq], n, 3, scores)
+        sc = timed_scans(fk, stores, lambda i: deps[i % nq], lambda i: q_d[i % nq], n, reps, scores)
+        p, s = stores[0]
+        fk.scan(p, s, deps[0], q_d[0], n, scores=scores)
+        fk.topk(scores, k, indices=idx, workspace=ws)
+        got = idx.cpu().numpy()
+        rec = [np.intersect1d(got[r], exact[r], assume_unique=True).size / k for r in range(H * G)]
+        TA = [plan_stats(x.cpu().numpy()) for x in deps]
+        T = np.mean([x[0] for x in TA], axis=0)
+        A = np.mean([x[1] for x in TA], axis=0)
+        med = float(np.median(sc))
+        rows.append({"plan": name, "param": param, "scan_ms": stats(sc),
+                     "scan_keys_per_s": H * n / (med / 1e3),
+                     "code_bits_mean": float(T.mean()),
+                     "total_bits_mean": float((T + A / 4.0).mean()),
+                     "recall_mean": round(float(np.mean(rec)), 4),
+                     "recall_min": round(float(np.min(rec)), 4),
+                     "alu_frac": round(roofline_of(T, A, G, n, med)["alu_frac"], 4)})
+    return {"workload": ctx["name"], "k": k,
+            "recall": "|top-k of the plan's scores & top-k of exact fp64 scores over the fp16 "
+                      "keys| / k per query head, query group 0",
+            "rows": rows}
+
+
+def run_gather(fk, args, ctx):
+    """fathom_gather from pinned host memory: the runs of the step's plans
+    (B as benchmarked) at the main workload, and GB/s against contiguous run
+    size (every channel at depth 4, so a channel's run is 4 * n / 8 bytes:
+    4 KB at n = 8192 ... 512 KB at n = 2^20), each beside a contiguous pinned
+    copy of the same byte count."""
+    import torch
+    stores, q_d, var_d, n, B = ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["B"]
+    H = q_d.shape[1]
+    nb = n // 64
+    reps = 10
+    dev = q_d.device
+
+    def copy_rate(nbytes, hsrc, ddst):
+        """GB/s of one contiguous pinned-to-device copy of nbytes (at most the
+        size of the two buffers)."""
+        m = min(nbytes // 8, hsrc.numel() * hsrc.element_size() // 8,
+                ddst.numel() * ddst.element_size() // 8)
+        nbytes = m * 8
+        src = hsrc.view(torch.int64).view(-1)[:m]
+        dst = ddst.view(torch.int64).view(-1)[:m]
+        dst.copy_(src, non_blocking=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return nbytes / (ev[0].elapsed_time(ev[1]) / reps / 1e3) / 1e9
+
+    def gather_ms(hp, hs, dep, nn, gp, gs):
+        fk.gather(hp, hs, dep, nn, gp, gs)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            fk.gather(hp, hs, dep, nn, gp, gs)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    hp = stores[0][0].view(torch.int64).cpu().pin_memory().view(torch.uint64)
+    hs = stores[0][1].view(torch.int16).cpu().pin_memory().view(torch.uint16)
+    gp, gs = fk.empty_store(H, nb, dev)
+    deps = [fk.plan(q_d[i % q_d.shape[0]], var_d, B) for i in range(4)]
+    g_ms = float(np.mean([gather_ms(hp, hs, dp, n, gp, gs) for dp in deps]))
+    g_bytes = float(np.mean([(lambda T, A: (T * nb * 8 + A * nb * 2).sum())(
+        *plan_stats(x.cpu().numpy())) for x in deps]))
+    step = {"ms": round(g_ms, 4), "bytes_per_call": int(g_bytes),
+            "host_GBps": round(g_bytes / (g_ms / 1e3) / 1e9, 2),
+            "contiguous_copy_GBps": round(copy_rate(int(g_bytes) // 8 * 8, hp, gp), 2),
+            "source": "pinned host store, all %d groups, the step's plans at B=%d" % (H, B)}
+    curve = []
+    full = fk.plan_fixed("uniform", 4, groups=H, G=q_d.shape[2])
+    for nn in [8192 << i for i in range(8)]:
+        if nn > n:
+            break
+        nbs = nn // 64
+        # a store of exactly nn keys per channel: a channel's 4 planes are one run
+        shp = (H, 128, 4, nbs)
+        hpp = torch.empty(shp, dtype=torch.int64, pin_memory=True)
+        hpp.copy_(stores[0][0].view(torch.int64)[..., :nbs])
+        hss = torch.empty((H, 128, nbs), dtype=torch.int16, pin_memory=True)
+        hss.copy_(stores[0][1].view(torch.int16)[..., :nbs])
+        dpp, dss = fk.empty_store(H, nbs, dev)
+        ms = gather_ms(hpp.view(torch.uint64), hss.view(torch.uint16), full, nn, dpp, dss)
+        nbytes = H * 128 * (4 * nbs * 8 + nbs * 2)
+        curve.append({"run_bytes": 4 * nbs * 8, "n": nn, "bytes": nbytes,
+                      "gather_GBps": round(nbytes / (ms / 1e3) / 1e9, 2),
+                      "contiguous_copy_GBps": round(copy_rate(nbytes // 8 * 8, hpp, dpp), 2)})
+        del hpp, hss, dpp, dss
+    del hp, hs, gp, gs
+    return {"step": step, "by_run_size": curve}
+
+
+def cpu_baseline(args, ins, qs, H, G, n, k, B):
+    """The CPU oracle as it stands, timed on this host: one full decode step
+    of the workload on all threads, and the same step for one KV head on one
+    thread (the step's work per key is the same for every head)."""
+    import oracle
+    info = host_info()
+    nthreads = info["affinity_cpus"] or 1
+    nb = n // 64
+    res = {}
+    for label, groups, th in (("all_threads", H, nthreads), ("one_thread", 1, 1)):
+        kk = np.ascontiguousarray(ins.k[:groups])
+        var = np.ascontiguousarray(ins.var[:groups])
+        op, os_, _ = oracle.encode(kk, nthreads=nthreads)            # resident store (setup)
+        kb = np.ascontiguousarray(kk[:, n - 64:, :])
+        steps, spent = 0, 0.0
+        while steps < 3 and (steps == 0 or spent < 10.0):
+            qh = np.ascontiguousarray(qs[steps % len(qs)][:groups])
+            t0 = time.perf_counter()
+            oracle.encode(kb, nb_store=nb, block_offset=nb - 1, planes=op, scales=os_, nthreads=th)
+            od, _, _ = oracle.plan(qh, var, B, nthreads=th)
+            sc = oracle.scan_ref32(op, os_, od, qh, n, nthreads=th)
+            oracle.topk(sc.reshape(-1, n), k, nthreads=th)
+            spent += time.perf_counter() - t0
+            steps += 1
+        res[label] = {"value": steps * groups * n / spent, "threads": th,
+                      "sample": "%d decode step(s) of %d KV head(s) x %d keys (1-block encode, "
+                                "plan, fp32 scan, full-sort top-k), %.1f s"
+                                % (steps, groups, n, spent)}
+        print("[bench] cpu baseline %s: %.3g keys/s" % (label, res[label]["value"]),
+              file=sys.stderr, flush=True)
+    a = res["all_threads"]
+    return {"value": a["value"], "unit": "keys/s", "cores": a["threads"], "kind": "oracle",
+            "sample": a["sample"], "threads": a["threads"],
+            "host_logical_cpus": info["logical_cpus"], "host_physical_cores": info["physical_cores"],
+            "cpu_model": info["cpu_model"], "sockets": info["sockets"],
+            "one_thread": res["one_thread"]}
+
+
 def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize)
         return
-    if args.sweep:
-        if args.gpus != 1:
-            print("bench.py runs on one GPU only (--gpus %d requested)" % args.gpus,
-                  file=sys.stderr)
-            sys.exit(2)
-        run_sweep(args)
-        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep(args)
+        return
 
     import torch
 
@@ -392,10 +712,16 @@ def main():
             basis_k = None
         del kws
 
-    # Resident store copies, encoded on the GPU.
-    stores = []
-    for _ in range(args.copies):
+    # Resident store copies, encoded on the GPU; the full-store encode timed.
+    stores = [fk.encode(src)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.copies - 1):
         stores.append(fk.encode(src))
+    e1.record()
+    torch.cuda.synchronize()
+    encode_full_ms = e0.elapsed_time(e1) / max(1, args.copies - 1)
     newest = src[:, n - 64:, :].contiguous()            # the block each step re-encodes
     del k_d, src
     qrot = torch.empty((H, G, d), dtype=torch.float32, device=dev)
@@ -408,9 +734,8 @@ def main():
     scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
     idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
     ws = fk.topk_workspace(H * G, n, k, dev)
-    torch.cuda.synchronize()
-
     fws = fk.scan_topk_workspace(H, G, n, k, dev)
+    torch.cuda.synchronize()
 
     def step(s, ev=None, scan_ev=None):
         """One decode step: append the newest block, plan, scan, select.
@@ -458,34 +783,39 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
 
-    # The timed steps: the scan's launch time for the roofline comes from
-    # events the scan kernels record themselves (fathom_scan_timed), so no
-    # marker packet sits between the calls.
-    sevs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
+    # The headline pass: K plain steps between two events, nothing between
+    # the calls.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step(args.warmup + s, scan_ev=sevs[s])
+        step(args.warmup + s)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    scan_ms_timed = float(np.mean([e[0].elapsed_time(e[1]) for e in sevs]))
+    ms_per_step = start.elapsed_time(end) / args.steps
 
-    # The same steps again with events between all stages, for the breakdown.
+    # The scan pass: the same steps with every scan through fathom_scan_timed.
+    sevs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        step(args.warmup + s, scan_ev=sevs[s])
+    torch.cuda.synchronize()
+    scan_list = [e[0].elapsed_time(e[1]) for e in sevs]
+    scan_st = stats(scan_list)
+
+    # The stage pass: events between all stages.
     evs = [[TimingEvent() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
         step(args.warmup + s, evs[s])
     torch.cuda.synchronize()
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
-    stage_ms = stage.mean(axis=0)
+    step_list = [e[0].elapsed_time(e[4]) for e in evs]
 
-    # The fused call on the same inputs, timed after the steps.
+    # The fused call on the same inputs.
     for s in range(args.warmup):
         fused(s, [TimingEvent() for _ in range(2)])
     fev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
@@ -493,50 +823,9 @@ def main():
     for s in range(args.steps):
         fused(args.warmup + s, fev[s])
     torch.cuda.synchronize()
-    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
-
-    # fathom_gather: the runs each step's plan reads, copied from a pinned host
-    # copy of the store into a device store (outside the step: the store the
-    # step scans is resident).
-    gather = None
-    if not args.no_gather:
-        hp = stores[0][0].view(torch.int64).cpu().pin_memory().view(torch.uint64)
-        hs = stores[0][1].view(torch.int16).cpu().pin_memory().view(torch.uint16)
-        gp, gs = fk.empty_store(H, nb, dev)
-        gdep = [fk.plan(query(i), var_d, B) for i in range(args.steps)]
-        for i in range(2):
-            fk.gather(hp, hs, gdep[i], n, gp, gs)
-        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for i in range(args.steps):
-            gev[i][0].record()
-            fk.gather(hp, hs, gdep[i], n, gp, gs)
-            gev[i][1].record()
-        torch.cuda.synchronize()
-        g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
-        g_bytes = float(np.mean([(lambda T, A: (T * nb * 8 + A * nb * 2).sum())(
-            *plan_stats(x.cpu().numpy())) for x in gdep]))
-        # The host link's own rate: one contiguous pinned-to-device copy of
-        # the same byte count.
-        nbytes = int(g_bytes) // 8 * 8
-        src = hp.view(torch.int64).view(-1)[: nbytes // 8]
-        dst = gp.view(torch.int64).view(-1)[: nbytes // 8]
-        dst.copy_(src, non_blocking=True)
-        cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        torch.cuda.synchronize()
-        cev[0].record()
-        for _ in range(args.steps):
-            dst.copy_(src, non_blocking=True)
-        cev[1].record()
-        torch.cuda.synchronize()
-        c_ms = cev[0].elapsed_time(cev[1]) / args.steps
-        gather = {"ms": round(g_ms, 4), "bytes_per_call": int(g_bytes),
-                  "host_GBps": round(g_bytes / (g_ms / 1e3) / 1e9, 2),
-                  "contiguous_copy_GBps": round(nbytes / (c_ms / 1e3) / 1e9, 2),
-                  "source": "pinned host store, all %d groups" % H}
-        del src, dst
-        del hp, hs, gp, gs
+    fused_st = stats([e[0].elapsed_time(e[1]) for e in fev])
+    print("[bench] passes done: %.4f ms/step, scan median %.4f ms"
+          % (ms_per_step, scan_st["median"]), file=sys.stderr, flush=True)
 
     # Algorithmic work of each timed step's scan (plans recomputed after timing).
     Ts, As = [], []
@@ -546,41 +835,32 @@ def main():
         Ts.append(T)
         As.append(A)
     Ts, As = np.array(Ts), np.array(As)
-    bytes_per_launch = float(np.mean((Ts * nb * 8 + As * nb * 2).sum(axis=1))) + H * G * n * 4
-    # Algorithmic ALU work: one integer op per plane bit and token, one fp32
-    # multiply-add per active channel, token and query head.
-    int_ops = float(np.mean(Ts.sum(axis=1))) * nb * 64
-    fma_ops = float(np.mean((G * As).sum(axis=1))) * nb * 64
-    ops_per_launch = int_ops + fma_ops
-    scan_s = scan_ms_timed / 1e3
-    hbm_gbps = bytes_per_launch / scan_s / 1e9
-    t_hbm = bytes_per_launch / (HBM_PEAK_GBPS * 1e9)
-    t_alu = int_ops / (INT_PEAK_TOPS * 1e12) + fma_ops / (FMA_PEAK_TOPS * 1e12)
-    alu_peak = ops_per_launch / t_alu / 1e12         # the op mix's own peak rate
-    alu_tops = ops_per_launch / scan_s / 1e12
-    bound = "alu" if t_alu >= t_hbm else "hbm"
-    traffic = recorded_traffic()
-    if bound == "alu":
-        roof = {"bound": "alu", "achieved": round(alu_tops, 3), "peak": round(alu_peak, 2),
-                "unit": "Tlane-op/s", "frac": round(alu_tops / alu_peak, 4), "traffic": traffic}
+    rf = roofline_of(Ts.mean(axis=0), As.mean(axis=0), G, n, scan_st["median"])
+    traffic = recorded_counter(TRAFFIC_FILE, "scan_hbm_bytes_per_launch")
+    if rf["bound"] == "alu":
+        roof = {"bound": "alu", "achieved": round(rf["alu_tops"], 3),
+                "peak": round(rf["alu_peak"], 2), "unit": "Tlane-op/s",
+                "frac": round(rf["alu_frac"], 4), "traffic": traffic}
     else:
-        roof = {"bound": "hbm", "achieved": round(hbm_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+        roof = {"bound": "hbm", "achieved": round(rf["hbm_gbps"], 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(rf["hbm_frac"], 4), "traffic": traffic}
+    valu = recorded_counter(INSTR_FILE, "scan_valu_instructions_per_launch")
+    scan_s = scan_st["median"] / 1e3
     roof.update({
         "kernel": "scan_main",
-        "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
-        "launch_ms": round(scan_ms_timed, 4),
-        "alg_bytes_per_launch": int(bytes_per_launch),
-        "alg_int_ops_per_launch": int(int_ops),
-        "alg_fma_ops_per_launch": int(fma_ops),
-        "alu_bound_ms": round(t_alu * 1e3, 4),
-        "hbm_bound_ms": round(t_hbm * 1e3, 4),
-        "hbm_GBps": round(hbm_gbps, 1), "hbm_frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
-    })
-    # VALU issue: wave64 VALU instructions per launch (SQ_INSTS_VALU, from the
-    # committed counter summary) over one issue per CU per clock.
-    valu = recorded_valu()
-    roof.update({
+        "traffic_unit": "HBM bytes per launch (read requests by size + write requests)",
+        "traffic_read_bytes": recorded_counter(TRAFFIC_FILE, "scan_hbm_read_bytes_per_launch"),
+        "traffic_over_algorithmic": (None if traffic is None else
+                                     round(traffic / rf["bytes"], 4)),
+        "launch_ms": scan_st["median"],
+        "launch_time": "median of the scan pass's event-timed launches",
+        "alg_bytes_per_launch": int(rf["bytes"]),
+        "alg_int_ops_per_launch": int(rf["int_ops"]),
+        "alg_fma_ops_per_launch": int(rf["fma_ops"]),
+        "alu_bound_ms": round(rf["t_alu_ms"], 4),
+        "hbm_bound_ms": round(rf["t_hbm_ms"], 4),
+        "hbm_GBps": round(rf["hbm_gbps"], 1), "hbm_frac": round(rf["hbm_frac"], 4),
+        "alu_frac_target": 0.70,
         "valu_instructions_per_launch": valu,
         "valu_issue_frac": (None if valu is None else
                             round(valu / (scan_s * CUS * CLOCK_GHZ * 1e9), 4)),
@@ -589,7 +869,7 @@ def main():
     keys = H * n
     value = keys / (ms_per_step / 1e3)
     out = {
-        "metric": "keys scanned/sec (and HBM GB/s, % roofline) at 1M keys, 92-bit budget",
+        "metric": METRIC,
         "value": value,
         "unit": "keys/s",
         "n_gpus": 1,
@@ -609,11 +889,14 @@ def main():
             "kv_heads": H, "G": G, "n": n, "budget_bits": B, "k": k,
             "store_copies": args.copies, "parallelism": "single GPU",
         },
-        "stages_ms": {"encode_block": round(stage_ms[0], 4), "plan": round(stage_ms[1], 4),
-                      "scan": round(stage_ms[2], 4), "topk": round(stage_ms[3], 4),
-                      "note": "a second pass of the steps with events between the stages"},
-        "fused_scan_topk_ms": round(fused_ms, 4),
-        "gather_from_host": gather,
+        "scan_keys_per_s": keys / scan_s,
+        "scan_ms": scan_st,
+        "step_ms": stats(step_list),
+        "stages_ms": {"encode_block": stats(stage[:, 0]), "plan": stats(stage[:, 1]),
+                      "scan": stats(stage[:, 2]), "topk": stats(stage[:, 3]),
+                      "note": "a pass of the steps with events between the stages"},
+        "fused_scan_topk_ms": fused_st,
+        "encode_full_store_ms": round(encode_full_ms, 4),
         "klt_store": klt,
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "plan": {"code_bits_mean": float(Ts.mean()), "active_channels_mean": float(As.mean()),
@@ -621,29 +904,22 @@ def main():
         "roofline": roof,
     }
 
+    ctx = {"name": w.name, "stores": stores, "q_d": q_d, "qs": qs, "var_d": var_d, "n": n,
+           "k": k, "B": B}
+    if not args.no_compare and args.store == "raw":
+        out["compare_plans"] = run_compare(fk, args, ctx, ins)
+        print("[bench] fixed-plan comparison done", file=sys.stderr, flush=True)
+    if not args.no_gather and args.store == "raw":
+        out["gather_from_host"] = run_gather(fk, args, ctx)
+        print("[bench] gather done", file=sys.stderr, flush=True)
+    if not args.no_configs and args.store == "raw":
+        del scores, ws, fws
+        out["configs"] = run_configs(fk, args, ctx if w.name == "q1m" else None)
+    del stores, ctx
+    torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline and args.store == "raw":
-        import oracle
-        nthreads = args.cpu_threads or min(H, os.cpu_count() or 1)
-        print("[bench] cpu baseline: oracle step on %d threads" % nthreads, file=sys.stderr,
-              flush=True)
-        op, os_, _ = oracle.encode(ins.k, nthreads=nthreads)           # resident store (setup)
-        kb = np.ascontiguousarray(ins.k[:, n - 64:, :])
-        cpu_steps = 3
-        t0 = time.perf_counter()
-        for s in range(cpu_steps):
-            qh = qs[(args.warmup + s) % args.queries]
-            oracle.encode(kb, nb_store=nb, block_offset=nb - 1, planes=op, scales=os_,
-                          nthreads=nthreads)
-            od, _, _ = oracle.plan(qh, ins.var, B, nthreads=nthreads)
-            sc = oracle.scan_ref32(op, os_, od, qh, n, nthreads=nthreads)
-            oracle.topk(sc.reshape(-1, n), k, nthreads=nthreads)
-        cpu_s = time.perf_counter() - t0
-        out["cpu_baseline"] = {
-            "value": cpu_steps * keys / cpu_s, "unit": "keys/s", "cores": nthreads,
-            "kind": "oracle",
-            "sample": "%d full decode steps of the same workload (1-block encode, plan, fp32 "
-                      "scan of all %d keys, full-sort top-k), %.1f s" % (cpu_steps, keys, cpu_s),
-        }
+        out["cpu_baseline"] = cpu_baseline(args, ins, qs, H, G, n, k, B)
     print(json.dumps(out), flush=True)
 
 
