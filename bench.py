@@ -130,6 +130,9 @@ def parse():
     ap.add_argument("--workload", default="q1m")
     ap.add_argument("--budget", type=int, default=92)
     ap.add_argument("--copies", type=int, default=4, help="store copies the steps rotate through")
+    ap.add_argument("--step-mode", choices=("fused", "separate"), default="fused",
+                    help="the headline step's scan and selection: fathom_scan_topk without a "
+                         "score buffer (fused), or fathom_scan then fathom_topk (separate)")
     ap.add_argument("--queries", type=int, default=8, help="distinct query groups drawn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--store", choices=("raw", "klt"), default="raw",
@@ -737,10 +740,13 @@ def main():
     fws = fk.scan_topk_workspace(H, G, n, k, dev)
     torch.cuda.synchronize()
 
-    def step(s, ev=None, scan_ev=None):
+    def step(s, ev=None, scan_ev=None, mode="separate"):
         """One decode step: append the newest block, plan, scan, select.
-        ev: five events between the stages; scan_ev: two events that
-        fathom_scan_timed records from the scan kernels' own timestamps."""
+        mode "fused": the scan and the selection as fathom_scan_topk without a
+        score buffer; "separate": fathom_scan then fathom_topk.
+        ev: five events between the stages (separate mode); scan_ev: two
+        events that fathom_scan_timed records from the scan kernels' own
+        timestamps."""
         planes, scales = stores[s % len(stores)]
         if ev is not None:
             ev[0].record()
@@ -751,6 +757,10 @@ def main():
         fk.plan(q, var_d, B, depths=depths)
         if ev is not None:
             ev[2].record()
+        if mode == "fused":
+            fk.scan_topk(planes, scales, depths, q, n, k, indices=idx, workspace=fws,
+                         write_scores=False)
+            return
         if scan_ev is not None:   # the scan kernels' own start and end timestamps
             fk.scan(planes, scales, depths, q, n, scores=scores,
                     events=(scan_ev[0].h, scan_ev[1].h))
@@ -762,13 +772,14 @@ def main():
         if ev is not None:
             ev[4].record()
 
-    def fused(s, ev):
+    def fused(s, ev, write_scores):
         """The scan and selection as the one call fathom_scan_topk."""
         planes, scales = stores[s % len(stores)]
         q = query(s)
         fk.plan(q, var_d, B, depths=depths)
         ev[0].record()
-        fk.scan_topk(planes, scales, depths, q, n, k, scores=scores, indices=idx, workspace=fws)
+        fk.scan_topk(planes, scales, depths, q, n, k, scores=scores, indices=idx, workspace=fws,
+                     write_scores=write_scores)
         ev[1].record()
 
     # Plain copy of known size, for scaling HBM byte counters (untimed).
@@ -778,24 +789,28 @@ def main():
         torch.neg(calib_src, out=calib_dst)
     del calib_src, calib_dst
 
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    print("[bench] warmup done; timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    def plain_pass(mode):
+        """W warm-up steps, then K steps between two events, nothing between
+        the calls: (ms per step, host wall seconds)."""
+        for s in range(args.warmup):
+            step(s, mode=mode)
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record()
+        for s in range(args.steps):
+            step(args.warmup + s, mode=mode)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, time.perf_counter() - wall0
 
-    # The headline pass: K plain steps between two events, nothing between
-    # the calls.
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(args.warmup + s)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = start.elapsed_time(end) / args.steps
+    # The headline pass in the chosen step mode, then the other mode.
+    other = "separate" if args.step_mode == "fused" else "fused"
+    ms_per_step, wall = plain_pass(args.step_mode)
+    ms_other, _ = plain_pass(other)
+    print("[bench] %s steps %.4f ms, %s steps %.4f ms" % (args.step_mode, ms_per_step, other,
+                                                       ms_other), file=sys.stderr, flush=True)
 
     # The scan pass: the same steps with every scan through fathom_scan_timed.
     sevs = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
@@ -815,15 +830,18 @@ def main():
     stage = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])
     step_list = [e[0].elapsed_time(e[4]) for e in evs]
 
-    # The fused call on the same inputs.
-    for s in range(args.warmup):
-        fused(s, [TimingEvent() for _ in range(2)])
-    fev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        fused(args.warmup + s, fev[s])
-    torch.cuda.synchronize()
-    fused_st = stats([e[0].elapsed_time(e[1]) for e in fev])
+    # The fused call on the same inputs, with and without a score buffer.
+    fused_st = {}
+    for ws_flag in (True, False):
+        for s in range(args.warmup):
+            fused(s, [TimingEvent() for _ in range(2)], ws_flag)
+        fev = [[TimingEvent() for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            fused(args.warmup + s, fev[s], ws_flag)
+        torch.cuda.synchronize()
+        fused_st["scores_written" if ws_flag else "no_scores"] = stats(
+            [e[0].elapsed_time(e[1]) for e in fev])
     print("[bench] passes done: %.4f ms/step, scan median %.4f ms"
           % (ms_per_step, scan_st["median"]), file=sys.stderr, flush=True)
 
@@ -889,6 +907,10 @@ def main():
             "kv_heads": H, "G": G, "n": n, "budget_bits": B, "k": k,
             "store_copies": args.copies, "parallelism": "single GPU",
         },
+        "step_mode": args.step_mode,
+        "step_mode_note": ("fused: the scan and the selection as fathom_scan_topk without a "
+                           "score buffer; separate: fathom_scan then fathom_topk"),
+        "ms_per_step_%s" % other: ms_other,
         "scan_keys_per_s": keys / scan_s,
         "scan_ms": scan_st,
         "step_ms": stats(step_list),
@@ -896,6 +918,7 @@ def main():
                       "scan": stats(stage[:, 2]), "topk": stats(stage[:, 3]),
                       "note": "a pass of the steps with events between the stages"},
         "fused_scan_topk_ms": fused_st,
+        "separate_scan_topk_ms": stats(stage[:, 2] + stage[:, 3]),
         "encode_full_store_ms": round(encode_full_ms, 4),
         "klt_store": klt,
         "wall_ms_per_step": wall * 1e3 / args.steps,

@@ -244,22 +244,31 @@ int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
 /*
  * fathom_scan_topk — fathom_scan followed by fathom_topk on its scores, with
  * the top-k candidates taken by the scan itself instead of by a second pass
- * over the scores.
+ * over the scores, and the scores written only when the caller wants them.
  *
  * Results are those of the two calls, bit for bit: scores as fathom_scan
- * writes them, indices as fathom_topk selects them (§2 order, ascending).
- * When n is a multiple of 65536 and the store takes the fast scan path
- * (nb_store a multiple of 8 blocks, scales 16-byte aligned), the rounds of
- * 2048 keys that fathom_topk samples are scanned first, the cut is set from
- * their scores, and the other rounds write every score at or above the cut
- * to a per-round candidate region as they are scanned; only the sampled
- * rounds are read back.  Otherwise the two calls run as they are.
+ * writes them (when `scores` is non-null), indices as fathom_topk selects
+ * them (§2 order, ascending).  When 65536 <= n <= 2^21, n is a multiple of
+ * 2048 and the store takes the fast scan path (nb_store a multiple of 8
+ * blocks, planes and scales 16-byte aligned): 16 tiles of 512 keys spread
+ * over each row are scored first, a cut tau per row is taken from that
+ * sample, and the scan
+ * then writes every score >= tau, per 512-key tile, to the row's candidate
+ * buffer, from which the selection is made.  A row whose candidates cannot
+ * give the selection (fewer than k of them, or a tile with more than its
+ * region holds: heavy ties) is selected from its scores: from `scores`, or,
+ * when `scores` is null, from a second scan of its group into the workspace.
+ * Otherwise the two calls run as they are (into the workspace when `scores`
+ * is null).
  *
  *   planes, scales, nb_store, depths, q, groups, G, d, n: as fathom_scan
- *   scores  [groups][G][n] fp32 output (always written)
+ *   scores  [groups][G][n] fp32 output, or NULL (no scores are written to
+ *           caller memory; the fused path then writes none at all unless a
+ *           row needs them)
  *   indices [groups * G][k] int32 output
  *   workspace: device scratch of at least fathom_scan_topk_workspace_bytes(
- *   groups, G, n, k) bytes, 256-byte aligned; contents on entry do not matter.
+ *   groups, G, n, k) bytes (it includes room for every row's scores),
+ *   256-byte aligned; contents on entry do not matter.
  *   1 <= k <= n.
  */
 size_t fathom_scan_topk_workspace_bytes(int64_t groups, int32_t G, int64_t n, int32_t k);

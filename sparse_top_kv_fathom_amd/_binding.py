@@ -248,12 +248,16 @@ def scan_topk_workspace(groups: int, G: int, n: int, k: int, device="cuda") -> t
 def scan_topk(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, q: torch.Tensor,
               n: int, k: int, scores: torch.Tensor | None = None,
               indices: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-              stream=None):
-    """fathom_scan_topk: (scores [groups][G][n] fp32, indices [groups*G][k] int32)."""
+              stream=None, write_scores: bool = True):
+    """fathom_scan_topk: (scores [groups][G][n] fp32 or None, indices
+    [groups*G][k] int32).  write_scores=False passes no score buffer (the
+    scores are then not returned)."""
     groups, G, d = q.shape
     nb_store = planes.shape[-1]
     ps, ss = store_shapes(groups, nb_store, d)
-    if scores is None:
+    if not write_scores:
+        scores = None
+    elif scores is None:
         scores = torch.empty((groups, G, n), dtype=torch.float32, device=q.device)
     if indices is None:
         indices = torch.empty((groups * G, k), dtype=torch.int32, device=q.device)
@@ -262,7 +266,7 @@ def scan_topk(planes: torch.Tensor, scales: torch.Tensor, depths: torch.Tensor, 
     st = lib().fathom_scan_topk(
         _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
         nb_store, _dev(depths, "depths", torch.uint8, (groups, d)), _dev(q, "q", torch.float32),
-        groups, G, d, int(n), int(k), _dev(scores, "scores", torch.float32, (groups, G, n)),
+        groups, G, d, int(n), int(k), _opt(scores, "scores", torch.float32, (groups, G, n)),
         _dev(indices, "indices", torch.int32, (groups * G, k)),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
     _check(st, "fathom_scan_topk")

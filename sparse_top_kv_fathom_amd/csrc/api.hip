@@ -180,8 +180,7 @@ int fathom_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_
                      const uint8_t* depths, const float* q, int64_t groups, int32_t G, int32_t d,
                      int64_t n, int32_t k, float* scores, int32_t* indices, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  if (!planes || !scales || !depths || !q || !scores || !indices || !workspace)
-    return FATHOM_ERR_NULL_ARG;
+  if (!planes || !scales || !depths || !q || !indices || !workspace) return FATHOM_ERR_NULL_ARG;
   if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups ||
       !valid_tokens(n))
     return FATHOM_ERR_BAD_SHAPE;

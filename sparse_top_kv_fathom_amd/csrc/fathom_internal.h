@@ -36,12 +36,13 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t n
 int64_t scan_max_workgroups(int64_t groups, int64_t n);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
-size_t topk_rounds_workspace_bytes(int64_t rows, int64_t n, int64_t R);
-hipError_t launch_topk_rounds_cut(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
-                                  void* ws, hipStream_t stream);
-hipError_t launch_topk_rounds_finish(const float* scores, int64_t rows, int64_t n, int64_t R,
-                                     int run, int sampled, int k, int32_t* indices, void* ws,
-                                     hipStream_t stream);
+// Pieces of fathom_scan_topk's selection (workspace layout: topk::FusedWs).
+hipError_t launch_fused_guess(const uint32_t* sample, int64_t rows, int64_t n, int64_t R,
+                              int nkeys, int target, void* ws, uint32_t* gflag, int G,
+                              hipStream_t stream);
+hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
+                                int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
+                                hipStream_t stream);
 size_t scan_topk_workspace_bytes(int64_t groups, int G, int64_t n, int k);
 hipError_t launch_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                             const uint8_t* depths, const float* q, int64_t groups, int G,

@@ -59,6 +59,9 @@
 // whose offsets exceed 32 bits or whose scale rows are not 16-byte aligned.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+#include <cmath>
+
 #include "fathom_internal.h"
 #include "topk_layout.h"
 
@@ -259,95 +262,70 @@ __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&ac
   asm volatile("" : "+v"(o));
 }
 
-// Epilogue: S = U + o (o of block b, head h sits in lane b * G + h); blocks
-// [0, store_to] of the tile are stored.  The offsets pass through the wave's
-// own kNB * G floats of LDS (`s_o`) and come back as broadcast reads, so the
-// adds take vector operands (dual issue) instead of one lane read and one
-// scalar-operand add per (block, head).
+// Epilogue: S = U + o (o of block b, head h sits in lane b * G + h), left in
+// acc; blocks [0, store_to] of the tile are stored when `out` is non-null.
+// The offsets pass through the wave's own kNB * G floats of LDS (`s_o`) and
+// come back as broadcast reads, so the adds take vector operands (dual issue)
+// instead of one lane read and one scalar-operand add per (block, head).
 template <int G>
-__device__ __forceinline__ void store_tile(const float (&acc)[kNB][G], float o, int store_to,
-                                           int64_t n, float* __restrict__ out, float* s_o) {
+__device__ __forceinline__ void finish_tile(float (&acc)[kNB][G], float o, int store_to, int64_t n,
+                                            float* __restrict__ out, float* s_o) {
   const int lane = lane_id();
   if (lane < kNB * G) s_o[lane] = o;
   wave_lds_sync();
 #pragma unroll
-  for (int b = 0; b < kNB; ++b) {
-    if (b <= store_to) {
+  for (int b = 0; b < kNB; ++b)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        __builtin_nontemporal_store(acc[b][h] + s_o[b * G + h], out + h * n + b * kBlock + lane);
+    for (int h = 0; h < G; ++h) acc[b][h] = acc[b][h] + s_o[b * G + h];
+  if (out != nullptr) {
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) {
+      if (b <= store_to) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          __builtin_nontemporal_store(acc[b][h], out + h * n + b * kBlock + lane);
+      }
     }
   }
 }
 
-// Scan with top-k candidate emission.  The row's rounds (kRoundBlocks blocks
-// = 2048 keys each) come in runs of 32; the first 4 of every run (one chunk
-// of 8192 keys in 8) are scanned first, their scores alone set the cut tau of
-// every row, and the other rounds then also write each score >= tau, as
-// (order key, index) in index order, to the round's region of the row's
-// candidate buffer (a round with more than its region holds flags the row).
-constexpr int kRunRounds = 32, kSampledRounds = 4;
+// Candidate emission of fathom_scan_topk.  Every wave tile (kNB blocks =
+// kTileKeys keys of a row) is one region of the row's candidate buffer: the
+// wave writes each score >= tau of head h, as (order key, index) in index
+// order, to region `tile` of row (group, h), and the region's count to the
+// segment table; no other wave takes part, so there is no barrier.  A tile
+// with more candidates than its region holds flags the row.
+constexpr int kTileKeys = kNB * kBlock;
+constexpr int64_t kFusedMinKeys = 65536;   // shorter rows: scan, then top-k
+constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stages
 
-struct EmitCtx {
-  void* tws;        // top-k workspace, one row per (group, head)
-  int64_t n;
-  int64_t round;    // the workgroup's round in its row
-};
-
-// Candidates of a wave tile: 8 blocks x G heads; `tf` the cuts as floats.
 template <int G>
-__device__ __forceinline__ void emit_tile(const float (&acc)[kNB][G], float o, const float (&tf)[G],
-                                          int64_t grp, int64_t blk0, const EmitCtx& ec,
-                                          uint32_t (*s_emit)[8]) {
+__device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float (&tf)[G],
+                                          int64_t grp, int64_t blk0, int64_t n, void* tws) {
   const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t cnt[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) cnt[h] = 0u;
-#pragma unroll
-  for (int b = 0; b < kNB; ++b)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float obh = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
-      cnt[h] += (uint32_t)__popcll(__ballot(acc[b][h] + obh >= tf[h]));
-    }
-  if (lane == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_emit[wave][h] = cnt[h];
-  __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int64_t tile = blk0 / kNB;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    uint32_t slot = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t c = s_emit[w][h];
-      slot += w < wave ? c : 0u;
-      total += c;
-    }
-    const topk::RowWs rw = topk::row_ws(ec.tws, ec.n, kRoundBlocks * kBlock, grp * G + h);
-    const uint32_t base = (uint32_t)ec.round * rw.region;
-    if (wave == 0 && lane == 0) {
-      rw.seg[2 * ec.round] = base;
-      rw.seg[2 * ec.round + 1] = total;
-      if (total > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
-    }
-    if (cnt[h] == 0u) continue;
+    const topk::RowWs rw = topk::row_ws(tws, n, kTileKeys, grp * G + h);
+    const uint32_t base = (uint32_t)tile * rw.region;
+    uint32_t cnt = 0;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      const float obh = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, o), b * G + h));
-      const float sc = acc[b][h] + obh;
-      const bool cand = sc >= tf[h];
+      const bool cand = sc[b][h] >= tf[h];
       const uint64_t m = __ballot(cand);
-      if (cand) {
-        const uint32_t sl = slot + (uint32_t)__popcll(m & below);
-        if (sl < rw.region)
+      if (m != 0ull) {
+        const uint32_t sl = cnt + (uint32_t)__popcll(m & below);
+        if (cand && sl < rw.region)
           reinterpret_cast<uint2*>(rw.cand)[base + sl] =
-              make_uint2(topk::order_key(sc), (uint32_t)((blk0 + b) * kBlock + lane));
+              make_uint2(topk::order_key(sc[b][h]), (uint32_t)((blk0 + b) * kBlock + lane));
+        cnt += (uint32_t)__popcll(m);
       }
-      slot += (uint32_t)__popcll(m);
+    }
+    if (lane == 0) {
+      rw.seg[2 * tile] = base;
+      rw.seg[2 * tile + 1] = cnt;
+      if (cnt > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
     }
   }
 }
@@ -548,18 +526,19 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int fir
   }
 }
 
-// MODE 0: every round; 1: the sampled rounds of the candidate emission
-// (first kSampledRounds of every kRunRounds); 2: the other rounds, which also
-// emit candidates.  Modes 1 and 2 need kRounds == 1 and whole runs.
+// MODE 0: scores only; 1: scores (when `scores` is non-null) and the top-k
+// candidates of every wave tile (fathom_scan_topk; needs kRounds == 1).
+// `gate` (nullable, per group): a group whose word is 0 is skipped (the
+// scan that fathom_scan_topk runs again for rows whose selection failed).
 template <int G, int MODE = 0>
 __global__ __launch_bounds__(kThreads) void scan_main(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t nrounds, int64_t n,
-    int64_t wgs_per_group, float* __restrict__ scores, void* tws) {
+    int64_t wgs_per_group, float* __restrict__ scores, void* tws,
+    const uint32_t* __restrict__ gate) {
   static_assert(kNB * G <= 64, "one lane per (block, head) in the offset fold");
   static_assert(MODE == 0 || kRounds == 1, "candidate emission runs one round per workgroup");
   __shared__ MainShared<G> sh;
-  __shared__ uint32_t s_emit[kWaves][8];
   __shared__ float s_o[kWaves][kNB * G];
 
   // XCD-aware remap of the workgroup id (bijective on [0, gridDim.x)).
@@ -568,19 +547,14 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   uint32_t id = blockIdx.x;
   if (id < per_xcd * kXcds) id = (id % kXcds) * per_xcd + id / kXcds;
   const int64_t grp = id / wgs_per_group;
-  int64_t round0 = (id % wgs_per_group) * kRounds;
-  if (MODE == 1)
-    round0 = (round0 / kSampledRounds) * kRunRounds + round0 % kSampledRounds;
-  else if (MODE == 2)
-    round0 = (round0 / (kRunRounds - kSampledRounds)) * kRunRounds + kSampledRounds +
-             round0 % (kRunRounds - kSampledRounds);
+  if (gate != nullptr && gate[grp] == 0u) return;   // uniform over the workgroup
+  const int64_t round0 = (id % wgs_per_group) * kRounds;
   const int nr = kRounds > 1 ? (int)min<int64_t>(kRounds, nrounds - round0) : 1;
-  float tf[G];   // MODE 2: the rows' cuts as floats
-  if (MODE == 2) {
+  float tf[G];   // MODE 1: the rows' cuts as floats
+  if (MODE == 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
-      tf[h] = topk::key_float(
-          topk::row_ws(tws, n, kRoundBlocks * kBlock, grp * G + h).st[topk::kS_TAU]);
+      tf[h] = topk::key_float(topk::row_ws(tws, n, kTileKeys, grp * G + h).st[topk::kS_TAU]);
   }
 
   const int tid = threadIdx.x;
@@ -590,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   const char* planes_g =
       reinterpret_cast<const char*>(planes + grp * kD * (int64_t)kPlanes * nb_store);
   const char* scales_g = reinterpret_cast<const char*>(scales + grp * kD * nb_store);
-  float* scores_g = scores + grp * G * n;
+  float* scores_g = scores != nullptr ? scores + grp * G * n : nullptr;
 
   // The plan's depths and the group's queries are requested together, so they
   // share one round trip to memory (the queries go straight to LDS: held in
@@ -696,8 +670,9 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     main_depth<2, G, true>(c, sh.tb, rc[0] + rc[1], rc[2], ChanIter{rm.lo[2], rm.hi[2]}, acc, o);
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
-    store_tile<G>(acc, o, kNB - 1, n, scores_g + blk0 * kBlock, s_o[wave]);
-    if (MODE == 2) emit_tile<G>(acc, o, tf, grp, blk0, EmitCtx{tws, n, round0}, s_emit);
+    finish_tile<G>(acc, o, kNB - 1, n, scores_g != nullptr ? scores_g + blk0 * kBlock : nullptr,
+                   s_o[wave]);
+    if (MODE == 1) emit_tile<G>(acc, tf, grp, blk0, n, tws);
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
@@ -781,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void scan_tail(
   tail_depth<3, G>(c, ChanIter{dm.lo[1], dm.hi[1]}, dm.count[1], acc, o);
   tail_depth<2, G>(c, ChanIter{dm.lo[2], dm.hi[2]}, dm.count[2], acc, o);
   tail_depth<1, G>(c, ChanIter{dm.lo[3], dm.hi[3]}, dm.count[3], acc, o);
-  store_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock, s_o[wave]);
+  finish_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock, s_o[wave]);
 }
 
 // With timing events, the first launch records ev_start and the last one
@@ -804,10 +779,12 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
     if (timed)
       hipExtLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, ev_start,
                             first < nblk ? nullptr : ev_stop, 0u, planes, scales, nb_store,
-                            depths, q, nrounds, n, wgs, scores, (void*)nullptr);
+                            depths, q, nrounds, n, wgs, scores, (void*)nullptr,
+                            (const uint32_t*)nullptr);
     else
       hipLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, planes, scales, nb_store,
-                         depths, q, nrounds, n, wgs, scores, (void*)nullptr);
+                         depths, q, nrounds, n, wgs, scores, (void*)nullptr,
+                         (const uint32_t*)nullptr);
   }
   if (first < nblk) {
     const int64_t wgs = (nblk - first + kRoundBlocks - 1) / kRoundBlocks;
@@ -822,34 +799,168 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
   }
 }
 
+// The sample of fathom_scan_topk: the scores of NT wave tiles (kNB blocks of
+// 64 keys each) spread evenly over a group's row, in fp32 but in no
+// particular order (only the cut tau is taken from them; the candidates are
+// then scored by the scan itself), written as order keys to
+// sample[group * G + h][i * kTileKeys + token] for sampled tile i.  One
+// workgroup per sampled tile stages the tile's plane words (each plane row of
+// the tile is 64 contiguous bytes), scales and the group's queries in LDS with
+// one round of loads; then waves 2b and 2b + 1 score block b of the tile over
+// channels [0, 64) and [64, 128), with the channel depths held in scalar
+// registers and the LDS reads of four channels issued together, and add their
+// two partial sums.
+constexpr int kSampleTiles = 16;   // sampled tiles per group at most (8192 keys)
+constexpr int kSampleThreads = 2 * kNB * 64;
+static_assert(kSampleTiles * kTileKeys <= topk::kMaxSampleKeys, "sample buffer");
+
+template <int G>
+__global__ __launch_bounds__(kSampleThreads) void fused_sample(
+    const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
+    const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t tile_stride,
+    uint32_t* __restrict__ sample) {
+  constexpr int kT = kSampleThreads;                   // 1024 threads, two waves per block
+  constexpr int kPieces = kD * kPlanes * 4 / kT;       // 16-byte pieces per thread
+  __shared__ uint64_t s_w[kD * kPlanes][kNB];          // 32 KB: row (channel, plane), block
+  __shared__ uint16_t s_sc[kD][kNB];
+  __shared__ float s_q[kD][G];
+  __shared__ float s_part[kNB][G][kBlock];
+  const int64_t grp = blockIdx.y, ti = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = wv >> 1, half = wv & 1;                     // block, channel half
+  const int64_t blk0 = ti * tile_stride * kNB;
+  {
+    // Piece i of thread t: row r = piece / 4 (of 512), blocks 2 (piece % 4)
+    // and 2 (piece % 4) + 1.
+    uint4 v[kPieces];
+    const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int piece = tid + i * kT;
+      v[i] = *reinterpret_cast<const uint4*>(pg + (int64_t)(piece >> 2) * nb_store +
+                                             2 * (piece & 3));
+    }
+    uint4 sv = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < kD) sv = *reinterpret_cast<const uint4*>(scales + (grp * kD + tid) * nb_store + blk0);
+    float qv[G];
+    if (tid < kD) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[h] = q[(grp * G + h) * kD + tid];
+    }
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int piece = tid + i * kT;
+      *reinterpret_cast<uint4*>(&s_w[piece >> 2][2 * (piece & 3)]) = v[i];
+    }
+    if (tid < kD) {
+      *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s_q[tid][h] = qv[h];
+    }
+  }
+  // The depths of this wave's 64 channels, four to a scalar register.
+  uint32_t dw[16];
+  const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(depths + grp * kD + 64 * half);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dw[i] = __builtin_amdgcn_readfirstlane(dsrc[i]);
+  __syncthreads();
+  const int hsel = lane >> 5, bit = lane & 31;
+  float acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t dq = dw[i];
+    if (dq == 0u) continue;
+    const int c0 = 64 * half + 4 * i;
+    uint32_t d[4][kPlanes];
+    float a[4], qv[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p)
+        d[u][p] = reinterpret_cast<const uint32_t*>(&s_w[(c0 + u) * kPlanes + p][b])[hsel];
+      a[u] = half_lo(s_sc[c0 + u][b]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[u][h] = s_q[c0 + u][h];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = min((int)((dq >> (8 * u)) & 0xffu), kPlanes);
+      if (t == 0) continue;
+      int c4 = 0;
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p) c4 = 2 * c4 + (int)((d[u][p] >> bit) & 1u);
+      const int cp = c4 >> (kPlanes - t);
+      // (c' + 1/2 - 2^(t-1)) * a / 2^(t-1)
+      const float kh = __builtin_ldexpf(((float)cp + 0.5f - (float)(1 << (t - 1))) * a[u], 1 - t);
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qv[u][h], kh, acc[h]);
+    }
+  }
+  if (half == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      sample[(grp * G + h) * (int64_t)topk::kMaxSampleKeys + ti * kTileKeys + b * kBlock + lane] =
+          topk::order_key(acc[h] + s_part[b][h][lane]);
+  }
+}
+
 }  // namespace
 
+// fathom_scan_topk.  Fused path (whole rounds, 64k to 2M keys, the main
+// kernel's store layout): sample -> cut per row -> scan that writes the scores
+// (when a buffer is given) and every score >= tau into its wave tile's
+// candidate region -> selection from the candidates.  Without a score buffer,
+// rows whose candidates cannot give the selection (fewer than k, or a region
+// overflowed) are flagged: their groups are scanned again into the
+// workspace's score area and selected from there; the other groups' work
+// ends at once.  Otherwise the two calls run as they are.
 template <int G>
 hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                               const uint8_t* depths, const float* q, int64_t groups, int64_t n,
                               int k, float* scores, int32_t* indices, void* ws,
                               hipStream_t stream) {
-  const int64_t rows = groups * G, R = (int64_t)kRoundBlocks * kBlock;
-  const int64_t nrounds = n / R;
-  const bool fused = kRounds == 1 && n % (R * kRunRounds) == 0 &&
-                     topk::sample_stride(n) * kSampledRounds * R == kRunRounds * R &&
-                     nb_store <= kMaxFastBlocks &&
+  const int64_t rows = groups * G, R = kTileKeys;
+  const int64_t nblk = n / kBlock, nrounds = nblk / kRoundBlocks;
+  const topk::FusedWs fw = topk::fused_ws(ws, rows, groups, n, R);
+  float* sc = scores != nullptr ? scores : fw.scores;
+  const bool fused = kRounds == 1 && n % ((int64_t)kRoundBlocks * kBlock) == 0 &&
+                     n >= kFusedMinKeys && n / R <= kFusedMaxTiles && nb_store <= kMaxFastBlocks &&
                      nb_store % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+                     (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(depths) & 3) == 0;
   if (!fused) {   // the two calls one after the other
-    launch_scan_g<G>(planes, scales, nb_store, depths, q, groups, n, scores, stream);
-    return launch_topk(scores, rows, n, k, indices, ws, stream);
+    launch_scan_g<G>(planes, scales, nb_store, depths, q, groups, n, sc, stream);
+    return launch_topk(sc, rows, n, k, indices, ws, stream);
   }
-  const int64_t nsampled = nrounds / kRunRounds * kSampledRounds;
-  hipLaunchKernelGGL((scan_main<G, 1>), dim3((unsigned)(nsampled * groups)), dim3(kThreads), 0,
-                     stream, planes, scales, nb_store, depths, q, nrounds, n, nsampled, scores, ws);
-  hipError_t e = launch_topk_rounds_cut(scores, rows, n, R, k, ws, stream);
+  const int64_t ntiles = nblk / kNB;
+  const int64_t nt = std::min<int64_t>(ntiles, kSampleTiles), tstride = ntiles / nt;
+  hipLaunchKernelGGL((fused_sample<G>), dim3((unsigned)nt, (unsigned)groups),
+                     dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, tstride,
+                     fw.sample);
+  // The cut leaves about 1.6x the sample's share of k (plus 16 sampled keys)
+  // at or above it, so that fewer than k candidates is rare.
+  const int nkeys = (int)(nt * kTileKeys);
+  const double share = (double)k * (double)nkeys / (double)n;
+  const int target = (int)std::min<double>((double)nkeys, std::ceil(1.6 * share + 16.0));
+  hipError_t e = launch_fused_guess(fw.sample, rows, n, R, nkeys, target, fw.rows, fw.gflag, G,
+                                    stream);
   if (e != hipSuccess) return e;
-  const int64_t nemit = nrounds - nsampled;
-  hipLaunchKernelGGL((scan_main<G, 2>), dim3((unsigned)(nemit * groups)), dim3(kThreads), 0,
-                     stream, planes, scales, nb_store, depths, q, nrounds, n, nemit, scores, ws);
-  return launch_topk_rounds_finish(scores, rows, n, R, kRunRounds, kSampledRounds, k, indices,
-                                   ws, stream);
+  const dim3 grid((unsigned)(nrounds * groups)), block(kThreads);
+  hipLaunchKernelGGL((scan_main<G, 1>), grid, block, 0, stream, planes, scales, nb_store, depths,
+                     q, nrounds, n, nrounds, scores, fw.rows, (const uint32_t*)nullptr);
+  e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
+  if (e != hipSuccess || scores != nullptr) return e;
+  hipLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, planes, scales, nb_store, depths,
+                     q, nrounds, n, nrounds, fw.scores, (void*)nullptr,
+                     (const uint32_t*)fw.gflag);
+  return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, stream);
 }
 
 int64_t scan_max_workgroups(int64_t groups, int64_t n) {
@@ -901,9 +1012,9 @@ hipError_t launch_scan(const uint64_t* planes, const uint16_t* scales, int64_t n
 
 size_t scan_topk_workspace_bytes(int64_t groups, int G, int64_t n, int k) {
   const int64_t rows = groups * G;
-  const size_t a = topk_rounds_workspace_bytes(rows, n, (int64_t)kRoundBlocks * kBlock);
-  const size_t b = topk_workspace_bytes(rows, n, k);
-  return a > b ? a : b;
+  (void)k;
+  return topk::fused_front_bytes(rows, groups, n, kTileKeys) +
+         topk::align256((size_t)rows * n * sizeof(float));
 }
 
 hipError_t launch_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,

@@ -16,14 +16,13 @@
 //   compact — one pass over the row writes every key >= tau (key, index) of
 //             a chunk, in index order, to that chunk's own region of the
 //             row's candidate buffer, and its count;
-//   resolve — one workgroup per row: stages the candidates' keys in LDS,
-//             finds the k-th largest key T with two radix digits counted
-//             from tau, the keys == T still needed, and per chunk (counted
-//             by one wave over the chunk's staged range) the number of keys
-//             > T and == T before it;
-//   order   — one wave per (chunk, row) writes the chunk's selected indices
-//             (every key > T, the earliest keys == T) at its prefix
-//             position, so the row comes out in index order without a sort.
+//   resolve — one workgroup per row: stages the candidates (key, index) in
+//             LDS, finds the k-th largest key T with two radix digits counted
+//             from tau and the keys == T still needed, counts per chunk the
+//             keys > T and == T, prefixes the counts and writes every chunk's
+//             selected indices (every key > T, the earliest keys == T) at its
+//             prefix position, so the row comes out in index order without a
+//             sort.
 // If the guess fails (fewer than k keys >= tau, or a chunk with more than
 // its region holds: heavy ties or adversarial rows), or the candidates do not
 // fit in LDS, the resolve workgroup does all of it alone, from the scores or
@@ -54,7 +53,7 @@ static_assert(kChunk == kSampleChunk, "the sample reads whole compaction chunks"
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
-constexpr int kLdsCand = 16384;                      // candidates staged in LDS at most
+constexpr int kLdsCand = 16368;                      // candidates staged in LDS at most
 
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
@@ -356,72 +355,6 @@ __global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict
   else compact_chunk<false>(src, n, c0, r, s_cnt);
 }
 
-// The scan's sampled rounds (R keys each: the first `sampled` of every `run`
-// rounds of a row) read back from the scores: every key >= tau, in index
-// order, to that round's region, as compact_chunk does for a chunk.
-// Workgroup = one sampled round of one row; R / 256 keys per thread.
-template <int kPer>
-__global__ __launch_bounds__(kThreads) void topk_compact_rounds(const float* __restrict__ scores,
-                                                                int run, int sampled, int64_t n,
-                                                                int64_t R, void* ws) {
-  __shared__ uint32_t s_cnt[kWavesPerWg];
-  const int64_t row = blockIdx.y, j = blockIdx.x;
-  const int64_t rd = (j / sampled) * run + j % sampled;   // the round's index in the row
-  const RowWs r = row_ws(ws, n, R, row);
-  const float tauf = key_float(r.st[kS_TAU]);
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const float* src = scores + row * n + rd * R + wave * (64 * kPer);
-  float v[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer / 4; ++i) {
-    const float4 x = *reinterpret_cast<const float4*>(src + (i * 64 + lane) * 4);
-    v[4 * i] = x.x;
-    v[4 * i + 1] = x.y;
-    v[4 * i + 2] = x.z;
-    v[4 * i + 3] = x.w;
-  }
-  uint32_t nw = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) nw += (uint32_t)__popcll(__ballot(v[e] >= tauf));
-  if (lane == 0) s_cnt[wave] = nw;
-  __syncthreads();
-  const uint32_t base = (uint32_t)rd * r.region;
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-#pragma unroll
-    for (int w = 0; w < kWavesPerWg; ++w) t += s_cnt[w];
-    r.seg[2 * rd] = base;
-    r.seg[2 * rd + 1] = t;
-    if (t > r.region) atomicOr(&r.st[kS_OVER], 1u);
-  }
-  if (nw != 0u) {
-    uint32_t slot = 0;
-    for (int w = 0; w < wave; ++w) slot += s_cnt[w];
-    const uint64_t below = lanes_below();
-#pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) {
-      uint64_t m[4];
-      uint32_t sl = slot;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        m[c] = __ballot(v[4 * i + c] >= tauf);
-        sl += (uint32_t)__popcll(m[c] & below);
-        slot += (uint32_t)__popcll(m[c]);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (v[4 * i + c] >= tauf) {
-          if (sl < r.region)
-            reinterpret_cast<uint2*>(r.cand)[base + sl] = make_uint2(
-                order_key(v[4 * i + c]),
-                (uint32_t)(rd * R + wave * (64 * kPer) + (i * 64 + lane) * 4 + c));
-          ++sl;
-        }
-      }
-    }
-  }
-}
-
 // The keys the one-workgroup path selects among: the candidate regions, or
 // (direct mode) the row itself.
 struct ResolveSrc {
@@ -495,22 +428,33 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
   }
 }
 
-// Per row: T (the k-th largest key) and the keys == T still needed.  Rows
-// whose candidates fit in LDS (the usual case) stage them there, resolve T
-// from LDS, and leave per-chunk prefix counts for topk_order, which writes
-// the chunks in parallel.  Other rows (the guess failed, or too many
-// candidates or chunks) are resolved and written here, by one workgroup.
+// Per row: T (the k-th largest key), the keys == T still needed, and the
+// ordered write.  Rows whose candidates fit in LDS (the usual case) stage
+// (key, index) there and do everything from LDS; other rows (the guess
+// failed, or too many candidates or chunks) are resolved and written from the
+// candidate regions or the scores, by the same workgroup.
+// mode 0: every row; a row whose candidates cannot give the selection goes to
+// the scores, or, when there are none (fathom_scan_topk without a score
+// buffer), is flagged (kS_FAIL, and its group in gflag) for a second pass.
+// mode 1: the flagged rows only, from the scores.
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
                                                                 int64_t n, int64_t R, int k,
                                                                 void* ws,
-                                                                int32_t* __restrict__ out) {
+                                                                int32_t* __restrict__ out,
+                                                                int mode, uint32_t* gflag,
+                                                                int G) {
   __shared__ uint32_t s_hist[2 * kBins];
-  __shared__ uint32_t s_gt[kGroups], s_eq[kGroups];
-  __shared__ uint32_t s_key[kLdsCand];
+  __shared__ uint32_t s_gt[kGroups];
+  // Staged candidates: keys and indices.  The path that does not stage them
+  // uses s_idx as its per-group count of keys == T (kGroups <= kLdsCand).
+  __shared__ uint32_t s_key[kLdsCand], s_idx[kLdsCand];
+  static_assert(kGroups <= kLdsCand, "s_eq aliases s_idx");
+  uint32_t* const s_eq = s_idx;
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
   const int64_t row = blockIdx.x;
   RowWs r = row_ws(ws, n, R, row);
+  if (mode == 1 && r.st[kS_FAIL] == 0u) return;   // uniform over the workgroup
   ResolveSrc src;
   src.cand = reinterpret_cast<const uint2*>(r.cand);
   src.seg = r.seg;
@@ -567,7 +511,14 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         run += t;
       }
   }
-  src.direct = ncand < (uint32_t)k || over != 0u;   // the guess failed
+  src.direct = ncand < (uint32_t)k || over != 0u || mode == 1;   // the guess failed
+  if (src.direct && scores == nullptr) {   // no scores to fall back on: flag the row
+    if (threadIdx.x == 0) {
+      r.st[kS_FAIL] = 1u;
+      gflag[row / G] = 1u;
+    }
+    return;
+  }
   const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;
   __syncthreads();
 
@@ -580,42 +531,55 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t o = lane + 64 * h;
-        if (o < cnt) s_key[s_gt[c] + o] = e[u][h].x;
+        if (o < cnt) {
+          s_key[s_gt[c] + o] = e[u][h].x;
+          s_idx[s_gt[c] + o] = e[u][h].y;
+        }
       }
     }
   }
   if (lds) {
-    // Stage the keys, chunk after chunk in index order: chunk c at
-    // [s_gt[c], s_gt[c] + count(c)).  Wave w copies chunks w, w + 16, ...,
-    // eight chunks' first 128 candidates per batch of loads (already loaded
-    // above when the row has at most 128 chunks), then any rest.
+    // Stage the candidates, chunk after chunk in index order: chunk c at
+    // [s_gt[c], s_gt[c] + count(c)).  With at most 128 chunks the first 128
+    // candidates of every chunk were loaded above; any rest follows, wave w
+    // taking chunks w, w + 16, ...  With more chunks, candidate i (in index
+    // order) belongs to the last chunk c with s_gt[c] <= i, found by binary
+    // search, and every thread keeps kU independent loads in flight.
     auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
-    for (int64_t cb = pre ? nc : wave; cb < nc; cb += kW * kU) {
-      uint2 e[kU][2];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t c = cb + u * kW;
-        const uint32_t cnt = c < nc ? count(c) : 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t o = lane + 64 * h;
-          e[u][h] = o < cnt ? src.cand[(uint32_t)c * src.region + o] : make_uint2(0u, 0u);
+    if (pre) {
+      for (int64_t c = wave; c < nc; c += kW)
+        for (uint32_t o = 128 + lane; o < count(c); o += 64) {
+          const uint2 e = src.cand[(uint32_t)c * src.region + o];
+          s_key[s_gt[c] + o] = e.x;
+          s_idx[s_gt[c] + o] = e.y;
         }
-      }
+    } else {
+      for (uint32_t i0 = threadIdx.x; i0 < ncand; i0 += kU * kResolveThreads) {
+        uint2 ev[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t c = cb + u * kW;
-        const uint32_t cnt = c < nc ? count(c) : 0u;
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t i = i0 + u * kResolveThreads;
+          ev[u] = make_uint2(0u, 0u);
+          if (i < ncand) {
+            int lo = 0, hi = (int)nc - 1;
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (s_gt[mid] <= i) lo = mid;
+              else hi = mid - 1;
+            }
+            ev[u] = src.cand[(uint32_t)lo * src.region + (i - s_gt[lo])];
+          }
+        }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t o = lane + 64 * h;
-          if (o < cnt) s_key[s_gt[c] + o] = e[u][h].x;
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t i = i0 + u * kResolveThreads;
+          if (i < ncand) {
+            s_key[i] = ev[u].x;
+            s_idx[i] = ev[u].y;
+          }
         }
       }
     }
-    for (int64_t c = wave; c < nc; c += kW)
-      for (uint32_t o = 128 + lane; o < count(c); o += 64)
-        s_key[s_gt[c] + o] = src.cand[(uint32_t)c * src.region + o].x;
   }
   __syncthreads();
 
@@ -702,31 +666,40 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   // > T and == T of every group, prefixed over the groups.
   const int64_t per_group = (nc + kGroups - 1) / kGroups;
   const int ngroups = (int)((nc + per_group - 1) / per_group);
-  if (lds) {   // per_group == 1: chunk c's keys are s_key[s_gt[c] .. s_gt[c + 1])
-    // Keys > T and == T per chunk, packed as gt | eq << 16 (both totals are
-    // at most kLdsCand < 2^16), prefixed in one pass; topk_order writes.
-    for (int64_t c = wave; c < nc; c += kW) {
-      const uint32_t o0 = s_gt[c], o1 = c + 1 < nc ? s_gt[c + 1] : ncand;
-      uint32_t gt = 0, eq = 0;
-      for (uint32_t o = o0; o < o1; o += 64) {
-        const bool v = o + lane < o1;
-        const uint32_t key = v ? s_key[o + lane] : 0u;
-        gt += (uint32_t)__popcll(__ballot(v && key > T));
-        eq += (uint32_t)__popcll(__ballot(v && key == T));
-      }
-      if (lane == 0) s_hist[c] = gt | (eq << 16);
+  if (lds) {
+    // The staged candidates are in index order, so the selection is written
+    // from one flat pass: wave w takes a contiguous segment of them, 64 at a
+    // time; its counts of keys > T and == T (packed as gt | eq << 16, both
+    // at most kLdsCand < 2^16) are prefixed over the waves, and a key's
+    // output position is (keys > T before it) + min(keys == T before it,
+    // need).
+    const uint32_t seg = ((ncand + kW * 64 - 1) / (kW * 64)) * 64;
+    const uint32_t s0 = min(ncand, (uint32_t)wave * seg), s1 = min(ncand, s0 + seg);
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t o = s0; o < s1; o += 64) {
+      const bool v = o + lane < s1;
+      const uint32_t key = v ? s_key[o + lane] : 0u;
+      gt += (uint32_t)__popcll(__ballot(v && key > T));
+      eq += (uint32_t)__popcll(__ballot(v && key == T));
     }
+    if (lane == 0) s_hist[wave] = gt | (eq << 16);
     __syncthreads();
-    block_prefix_inplace<kResolveThreads>(s_hist, (int)nc, s_tmp);
-    __syncthreads();
-    for (int c = threadIdx.x; c < (int)nc; c += kResolveThreads) {
-      r.ord[2 * c] = s_hist[c] & 0xffffu;
-      r.ord[2 * c + 1] = s_hist[c] >> 16;
-    }
-    if (threadIdx.x == 0) {
-      r.st[kS_T] = T;
-      r.st[kS_NEED] = need;
-      r.st[kS_ORDER] = 1u;
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_hist[w];
+    const uint64_t below = lanes_below();
+    uint32_t eq_seen = before >> 16;
+    uint32_t pos = (before & 0xffffu) + min(eq_seen, need);
+    for (uint32_t o = s0; o < s1; o += 64) {
+      const bool v = o + lane < s1;
+      const uint2 e = v ? make_uint2(s_key[o + lane], s_idx[o + lane]) : make_uint2(0u, 0u);
+      const bool g = v && e.x > T, q = v && e.x == T;
+      const uint64_t eqm = __ballot(q);
+      const bool take = g || (q && eq_seen + (uint32_t)__popcll(eqm & below) < need);
+      const uint64_t tm = __ballot(take);
+      const uint32_t p = pos + (uint32_t)__popcll(tm & below);
+      if (take && p < (uint32_t)k) dst[p] = (int32_t)e.y;   // p < k by construction
+      pos += (uint32_t)__popcll(tm);
+      eq_seen += (uint32_t)__popcll(eqm);
     }
     return;
   } else {
@@ -742,7 +715,6 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   block_prefix_inplace<kResolveThreads>(s_gt, ngroups, s_tmp);
   block_prefix_inplace<kResolveThreads>(s_eq, ngroups, s_tmp);
   __syncthreads();
-  if (threadIdx.x == 0) r.st[kS_ORDER] = 0u;
   const uint64_t below = lanes_below();
   // One wave per group writes its selected indices in index order.
   for (int g = wave; g < ngroups; g += kResolveThreads / 64) {
@@ -762,36 +734,81 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
 }
 
-// Rows resolved in LDS: one wave per (chunk, row) writes the chunk's selected
-// indices in index order at the chunk's prefix position.
-__global__ __launch_bounds__(64) void topk_order(int64_t n, int64_t R, int k, const void* ws,
-                                                 int32_t* __restrict__ out) {
-  const int64_t row = blockIdx.y, c = blockIdx.x;
-  const RowWs r = row_ws(const_cast<void*>(ws), n, R, row);
-  if (r.st[kS_ORDER] == 0u) return;
-  const uint32_t T = r.st[kS_T], need = r.st[kS_NEED];
-  const uint32_t s0 = r.seg[2 * c], cnt = r.seg[2 * c + 1];
-  uint32_t pos = r.ord[2 * c], eq_seen = r.ord[2 * c + 1];
-  pos += min(eq_seen, need);
-  const uint2* cand = reinterpret_cast<const uint2*>(r.cand);
-  int32_t* dst = out + row * (int64_t)k;
-  const int lane = lane_id();
-  const uint64_t below = lanes_below();
-  for (uint32_t o = 0; o < cnt; o += 64) {
-    const bool v = o + lane < cnt;
-    const uint2 e = v ? cand[s0 + o + lane] : make_uint2(0u, 0u);
-    const bool gt = v && e.x > T, eq = v && e.x == T;
-    const uint64_t eqm = __ballot(eq);
-    const bool take = gt || (eq && eq_seen + (uint32_t)__popcll(eqm & below) < need);
-    const uint64_t tm = __ballot(take);
-    const uint32_t p = pos + (uint32_t)__popcll(tm & below);
-    if (take && p < (uint32_t)k) dst[p] = (int32_t)e.y;   // p < k by construction
-    pos += (uint32_t)__popcll(tm);
-    eq_seen += (uint32_t)__popcll(eqm);
+// The cut of fathom_scan_topk, from its sample: tau = the target-th largest of
+// the row's nkeys sampled order keys (three radix digits over keys held in
+// registers), so that about target * n / nkeys keys of the row are at or
+// above it.  Also clears the row's flags and its group's.
+__global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* __restrict__ sample,
+                                                               int64_t n, int64_t R, int nkeys,
+                                                               int target, void* ws,
+                                                               uint32_t* gflag, int G) {
+  __shared__ uint32_t s_hist[kBins];
+  __shared__ uint32_t s_tmp[kResolveThreads / 64];
+  __shared__ uint32_t s_sel[2];
+  constexpr int kPerT = kMaxSampleKeys / kResolveThreads;
+  const int64_t row = blockIdx.x;
+  RowWs r = row_ws(ws, n, R, row);
+  const uint32_t* src = sample + row * (int64_t)kMaxSampleKeys;
+  uint32_t key[kPerT];
+#pragma unroll
+  for (int u = 0; u < kPerT; ++u) {
+    const int i = threadIdx.x + u * kResolveThreads;
+    key[u] = i < nkeys ? src[i] : 0u;
+  }
+  uint32_t prefix = 0, need = (uint32_t)target;
+  for (int level = 0; level < 3; ++level) {
+    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+    const int bits = level == 2 ? 10 : 11;
+    const int hi = shift + bits;   // bits at and above hi are fixed
+    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      const int i = threadIdx.x + u * kResolveThreads;
+      const bool in = i < nkeys && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
+      if (in) atomicAdd(&s_hist[(key[u] >> shift) & ((1u << bits) - 1u)], 1u);
+    }
+    __syncthreads();
+    constexpr int kPer = kBins / kResolveThreads;
+    uint32_t h[kPer];
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+      const int bin = threadIdx.x * kPer + b;
+      h[b] = bin < (1 << bits) ? s_hist[bin] : 0u;
+    }
+    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    need = s_sel[1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    r.st[kS_TAU] = prefix;
+    r.st[kS_OVER] = 0u;
+    r.st[kS_FAIL] = 0u;
+    if (row % G == 0) gflag[row / G] = 0u;
   }
 }
 
 }  // namespace
+
+hipError_t launch_fused_guess(const uint32_t* sample, int64_t rows, int64_t n, int64_t R,
+                              int nkeys, int target, void* ws, uint32_t* gflag, int G,
+                              hipStream_t stream) {
+  if (nkeys < 1 || nkeys > kMaxSampleKeys || target < 1 || target > nkeys)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fused_guess, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, sample,
+                     n, R, nkeys, target, ws, gflag, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
+                                int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
+                     n, R, k, ws, indices, mode, gflag, G);
+  return hipGetLastError();
+}
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
   (void)k;
@@ -809,8 +826,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int3
   hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
   hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
-                     ws, indices);
-  hipLaunchKernelGGL(topk_order, grid_chunks, dim3(64), 0, stream, n, R, k, ws, indices);
+                     ws, indices, 0, (uint32_t*)nullptr, 1);
   return hipGetLastError();
 }
 
@@ -858,38 +874,6 @@ hipError_t launch_topk_noalloc(const float* scores, int64_t rows, int64_t n, int
   // histograms in their own slots, the cut and flags set by the guess), so
   // nothing of the previous call's contents needs clearing.
   return launch_topk(scores, rows, n, k, indices, ws, stream);
-}
-
-// Pieces of the selection for candidates the scan emits itself, per region
-// of R = 2048 keys (one scan round); the first `sampled` of every `run` rounds
-// are scanned first (the chunks of 8192 keys that the sample reads).
-size_t topk_rounds_workspace_bytes(int64_t rows, int64_t n, int64_t R) {
-  const size_t bytes = (size_t)rows * row_words(n, R) * sizeof(uint32_t);
-  return (bytes + 255) & ~(size_t)255;
-}
-
-hipError_t launch_topk_rounds_cut(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
-                                  void* ws, hipStream_t stream) {
-  const unsigned ns = (unsigned)n_samples(n);
-  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
-                     R, ws);
-  hipLaunchKernelGGL(topk_guess, dim3((unsigned)rows), dim3(kThreads), 0, stream, n, R, k, ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_rounds_finish(const float* scores, int64_t rows, int64_t n, int64_t R,
-                                     int run, int sampled, int k, int32_t* indices, void* ws,
-                                     hipStream_t stream) {
-  const int64_t nr = n / R;
-  if (R != 8 * kThreads || kChunk != sampled * R || run != sample_stride(n) * sampled)
-    return hipErrorInvalidValue;   // the sampled rounds are the sampled chunks
-  hipLaunchKernelGGL(topk_compact_rounds<8>, dim3((unsigned)(nr / run * sampled), (unsigned)rows),
-                     dim3(kThreads), 0, stream, scores, run, sampled, n, R, ws);
-  hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
-                     n, R, k, ws, indices);
-  hipLaunchKernelGGL(topk_order, dim3((unsigned)nr, (unsigned)rows), dim3(64), 0, stream, n, R, k,
-                     ws, indices);
-  return hipGetLastError();
 }
 
 }  // namespace fathom

@@ -17,7 +17,7 @@ enum : int {
   kS_OVER,          // nonzero: a chunk had more candidates than its region
   kS_T,             // the k-th largest key (set by the resolve)
   kS_NEED,          // keys == T to take
-  kS_ORDER,         // 1: the ordered write is left to topk_order
+  kS_FAIL,          // 1: fathom_scan_topk could not select from the candidates
   kS_WORDS = 16
 };
 
@@ -35,12 +35,14 @@ __host__ __device__ inline uint32_t region(int64_t n, int64_t R) {
   return (uint32_t)(cand_cap(n) / n_chunks(n, R));
 }
 
-// The sample: every stride-th chunk of 8192 keys, stride 8, raised so that
-// at most 64 chunks are sampled; each sampled chunk has its own histogram.
+// The sample: every stride-th chunk of 8192 keys, stride 8 (1/8 of a long
+// row), raised so that at most 64 chunks are sampled; each sampled chunk has
+// its own histogram.
+constexpr int64_t kSampleStride = 8;
 __host__ __device__ inline int64_t sample_stride(int64_t n) {
   const int64_t nc = n_chunks(n, kSampleChunk);
   const int64_t s = (nc + kMaxSamples - 1) / kMaxSamples;
-  return s < 8 ? 8 : s;
+  return s < kSampleStride ? kSampleStride : s;
 }
 __host__ __device__ inline int64_t n_samples(int64_t n) {
   return (n_chunks(n, kSampleChunk) + sample_stride(n) - 1) / sample_stride(n);
@@ -70,6 +72,41 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   r.seg = r.cand + 2 * (size_t)cand_cap(n);
   r.ord = r.seg + 2 * (size_t)n_chunks(n, R);
   return r;
+}
+
+// Workspace of fathom_scan_topk: per-row selection state with one candidate
+// region per scan wave tile (R = 512 keys), the sample's order keys, a flag
+// per group (a row of the group must be selected again from its scores), and
+// room for the scores of every row (used only when the caller passes no score
+// buffer and a row's selection fails, or when the call cannot take the fused
+// path).
+constexpr int kMaxSampleKeys = 16384;   // sampled keys per row at most
+struct FusedWs {
+  void* rows;        // [rows] RowWs with R = the scan's tile
+  uint32_t* sample;  // [rows][kMaxSampleKeys] order keys of the sampled scores
+  uint32_t* gflag;   // [groups]
+  float* scores;     // [rows][n]
+};
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t fused_front_bytes(int64_t rows, int64_t groups, int64_t n,
+                                                    int64_t R) {
+  // The fused layout, or fathom_topk's (used when the call is not fused),
+  // whichever is larger; the score area follows.
+  const size_t fused = align256((size_t)rows * row_words(n, R) * 4) +
+                       align256((size_t)rows * kMaxSampleKeys * 4) + align256((size_t)groups * 4);
+  const size_t plain = align256((size_t)rows * row_words(n, kSampleChunk) * 4);
+  return fused > plain ? fused : plain;
+}
+__host__ __device__ inline FusedWs fused_ws(void* ws, int64_t rows, int64_t groups, int64_t n,
+                                            int64_t R) {
+  char* p = reinterpret_cast<char*>(ws);
+  FusedWs f;
+  f.rows = p;
+  f.sample = reinterpret_cast<uint32_t*>(p + align256((size_t)rows * row_words(n, R) * 4));
+  f.gflag = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(f.sample) +
+                                        align256((size_t)rows * kMaxSampleKeys * 4));
+  f.scores = reinterpret_cast<float*>(p + fused_front_bytes(rows, groups, n, R));
+  return f;
 }
 
 __device__ __forceinline__ uint32_t order_key(float x) {

@@ -128,14 +128,18 @@ def test_scan_topk_validation(L):
     L.fathom_scan_topk_workspace_bytes.restype = ctypes.c_size_t
     need = L.fathom_scan_topk_workspace_bytes(2, 4, 1 << 17, 256)
     assert need >= L.fathom_topk_workspace_bytes(8, 1 << 17, 256) > 0
+    assert need >= 8 * (1 << 17) * 4          # room for every row's scores
     assert L.fathom_scan_topk_workspace_bytes(2, 4, 1 << 17, 0) == 0
     assert L.fathom_scan_topk_workspace_bytes(2, 9, 1 << 17, 1) == 0
     f = L.fathom_scan_topk
     args = [FAKE, FAKE, 2048, FAKE, FAKE, 2, 4, 128, 1 << 17, 256, FAKE, FAKE, FAKE, need, None]
-    for i in (0, 1, 3, 4, 10, 11, 12):
+    for i in (0, 1, 3, 4, 11, 12):
         a = list(args)
         a[i] = None
         assert f(*a) == NULL_ARG, i
+    a = list(args)
+    a[10] = None                               # no score buffer: a valid call
+    assert f(*a) in (NO_DEVICE, OK) or _gpu_visible()
     for i, v in ((6, 9), (7, 64), (8, 1000), (2, 100)):
         a = list(args)
         a[i] = v

@@ -299,9 +299,12 @@ def test_fixed_plans_through_the_scan(fk, mode, param):
     assert_topk_valid(gi, s64, l1, k)
 
 
-def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None):
-    """fathom_scan_topk against the oracle's scan and top-k."""
-    ins = fathom_inputs.make_inputs(groups, 4, n, seed=seed)
+def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=True, ins=None):
+    """fathom_scan_topk against the oracle's scan and top-k (scores compared
+    when the call writes them; index sets always, and against the fp64
+    definition)."""
+    if ins is None:
+        ins = fathom_inputs.make_inputs(groups, 4, n, seed=seed)
     planes, scales = fk.encode(to_dev(ins.k))
     if depths is None:
         dd = fk.plan(to_dev(ins.q), to_dev(ins.var), budget)
@@ -309,31 +312,60 @@ def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None):
     else:
         dd = to_dev(depths)
         od = depths
-    scores, idx = fk.scan_topk(planes, scales, dd, to_dev(ins.q), n, k)
-    gsc, gi = to_host(scores), to_host(idx)
+    scores, idx = fk.scan_topk(planes, scales, dd, to_dev(ins.q), n, k, write_scores=write_scores)
+    gi = to_host(idx)
     op, os_, _ = oracle.encode(ins.k)
     ref = oracle.scan_ref32(op, os_, od, ins.q, n)
-    assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
+    if write_scores:
+        gsc = to_host(scores)
+        assert np.array_equal(gsc.view(np.uint32), ref.view(np.uint32)), first_mismatch(gsc, ref)
+    else:
+        assert scores is None
     oi = oracle.topk(ref.reshape(-1, n), k)
     assert np.array_equal(gi, oi), first_mismatch(gi, oi)
     s64, l1 = oracle.scan_f64(op, os_, od, ins.q, n)
-    assert_scores_within_band(gsc, s64, l1)
     assert_topk_valid(gi, s64, l1, k)
 
 
+@pytest.mark.parametrize("write_scores", [True, False])
 @pytest.mark.parametrize("groups,n,k", [(2, 1 << 17, 512), (3, 1 << 16, 64), (1, 1 << 18, 4096),
                                         (2, 3 * 4096, 100), (1, 65536 + 2048, 300)])
-def test_scan_topk_matches_scan_then_topk(fk, groups, n, k):
-    """Fused (n a multiple of 65536) and unfused (other n) paths."""
-    say("scan_topk groups=%d n=%d k=%d" % (groups, n, k))
-    _scan_topk_case(fk, groups, n, k, 92, seed=90 + groups)
+def test_scan_topk_matches_scan_then_topk(fk, groups, n, k, write_scores):
+    """Fused (64k <= n <= 2M, n a multiple of 2048) and unfused (other n)
+    paths, with and without a score buffer."""
+    say("scan_topk groups=%d n=%d k=%d write_scores=%s" % (groups, n, k, write_scores))
+    _scan_topk_case(fk, groups, n, k, 92, seed=90 + groups, write_scores=write_scores)
 
 
-def test_scan_topk_heavy_ties_fall_back(fk):
+@pytest.mark.parametrize("write_scores", [True, False])
+def test_scan_topk_heavy_ties_fall_back(fk, write_scores):
     """One active channel at depth 1: every score takes one of two values per
-    block, so the candidate regions overflow and rows take the direct path."""
+    block, so the candidate regions overflow and rows are selected from their
+    scores (the caller's, or a second scan into the workspace)."""
     n, k = 1 << 17, 1000
     depths = np.zeros((2, 128), dtype=np.uint8)
     depths[:, 5] = 1
-    say("scan_topk heavy ties")
-    _scan_topk_case(fk, 2, n, k, 0, seed=97, depths=depths)
+    say("scan_topk heavy ties write_scores=%s" % write_scores)
+    _scan_topk_case(fk, 2, n, k, 0, seed=97, depths=depths, write_scores=write_scores)
+
+
+@pytest.mark.parametrize("write_scores", [True, False])
+def test_scan_topk_unrepresentative_sample_falls_back(fk, write_scores):
+    """Keys aligned with the queries planted in every sampled tile (the 16
+    tiles of 512 keys every 8192 keys at n = 2^17): the cut taken from the
+    sample lies above all but a few hundred keys of the row, fewer than k, so
+    the rows are selected from their scores."""
+    groups, G, n, k = 2, 4, 1 << 17, 2000
+    ins = fathom_inputs.make_inputs(groups, G, n, seed=99)
+    rng = np.random.default_rng(98)
+    ntiles = n // 512
+    tstride = ntiles // min(ntiles, 16)
+    for g in range(groups):
+        qn = ins.q[g].astype(np.float64).sum(axis=0)
+        qn /= np.abs(qn).max()
+        top = 4.0 * float(np.abs(ins.k[g]).max())
+        for t in range(0, ntiles, tstride):
+            mag = top * rng.uniform(0.5, 1.0, 512)
+            ins.k[g, t * 512:(t + 1) * 512] = (mag[:, None] * qn[None, :]).astype(np.float16)
+    say("scan_topk unrepresentative sample write_scores=%s" % write_scores)
+    _scan_topk_case(fk, groups, n, k, 92, seed=0, write_scores=write_scores, ins=ins)

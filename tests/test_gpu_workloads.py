@@ -38,6 +38,7 @@ def _check_layer(fk, ins, n, k, budgets, planes, scales, op, os_, fused=False):
         idx = fk.topk(scores, k)
         if fused:
             fs, fi = fk.scan_topk(planes, scales, depths, q_d, n, k)
+            _, fi2 = fk.scan_topk(planes, scales, depths, q_d, n, k, write_scores=False)
         torch.cuda.synchronize()
         gd, gsc, gi = to_host(depths), to_host(scores), to_host(idx)
         od, _, _ = oracle.plan(ins.q, ins.var, B)
@@ -52,6 +53,7 @@ def _check_layer(fk, ins, n, k, budgets, planes, scales, op, os_, fused=False):
         if fused:
             assert np.array_equal(to_host(fs).view(np.uint32), ref.view(np.uint32))
             assert np.array_equal(to_host(fi), oi)
+            assert np.array_equal(to_host(fi2), oi)
 
 
 @pytest.mark.timeout(600)
