@@ -250,10 +250,10 @@ int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
  * writes them (when `scores` is non-null), indices as fathom_topk selects
  * them (§2 order, ascending).  When 65536 <= n <= 2^21, n is a multiple of
  * 2048 and the store takes the fast scan path (nb_store a multiple of 8
- * blocks, planes and scales 16-byte aligned): 16 tiles of 512 keys spread
- * over each row are scored first, a cut tau per row is taken from that
- * sample, and the scan
- * then writes every score >= tau, per 512-key tile, to the row's candidate
+ * blocks, planes and scales 16-byte aligned): 8 runs of 1024 keys spread
+ * evenly over each row are scored first, a cut tau per row is taken from
+ * that sample, and the scan then writes every score >= tau, per 512-key
+ * tile, to the row's candidate
  * buffer, from which the selection is made.  A row whose candidates cannot
  * give the selection (fewer than k of them, or a tile with more than its
  * region holds: heavy ties) is selected from its scores: from `scores`, or,

@@ -799,105 +799,114 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
   }
 }
 
-// The sample of fathom_scan_topk: the scores of NT wave tiles (kNB blocks of
-// 64 keys each) spread evenly over a group's row, in fp32 but in no
+// The sample of fathom_scan_topk: the scores of 2 * kSampleRuns wave tiles
+// per group, runs of two adjacent tiles (each plane row of a run is one
+// 128-byte line) spread evenly over the group's row, in fp32 but in no
 // particular order (only the cut tau is taken from them; the candidates are
 // then scored by the scan itself), written as order keys to
 // sample[group * G + h][i * kTileKeys + token] for sampled tile i.  One
-// workgroup per sampled tile stages the tile's plane words (each plane row of
-// the tile is 64 contiguous bytes), scales and the group's queries in LDS with
-// one round of loads; then waves 2b and 2b + 1 score block b of the tile over
-// channels [0, 64) and [64, 128), with the channel depths held in scalar
-// registers and the LDS reads of four channels issued together, and add their
-// two partial sums.
-constexpr int kSampleTiles = 16;   // sampled tiles per group at most (8192 keys)
+// workgroup per sampled tile: a first round of loads brings the depths, the
+// tile's block scales and the group's queries, a second the plane rows the
+// plan reads (row (j, p) with p < t_j, 64 bytes for the tile's 8 blocks), all
+// into LDS.  Then waves 2b and 2b + 1 score block b over the active channels
+// of [0, 64) and [64, 128) (one ballot mask per depth, so that each channel
+// reads its t_j planes and no more), and add their two partial sums.
+constexpr int kSampleRuns = 8;   // runs of two wave tiles per group (8192 keys)
 constexpr int kSampleThreads = 2 * kNB * 64;
-static_assert(kSampleTiles * kTileKeys <= topk::kMaxSampleKeys, "sample buffer");
+static_assert(2 * kSampleRuns * kTileKeys <= topk::kMaxSampleKeys, "sample buffer");
+
+// The sample's channels of depth T (mask m over the wave's half of the
+// channels) for lane `bit` of half `hsel` of block `b`, four at a time: the
+// LDS reads (T plane words and the scale) and scalar reads (the G weights) of
+// the four are issued together, then their arithmetic.  A slot past the end
+// of the mask reads the half's first channel and adds 0.
+template <int T, int G>
+__device__ __forceinline__ void sample_depth(const uint64_t (*s_w)[kNB],
+                                             const uint16_t (*s_sc)[kNB],
+                                             const float* __restrict__ qg, uint64_t m, int half,
+                                             int b, int hsel, int bit, float (&acc)[G]) {
+  while (m != 0ull) {
+    int c[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ok[u] = m != 0ull;
+      c[u] = 64 * half + (ok[u] ? __builtin_ctzll(m) : 0);
+      m &= m - 1;   // stays 0 once empty
+    }
+    uint32_t w[4][T];
+    float a[4], qv[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // Plane p of channel c is row 4c + p; the lane's word is word hsel of
+      // the row's block b.
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[c[u] * kPlanes][b]) + hsel;
+#pragma unroll
+      for (int p = 0; p < T; ++p) w[u][p] = wp[p * 2 * kNB];
+      a[u] = half_lo(s_sc[c[u]][b]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[u][h] = qg[h * kD + c[u]];   // uniform: scalar loads
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every read above is issued before the arithmetic
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t cp = 0u;
+#pragma unroll
+      for (int p = 0; p < T; ++p) cp = 2 * cp + ((w[u][p] >> bit) & 1u);
+      // (c' + 1/2 - 2^(T-1)) * a / 2^(T-1)
+      float kh = __builtin_ldexpf(((float)cp + (0.5f - (float)(1 << (T - 1)))) * a[u], 1 - T);
+      kh = ok[u] ? kh : 0.0f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qv[u][h], kh, acc[h]);
+    }
+  }
+}
 
 template <int G>
 __global__ __launch_bounds__(kSampleThreads) void fused_sample(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
-    const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t tile_stride,
+    const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t run_stride,
     uint32_t* __restrict__ sample) {
   constexpr int kT = kSampleThreads;                   // 1024 threads, two waves per block
-  constexpr int kPieces = kD * kPlanes * 4 / kT;       // 16-byte pieces per thread
+  static_assert(kD * kPlanes * 4 == 2 * kT, "two 16-byte pieces per thread");
   __shared__ uint64_t s_w[kD * kPlanes][kNB];          // 32 KB: row (channel, plane), block
   __shared__ uint16_t s_sc[kD][kNB];
-  __shared__ float s_q[kD][G];
   __shared__ float s_part[kNB][G][kBlock];
   const int64_t grp = blockIdx.y, ti = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = wv >> 1, half = wv & 1;                     // block, channel half
-  const int64_t blk0 = ti * tile_stride * kNB;
-  {
-    // Piece i of thread t: row r = piece / 4 (of 512), blocks 2 (piece % 4)
-    // and 2 (piece % 4) + 1.
-    uint4 v[kPieces];
-    const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0;
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int piece = tid + i * kT;
-      v[i] = *reinterpret_cast<const uint4*>(pg + (int64_t)(piece >> 2) * nb_store +
-                                             2 * (piece & 3));
-    }
-    uint4 sv = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < kD) sv = *reinterpret_cast<const uint4*>(scales + (grp * kD + tid) * nb_store + blk0);
-    float qv[G];
-    if (tid < kD) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) qv[h] = q[(grp * G + h) * kD + tid];
-    }
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int piece = tid + i * kT;
-      *reinterpret_cast<uint4*>(&s_w[piece >> 2][2 * (piece & 3)]) = v[i];
-    }
-    if (tid < kD) {
-      *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
-#pragma unroll
-      for (int h = 0; h < G; ++h) s_q[tid][h] = qv[h];
-    }
-  }
-  // The depths of this wave's 64 channels, four to a scalar register.
-  uint32_t dw[16];
-  const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(depths + grp * kD + 64 * half);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dw[i] = __builtin_amdgcn_readfirstlane(dsrc[i]);
+  const int b = wv >> 1, half = wv & 1;                // block, channel half
+  const int64_t blk0 = ((ti >> 1) * run_stride + (ti & 1)) * kNB;
+  const uint8_t* dg = depths + grp * kD;
+  const float* qg = q + grp * G * kD;
+  // First round of loads: this lane's channel for the compute phase, the
+  // channels of the thread's two pieces (piece tid + 1024 i: row
+  // (tid + 1024 i) / 4, i.e. channel 64 i + tid / 16, plane (tid / 4) % 4),
+  // and the block scales.
+  const int tl = min((int)dg[64 * half + lane], kPlanes);
+  const int tp0 = dg[tid >> 4], tp1 = dg[64 + (tid >> 4)];
+  uint4 sv = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < kD) sv = *reinterpret_cast<const uint4*>(scales + (grp * kD + tid) * nb_store + blk0);
+  // Second round: the plane rows the plan reads.  A thread whose row is past
+  // its channel's depth loads the group's first row instead (a line every
+  // workgroup of the group reads anyway) and its LDS copy is never read.
+  const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 + 2 * (tid & 3);
+  const int pl = (tid >> 2) & (kPlanes - 1);
+  const int r0 = tid >> 2, r1 = (tid + kT) >> 2;
+  const uint4 v0 = *reinterpret_cast<const uint4*>(pg + (pl < tp0 ? (int64_t)r0 * nb_store : 0));
+  const uint4 v1 = *reinterpret_cast<const uint4*>(pg + (pl < tp1 ? (int64_t)r1 * nb_store : 0));
+  if (tid < kD) *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
+  *reinterpret_cast<uint4*>(&s_w[r0][2 * (tid & 3)]) = v0;
+  *reinterpret_cast<uint4*>(&s_w[r1][2 * (tid & 3)]) = v1;
   __syncthreads();
   const int hsel = lane >> 5, bit = lane & 31;
   float acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t dq = dw[i];
-    if (dq == 0u) continue;
-    const int c0 = 64 * half + 4 * i;
-    uint32_t d[4][kPlanes];
-    float a[4], qv[4][G];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int p = 0; p < kPlanes; ++p)
-        d[u][p] = reinterpret_cast<const uint32_t*>(&s_w[(c0 + u) * kPlanes + p][b])[hsel];
-      a[u] = half_lo(s_sc[c0 + u][b]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) qv[u][h] = s_q[c0 + u][h];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = min((int)((dq >> (8 * u)) & 0xffu), kPlanes);
-      if (t == 0) continue;
-      int c4 = 0;
-#pragma unroll
-      for (int p = 0; p < kPlanes; ++p) c4 = 2 * c4 + (int)((d[u][p] >> bit) & 1u);
-      const int cp = c4 >> (kPlanes - t);
-      // (c' + 1/2 - 2^(t-1)) * a / 2^(t-1)
-      const float kh = __builtin_ldexpf(((float)cp + 0.5f - (float)(1 << (t - 1))) * a[u], 1 - t);
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qv[u][h], kh, acc[h]);
-    }
-  }
+  sample_depth<4, G>(s_w, s_sc, qg, __ballot(tl == 4), half, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, qg, __ballot(tl == 3), half, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, qg, __ballot(tl == 2), half, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, qg, __ballot(tl == 1), half, b, hsel, bit, acc);
   if (half == 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
@@ -939,14 +948,13 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
     launch_scan_g<G>(planes, scales, nb_store, depths, q, groups, n, sc, stream);
     return launch_topk(sc, rows, n, k, indices, ws, stream);
   }
-  const int64_t ntiles = nblk / kNB;
-  const int64_t nt = std::min<int64_t>(ntiles, kSampleTiles), tstride = ntiles / nt;
-  hipLaunchKernelGGL((fused_sample<G>), dim3((unsigned)nt, (unsigned)groups),
-                     dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, tstride,
+  const int64_t ntiles = nblk / kNB, rstride = ntiles / kSampleRuns;   // >= 16 tiles
+  hipLaunchKernelGGL((fused_sample<G>), dim3(2 * kSampleRuns, (unsigned)groups),
+                     dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, rstride,
                      fw.sample);
   // The cut leaves about 1.6x the sample's share of k (plus 16 sampled keys)
   // at or above it, so that fewer than k candidates is rare.
-  const int nkeys = (int)(nt * kTileKeys);
+  const int nkeys = 2 * kSampleRuns * kTileKeys;
   const double share = (double)k * (double)nkeys / (double)n;
   const int target = (int)std::min<double>((double)nkeys, std::ceil(1.6 * share + 16.0));
   hipError_t e = launch_fused_guess(fw.sample, rows, n, R, nkeys, target, fw.rows, fw.gflag, G,

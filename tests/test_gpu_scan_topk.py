@@ -351,21 +351,20 @@ def test_scan_topk_heavy_ties_fall_back(fk, write_scores):
 
 @pytest.mark.parametrize("write_scores", [True, False])
 def test_scan_topk_unrepresentative_sample_falls_back(fk, write_scores):
-    """Keys aligned with the queries planted in every sampled tile (the 16
-    tiles of 512 keys every 8192 keys at n = 2^17): the cut taken from the
+    """Keys aligned with the queries planted in every sampled run (the 8
+    runs of 1024 keys every 16384 keys at n = 2^17): the cut taken from the
     sample lies above all but a few hundred keys of the row, fewer than k, so
     the rows are selected from their scores."""
     groups, G, n, k = 2, 4, 1 << 17, 2000
     ins = fathom_inputs.make_inputs(groups, G, n, seed=99)
     rng = np.random.default_rng(98)
-    ntiles = n // 512
-    tstride = ntiles // min(ntiles, 16)
+    run, stride = 1024, n // 8
     for g in range(groups):
         qn = ins.q[g].astype(np.float64).sum(axis=0)
         qn /= np.abs(qn).max()
         top = 4.0 * float(np.abs(ins.k[g]).max())
-        for t in range(0, ntiles, tstride):
-            mag = top * rng.uniform(0.5, 1.0, 512)
-            ins.k[g, t * 512:(t + 1) * 512] = (mag[:, None] * qn[None, :]).astype(np.float16)
+        for s0 in range(0, n, stride):
+            mag = top * rng.uniform(0.5, 1.0, run)
+            ins.k[g, s0:s0 + run] = (mag[:, None] * qn[None, :]).astype(np.float16)
     say("scan_topk unrepresentative sample write_scores=%s" % write_scores)
     _scan_topk_case(fk, groups, n, k, 92, seed=0, write_scores=write_scores, ins=ins)
