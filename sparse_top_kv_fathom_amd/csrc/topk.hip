@@ -735,9 +735,11 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 }
 
 // The cut of fathom_scan_topk, from its sample: tau = the target-th largest of
-// the row's nkeys sampled order keys (three radix digits over keys held in
-// registers), so that about target * n / nkeys keys of the row are at or
-// above it.  Also clears the row's flags and its group's.
+// the row's nkeys sampled order keys with its low 10 bits cleared (two radix
+// digits of 11 bits over keys held in registers: the cut is exact to 2^-13 of
+// the score, and may only sit lower than the sample's own target-th key), so
+// that about target * n / nkeys keys of the row are at or above it.  Also
+// clears the row's flags and its group's.
 __global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* __restrict__ sample,
                                                                int64_t n, int64_t R, int nkeys,
                                                                int target, void* ws,
@@ -756,9 +758,9 @@ __global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* _
     key[u] = i < nkeys ? src[i] : 0u;
   }
   uint32_t prefix = 0, need = (uint32_t)target;
-  for (int level = 0; level < 3; ++level) {
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int bits = level == 2 ? 10 : 11;
+  for (int level = 0; level < 2; ++level) {
+    const int shift = level == 0 ? 21 : 10;
+    const int bits = 11;
     const int hi = shift + bits;   // bits at and above hi are fixed
     for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
     __syncthreads();
