@@ -492,6 +492,63 @@ def run_configs(fk, args, main_ctx):
     return out
 
 
+def run_layouts(fk, args, ctx):
+    """Store layouts and row lengths off the main kernel's 16-byte path: the
+    scan on a copy of the store with capacity n/64 + 3 blocks (scale rows not
+    16-byte aligned) beside the store itself, and fathom_scan_topk on a ragged
+    row length (whole rounds plus a tail) beside scan then top-k.  Event
+    medians in ms."""
+    import torch
+    stores, q_d, var_d, n, k, B = (ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["k"],
+                                   ctx["B"])
+    dev = q_d.device
+    reps = max(10, args.steps)
+    H, G = q_d.shape[1], q_d.shape[2]
+    nb = n // 64
+    p0, s0 = stores[0]
+    p3, s3 = fk.empty_store(H, nb + 3, dev)
+    p3[..., :nb].copy_(p0)
+    s3[..., :nb].copy_(s0)
+    depths = fk.plan(q_d[0], var_d, B)
+    scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
+    out = {}
+    odd = {}
+    for tag, (pp, ss) in (("aligned", (p0, s0)), ("odd", (p3, s3))):
+        timed_scans(fk, [(pp, ss)], lambda i: depths, lambda i: q_d[0], n, 3, scores)
+        odd[tag] = stats(timed_scans(fk, [(pp, ss)], lambda i: depths, lambda i: q_d[0], n, reps,
+                                     scores))
+    out["odd_capacity"] = {"nb_store": nb + 3, "scan_ms": odd["odd"],
+                           "scan_ms_nb_store_n_over_64": odd["aligned"]}
+    nr = n - 64 * 37
+    idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+    fws = fk.scan_topk_workspace(H, G, nr, k, dev)
+    tws = fk.topk_workspace(H * G, nr, k, dev)
+    sr = torch.empty((H, G, nr), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        evs = [[TimingEvent() for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            evs[i][0].record()
+            fn()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return stats([e[0].elapsed_time(e[1]) for e in evs])
+
+    out["ragged_n"] = {
+        "n": nr,
+        "fused_scan_topk_ms": timed(lambda: fk.scan_topk(p0, s0, depths, q_d[0], nr, k,
+                                                         indices=idx, workspace=fws,
+                                                         write_scores=False)),
+        "separate_scan_topk_ms": timed(lambda: (fk.scan(p0, s0, depths, q_d[0], nr, scores=sr),
+                                                fk.topk(sr, k, indices=idx, workspace=tws))),
+    }
+    del p3, s3, scores, fws, tws, sr
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_compare(fk, args, ctx, ins):
     """The pages' comparison reads through the same store, scan and top-k at
     the main workload: Fathom at several budgets, SparQ's top-r channels at
@@ -930,6 +987,8 @@ def main():
     ctx = {"name": w.name, "stores": stores, "q_d": q_d, "qs": qs, "var_d": var_d, "n": n,
            "k": k, "B": B}
     if not args.no_compare and args.store == "raw":
+        out["layouts"] = run_layouts(fk, args, ctx)
+        print("[bench] layouts done", file=sys.stderr, flush=True)
         out["compare_plans"] = run_compare(fk, args, ctx, ins)
         print("[bench] fixed-plan comparison done", file=sys.stderr, flush=True)
     if not args.no_gather and args.store == "raw":

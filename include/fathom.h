@@ -175,6 +175,14 @@ int fathom_plan_fixed(const float* q, const float* stat, int64_t groups, int32_t
  *   (scales must be 4-byte aligned here); blocks [0, n/64) are scanned.
  *   depths [groups][d] uint8 (0..4), q [groups][G][d] fp32,
  *   scores [groups][G][n] fp32 output.
+ *
+ * Any capacity and alignment the arguments allow take the same kernels:
+ * whole runs of 2048 keys in the main kernel, the blocks after the last
+ * whole run in a small tail kernel.  Scale rows load as 16-byte vectors
+ * when nb_store is a multiple of 8 and scales is 16-byte aligned, else one
+ * 2-byte load per block (a few loads more per workgroup; no other
+ * difference).  Only a group whose plane array exceeds 4 GiB (nb_store
+ * beyond 2^20 - 1, i.e. 67M keys) is scanned by the tail kernel alone.
  */
 int fathom_scan(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                 const uint8_t* depths, const float* q, int64_t groups, int32_t G,
@@ -248,13 +256,12 @@ int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
  *
  * Results are those of the two calls, bit for bit: scores as fathom_scan
  * writes them (when `scores` is non-null), indices as fathom_topk selects
- * them (§2 order, ascending).  When 65536 <= n <= 2^21, n is a multiple of
- * 2048 and the store takes the fast scan path (nb_store a multiple of 8
- * blocks, planes and scales 16-byte aligned): 8 runs of 1024 keys spread
- * evenly over each row are scored first, a cut tau per row is taken from
- * that sample, and the scan then writes every score >= tau, per 512-key
- * tile, to the row's candidate
- * buffer, from which the selection is made.  A row whose candidates cannot
+ * them (§2 order, ascending).  When 65536 <= n <= 2^21 (and the group's
+ * plane array is under 4 GiB): 8 runs of 1024 keys spread evenly over each
+ * row are scored first, a cut tau per row is taken from that sample, and the
+ * scan then writes every score >= tau, per 512-key tile (the last one
+ * possibly partial), to the row's candidate buffer, from which the selection
+ * is made.  A row whose candidates cannot
  * give the selection (fewer than k of them, or a tile with more than its
  * region holds: heavy ties) is selected from its scores: from `scores`, or,
  * when `scores` is null, from a second scan of its group into the workspace.

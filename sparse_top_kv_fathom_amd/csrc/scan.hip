@@ -61,6 +61,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "fathom_internal.h"
 #include "topk_layout.h"
@@ -301,7 +302,8 @@ constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stag
 
 template <int G>
 __device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float (&tf)[G],
-                                          int64_t grp, int64_t blk0, int64_t n, void* tws) {
+                                          int64_t grp, int64_t blk0, int64_t n, void* tws,
+                                          int last = kNB - 1) {
   const int lane = lane_id();
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int64_t tile = blk0 / kNB;
@@ -312,6 +314,7 @@ __device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float
     uint32_t cnt = 0;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
+      if (b > last) break;   // past the row's end (a partial last tile)
       const bool cand = sc[b][h] >= tf[h];
       const uint64_t m = __ballot(cand);
       if (m != 0ull) {
@@ -442,8 +445,8 @@ __device__ __forceinline__ void main_depth(const MainCtx& c, const SlotTables<G>
 // in registers until they are staged) and TOUCHES per 256-byte plane-row
 // segment (one 4-byte load per 64 / TOUCHES... bytes), which pull the round's
 // plane lines into L2 ahead of the scalar loads.  Thread 4s + k loads scales
-// [8k, 8k + 8) of slot s (16 aligned bytes: the capacity is a multiple of 8
-// blocks).
+// [8k, 8k + 8) of slot s: 16 aligned bytes when the capacity is a multiple
+// of 8 blocks and the scales 16-byte aligned, else eight 2-byte loads.
 #ifndef SCAN_TOUCHES
 #define SCAN_TOUCHES 2
 #endif
@@ -451,6 +454,7 @@ constexpr int kTouches = SCAN_TOUCHES;                                  // per r
 constexpr int kTouchPerThread = kD * kPlanes * kTouches / kThreads;
 struct Stage {
   uint4 st[kScalePasses];
+  uint32_t sh[kScalePasses][8];   // the same scales, one load each (rows not 16-byte aligned)
   uint32_t tv[kTouchPerThread > 0 ? kTouchPerThread : 1];
 };
 
@@ -467,7 +471,7 @@ __device__ __forceinline__ void retire_touches(const Stage& S, uint32_t& sink) {
 template <int G>
 __device__ __forceinline__ void issue_scales(const MainShared<G>& sh, int nact,
                                              const char* scales_g, int64_t nb_store, int64_t r0,
-                                             Stage& S) {
+                                             bool sv, Stage& S) {
   int tid = threadIdx.x;
   opaque_v(tid);
 #pragma unroll
@@ -475,7 +479,13 @@ __device__ __forceinline__ void issue_scales(const MainShared<G>& sh, int nact,
     const int k = tid + i * kThreads;
     const int slot = k >> 2;
     const int64_t ch = slot < nact ? (int64_t)sh.sj[slot] : 0;
-    S.st[i] = *reinterpret_cast<const uint4*>(scales_g + (ch * nb_store + r0) * 2 + (k & 3) * 16);
+    const char* sp = scales_g + (ch * nb_store + r0) * 2 + (k & 3) * 16;
+    if (sv) {
+      S.st[i] = *reinterpret_cast<const uint4*>(sp);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) S.sh[i][u] = reinterpret_cast<const uint16_t*>(sp)[u];
+    }
   }
 }
 
@@ -503,7 +513,7 @@ __device__ __forceinline__ void issue_touches(const MainShared<G>& sh, int nrows
 // waits for the scales only: the touches stay in flight while the first
 // channels are computed.
 template <int G>
-__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int first1,
+__device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int first1, bool sv,
                                             const Stage& S) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -511,7 +521,11 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int fir
     const int k = tid + i * kThreads;
     const int slot = k >> 2, part = k & 3;
     if (slot < nact) {
-      const uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
+      uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
+      if (!sv) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wd[u] = S.sh[i][2 * u] | (S.sh[i][2 * u + 1] << 16);
+      }
       const int ex = slot >= first1 ? -10 : 13;   // depth-1 slots hold a * 2^-10
       float f[8];
 #pragma unroll
@@ -564,6 +578,8 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   const char* planes_g =
       reinterpret_cast<const char*>(planes + grp * kD * (int64_t)kPlanes * nb_store);
   const char* scales_g = reinterpret_cast<const char*>(scales + grp * kD * nb_store);
+  // Scale rows as 16-byte vectors, or one 2-byte load per block.
+  const bool sv = (nb_store & 7) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
   float* scores_g = scores != nullptr ? scores + grp * G * n : nullptr;
 
   // The plan's depths and the group's queries are requested together, so they
@@ -620,10 +636,10 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
   uint32_t sink = 0u;
   Stage S;
-  issue_scales<G>(sh, nact, scales_g, nb_store, round0 * kRoundBlocks, S);
+  issue_scales<G>(sh, nact, scales_g, nb_store, round0 * kRoundBlocks, sv, S);
   issue_touches<G>(sh, nrows, planes_g, round0 * kRoundBlocks, S);
   const int first1 = cnt[0] + cnt[1] + cnt[2];   // first depth-1 slot
-  round_stage<G>(sh, nact, first1, S);
+  round_stage<G>(sh, nact, first1, sv, S);
   __syncthreads();
 
   const bool olane = lane < kNB * G;
@@ -636,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     const int64_t r0 = (round0 + r) * kRoundBlocks;
     if (r + 1 < nr) {
       retire_touches(S, sink);
-      issue_scales<G>(sh, nact, scales_g, nb_store, r0 + kRoundBlocks, S);
+      issue_scales<G>(sh, nact, scales_g, nb_store, r0 + kRoundBlocks, sv, S);
       issue_touches<G>(sh, nrows, planes_g, r0 + kRoundBlocks, S);
     }
 
@@ -676,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
-      round_stage<G>(sh, nact, first1, S);
+      round_stage<G>(sh, nact, first1, sv, S);
       __syncthreads();
     }
   }
@@ -685,78 +701,127 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 }
 
 // ---------------------------------------------------------------------------
-// Tail kernel: per-block clamped loads, blocks [first_blk, nblk) of a group
+// Tail kernel: the wave tiles from first_blk on (the blocks after the last
+// whole round; every block of a group whose plane array needs 64-bit
+// offsets), one workgroup per tile, one wave per block, lane i = token i.
 // ---------------------------------------------------------------------------
+//
+// The tile's plane rows with p < t_j and its scales are staged in LDS (one
+// round of loads after the depths; blocks past the row's end read the last
+// block, and rows past a channel's depth are not loaded), then every lane
+// folds its own token in the stated order: depths 4 to 1, ascending j,
+//   U_h = fma(w_hj, m_j, U_h),  o_h = fma(e_hj, a_j, o_h),  S_h = U_h + o_h,
+// with m_j = c'_j * (a_j * 2^-10) (exact: a 4-bit by 11-bit product), the
+// same values the main kernel folds per block.  8- and 2-byte loads only,
+// so any capacity and alignment the arguments allow.
+constexpr int kTailThreads = kNB * 64;   // one wave per block of the tile
+static_assert(kTailThreads == kD * kPlanes, "one thread per plane row of the tile");
 
-struct TailCtx {
-  const uint64_t* planes;   // the group's plane rows
-  const uint16_t* scales;   // the group's scale rows
-  const float* q;           // the group's query heads
-  int64_t nb_store;
-  int64_t blk0;             // first block of the tile
-  int last;                 // last valid block offset in the tile
-  int ob_c, oh;             // this lane's (clamped) block and head in the offset fold
-};
-
-template <int T, int G>
-__device__ __forceinline__ void tail_depth(const TailCtx& c, ChanIter it, int cnt,
-                                           float (&acc)[kNB][G], float& o) {
-  const float sw = __builtin_ldexpf(1.0f, 11 - T);
-  const float se = __builtin_ldexpf(1.0f, -T) - 1.0f;
-  for (int i = 0; i < cnt; ++i) {
-    const int64_t j = it.next();
-    ChanLoad<T, G> L;
-    const uint64_t* rp = c.planes + j * kPlanes * c.nb_store + c.blk0;
-#pragma unroll
-    for (int p = 0; p < T; ++p)
-#pragma unroll
-      for (int b = 0; b < kNB; ++b) L.pw[p][b] = rp[p * c.nb_store + min(b, c.last)];
-    const uint16_t* sp = c.scales + j * c.nb_store + c.blk0;
-    constexpr int ex = T == 1 ? -10 : 13;   // depth 1 takes a * 2^-10, as staged
-#pragma unroll
-    for (int b = 0; b < kNB; ++b) L.A[b] = __builtin_ldexpf(half_lo(sp[min(b, c.last)]), ex);
-#pragma unroll
-    for (int h = 0; h < G; ++h) L.w[h] = c.q[h * kD + j] * sw;
-    L.e = c.q[c.oh * kD + j] * se;
-    L.oa = __builtin_ldexpf(half_lo(sp[c.ob_c]), ex);
-    compute_chan<T, G>(L, acc, o, [] {});
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kThreads) void scan_tail(
+template <int G, int MODE = 0>
+__global__ __launch_bounds__(kTailThreads) void scan_tail(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t first_blk,
-    int64_t nblk, int64_t n, int64_t wgs_per_group, float* __restrict__ scores) {
-  __shared__ float s_o[kWaves][kNB * G];
-  const int64_t grp = blockIdx.x / wgs_per_group;
-  const int64_t wg = blockIdx.x % wgs_per_group;
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  TailCtx c;
-  c.blk0 = first_blk + (wg * kWaves + wave) * kNB;
-  if (c.blk0 >= nblk) return;
-  c.planes = planes + grp * kD * (int64_t)kPlanes * nb_store;
-  c.scales = scales + grp * kD * nb_store;
-  c.q = q + grp * G * kD;
-  c.nb_store = nb_store;
-  c.last = (int)min<int64_t>(kNB, nblk - c.blk0) - 1;
-  const bool olane = lane < kNB * G;
-  c.ob_c = min(olane ? lane / G : 0, c.last);
-  c.oh = olane ? lane % G : 0;
-  const DepthMasks dm = depth_masks(depths[grp * kD + lane], depths[grp * kD + 64 + lane]);
+    int64_t nblk, int64_t n, float* __restrict__ scores, void* tws,
+    const uint32_t* __restrict__ gate) {
+  __shared__ uint64_t s_w[kD * kPlanes][kNB];   // row (channel, plane), block of the tile
+  __shared__ uint16_t s_sc[kD][kNB];
+  __shared__ float s_q[G][kD];
+  __shared__ uint32_t s_cnt[G][kNB];
+  const int64_t grp = blockIdx.y;
+  if (gate != nullptr && gate[grp] == 0u) return;   // uniform over the workgroup
+  const int tid = threadIdx.x, lane = lane_id();
+  const int b = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's block
+  const int64_t blk0 = first_blk + (int64_t)blockIdx.x * kNB;
+  const int last = (int)min<int64_t>(kNB, nblk - blk0) - 1;  // last block of the tile in the row
+  const uint8_t* dg = depths + grp * kD;
+  const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0;
+  const uint16_t* sg = scales + grp * kD * nb_store + blk0;
+  // Thread r stages plane row r = (channel r / 4, plane r % 4); threads below
+  // kD also the scale row and the queries of channel tid.
+  const int tr = min((int)dg[tid >> 2], kPlanes);
+  const int tl0 = min((int)dg[lane], kPlanes), tl1 = min((int)dg[64 + lane], kPlanes);
+  if (tid < kD) {
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) s_sc[tid][u] = sg[(int64_t)tid * nb_store + min(u, last)];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_q[h][tid] = q[(grp * G + h) * kD + tid];
+  }
+  if ((tid & (kPlanes - 1)) < tr) {
+    const uint64_t* rp = pg + (int64_t)tid * nb_store;
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) s_w[tid][u] = rp[min(u, last)];
+  }
+  __syncthreads();
 
-  float acc[kNB][G];
+  float U[G], o[G];
 #pragma unroll
-  for (int b = 0; b < kNB; ++b)
+  for (int h = 0; h < G; ++h) U[h] = o[h] = 0.0f;
+  const int hsel = lane >> 5, bit = lane & 31;
 #pragma unroll
-    for (int h = 0; h < G; ++h) acc[b][h] = 0.0f;
-  float o = 0.0f;
-  tail_depth<4, G>(c, ChanIter{dm.lo[0], dm.hi[0]}, dm.count[0], acc, o);
-  tail_depth<3, G>(c, ChanIter{dm.lo[1], dm.hi[1]}, dm.count[1], acc, o);
-  tail_depth<2, G>(c, ChanIter{dm.lo[2], dm.hi[2]}, dm.count[2], acc, o);
-  tail_depth<1, G>(c, ChanIter{dm.lo[3], dm.hi[3]}, dm.count[3], acc, o);
-  finish_tile<G>(acc, o, c.last, n, scores + grp * G * n + c.blk0 * kBlock, s_o[wave]);
+  for (int t = kPlanes; t >= 1; --t) {
+    // The channels of depth t, ascending.
+    ChanIter it{__ballot(tl0 == t), __ballot(tl1 == t)};
+    const int cnt = __popcll(it.lo) + __popcll(it.hi);
+    const float sw = __builtin_ldexpf(1.0f, 11 - t), se = __builtin_ldexpf(1.0f, -t) - 1.0f;
+    for (int i = 0; i < cnt; ++i) {
+      const int j = it.next();
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[j * kPlanes][b]) + hsel;
+      uint32_t cp = 0u;
+      for (int p = 0; p < t; ++p) cp = 2 * cp + ((wp[p * 2 * kNB] >> bit) & 1u);
+      const float a = half_lo(s_sc[j][b]);
+      const float m = (float)cp * __builtin_ldexpf(a, -10);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float qv = s_q[h][j];
+        U[h] = __builtin_fmaf(qv * sw, m, U[h]);
+        o[h] = __builtin_fmaf(qv * se, a, o[h]);
+      }
+    }
+  }
+  float S[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) S[h] = U[h] + o[h];
+  if (scores != nullptr && b <= last) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) scores[(grp * G + h) * n + (blk0 + b) * kBlock + lane] = S[h];
+  }
+  if (MODE == 1) {
+    // The tile's candidates in index order: per head, block b's count of
+    // scores >= tau, prefixed over the blocks in LDS.
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int64_t tile = blk0 / kNB;
+    bool cand[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const topk::RowWs rw = topk::row_ws(tws, n, kTileKeys, grp * G + h);
+      cand[h] = b <= last && S[h] >= topk::key_float(rw.st[topk::kS_TAU]);
+      const uint64_t mk = __ballot(cand[h]);
+      if (lane == 0) s_cnt[h][b] = (uint32_t)__popcll(mk);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const topk::RowWs rw = topk::row_ws(tws, n, kTileKeys, grp * G + h);
+      const uint32_t base = (uint32_t)tile * rw.region;
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int u = 0; u < kNB; ++u) {
+        const uint32_t c = s_cnt[h][u];
+        before += u < b ? c : 0u;
+        total += c;
+      }
+      const uint64_t mk = __ballot(cand[h]);
+      const uint32_t sl = before + (uint32_t)__popcll(mk & below);
+      if (cand[h] && sl < rw.region)
+        reinterpret_cast<uint2*>(rw.cand)[base + sl] =
+            make_uint2(topk::order_key(S[h]), (uint32_t)((blk0 + b) * kBlock + lane));
+      if (tid == 0) {
+        rw.seg[2 * tile] = base;
+        rw.seg[2 * tile + 1] = total;
+        if (total > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
+      }
+    }
+  }
 }
 
 // With timing events, the first launch records ev_start and the last one
@@ -767,9 +832,8 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
                    float* scores, hipStream_t stream, hipEvent_t ev_start = nullptr,
                    hipEvent_t ev_stop = nullptr) {
   const int64_t nblk = n / kBlock;
-  // Main kernel: 32-bit offsets and 16-byte aligned scale rows.
-  const bool fast = nb_store <= kMaxFastBlocks && nb_store % 8 == 0 &&
-                    (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
+  // Main kernel: 32-bit offsets into a group's plane array.
+  const bool fast = nb_store <= kMaxFastBlocks;
   const int64_t nrounds = fast ? nblk / kRoundBlocks : 0;
   const int64_t first = nrounds * kRoundBlocks;
   const bool timed = ev_start != nullptr || ev_stop != nullptr;
@@ -787,15 +851,17 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
                          (const uint32_t*)nullptr);
   }
   if (first < nblk) {
-    const int64_t wgs = (nblk - first + kRoundBlocks - 1) / kRoundBlocks;
-    const dim3 grid((unsigned)(wgs * groups)), block(kThreads);
+    const dim3 grid((unsigned)((nblk - first + kNB - 1) / kNB), (unsigned)groups),
+        block(kTailThreads);
     if (timed)
-      hipExtLaunchKernelGGL(scan_tail<G>, grid, block, 0, stream,
+      hipExtLaunchKernelGGL((scan_tail<G, 0>), grid, block, 0, stream,
                             nrounds > 0 ? nullptr : ev_start, ev_stop, 0u, planes, scales,
-                            nb_store, depths, q, first, nblk, n, wgs, scores);
+                            nb_store, depths, q, first, nblk, n, scores, (void*)nullptr,
+                            (const uint32_t*)nullptr);
     else
-      hipLaunchKernelGGL(scan_tail<G>, grid, block, 0, stream, planes, scales, nb_store, depths,
-                         q, first, nblk, n, wgs, scores);
+      hipLaunchKernelGGL((scan_tail<G, 0>), grid, block, 0, stream, planes, scales, nb_store,
+                         depths, q, first, nblk, n, scores, (void*)nullptr,
+                         (const uint32_t*)nullptr);
   }
 }
 
@@ -885,16 +951,38 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
   // and the block scales.
   const int tl = min((int)dg[64 * half + lane], kPlanes);
   const int tp0 = dg[tid >> 4], tp1 = dg[64 + (tid >> 4)];
+  // 16-byte loads when the store's rows allow them, else 8- and 2-byte ones.
+  const bool vec = (nb_store & 7) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
   uint4 sv = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < kD) sv = *reinterpret_cast<const uint4*>(scales + (grp * kD + tid) * nb_store + blk0);
+  if (tid < kD) {
+    const uint16_t* sp = scales + (grp * kD + tid) * nb_store + blk0;
+    if (vec) {
+      sv = *reinterpret_cast<const uint4*>(sp);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = sp[2 * u] | ((uint32_t)sp[2 * u + 1] << 16);
+      sv = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
   // Second round: the plane rows the plan reads.  A thread whose row is past
   // its channel's depth loads the group's first row instead (a line every
   // workgroup of the group reads anyway) and its LDS copy is never read.
   const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 + 2 * (tid & 3);
   const int pl = (tid >> 2) & (kPlanes - 1);
   const int r0 = tid >> 2, r1 = (tid + kT) >> 2;
-  const uint4 v0 = *reinterpret_cast<const uint4*>(pg + (pl < tp0 ? (int64_t)r0 * nb_store : 0));
-  const uint4 v1 = *reinterpret_cast<const uint4*>(pg + (pl < tp1 ? (int64_t)r1 * nb_store : 0));
+  const uint64_t* a0 = pg + (pl < tp0 ? (int64_t)r0 * nb_store : 0);
+  const uint64_t* a1 = pg + (pl < tp1 ? (int64_t)r1 * nb_store : 0);
+  uint4 v0, v1;
+  if (vec) {
+    v0 = *reinterpret_cast<const uint4*>(a0);
+    v1 = *reinterpret_cast<const uint4*>(a1);
+  } else {
+    const uint64_t x0 = a0[0], y0 = a0[1], x1 = a1[0], y1 = a1[1];
+    v0 = make_uint4((uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)y0, (uint32_t)(y0 >> 32));
+    v1 = make_uint4((uint32_t)x1, (uint32_t)(x1 >> 32), (uint32_t)y1, (uint32_t)(y1 >> 32));
+  }
   if (tid < kD) *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
   *reinterpret_cast<uint4*>(&s_w[r0][2 * (tid & 3)]) = v0;
   *reinterpret_cast<uint4*>(&s_w[r1][2 * (tid & 3)]) = v1;
@@ -922,28 +1010,26 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
 
 }  // namespace
 
-// fathom_scan_topk.  Fused path (whole rounds, 64k to 2M keys, the main
-// kernel's store layout): sample -> cut per row -> scan that writes the scores
+// fathom_scan_topk.  Fused path (64k to 2M keys, 32-bit offsets into a
+// group's plane array): sample -> cut per row -> scan that writes the scores
 // (when a buffer is given) and every score >= tau into its wave tile's
-// candidate region -> selection from the candidates.  Without a score buffer,
-// rows whose candidates cannot give the selection (fewer than k, or a region
-// overflowed) are flagged: their groups are scanned again into the
-// workspace's score area and selected from there; the other groups' work
-// ends at once.  Otherwise the two calls run as they are.
+// candidate region (whole rounds in the main kernel, the blocks after the
+// last whole round in the tail kernel) -> selection from the candidates.
+// Without a score buffer, rows whose candidates cannot give the selection
+// (fewer than k, or a region overflowed) are flagged: their groups are
+// scanned again into the workspace's score area and selected from there; the
+// other groups' work ends at once.  Otherwise the two calls run as they are.
 template <int G>
 hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                               const uint8_t* depths, const float* q, int64_t groups, int64_t n,
                               int k, float* scores, int32_t* indices, void* ws,
                               hipStream_t stream) {
   const int64_t rows = groups * G, R = kTileKeys;
-  const int64_t nblk = n / kBlock, nrounds = nblk / kRoundBlocks;
+  const int64_t nblk = n / kBlock, nrounds = nblk / kRoundBlocks, first = nrounds * kRoundBlocks;
   const topk::FusedWs fw = topk::fused_ws(ws, rows, groups, n, R);
   float* sc = scores != nullptr ? scores : fw.scores;
-  const bool fused = kRounds == 1 && n % ((int64_t)kRoundBlocks * kBlock) == 0 &&
-                     n >= kFusedMinKeys && n / R <= kFusedMaxTiles && nb_store <= kMaxFastBlocks &&
-                     nb_store % 8 == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(depths) & 3) == 0;
+  const bool fused = kRounds == 1 && n >= kFusedMinKeys && topk::n_chunks(n, R) <= kFusedMaxTiles &&
+                     nb_store <= kMaxFastBlocks;
   if (!fused) {   // the two calls one after the other
     launch_scan_g<G>(planes, scales, nb_store, depths, q, groups, n, sc, stream);
     return launch_topk(sc, rows, n, k, indices, ws, stream);
@@ -960,14 +1046,23 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
   hipError_t e = launch_fused_guess(fw.sample, rows, n, R, nkeys, target, fw.rows, fw.gflag, G,
                                     stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(nrounds * groups)), block(kThreads);
-  hipLaunchKernelGGL((scan_main<G, 1>), grid, block, 0, stream, planes, scales, nb_store, depths,
-                     q, nrounds, n, nrounds, scores, fw.rows, (const uint32_t*)nullptr);
+  // The scan (MODE 1: with candidates; MODE 0 gated: the second pass).
+  auto scan = [&](auto mode, float* out, const uint32_t* gate) {
+    constexpr int M = decltype(mode)::value;
+    void* tws = M == 1 ? fw.rows : nullptr;
+    hipLaunchKernelGGL((scan_main<G, M>), dim3((unsigned)(nrounds * groups)), dim3(kThreads), 0,
+                       stream, planes, scales, nb_store, depths, q, nrounds, n, nrounds, out, tws,
+                       gate);
+    if (first < nblk)
+      hipLaunchKernelGGL((scan_tail<G, M>), dim3((unsigned)((nblk - first + kNB - 1) / kNB),
+                                                 (unsigned)groups),
+                         dim3(kTailThreads), 0, stream, planes, scales, nb_store, depths, q, first,
+                         nblk, n, out, tws, gate);
+  };
+  scan(std::integral_constant<int, 1>(), scores, nullptr);
   e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
   if (e != hipSuccess || scores != nullptr) return e;
-  hipLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, planes, scales, nb_store, depths,
-                     q, nrounds, n, nrounds, fw.scores, (void*)nullptr,
-                     (const uint32_t*)fw.gflag);
+  scan(std::integral_constant<int, 0>(), fw.scores, fw.gflag);
   return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, stream);
 }
 

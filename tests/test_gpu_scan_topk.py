@@ -81,13 +81,45 @@ def test_scan_random_depths_and_store_capacity(fk):
         _check_scores(gpu, planes, scales, depths, ins.q, n)
 
 
+def _misaligned(t, elems):
+    """The same values in a contiguous device view whose first element sits
+    `elems` elements past a fresh allocation's (aligned) start."""
+    import torch
+    flat = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = flat[elems:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("nb_extra,scale_shift", [(3, 0), (8, 2), (5, 6)])
+def test_scan_odd_capacity_and_unaligned_scales(fk, nb_extra, scale_shift):
+    """The main kernel on stores whose scale rows are not 16-byte aligned: a
+    capacity that is not a multiple of 8 blocks (n/64 + 3, n/64 + 5), and
+    scales starting 4 or 12 bytes past a 16-byte boundary; whole rounds plus a
+    tail (n = 64 * 1000)."""
+    import torch
+    n = 64 * 1000
+    ins = fathom_inputs.make_inputs(2, 4, n, seed=47 + nb_extra)
+    planes, scales, _ = oracle.encode(ins.k, nb_store=n // 64 + nb_extra)
+    depths, _, _ = oracle.plan(ins.q, ins.var, 92)
+    ds = to_dev(scales)
+    if scale_shift:
+        ds = _misaligned(ds, scale_shift)
+        assert ds.data_ptr() % 16 != 0
+    say("scan nb_store=%d scale shift %d" % (n // 64 + nb_extra, scale_shift))
+    s = fk.scan(to_dev(planes), ds, to_dev(depths), to_dev(ins.q), n)
+    torch.cuda.synchronize()
+    _check_scores(to_host(s), planes, scales, depths, ins.q, n)
+
+
 def test_scan_timed_same_scores(fk):
     """fathom_scan_timed: the same scores bit for bit, and a positive kernel
     time in its events, with the main kernel only (n = 64 * 64), the main
-    and the tail kernel (64 * 101) and the tail kernel only (64 * 5)."""
+    and the tail kernel (64 * 101) and the tail kernel only (64 * 5), on a
+    store of 104 blocks (a multiple of 8: 16-byte scale rows)."""
     import torch
     ins = fathom_inputs.make_inputs(2, 4, 64 * 101, seed=41)
-    planes, scales, _ = oracle.encode(ins.k)
+    planes, scales, _ = oracle.encode(ins.k, nb_store=104)
     depths, _, _ = oracle.plan(ins.q, ins.var, 92)
     dp, ds, dd, dq = to_dev(planes), to_dev(scales), to_dev(depths), to_dev(ins.q)
     for n in (64 * 64, 64 * 101, 64 * 5):
@@ -299,13 +331,21 @@ def test_fixed_plans_through_the_scan(fk, mode, param):
     assert_topk_valid(gi, s64, l1, k)
 
 
-def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=True, ins=None):
+def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=True, ins=None,
+                    nb_store=None, scale_shift=0):
     """fathom_scan_topk against the oracle's scan and top-k (scores compared
     when the call writes them; index sets always, and against the fp64
-    definition)."""
+    definition).  nb_store / scale_shift: the store built by the oracle with
+    that capacity, its scales `scale_shift` elements past an aligned start."""
     if ins is None:
         ins = fathom_inputs.make_inputs(groups, 4, n, seed=seed)
-    planes, scales = fk.encode(to_dev(ins.k))
+    if nb_store is None:
+        planes, scales = fk.encode(to_dev(ins.k))
+    else:
+        hp, hs, _ = oracle.encode(ins.k, nb_store=nb_store)
+        planes, scales = to_dev(hp), to_dev(hs)
+    if scale_shift:
+        scales = _misaligned(scales, scale_shift)
     if depths is None:
         dd = fk.plan(to_dev(ins.q), to_dev(ins.var), budget)
         od, _, _ = oracle.plan(ins.q, ins.var, budget)
@@ -314,7 +354,7 @@ def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=Tr
         od = depths
     scores, idx = fk.scan_topk(planes, scales, dd, to_dev(ins.q), n, k, write_scores=write_scores)
     gi = to_host(idx)
-    op, os_, _ = oracle.encode(ins.k)
+    op, os_, _ = oracle.encode(ins.k, nb_store=nb_store)
     ref = oracle.scan_ref32(op, os_, od, ins.q, n)
     if write_scores:
         gsc = to_host(scores)
@@ -329,12 +369,27 @@ def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=Tr
 
 @pytest.mark.parametrize("write_scores", [True, False])
 @pytest.mark.parametrize("groups,n,k", [(2, 1 << 17, 512), (3, 1 << 16, 64), (1, 1 << 18, 4096),
-                                        (2, 3 * 4096, 100), (1, 65536 + 2048, 300)])
+                                        (2, 3 * 4096, 100), (1, 65536 + 2048, 300),
+                                        (2, 65536 + 64 * 37, 500)])
 def test_scan_topk_matches_scan_then_topk(fk, groups, n, k, write_scores):
-    """Fused (64k <= n <= 2M, n a multiple of 2048) and unfused (other n)
+    """Fused (64k <= n <= 2M: whole rounds in the main kernel, the rest, down
+    to a partial last tile, in the tail kernel) and unfused (shorter rows)
     paths, with and without a score buffer."""
     say("scan_topk groups=%d n=%d k=%d write_scores=%s" % (groups, n, k, write_scores))
     _scan_topk_case(fk, groups, n, k, 92, seed=90 + groups, write_scores=write_scores)
+
+
+@pytest.mark.parametrize("write_scores", [True, False])
+@pytest.mark.parametrize("nb_extra,scale_shift", [(3, 0), (0, 2)])
+def test_scan_topk_odd_capacity_and_unaligned_scales(fk, nb_extra, scale_shift, write_scores):
+    """The fused path on a store of n/64 + 3 blocks (8-byte plane loads,
+    2-byte scale loads in the sample) and on scales 4 bytes past a 16-byte
+    boundary, with a ragged n (whole rounds plus a tail)."""
+    n, k = 65536 + 64 * 45, 700
+    say("scan_topk nb_store=n/64+%d scale shift %d write_scores=%s"
+        % (nb_extra, scale_shift, write_scores))
+    _scan_topk_case(fk, 2, n, k, 92, seed=95, write_scores=write_scores,
+                    nb_store=n // 64 + nb_extra, scale_shift=scale_shift)
 
 
 @pytest.mark.parametrize("write_scores", [True, False])
