@@ -51,7 +51,9 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        lib = ctypes.CDLL(build())
+        # FATHOM_ORACLE_LIB: a build of fathom_oracle.c made elsewhere (the
+        # sanitizer test's instrumented one) instead of the default build.
+        lib = ctypes.CDLL(os.environ.get("FATHOM_ORACLE_LIB") or build())
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         I = ctypes.c_int
