@@ -192,6 +192,23 @@ def summarize(dirs):
                 print("%-60s %6s %12.2f %12.1f %7.2f" % (
                     short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
                     float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+        for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            # The scan and selection kernels per launch shape (grid threads),
+            # so that one workload's launches can be read apart from the
+            # others a run makes.
+            per = {}
+            for r in csv.DictReader(open(f)):
+                name = short_name(r["Kernel_Name"])
+                if not name.startswith(("fathom::scan", "fathom::fused", "fathom::topk")):
+                    continue
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                per.setdefault((name, grid), []).append(dur)
+            print("## per launch shape: %s" % os.path.relpath(f, d))
+            print("%-44s %12s %6s %10s %10s" % ("kernel", "grid", "calls", "avg_us", "median_us"))
+            for (name, grid), v in sorted(per.items()):
+                print("%-44s %12d %6d %10.2f %10.2f" % (name[:44], grid, len(v), sum(v) / len(v),
+                                                       float(np.median(v))))
         for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
                                   recursive=True)):
             print("## counters: %s" % os.path.relpath(f, d))
@@ -241,6 +258,19 @@ def summarize(dirs):
             print("scan_hbm_write_bytes_per_launch: %.0f" % scan_w)
             print("scan_hbm_bytes_per_launch: %.0f" % total)
             print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
+    # The same from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled
+    # by the plain copy's factor; FETCH_SIZE weighs a request by the copy's
+    # request size, so it over- or under-states other request mixes.
+    fw = [get(f, c) for f in (scan_key, is_copy) for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    if all(x is not None for x in fw):
+        ffac, wfac = CALIB_BYTES / (fw[2] * 1024), CALIB_BYTES / (fw[3] * 1024)
+        fb, wb = fw[0] * 1024 * ffac, fw[1] * 1024 * wfac
+        print("## scan traffic (FETCH_SIZE / WRITE_SIZE, scaled by the plain-copy factors "
+              "%.4f / %.4f)" % (ffac, wfac))
+        print("scan_fetch_bytes_per_launch: %.0f" % fb)
+        print("scan_write_bytes_per_launch: %.0f" % wb)
+        print("scan_fetch_write_bytes_per_launch: %.0f" % (fb + wb))
+        print("scan_source_sha256: %s" % source_sha(SCAN_SRC))
 
 
 def plan_stats(depths: np.ndarray):
@@ -925,6 +955,8 @@ def main():
         "kernel": "scan_main",
         "traffic_unit": "HBM bytes per launch (read requests by size + write requests)",
         "traffic_read_bytes": recorded_counter(TRAFFIC_FILE, "scan_hbm_read_bytes_per_launch"),
+        "traffic_fetch_write_size": recorded_counter(TRAFFIC_FILE,
+                                                     "scan_fetch_write_bytes_per_launch"),
         "traffic_over_algorithmic": (None if traffic is None else
                                      round(traffic / rf["bytes"], 4)),
         "launch_ms": scan_st["median"],

@@ -26,10 +26,11 @@
 // A = a * 2^13 gives m = A * x - A = a * c' * 2^-10 exactly (all operands in
 // vector registers, which issue faster than the mixed-precision form).  Each head
 // then costs one fp32 FMA: t + 1 + G VALU instructions per channel and
-// block.  At depth 1, m is 0 or a * 2^-10 (staged as such), so the G head
-// FMAs run with the plane word as the execution mask: G instructions.  The
-// block offsets o fold on 8 * G lanes (lane = block * G + head), one
-// instruction per channel, and are added in the epilogue.
+// block.  At depth 1, m is 0 or a * 2^-10 (staged as such): one select with
+// the plane word as its lane mask, then the G head FMAs (fma(w, +0, U) = U,
+// as U is never -0): 1 + G instructions.  The block offsets o fold on 8 * G
+// lanes (lane = block * G + head), one instruction per channel, and are added
+// in the epilogue.
 //
 // Resources.  The scalar-load path of gfx950 moves only a few bytes per clock
 // per CU, so it carries nothing but plane words (the bytes the method reads).
@@ -170,42 +171,19 @@ struct ChanLoad {
   float oa;               // the scale of this lane's block as in A (offset fold)
 };
 
-// acc[h] = fma(w[h], m, acc[h]) for NH heads, in the lanes whose bit is set
-// in `mask` only (EXEC is narrowed to the mask and restored inside the one
-// asm statement, so no other instruction runs under it).
-template <int NH>
-__device__ __forceinline__ void masked_fmac(uint64_t mask, float* acc, const float* w, float m) {
-  uint64_t save;
-  if constexpr (NH == 1) {
-    asm volatile("s_and_saveexec_b64 %0, %2\n\tv_fmac_f32 %1, %3, %4\n\ts_mov_b64 exec, %0"
-                 : "=&s"(save), "+v"(acc[0]) : "s"(mask), "v"(w[0]), "v"(m) : "scc");
-  } else if constexpr (NH == 2) {
-    asm volatile("s_and_saveexec_b64 %0, %3\n\tv_fmac_f32 %1, %4, %6\n\tv_fmac_f32 %2, %5, %6\n\t"
-                 "s_mov_b64 exec, %0"
-                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1])
-                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(m) : "scc");
-  } else if constexpr (NH == 3) {
-    asm volatile("s_and_saveexec_b64 %0, %4\n\tv_fmac_f32 %1, %5, %8\n\tv_fmac_f32 %2, %6, %8\n\t"
-                 "v_fmac_f32 %3, %7, %8\n\ts_mov_b64 exec, %0"
-                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2])
-                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(m) : "scc");
-  } else {
-    static_assert(NH == 4, "one to four heads per masked statement");
-    asm volatile("s_and_saveexec_b64 %0, %5\n\tv_fmac_f32 %1, %6, %10\n\tv_fmac_f32 %2, %7, %10\n\t"
-                 "v_fmac_f32 %3, %8, %10\n\tv_fmac_f32 %4, %9, %10\n\ts_mov_b64 exec, %0"
-                 : "=&s"(save), "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3])
-                 : "s"(mask), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(m) : "scc");
-  }
+// m = A in the lanes whose bit is set in the plane word `mask`, +0 in the
+// others (one select with the word as its lane mask).  The _ordered form is
+// a volatile statement, so it stays where it is written when it opens a
+// channel (it carries the wait for the channel's loads).
+__device__ __forceinline__ float select_plane(uint64_t mask, float A) {
+  float m;
+  asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(m) : "v"(A), "s"(mask));
+  return m;
 }
-
-template <int G, int H0 = 0>
-__device__ __forceinline__ void masked_heads(uint64_t mask, float (&acc)[G], const float (&w)[G],
-                                             float m) {
-  if constexpr (H0 < G) {
-    constexpr int NH = G - H0 < 4 ? G - H0 : 4;
-    masked_fmac<NH>(mask, acc + H0, w + H0, m);
-    masked_heads<G, H0 + NH>(mask, acc, w, m);
-  }
+__device__ __forceinline__ float select_plane_ordered(uint64_t mask, float A) {
+  float m;
+  asm volatile("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(m) : "v"(A), "s"(mask));
+  return m;
 }
 
 // Channel of depth T for the wave tile.  `issue_next` runs right after the
@@ -217,18 +195,23 @@ template <int T, int G, class F>
 __device__ __forceinline__ void compute_chan(const ChanLoad<T, G>& L, float (&acc)[kNB][G],
                                              float& o, F&& issue_next) {
   if constexpr (T == 1) {
-    // Depth 1: c' is the plane bit, so m = a * c' * 2^-10 is either 0, which
-    // leaves every accumulator unchanged (fma(w, 0, U) = U, U never -0), or
-    // a * 2^-10, staged as A for depth-1 channels.  The head FMAs run in the
-    // lanes whose bit is set, with the plane word as the execution mask: the
-    // same results as the general form without its two per-block steps.
+    // Depth 1: c' is the plane bit, so m = a * c' * 2^-10 is either 0 or
+    // a * 2^-10 (staged as A for depth-1 channels): one select with the plane
+    // word as the lane mask gives m, the same value the general form computes
+    // in two steps.
     __builtin_amdgcn_sched_barrier(0);
-    masked_heads<G>(L.pw[0][0], acc[0], L.w, L.A[0]);   // waits for this channel's loads
+    const float m0 = select_plane_ordered(L.pw[0][0], L.A[0]);   // waits for the loads
     __builtin_amdgcn_sched_barrier(0);
     issue_next();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int b = 1; b < kNB; ++b) masked_heads<G>(L.pw[0][b], acc[b], L.w, L.A[b]);
+    for (int h = 0; h < G; ++h) acc[0][h] = __builtin_fmaf(L.w[h], m0, acc[0][h]);
+#pragma unroll
+    for (int b = 1; b < kNB; ++b) {
+      const float m = select_plane(L.pw[0][b], L.A[b]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[b][h] = __builtin_fmaf(L.w[h], m, acc[b][h]);
+    }
     o = __builtin_fmaf(L.e, __builtin_ldexpf(L.oa, 10), o);
     asm volatile("" : "+v"(o));
     return;
@@ -299,6 +282,7 @@ __device__ __forceinline__ void finish_tile(float (&acc)[kNB][G], float o, int s
 constexpr int kTileKeys = kNB * kBlock;
 constexpr int64_t kFusedMinKeys = 65536;   // shorter rows: scan, then top-k
 constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stages
+constexpr int kRescanRounds = 8;           // rounds per workgroup of the gated second pass
 
 template <int G>
 __device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float (&tf)[G],
@@ -541,17 +525,21 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int fir
 }
 
 // MODE 0: scores only; 1: scores (when `scores` is non-null) and the top-k
-// candidates of every wave tile (fathom_scan_topk; needs kRounds == 1).
+// candidates of every wave tile (fathom_scan_topk; needs kRounds == 1);
+// 2: as 0, for fathom_scan_topk's second pass over the flagged groups (its
+// own instance, so that profiles tell it from full scans).
 // `gate` (nullable, per group): a group whose word is 0 is skipped (the
 // scan that fathom_scan_topk runs again for rows whose selection failed).
-template <int G, int MODE = 0>
+// NR: rounds per workgroup (the second pass takes several, so that its grid,
+// launched on every call and empty unless a row failed, is small).
+template <int G, int MODE = 0, int NR = kRounds>
 __global__ __launch_bounds__(kThreads) void scan_main(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t nrounds, int64_t n,
     int64_t wgs_per_group, float* __restrict__ scores, void* tws,
     const uint32_t* __restrict__ gate) {
   static_assert(kNB * G <= 64, "one lane per (block, head) in the offset fold");
-  static_assert(MODE == 0 || kRounds == 1, "candidate emission runs one round per workgroup");
+  static_assert(MODE != 1 || NR == 1, "candidate emission runs one round per workgroup");
   __shared__ MainShared<G> sh;
   __shared__ float s_o[kWaves][kNB * G];
 
@@ -562,8 +550,8 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   if (id < per_xcd * kXcds) id = (id % kXcds) * per_xcd + id / kXcds;
   const int64_t grp = id / wgs_per_group;
   if (gate != nullptr && gate[grp] == 0u) return;   // uniform over the workgroup
-  const int64_t round0 = (id % wgs_per_group) * kRounds;
-  const int nr = kRounds > 1 ? (int)min<int64_t>(kRounds, nrounds - round0) : 1;
+  const int64_t round0 = (id % wgs_per_group) * NR;
+  const int nr = NR > 1 ? (int)min<int64_t>(NR, nrounds - round0) : 1;
   float tf[G];   // MODE 1: the rows' cuts as floats
   if (MODE == 1) {
 #pragma unroll
@@ -679,7 +667,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     // here (the empty asm keeps the compiler from sinking the XORs to the end)
     // frees their registers for the pipelined depths below: 78 at G = 4,
     // which fits 6 waves per SIMD instead of 5.
-    if (kRounds == 1) {
+    if (NR == 1) {
       retire_touches(S, sink);
       asm volatile("" : "+v"(sink));
     }
@@ -696,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
       __syncthreads();
     }
   }
-  if (kRounds > 1) retire_touches(S, sink);
+  if (NR > 1) retire_touches(S, sink);
   asm volatile("" ::"v"(sink));   // keeps the L2 touches alive
 }
 
@@ -717,6 +705,8 @@ __global__ __launch_bounds__(kThreads) void scan_main(
 constexpr int kTailThreads = kNB * 64;   // one wave per block of the tile
 static_assert(kTailThreads == kD * kPlanes, "one thread per plane row of the tile");
 
+// MODE and `gate` as in scan_main (with MODE 1 the tail's tiles, the last one
+// possibly partial, emit their candidates).
 template <int G, int MODE = 0>
 __global__ __launch_bounds__(kTailThreads) void scan_tail(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
@@ -1046,12 +1036,14 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
   hipError_t e = launch_fused_guess(fw.sample, rows, n, R, nkeys, target, fw.rows, fw.gflag, G,
                                     stream);
   if (e != hipSuccess) return e;
-  // The scan (MODE 1: with candidates; MODE 0 gated: the second pass).
+  // The scan (MODE 1: with candidates; MODE 2, gated: the second pass).
   auto scan = [&](auto mode, float* out, const uint32_t* gate) {
     constexpr int M = decltype(mode)::value;
+    constexpr int NR = M == 2 ? kRescanRounds : 1;
     void* tws = M == 1 ? fw.rows : nullptr;
-    hipLaunchKernelGGL((scan_main<G, M>), dim3((unsigned)(nrounds * groups)), dim3(kThreads), 0,
-                       stream, planes, scales, nb_store, depths, q, nrounds, n, nrounds, out, tws,
+    const int64_t wgs = (nrounds + NR - 1) / NR;
+    hipLaunchKernelGGL((scan_main<G, M, NR>), dim3((unsigned)(wgs * groups)), dim3(kThreads), 0,
+                       stream, planes, scales, nb_store, depths, q, nrounds, n, wgs, out, tws,
                        gate);
     if (first < nblk)
       hipLaunchKernelGGL((scan_tail<G, M>), dim3((unsigned)((nblk - first + kNB - 1) / kNB),
@@ -1062,7 +1054,7 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
   scan(std::integral_constant<int, 1>(), scores, nullptr);
   e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
   if (e != hipSuccess || scores != nullptr) return e;
-  scan(std::integral_constant<int, 0>(), fw.scores, fw.gflag);
+  scan(std::integral_constant<int, 2>(), fw.scores, fw.gflag);
   return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, stream);
 }
 

@@ -7,12 +7,11 @@
 //
 // Scores map to order-preserving 32-bit keys (fp32 bits with the sign
 // folded, -0 mapped to +0).  Per row:
-//   sample  — per sampled chunk of 8192 keys (every 8th, at most 64 per
-//             row), an 11-bit histogram of the top key bits, in its own slot
-//             (nothing to clear beforehand);
-//   guess   — sums the slots; a cut tau that leaves, by the sample,
-//             comfortably more than k keys at or above it (placed inside the
-//             histogram bin); clears the row's overflow flag;
+//   cut     — one workgroup per row takes 16 runs of 1024 keys spread over
+//             the row (the whole row when it is short) and places a cut tau
+//             that leaves, by that sample, comfortably more than k keys at or
+//             above it (two radix digits over the sampled keys); clears the
+//             row's overflow flag;
 //   compact — one pass over the row writes every key >= tau (key, index) of
 //             a chunk, in index order, to that chunk's own region of the
 //             row's candidate buffer, and its count;
@@ -23,7 +22,7 @@
 //             selected indices (every key > T, the earliest keys == T) at its
 //             prefix position, so the row comes out in index order without a
 //             sort.
-// If the guess fails (fewer than k keys >= tau, or a chunk with more than
+// If the cut fails (fewer than k keys >= tau, or a chunk with more than
 // its region holds: heavy ties or adversarial rows), or the candidates do not
 // fit in LDS, the resolve workgroup does all of it alone, from the scores or
 // the regions: same result, many more passes.
@@ -49,7 +48,7 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerWg = kThreads / 64;
 constexpr int kPerThread = 32;                       // keys per thread in a chunk
 constexpr int kChunk = kThreads * kPerThread;        // 8192 keys per workgroup chunk
-static_assert(kChunk == kSampleChunk, "the sample reads whole compaction chunks");
+static_assert(kChunk == kCompactChunk, "compaction regions are whole chunks");
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
@@ -186,95 +185,86 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t nee
 
 // ---------------------------------------------------------------------------
 
-// Histogram of the top 11 key bits of one sampled chunk.  Lanes that share a bin serialise in the LDS
-// unit, which is cheaper than combining them first.
-template <bool F>
-__device__ __forceinline__ void sample_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
-                                             uint32_t* s_hist) {
-  ChunkVals V;
-  load_vals<F>(src, n, c0, V);
-#pragma unroll
-  for (int i = 0; i < kPerThread / 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (valid<F>(c0, i, c, n)) atomicAdd(&s_hist[order_key(V.v[i][c]) >> 21], 1u);
-}
+// Per row: the cut tau from a sample of the row, in one workgroup: 16 runs of
+// 1024 keys spread evenly over the row (the whole row when it has at most
+// 16384 keys), held 16 per thread; tau = the target-th largest sampled order
+// key with its low 10 bits cleared (two radix digits of 11 bits), target =
+// the sample's share of k raised by 60% plus 16 keys (k itself for a whole
+// row, where the cut then lies at or just below the k-th key).  Clears the
+// row's overflow flag.
+constexpr int kCutRuns = 16, kCutRun = 1024, kCutPer = kCutRuns * kCutRun / kResolveThreads;
+static_assert(kCutPer == 16, "16 sampled keys per thread");
 
-// Sample blockIdx.x of row blockIdx.y: chunk blockIdx.x * sample_stride(n)
-// of the row's n keys at scores + row * n, its histogram to slot blockIdx.x.
-__global__ __launch_bounds__(kThreads) void topk_sample(const float* __restrict__ scores,
-                                                        int64_t n, int64_t R, void* ws) {
+__global__ __launch_bounds__(kResolveThreads) void topk_cut(const float* __restrict__ scores,
+                                                            int64_t n, int64_t R, int k,
+                                                            void* ws) {
   __shared__ uint32_t s_hist[kBins];
-  const int64_t row = blockIdx.y;
-  RowWs r = row_ws(ws, n, R, row);
-  for (int i = threadIdx.x; i < kBins; i += kThreads) s_hist[i] = 0u;
-  __syncthreads();
-  const int64_t c0 = (int64_t)blockIdx.x * sample_stride(n) * kChunk;
-  const float* src = scores + row * n;
-  if (chunk_full(src, n, c0)) sample_chunk<true>(src, n, c0, s_hist);
-  else sample_chunk<false>(src, n, c0, s_hist);
-  __syncthreads();
-  uint4* dst = reinterpret_cast<uint4*>(r.hist + (int64_t)blockIdx.x * kBins);
-  for (int i = threadIdx.x; i < kBins / 4; i += kThreads)
-    dst[i] = *reinterpret_cast<const uint4*>(&s_hist[4 * i]);
-}
-
-// Per row: the cut tau.  With the whole row sampled the target is exactly k
-// (tau is the low edge of the bin holding the k-th largest key); otherwise
-// the sample's share of k is raised by a quarter plus 64 keys and tau is
-// placed inside that key's bin.
-__global__ __launch_bounds__(kThreads) void topk_guess(int64_t n, int64_t R, int k, void* ws) {
-  __shared__ uint32_t s_tmp[kWavesPerWg];
+  __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
-  __shared__ uint32_t s_h[kBins];
-  constexpr int kPer = kBins / kThreads;
-  static_assert(kPer == 8, "two 16-byte loads per slot and thread");
-  RowWs r = row_ws(ws, n, R, blockIdx.x);
-  const int64_t nsl = n_samples(n), stride = sample_stride(n);
-  int64_t ns = 0;   // keys sampled
-  for (int64_t sl = 0; sl < nsl; ++sl) ns += min<int64_t>(kChunk, n - sl * stride * kChunk);
-  uint32_t h[kPer];
+  const int64_t row = blockIdx.x;
+  RowWs r = row_ws(ws, n, R, row);
+  const float* src = scores + row * n;
+  const int tid = threadIdx.x;
+  const bool whole = n <= (int64_t)kCutRuns * kCutRun;
+  const int nkeys = whole ? (int)n : kCutRuns * kCutRun;
+  uint32_t key[kCutPer];
+  if (whole) {
 #pragma unroll
-  for (int b = 0; b < kPer; ++b) h[b] = 0u;
-  // Eight slots' loads in flight at a time, added in slot order.
-  for (int64_t s0 = 0; s0 < nsl; s0 += 8) {
-    uint4 a[8], c[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t sl = s0 + u;
-      const uint4* src = reinterpret_cast<const uint4*>(r.hist + sl * kBins + threadIdx.x * kPer);
-      a[u] = sl < nsl ? src[0] : make_uint4(0u, 0u, 0u, 0u);
-      c[u] = sl < nsl ? src[1] : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < kCutPer; ++u) {
+      const int64_t i = tid + (int64_t)u * kResolveThreads;
+      key[u] = i < n ? order_key(src[i]) : 0u;
     }
+  } else {
+    // Run c = tid / 64 starts at c * (n - 1024) / 15 (rounded down to 4
+    // keys); lane l takes its keys [16 l, 16 l + 16).
+    const int64_t start = ((tid >> 6) * ((n - kCutRun) / (kCutRuns - 1))) & ~(int64_t)3;
+    const float* p = src + start + (tid & 63) * kCutPer;
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+      typedef float f4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      h[0] += a[u].x; h[1] += a[u].y; h[2] += a[u].z; h[3] += a[u].w;
-      h[4] += c[u].x; h[5] += c[u].y; h[6] += c[u].z; h[7] += c[u].w;
+      for (int u = 0; u < kCutPer / 4; ++u) {
+        const f4 x = *reinterpret_cast<const f4*>(p + 4 * u);
+        key[4 * u] = order_key(x.x);
+        key[4 * u + 1] = order_key(x.y);
+        key[4 * u + 2] = order_key(x.z);
+        key[4 * u + 3] = order_key(x.w);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kCutPer; ++u) key[u] = order_key(p[u]);
     }
   }
-#pragma unroll
-  for (int b = 0; b < kPer; ++b) s_h[threadIdx.x * kPer + b] = h[b];
-  uint32_t target = (uint32_t)k;
-  if (ns < n) {
-    const double share = (double)k * (double)ns / (double)n;
-    target = (uint32_t)min<double>((double)ns, share * 1.25 + 64.0);
+  const bool valid_last = whole;   // only a whole-row sample has keys past nkeys to skip
+  uint32_t need = (uint32_t)k;
+  if (!whole) {
+    const double share = (double)k * (double)nkeys / (double)n;
+    need = (uint32_t)min<double>((double)nkeys, ceil(1.6 * share + 16.0));
   }
-  s_sel[0] = 0u;
-  __syncthreads();
-  pick_bin<kThreads, kPer>(h, target, s_tmp, s_sel);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t bin = s_sel[0];
-    uint32_t tau = bin << 21;
-    if (ns < n) {
-      // Inside the bin, place the cut by the share of the bin's sample that
-      // is needed, doubled: densities fall towards the top of a tail bin, so
-      // the top fraction f of the keys spans more than f of the bin's range.
-      const double f = min(1.0, 2.0 * (double)s_sel[1] / (double)max(s_h[bin], 1u));
-      const uint64_t top = ((uint64_t)bin + 1) << 21;
-      tau = (uint32_t)max<uint64_t>((uint64_t)bin << 21, top - (uint64_t)(f * (double)(1u << 21)));
+  uint32_t prefix = 0;
+  for (int level = 0; level < 2; ++level) {
+    const int shift = level == 0 ? 21 : 10;
+    const int hi = shift + 11;   // bits at and above hi are fixed
+    for (int i = tid; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCutPer; ++u) {
+      const bool ok = !valid_last || tid + (int64_t)u * kResolveThreads < n;
+      const bool in = ok && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
+      if (in) atomicAdd(&s_hist[(key[u] >> shift) & (kBins - 1)], 1u);
     }
-    r.st[kS_TAU] = tau;
+    __syncthreads();
+    constexpr int kPer = kBins / kResolveThreads;
+    uint32_t h[kPer];
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) h[b] = s_hist[tid * kPer + b];
+    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    need = s_sel[1];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    r.st[kS_TAU] = prefix;
     r.st[kS_OVER] = 0u;
   }
 }
@@ -430,7 +420,7 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
 
 // Per row: T (the k-th largest key), the keys == T still needed, and the
 // ordered write.  Rows whose candidates fit in LDS (the usual case) stage
-// (key, index) there and do everything from LDS; other rows (the guess
+// (key, index) there and do everything from LDS; other rows (the cut
 // failed, or too many candidates or chunks) are resolved and written from the
 // candidate regions or the scores, by the same workgroup.
 // mode 0: every row; a row whose candidates cannot give the selection goes to
@@ -511,7 +501,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         run += t;
       }
   }
-  src.direct = ncand < (uint32_t)k || over != 0u || mode == 1;   // the guess failed
+  src.direct = ncand < (uint32_t)k || over != 0u || mode == 1;   // the cut failed
   if (src.direct && scores == nullptr) {   // no scores to fall back on: flag the row
     if (threadIdx.x == 0) {
       r.st[kS_FAIL] = 1u;
@@ -821,11 +811,8 @@ size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* ws, hipStream_t stream) {
   const int64_t R = kChunk, nc = n_chunks(n, R);
-  const unsigned ns = (unsigned)n_samples(n);
   const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
-  hipLaunchKernelGGL(topk_sample, dim3(ns, (unsigned)rows), dim3(kThreads), 0, stream, scores, n,
-                     R, ws);
-  hipLaunchKernelGGL(topk_guess, grid_rows, dim3(kThreads), 0, stream, n, R, k, ws);
+  hipLaunchKernelGGL(topk_cut, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
   hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
                      ws, indices, 0, (uint32_t*)nullptr, 1);
@@ -872,9 +859,9 @@ hipError_t launch_topk_noalloc(const float* scores, int64_t rows, int64_t n, int
   if (e != hipSuccess) return e;
   void* ws = nullptr;
   if ((e = scratch_ptr(dev, &ws)) != hipSuccess) return e;
-  // Every kernel of the selection writes what it later reads (per-chunk
-  // histograms in their own slots, the cut and flags set by the guess), so
-  // nothing of the previous call's contents needs clearing.
+  // Every kernel of the selection writes what it later reads (the cut and
+  // the overflow flag set by the cut kernel, every chunk's count by the
+  // compaction), so nothing of the previous call's contents needs clearing.
   return launch_topk(scores, rows, n, k, indices, ws, stream);
 }
 

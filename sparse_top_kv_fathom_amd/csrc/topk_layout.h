@@ -7,9 +7,8 @@
 namespace fathom {
 namespace topk {
 
-constexpr int kBins = 2048;          // radix digit: 11 bits
-constexpr int kSampleChunk = 8192;   // keys per sampled chunk
-constexpr int kMaxSamples = 64;      // sampled chunks per row at most
+constexpr int kBins = 2048;           // radix digit: 11 bits
+constexpr int kCompactChunk = 8192;   // keys per region when compacting from scores
 
 // Per-row workspace (32-bit words).
 enum : int {
@@ -21,8 +20,9 @@ enum : int {
   kS_WORDS = 16
 };
 
-// Candidates are kept per region of R consecutive keys of a row: R = kChunk
-// when compacting from scores, the scan's round when the scan emits them.
+// Candidates are kept per region of R consecutive keys of a row: R =
+// kCompactChunk when compacting from scores, the scan's wave tile when the
+// scan emits them.
 __host__ __device__ inline int64_t n_chunks(int64_t n, int64_t R) { return (n + R - 1) / R; }
 
 // Candidate buffer capacity: n / 8, between 8192 and 65536 keys, shared
@@ -35,26 +35,11 @@ __host__ __device__ inline uint32_t region(int64_t n, int64_t R) {
   return (uint32_t)(cand_cap(n) / n_chunks(n, R));
 }
 
-// The sample: every stride-th chunk of 8192 keys, stride 8 (1/8 of a long
-// row), raised so that at most 64 chunks are sampled; each sampled chunk has
-// its own histogram.
-constexpr int64_t kSampleStride = 8;
-__host__ __device__ inline int64_t sample_stride(int64_t n) {
-  const int64_t nc = n_chunks(n, kSampleChunk);
-  const int64_t s = (nc + kMaxSamples - 1) / kMaxSamples;
-  return s < kSampleStride ? kSampleStride : s;
-}
-__host__ __device__ inline int64_t n_samples(int64_t n) {
-  return (n_chunks(n, kSampleChunk) + sample_stride(n) - 1) / sample_stride(n);
-}
-
 __host__ __device__ inline size_t row_words(int64_t n, int64_t R) {
-  return (size_t)kBins * n_samples(n) + kS_WORDS + 2 * (size_t)cand_cap(n) +
-         4 * (size_t)n_chunks(n, R);
+  return kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n, R);
 }
 
 struct RowWs {
-  uint32_t* hist;    // [n_samples][kBins]: one histogram per sampled chunk
   uint32_t* st;      // [kS_WORDS]
   uint32_t* cand;    // [nchunks][region][2]: key, index
   uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
@@ -66,8 +51,7 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   uint32_t* p = reinterpret_cast<uint32_t*>(ws) + row_words(n, R) * row;
   RowWs r;
   r.region = region(n, R);
-  r.hist = p;
-  r.st = p + kBins * n_samples(n);
+  r.st = p;
   r.cand = r.st + kS_WORDS;
   r.seg = r.cand + 2 * (size_t)cand_cap(n);
   r.ord = r.seg + 2 * (size_t)n_chunks(n, R);
@@ -94,7 +78,7 @@ __host__ __device__ inline size_t fused_front_bytes(int64_t rows, int64_t groups
   // whichever is larger; the score area follows.
   const size_t fused = align256((size_t)rows * row_words(n, R) * 4) +
                        align256((size_t)rows * kMaxSampleKeys * 4) + align256((size_t)groups * 4);
-  const size_t plain = align256((size_t)rows * row_words(n, kSampleChunk) * 4);
+  const size_t plain = align256((size_t)rows * row_words(n, kCompactChunk) * 4);
   return fused > plain ? fused : plain;
 }
 __host__ __device__ inline FusedWs fused_ws(void* ws, int64_t rows, int64_t groups, int64_t n,
