@@ -5,19 +5,28 @@
 // s = a/8, code = clamp(floor(k/s) + 8, 0, 15); bit p of the 64 codes (p = 0
 // the MSB) is one 64-bit plane word with token i in bit i.
 //
-// Mapping: one wave64 per 64-token block, lane i = token i, so each plane word
-// is a single wave ballot.  The block max is a wave max of |k| taken on the
-// fp16 bit patterns (positive fp16 patterns order like their values), two
-// channels per 32-bit lane word.  A workgroup of 4 waves encodes 4 consecutive
-// blocks; words and scales are staged in LDS and written as contiguous runs
-// per (channel, plane).  Calls with few blocks use a column-split kernel
-// instead (below).
+// The code is found bit by bit, MSB first, by comparing k with a threshold
+// that is an integer multiple of s (exact in fp32), so a channel and token
+// cost four compares, three selects and two adds (code_bits below).
+//
+// Whole stores: one wave64 per 64-token block, lane l owns channels 2l and
+// 2l + 1 (one 32-bit word of every token row: the wave's loads of one token
+// are 256 contiguous bytes), holds the block's 64 words in registers, takes
+// the block max of both channels with packed 16-bit maxima of the fp16
+// magnitude bits (positive fp16 patterns order like their values), then
+// walks the tokens from 63 down to 0 and shifts each code bit into its
+// plane word through the carry-in of one add, so the lane ends with its two
+// channels' 8 plane words.  A workgroup of 8 waves encodes 8 consecutive
+// blocks; words and scales are staged in LDS and written as 64-byte runs per
+// (channel, plane).  Calls with few blocks use a column-split kernel instead
+// (below), which spreads a block's channels over waves with lane = token.
 #include "fathom_internal.h"
 
 namespace fathom {
 namespace {
 
-constexpr int kWavesPerWg = 4;
+constexpr int kWavesPerWg = 4;    // column-split kernel
+constexpr int kStoreWaves = 8;    // whole-store kernel: blocks per workgroup
 
 // Max of two packed 16-bit lanes.
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
@@ -49,78 +58,172 @@ __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// 4-bit code of k (fp16 bits) in a block with max magnitude a (fp16 bits).
-// floor(k / s) is formed from a reciprocal estimate and then corrected with
-// exact products: m*s and (m+1)*s are exact in fp32 for |m| <= 9.
-__device__ __forceinline__ uint32_t code_of(uint32_t kbits, uint32_t abits) {
-  if (abits == 0) return 8u;
-  const float a = f16_bits_to_float(abits);
-  const float s = a * 0.125f;
-  const float kf = f16_bits_to_float(kbits);
-  float m = floorf(kf * (8.0f * __builtin_amdgcn_rcpf(a)));
-  m = fminf(fmaxf(m, -9.0f), 9.0f);
-  if (m * s > kf) m -= 1.0f;
-  if ((m + 1.0f) * s <= kf) m += 1.0f;
-  int c = (int)m + 8;
-  c = c < 0 ? 0 : (c > 15 ? 15 : c);
-  return (uint32_t)c;
+// The 4 plane words of one channel of a block, lane i holding token i's value
+// kf (an fp16 value in fp32) and every lane the block's max magnitude `ab`
+// (fp16 bits).  The code c = clamp(floor(k/s) + 8, 0, 15), s = a/8, is the
+// largest c in [0, 15] with (c - 8) s <= k: taken MSB first, bit p is 1 when
+// k >= (c_p + 2^(3-p) - 8) s, c_p the bits above it.  Every threshold is
+// +-4s, then +-2s, then +-s added: an integer multiple of s below 8s in
+// magnitude, exact in fp32 (s has an fp16 mantissa; a/8 is exact), so each
+// compare is exact and its lane mask is plane word p.  a = 0 (all-zero block)
+// gives code 8: plane 0 all ones (every k is +-0), the others 0.
+struct Planes4 {
+  uint64_t w[kPlanes];
+};
+
+__device__ __forceinline__ Planes4 code_planes(float kf, uint32_t ab) {
+  const float a = f16_bits_to_float(ab);
+  const float s4 = a * 0.5f, s2 = a * 0.25f, s1 = a * 0.125f;
+  const bool b0 = kf >= 0.0f;
+  const float t1 = b0 ? s4 : -s4;
+  const bool b1 = kf >= t1;
+  const float t2 = t1 + (b1 ? s2 : -s2);
+  const bool b2 = kf >= t2;
+  const float t3 = t2 + (b2 ? s1 : -s1);
+  const bool b3 = kf >= t3;
+  const uint64_t nz = ab != 0u ? ~0ull : 0ull;   // uniform
+  Planes4 r;
+  r.w[0] = __ballot(b0);
+  r.w[1] = __ballot(b1) & nz;
+  r.w[2] = __ballot(b2) & nz;
+  r.w[3] = __ballot(b3) & nz;
+  return r;
 }
 
-__global__ __launch_bounds__(256) void encode_kernel(
+// x <- 2x + (this lane's bit of `mask`): the mask is the carry-in of one add;
+// the carry-out (always 0: 32 steps from 0 stay below 2^32) goes to a scratch
+// scalar pair.
+__device__ __forceinline__ uint32_t shift_in(uint32_t x, uint64_t mask) {
+  uint32_t r;
+  uint64_t co;
+  asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(r), "=&s"(co) : "v"(x), "s"(mask));
+  return r;
+}
+
+// One token of one channel in the whole-store kernel: the four code bits of
+// kf (see code_planes) shifted into the lane's plane-word halves w[0..3].
+__device__ __forceinline__ void code_bits(float kf, float s4, float s2, float s1,
+                                          uint32_t (&w)[kPlanes]) {
+  const bool b0 = kf >= 0.0f;
+  w[0] = shift_in(w[0], __ballot(b0));
+  const float t1 = b0 ? s4 : -s4;
+  const bool b1 = kf >= t1;
+  w[1] = shift_in(w[1], __ballot(b1));
+  const float t2 = t1 + (b1 ? s2 : -s2);
+  const bool b2 = kf >= t2;
+  w[2] = shift_in(w[2], __ballot(b2));
+  const float t3 = t2 + (b2 ? s1 : -s1);
+  w[3] = shift_in(w[3], __ballot(kf >= t3));
+}
+
+// Lane LANE of `old` set to the wave-uniform `val` (the lane is an inline
+// constant, so no lane-select hazard).
+template <int LANE>
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val) {
+  static_assert(LANE >= 0 && LANE < 64, "a lane of the wave");
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(val), "i"(LANE));
+  return old;
+}
+
+// The plane words and scales of 8 channels of a block (one 16-byte column of
+// the token rows: lane i holds token i's 8 values): word dword L % 2 of
+// (channel L / 8, plane (L / 2) % 4) in lane L of `words`, the scale of
+// channel L in lane L < 8 of `sc`.
+template <int JJ>
+__device__ __forceinline__ void encode_chan(uint32_t kb, uint32_t ab, uint32_t& words,
+                                            uint32_t& sc, bool& bad) {
+  bad |= ab >= 0x7c00u;   // Inf or NaN somewhere in the block
+  const Planes4 P = code_planes(f16_bits_to_float(kb), ab);
+  words = write_lane<JJ * 8 + 0>(words, (uint32_t)P.w[0]);
+  words = write_lane<JJ * 8 + 1>(words, (uint32_t)(P.w[0] >> 32));
+  words = write_lane<JJ * 8 + 2>(words, (uint32_t)P.w[1]);
+  words = write_lane<JJ * 8 + 3>(words, (uint32_t)(P.w[1] >> 32));
+  words = write_lane<JJ * 8 + 4>(words, (uint32_t)P.w[2]);
+  words = write_lane<JJ * 8 + 5>(words, (uint32_t)(P.w[2] >> 32));
+  words = write_lane<JJ * 8 + 6>(words, (uint32_t)P.w[3]);
+  words = write_lane<JJ * 8 + 7>(words, (uint32_t)(P.w[3] >> 32));
+  sc = write_lane<JJ>(sc, ab);
+}
+
+// Channels 2U and 2U + 1 of the column (the two halves of lane word w).
+template <int U>
+__device__ __forceinline__ void encode_pair(uint32_t w, uint32_t& words, uint32_t& sc, bool& bad) {
+  const uint32_t amax2 = wave_max_u16x2(w & 0x7fff7fffu);
+  encode_chan<2 * U>(w & 0xffffu, amax2 & 0xffffu, words, sc, bad);
+  encode_chan<2 * U + 1>(w >> 16, amax2 >> 16, words, sc, bad);
+}
+
+__device__ __forceinline__ void encode_column(const uint4 v, uint32_t& words, uint32_t& sc,
+                                              bool& bad) {
+  const uint32_t w32[4] = {v.x, v.y, v.z, v.w};
+  encode_pair<0>(w32[0], words, sc, bad);
+  encode_pair<1>(w32[1], words, sc, bad);
+  encode_pair<2>(w32[2], words, sc, bad);
+  encode_pair<3>(w32[3], words, sc, bad);
+}
+
+__global__ __launch_bounds__(kStoreWaves * 64) void encode_kernel(
     const uint16_t* __restrict__ k, int64_t n, int64_t nblk, int64_t nb_store,
     int64_t block_offset, uint64_t* __restrict__ planes, uint16_t* __restrict__ scales,
     uint32_t* __restrict__ flag) {
-  __shared__ uint64_t s_words[kD][kPlanes][kWavesPerWg];
-  __shared__ uint16_t s_scale[kD][kWavesPerWg];
+  __shared__ uint64_t s_words[kD][kPlanes][kStoreWaves];
+  __shared__ uint16_t s_scale[kD][kStoreWaves];
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int64_t g = blockIdx.y;
-  const int64_t blk0 = (int64_t)blockIdx.x * kWavesPerWg;
+  const int64_t blk0 = (int64_t)blockIdx.x * kStoreWaves;
   const int64_t blk = blk0 + wave;
-  const int nvalid = (int)min<int64_t>(kWavesPerWg, nblk - blk0);
+  const int nvalid = (int)min<int64_t>(kStoreWaves, nblk - blk0);
   bool bad = false;
 
   if (wave < nvalid) {
-    // Token row of this lane: 128 fp16 = 16 x 16 bytes.
-    const uint4* row = reinterpret_cast<const uint4*>(k + ((g * n) + blk * kBlock + lane) * kD);
-    for (int c = 0; c < kD / 8; ++c) {
-      const uint4 v = row[c];
-      const uint32_t w32[4] = {v.x, v.y, v.z, v.w};
+    // Word l (channels 2l, 2l + 1) of the block's 64 token rows.
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(k + (g * n + blk * kBlock) * kD) + lane;
+    uint32_t v[kBlock];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t amax2 = wave_max_u16x2(w32[u] & 0x7fff7fffu);
+    for (int t = 0; t < kBlock; ++t) v[t] = src[t * (kD / 2)];
+    uint32_t amax2 = 0u;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int j = c * 8 + u * 2 + half;
-          const uint32_t kb = (w32[u] >> (16 * half)) & 0xffffu;
-          const uint32_t ab = (amax2 >> (16 * half)) & 0xffffu;
-          bad |= ab >= 0x7c00u;  // Inf or NaN somewhere in the block
-          const uint32_t code = code_of(kb, ab);
+    for (int t = 0; t < kBlock; ++t) amax2 = max_u16x2(amax2, v[t] & 0x7fff7fffu);
+    bad = (amax2 & 0xffffu) >= 0x7c00u || (amax2 >> 16) >= 0x7c00u;   // Inf or NaN
 #pragma unroll
-          for (int p = 0; p < kPlanes; ++p) {
-            const uint64_t word = __ballot((code >> (3 - p)) & 1u);
-            if (lane == p) s_words[j][p][wave] = word;
-          }
-          if (lane == 4) s_scale[j][wave] = (uint16_t)ab;
-        }
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t ab = (amax2 >> (16 * h)) & 0xffffu;
+      const float a = f16_bits_to_float(ab);
+      const float s4 = a * 0.5f, s2 = a * 0.25f, s1 = a * 0.125f;
+      uint32_t hi[kPlanes] = {0u, 0u, 0u, 0u}, lo[kPlanes] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = kBlock - 1; t >= 32; --t)
+        code_bits(f16_bits_to_float((v[t] >> (16 * h)) & 0xffffu), s4, s2, s1, hi);
+#pragma unroll
+      for (int t = 31; t >= 0; --t)
+        code_bits(f16_bits_to_float((v[t] >> (16 * h)) & 0xffffu), s4, s2, s1, lo);
+      // a = 0 (all-zero block): code 8 in every token.
+      const int c = 2 * lane + h;
+#pragma unroll
+      for (int p = 0; p < kPlanes; ++p) {
+        uint64_t w = ((uint64_t)hi[p] << 32) | lo[p];
+        if (ab == 0u) w = p == 0 ? ~0ull : 0ull;
+        s_words[c][p][wave] = w;
       }
+      s_scale[c][wave] = (uint16_t)ab;
     }
   }
-  if (flag != nullptr && bad && lane == 0) atomicOr(flag, 1u);
+  if (flag != nullptr && __ballot(bad) != 0ull && lane == 0) atomicOr(flag, 1u);
   __syncthreads();
 
   // Contiguous writes: for each (channel, plane), nvalid consecutive words.
-  for (int idx = threadIdx.x; idx < kD * kPlanes * kWavesPerWg; idx += blockDim.x) {
-    const int b = idx % kWavesPerWg;
-    const int jp = idx / kWavesPerWg;
+  for (int idx = threadIdx.x; idx < kD * kPlanes * kStoreWaves; idx += blockDim.x) {
+    const int b = idx % kStoreWaves;
+    const int jp = idx / kStoreWaves;
     const int j = jp / kPlanes, p = jp % kPlanes;
     if (b < nvalid)
       planes[((g * kD + j) * kPlanes + p) * nb_store + block_offset + blk0 + b] = s_words[j][p][b];
   }
-  for (int idx = threadIdx.x; idx < kD * kWavesPerWg; idx += blockDim.x) {
-    const int b = idx % kWavesPerWg;
-    const int j = idx / kWavesPerWg;
+  for (int idx = threadIdx.x; idx < kD * kStoreWaves; idx += blockDim.x) {
+    const int b = idx % kStoreWaves;
+    const int j = idx / kStoreWaves;
     if (b < nvalid) scales[(g * kD + j) * nb_store + block_offset + blk0 + b] = s_scale[j][b];
   }
 }
@@ -129,7 +232,7 @@ __global__ __launch_bounds__(256) void encode_kernel(
 // are spread over 16 waves, one 16-byte column (8 channels) each, so the work
 // of a block is not one wave's serial loop.  Grid: (blocks, groups, 4); the
 // 4 waves of a workgroup take columns 4z .. 4z+3.  Words and scales are
-// written directly (8 and 2 bytes per channel).
+// written directly, one 32-bit half of a word per lane.
 __global__ __launch_bounds__(256) void encode_cols_kernel(
     const uint16_t* __restrict__ k, int64_t n, int64_t nb_store, int64_t block_offset,
     uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag) {
@@ -138,26 +241,14 @@ __global__ __launch_bounds__(256) void encode_cols_kernel(
   const int64_t g = blockIdx.y;
   const int64_t blk = blockIdx.x;
   const uint4 v = *reinterpret_cast<const uint4*>(k + ((g * n) + blk * kBlock + lane) * kD + col * 8);
-  const uint32_t w32[4] = {v.x, v.y, v.z, v.w};
   bool bad = false;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const uint32_t amax2 = wave_max_u16x2(w32[u] & 0x7fff7fffu);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t j = col * 8 + u * 2 + half;
-      const uint32_t kb = (w32[u] >> (16 * half)) & 0xffffu;
-      const uint32_t ab = (amax2 >> (16 * half)) & 0xffffu;
-      bad |= ab >= 0x7c00u;
-      const uint32_t code = code_of(kb, ab);
-#pragma unroll
-      for (int p = 0; p < kPlanes; ++p) {
-        const uint64_t word = __ballot((code >> (3 - p)) & 1u);
-        if (lane == p) planes[((g * kD + j) * kPlanes + p) * nb_store + block_offset + blk] = word;
-      }
-      if (lane == 4) scales[(g * kD + j) * nb_store + block_offset + blk] = (uint16_t)ab;
-    }
-  }
+  uint32_t words = 0u, sc = 0u;
+  encode_column(v, words, sc, bad);
+  const int64_t slot = block_offset + blk;
+  const int64_t j = col * 8 + lane / 8;
+  reinterpret_cast<uint32_t*>(planes + ((g * kD + j) * kPlanes + (lane / 2) % kPlanes) * nb_store +
+                              slot)[lane % 2] = words;
+  if (lane < 8) scales[(g * kD + col * 8 + lane) * nb_store + slot] = (uint16_t)sc;
   if (flag != nullptr && bad && lane == 0) atomicOr(flag, 1u);
 }
 
@@ -176,8 +267,8 @@ hipError_t launch_encode(const uint16_t* k, int64_t groups, int64_t n, int64_t n
                        nb_store, block_offset, planes, scales, nonfinite_flag);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)((nblk + kWavesPerWg - 1) / kWavesPerWg), (unsigned)groups);
-  hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kWavesPerWg), 0, stream, k, n, nblk,
+  dim3 grid((unsigned)((nblk + kStoreWaves - 1) / kStoreWaves), (unsigned)groups);
+  hipLaunchKernelGGL(encode_kernel, grid, dim3(64 * kStoreWaves), 0, stream, k, n, nblk,
                      nb_store, block_offset, planes, scales, nonfinite_flag);
   return hipGetLastError();
 }
