@@ -44,6 +44,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -221,8 +222,8 @@ def summarize(dirs):
                 print("%-60s %-24s %6d %14.1f" % (kname, cname, len(v), sum(v) / len(v)))
                 means[(kname, cname)] = sum(v) / len(v)
 
-    def scan_key(k):
-        return k[0].startswith("fathom::scan_main<") and k[0].endswith(", 0>")
+    def scan_key(k):   # the full scan: scan_main<G, 0> (any rounds per workgroup)
+        return re.fullmatch(r"fathom::scan_main<\d+, 0(, \d+)?>", k[0]) is not None
     valu = [v for k, v in means.items() if scan_key(k) and k[1] == "SQ_INSTS_VALU"]
     if valu:
         print("scan_valu_instructions_per_launch: %.0f" % valu[0])
