@@ -332,13 +332,13 @@ def test_fixed_plans_through_the_scan(fk, mode, param):
 
 
 def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=True, ins=None,
-                    nb_store=None, scale_shift=0):
+                    nb_store=None, scale_shift=0, G=4):
     """fathom_scan_topk against the oracle's scan and top-k (scores compared
     when the call writes them; index sets always, and against the fp64
     definition).  nb_store / scale_shift: the store built by the oracle with
     that capacity, its scales `scale_shift` elements past an aligned start."""
     if ins is None:
-        ins = fathom_inputs.make_inputs(groups, 4, n, seed=seed)
+        ins = fathom_inputs.make_inputs(groups, G, n, seed=seed)
     if nb_store is None:
         planes, scales = fk.encode(to_dev(ins.k))
     else:
@@ -377,6 +377,15 @@ def test_scan_topk_matches_scan_then_topk(fk, groups, n, k, write_scores):
     paths, with and without a score buffer."""
     say("scan_topk groups=%d n=%d k=%d write_scores=%s" % (groups, n, k, write_scores))
     _scan_topk_case(fk, groups, n, k, 92, seed=90 + groups, write_scores=write_scores)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 8])
+def test_scan_topk_query_heads_per_group(fk, G):
+    """The fused path for other group sizes (the sample's per-head partial
+    sums, the candidate regions of every head), with a ragged n."""
+    n, k = 65536 + 64 * 9, 300
+    say("scan_topk G=%d n=%d" % (G, n))
+    _scan_topk_case(fk, 2, n, k, 92, seed=110 + G, write_scores=(G % 2 == 0), G=G)
 
 
 @pytest.mark.parametrize("write_scores", [True, False])
