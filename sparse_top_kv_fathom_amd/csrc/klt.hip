@@ -12,9 +12,10 @@
 // Fit (fp64):
 //   klt_mean  — per (chunk of tokens, group): fp64 column sums;
 //   klt_cov   — per (chunk, group): the upper triangle of the 128 x 128 sums
-//               of centred products, one 8 x 8 tile per thread and half of
-//               the chunk's tokens (272 threads: 136 tiles x 2 halves),
-//               tokens staged in LDS as fp64;
+//               of centred products on the fp64 matrix cores: the 36
+//               upper-triangle 16 x 16 tiles, 9 per wave, each a chain of
+//               16 x 16 x 4 fp64 MFMAs over the chunk's tokens, which are
+//               staged in LDS 64 at a time as centred fp64 values;
 //   klt_reduce— per (element block, group): the partial sums added in a
 //               fixed order, divided by n - 1;
 //   klt_eig   — per group, one 1024-thread workgroup: cyclic Jacobi on the
@@ -32,9 +33,11 @@
 namespace fathom {
 namespace {
 
-constexpr int kCovThreads = 272;    // 136 upper-triangle 8 x 8 tiles x 2 token halves
-constexpr int kCovTiles = 136;
-constexpr int kCovTok = 32;          // tokens staged per step of klt_cov
+constexpr int kCovThreads = 256;    // 4 waves, 9 of the 36 upper-triangle 16 x 16 tiles each
+constexpr int kCovTiles = 36;
+constexpr int kCovTok = 64;          // tokens staged per step of klt_cov
+constexpr int kCovPitch = kD + 16;   // doubles per staged token row: the 4 rows a fragment
+                                     // read spans start 32 banks apart
 constexpr int kEigThreads = 1024;
 constexpr int kPairs = kD / 2;       // disjoint rotations per Jacobi step
 constexpr int kPacked = kD * (kD + 1) / 2;
@@ -63,7 +66,7 @@ __device__ __forceinline__ int tri(int a, int b) {
 
 struct FitLayout {
   double* mean;   // [groups][P][d]       column sums per chunk
-  double* cov;    // [groups][2P][d][d]   centred product sums per chunk half (r <= c)
+  double* cov;    // [groups][P][d][d]    centred product sums per chunk (r <= c)
   double* csum;   // [groups][d][d]       the covariance (r <= c)
 };
 
@@ -71,7 +74,7 @@ __host__ __device__ inline FitLayout fit_layout(void* ws, int64_t groups, int64_
   FitLayout L;
   L.mean = static_cast<double*>(ws);
   L.cov = L.mean + groups * P * kD;
-  L.csum = L.cov + groups * 2 * P * kD * kD;
+  L.csum = L.cov + groups * P * kD * kD;
   return L;
 }
 
@@ -123,85 +126,154 @@ __global__ __launch_bounds__(256) void klt_mean(const uint16_t* __restrict__ k, 
   }
 }
 
-// Sums of centred products of chunk blockIdx.x of group blockIdx.y.  Thread
-// t owns tile t % 136 of the upper triangle (8 x 8 tiles (ti, tj), ti <= tj,
-// row by row) over the staged tokens u with u % 2 == t / 136, and writes them
-// as partial 2 * chunk + t / 136.
+// Sums of centred products of chunk blockIdx.x of group blockIdx.y, on the
+// fp64 matrix cores.  Tile (ti, tj), ti <= tj, of the 8 x 8 grid of 16 x 16
+// tiles is C += X_i^T X_j over the chunk's tokens, four at a time:
+// v_mfma_f64_16x16x4f64 takes A[r][k] and B[k][c] in lane 16 k + r (resp.
+// 16 k + c) and leaves C[4 e + l / 16][l % 16] in element e of lane l.  With
+// A = X_i^T and B = X_j both operands are the same fragment shape: lane
+// 16 k + r holds X[token k][16 b + r] for channel block b, so a wave loads
+// the 8 blocks' fragments of a step once and feeds its 9 tiles from them.
+// Wave w takes tiles w, w + 4, ... of the 36 in row order.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int kCovTilesPerWave = kCovTiles / (kCovThreads / 64);
+
+// Row and column block of upper-triangle tile idx, in row order.
+constexpr int cov_tile_row(int idx) {
+  int r = 0;
+  while (idx >= 8 - r) {
+    idx -= 8 - r;
+    ++r;
+  }
+  return r;
+}
+constexpr int cov_tile_col(int idx) {
+  int r = 0;
+  while (idx >= 8 - r) {
+    idx -= 8 - r;
+    ++r;
+  }
+  return r + idx;
+}
+struct CovTileTable {
+  int row[kCovTiles], col[kCovTiles];
+  constexpr CovTileTable() : row(), col() {
+    for (int i = 0; i < kCovTiles; ++i) {
+      row[i] = cov_tile_row(i);
+      col[i] = cov_tile_col(i);
+    }
+  }
+};
+constexpr CovTileTable kCovTable{};
+
+// The staged tokens' MFMA steps for wave W's tiles W, W + 4, ... (their row
+// and column blocks are compile-time constants, so the fragments are read
+// straight from registers).
+template <int W>
+__device__ __forceinline__ void cov_steps(const double (*s_x)[kCovPitch], int lane,
+                                          f64x4 (&acc)[kCovTilesPerWave]) {
+#pragma unroll 2
+  for (int k4 = 0; k4 < kCovTok; k4 += 4) {
+    double f[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) f[b] = s_x[k4 + (lane >> 4)][16 * b + (lane & 15)];
+#pragma unroll
+    for (int u = 0; u < kCovTilesPerWave; ++u)
+      acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(f[kCovTable.row[W + 4 * u]],
+                                                    f[kCovTable.col[W + 4 * u]], acc[u], 0, 0, 0);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void cov_store(double* dst, int lane,
+                                          const f64x4 (&acc)[kCovTilesPerWave]) {
+#pragma unroll
+  for (int u = 0; u < kCovTilesPerWave; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dst[(16 * kCovTable.row[W + 4 * u] + 4 * e + (lane >> 4)) * kD +
+          16 * kCovTable.col[W + 4 * u] + (lane & 15)] = acc[u][e];
+}
+
 __global__ __launch_bounds__(kCovThreads) void klt_cov(const uint16_t* __restrict__ k, int64_t n,
                                                        int64_t per, int64_t P, void* ws,
                                                        int64_t groups) {
   __shared__ double s_mu[kD];
-  __shared__ double s_x[kCovTok][kD];
+  __shared__ double s_x[kCovTok][kCovPitch];
   const int64_t g = blockIdx.y, p = blockIdx.x;
   const int64_t t0 = p * per, t1 = min(n, t0 + per);
   const FitLayout L = fit_layout(ws, groups, P);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (threadIdx.x < kD) {
     double s = 0.0;
     for (int64_t i = 0; i < P; ++i) s += L.mean[(g * P + i) * kD + threadIdx.x];
     s_mu[threadIdx.x] = s / (double)n;
   }
-  const int half = threadIdx.x / kCovTiles;
-  int ti = 0, rest = threadIdx.x % kCovTiles;
-  while (rest >= 16 - ti) {
-    rest -= 16 - ti;
-    ++ti;
-  }
-  const int tj = ti + rest;
-  double acc[8][8];
+  f64x4 acc[kCovTilesPerWave];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
-  // Staging (threads < 256): token t / 8 of the step, channels 16 (t % 8) .. +15.
-  const int lt = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 16;
-  for (int64_t s0 = t0; s0 < t1; s0 += kCovTok) {
-    __syncthreads();
+  for (int u = 0; u < kCovTilesPerWave; ++u) acc[u] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // Staging: thread t converts token t / 4 of the step, channels
+  // 32 (t % 4) .. +31 (four 16-byte loads), centred, to fp64.  The next
+  // step's loads are issued before this step's products, so they are in
+  // flight while the matrix cores work.
+  const int lt = threadIdx.x >> 2, lc = (threadIdx.x & 3) * 32;
+  auto load = [&](int64_t s0, uint4 (&v)[4]) {
     const int64_t tok = s0 + lt;
-    if (threadIdx.x < 256 && tok < t1) {
+    if (tok < t1) {
       const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok) * kD + lc);
-      const uint4 w0 = src[0], w1 = src[1];
-      const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s_x[lt][lc + 2 * e] = f16_to_f64((uint16_t)(w[e] & 0xffffu)) - s_mu[lc + 2 * e];
-        s_x[lt][lc + 2 * e + 1] = f16_to_f64((uint16_t)(w[e] >> 16)) - s_mu[lc + 2 * e + 1];
+      for (int i = 0; i < 4; ++i) v[i] = src[i];
+    }
+  };
+  uint4 v[4];
+  load(t0, v);
+  for (int64_t s0 = t0; s0 < t1; s0 += kCovTok) {
+    __syncthreads();   // the previous step's products are done with s_x
+    if (s0 + lt < t1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = lc + 8 * i + 2 * e;
+          s_x[lt][c] = f16_to_f64((uint16_t)(w[e] & 0xffffu)) - s_mu[c];
+          s_x[lt][c + 1] = f16_to_f64((uint16_t)(w[e] >> 16)) - s_mu[c + 1];
+        }
       }
-    } else if (threadIdx.x < 256) {
+    } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_x[lt][lc + e] = 0.0;
+      for (int e = 0; e < 32; ++e) s_x[lt][lc + e] = 0.0;
     }
     __syncthreads();
-#pragma unroll 2
-    for (int u = half; u < kCovTok; u += 2) {
-      double ra[8], cb[8];
-#pragma unroll
-      for (int a = 0; a < 8; ++a) ra[a] = s_x[u][8 * ti + a];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) cb[b] = s_x[u][8 * tj + b];
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fma(ra[a], cb[b], acc[a][b]);
+    if (s0 + kCovTok < t1) load(s0 + kCovTok, v);
+    switch (wave) {
+      case 0: cov_steps<0>(s_x, lane, acc); break;
+      case 1: cov_steps<1>(s_x, lane, acc); break;
+      case 2: cov_steps<2>(s_x, lane, acc); break;
+      default: cov_steps<3>(s_x, lane, acc); break;
     }
   }
-  double* dst = L.cov + (g * 2 * P + 2 * p + half) * kD * kD;
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) dst[(8 * ti + a) * kD + 8 * tj + b] = acc[a][b];
+  double* dst = L.cov + (g * P + p) * kD * kD;
+  switch (wave) {
+    case 0: cov_store<0>(dst, lane, acc); break;
+    case 1: cov_store<1>(dst, lane, acc); break;
+    case 2: cov_store<2>(dst, lane, acc); break;
+    default: cov_store<3>(dst, lane, acc); break;
+  }
 }
 
 // The covariance: element e = blockIdx.x * 256 + t of group blockIdx.y (row
-// e / 128, column e % 128, upper triangle only) summed over the 2P partials
+// e / 128, column e % 128, upper triangle only) summed over the P partials
 // in index order, times 1 / (n - 1).
 __global__ __launch_bounds__(256) void klt_reduce(int64_t n, int64_t P, void* ws, int64_t groups) {
   const int64_t g = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e / kD > e % kD) return;
   const FitLayout L = fit_layout(ws, groups, P);
-  const double* src = L.cov + g * 2 * P * kD * kD + e;
+  const double* src = L.cov + g * P * kD * kD + e;
   double s = 0.0;
-  for (int64_t i = 0; i < 2 * P; ++i) s += src[i * kD * kD];
+  for (int64_t i = 0; i < P; ++i) s += src[i * kD * kD];
   L.csum[g * kD * kD + e] = s * (1.0 / (double)(n - 1));
 }
 
@@ -463,7 +535,7 @@ int64_t fit_chunks(int64_t groups, int64_t n) {
 
 size_t klt_fit_workspace_bytes(int64_t groups, int64_t n) {
   const int64_t P = fit_chunks(groups, n);
-  return (size_t)(groups * (P * kD + 2 * P * kD * kD + kD * kD)) * sizeof(double);
+  return (size_t)(groups * (P * kD + P * kD * kD + kD * kD)) * sizeof(double);
 }
 
 hipError_t launch_klt_fit(const uint16_t* k, int64_t groups, int64_t n, float* mu, float* basis,

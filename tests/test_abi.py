@@ -176,8 +176,8 @@ def test_gather_validation(L):
 
 
 def test_klt_validation(L):
-    def fit_bytes(groups, P):     # mean partials, product partials (two per chunk), covariance
-        return groups * (P * 128 + 2 * P * 128 * 128 + 128 * 128) * 8
+    def fit_bytes(groups, P):     # mean partials, product partials (one per chunk), covariance
+        return groups * (P * 128 + P * 128 * 128 + 128 * 128) * 8
     assert L.fathom_klt_fit_workspace_bytes(8, 1 << 20, 128) == fit_bytes(8, 64)
     assert L.fathom_klt_fit_workspace_bytes(128, 1 << 17, 128) == fit_bytes(128, 4)
     assert L.fathom_klt_fit_workspace_bytes(1, 64, 128) == fit_bytes(1, 1)
