@@ -53,11 +53,12 @@
 // its arithmetic.  Depths 3 and 4 (64-128 plane registers) load and compute
 // one at a time.
 //
-// Grid.  Main kernel: whole rounds only; workgroup ids are remapped so that
-// consecutive rounds of a group run on the same XCD (workgroups are dealt to
-// the 8 XCDs round-robin).  The blocks after the last whole round go to a
-// small tail kernel with per-block clamped loads, which also serves stores
-// whose offsets exceed 32 bits or whose scale rows are not 16-byte aligned.
+// Grid.  Main kernel: whole rounds only (4 waves, 32 blocks, 2048 tokens per
+// workgroup; 8-wave workgroups measured the same), workgroup ids remapped so
+// that consecutive rounds of a group run on the same XCD (workgroups are
+// dealt to the 8 XCDs round-robin).  The blocks after the last whole round
+// go to a small tail kernel (one workgroup per 512-token tile, staged in
+// LDS), which also serves groups whose plane array needs 64-bit offsets.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -329,7 +330,8 @@ struct SlotTables {
 // Main kernel: whole rounds, L2 prefetch, scales staged in LDS
 // ---------------------------------------------------------------------------
 
-constexpr int kScalePasses = kD * kRoundBlocks / 8 / kThreads;                      // 2
+constexpr int kScaleParts = kRoundBlocks / 8;   // 16-byte parts of a slot's round of scales
+constexpr int kScalePasses = kD * kScaleParts / kThreads;                            // 2
 
 template <int G>
 struct MainShared {
@@ -426,11 +428,12 @@ __device__ __forceinline__ void main_depth(const MainCtx& c, const SlotTables<G>
 }
 
 // The vector loads of one round: the block scales of every active slot (kept
-// in registers until they are staged) and TOUCHES per 256-byte plane-row
-// segment (one 4-byte load per 64 / TOUCHES... bytes), which pull the round's
-// plane lines into L2 ahead of the scalar loads.  Thread 4s + k loads scales
-// [8k, 8k + 8) of slot s: 16 aligned bytes when the capacity is a multiple
-// of 8 blocks and the scales 16-byte aligned, else eight 2-byte loads.
+// in registers until they are staged) and TOUCHES per plane-row segment of
+// the round (kRoundBlocks * 8 = 256 bytes: one 4-byte load per 128-byte
+// line), which pull the round's plane lines into L2 ahead of the scalar
+// loads.  Thread kScaleParts * s + k loads scales [8k, 8k + 8) of slot s: 16
+// aligned bytes when the capacity is a multiple of 8 blocks and the scales
+// 16-byte aligned, else eight 2-byte loads.
 #ifndef SCAN_TOUCHES
 #define SCAN_TOUCHES 2
 #endif
@@ -449,9 +452,9 @@ __device__ __forceinline__ void retire_touches(const Stage& S, uint32_t& sink) {
   for (int i = 0; i < kTouchPerThread; ++i) sink ^= S.tv[i];
 }
 
-// The round's block scales of every active slot: thread 4s + k loads scales
-// [8k, 8k + 8) of slot s (threads past the active slots load channel 0's and
-// ignore them, so every load is issued unconditionally).
+// The round's block scales of every active slot: thread kScaleParts * s + k
+// loads scales [8k, 8k + 8) of slot s (threads past the active slots load
+// channel 0's and ignore them, so every load is issued unconditionally).
 template <int G>
 __device__ __forceinline__ void issue_scales(const MainShared<G>& sh, int nact,
                                              const char* scales_g, int64_t nb_store, int64_t r0,
@@ -461,9 +464,9 @@ __device__ __forceinline__ void issue_scales(const MainShared<G>& sh, int nact,
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int slot = k >> 2;
+    const int slot = k / kScaleParts;
     const int64_t ch = slot < nact ? (int64_t)sh.sj[slot] : 0;
-    const char* sp = scales_g + (ch * nb_store + r0) * 2 + (k & 3) * 16;
+    const char* sp = scales_g + (ch * nb_store + r0) * 2 + (k % kScaleParts) * 16;
     if (sv) {
       S.st[i] = *reinterpret_cast<const uint4*>(sp);
     } else {
@@ -503,7 +506,7 @@ __device__ __forceinline__ void round_stage(MainShared<G>& sh, int nact, int fir
 #pragma unroll
   for (int i = 0; i < kScalePasses; ++i) {
     const int k = tid + i * kThreads;
-    const int slot = k >> 2, part = k & 3;
+    const int slot = k / kScaleParts, part = k % kScaleParts;
     if (slot < nact) {
       uint32_t wd[4] = {S.st[i].x, S.st[i].y, S.st[i].z, S.st[i].w};
       if (!sv) {
