@@ -185,13 +185,45 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t nee
 
 // ---------------------------------------------------------------------------
 
+// The need-th largest of the workgroup's keys (PER per thread; key u of a
+// thread counts when valid(u)) with its low 10 bits cleared: two radix
+// digits of 11 bits over an LDS histogram.  The result is at most 2^-13 of
+// the score below that key, never above it.
+template <int PER, class V>
+__device__ __forceinline__ uint32_t radix_cut(const uint32_t (&key)[PER], V&& valid,
+                                              uint32_t need, uint32_t* s_hist, uint32_t* s_tmp,
+                                              uint32_t* s_sel) {
+  uint32_t prefix = 0;
+  for (int level = 0; level < 2; ++level) {
+    const int shift = level == 0 ? 21 : 10;
+    const int hi = shift + 11;   // bits at and above hi are fixed
+    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const bool in = valid(u) && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
+      if (in) atomicAdd(&s_hist[(key[u] >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    constexpr int kPer = kBins / kResolveThreads;
+    uint32_t h[kPer];
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+    __syncthreads();
+    prefix |= s_sel[0] << shift;
+    need = s_sel[1];
+    __syncthreads();
+  }
+  return prefix;
+}
+
 // Per row: the cut tau from a sample of the row, in one workgroup: 16 runs of
 // 1024 keys spread evenly over the row (the whole row when it has at most
-// 16384 keys), held 16 per thread; tau = the target-th largest sampled order
-// key with its low 10 bits cleared (two radix digits of 11 bits), target =
-// the sample's share of k raised by 60% plus 16 keys (k itself for a whole
-// row, where the cut then lies at or just below the k-th key).  Clears the
-// row's overflow flag.
+// 16384 keys), held 16 per thread; tau = radix_cut of them at the target-th
+// largest, target = the sample's share of k raised by 60% plus 16 keys (k
+// itself for a whole row, where the cut then lies at or just below the k-th
+// key).  Clears the row's overflow flag.
 constexpr int kCutRuns = 16, kCutRun = 1024, kCutPer = kCutRuns * kCutRun / kResolveThreads;
 static_assert(kCutPer == 16, "16 sampled keys per thread");
 
@@ -234,35 +266,15 @@ __global__ __launch_bounds__(kResolveThreads) void topk_cut(const float* __restr
       for (int u = 0; u < kCutPer; ++u) key[u] = order_key(p[u]);
     }
   }
-  const bool valid_last = whole;   // only a whole-row sample has keys past nkeys to skip
   uint32_t need = (uint32_t)k;
   if (!whole) {
     const double share = (double)k * (double)nkeys / (double)n;
     need = (uint32_t)min<double>((double)nkeys, ceil(1.6 * share + 16.0));
   }
-  uint32_t prefix = 0;
-  for (int level = 0; level < 2; ++level) {
-    const int shift = level == 0 ? 21 : 10;
-    const int hi = shift + 11;   // bits at and above hi are fixed
-    for (int i = tid; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kCutPer; ++u) {
-      const bool ok = !valid_last || tid + (int64_t)u * kResolveThreads < n;
-      const bool in = ok && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
-      if (in) atomicAdd(&s_hist[(key[u] >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    constexpr int kPer = kBins / kResolveThreads;
-    uint32_t h[kPer];
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) h[b] = s_hist[tid * kPer + b];
-    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    need = s_sel[1];
-    __syncthreads();
-  }
+  // Only a whole-row sample has slots past the row's end to skip.
+  const uint32_t prefix = radix_cut(
+      key, [&](int u) { return !whole || tid + (int64_t)u * kResolveThreads < n; }, need, s_hist,
+      s_tmp, s_sel);
   if (tid == 0) {
     r.st[kS_TAU] = prefix;
     r.st[kS_OVER] = 0u;
@@ -724,12 +736,10 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
 }
 
-// The cut of fathom_scan_topk, from its sample: tau = the target-th largest of
-// the row's nkeys sampled order keys with its low 10 bits cleared (two radix
-// digits of 11 bits over keys held in registers: the cut is exact to 2^-13 of
-// the score, and may only sit lower than the sample's own target-th key), so
-// that about target * n / nkeys keys of the row are at or above it.  Also
-// clears the row's flags and its group's.
+// The cut of fathom_scan_topk, from its sample: tau = radix_cut of the row's
+// nkeys sampled order keys at the target-th largest, so that about
+// target * n / nkeys keys of the row are at or above it.  Also clears the
+// row's flags and its group's.
 __global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* __restrict__ sample,
                                                                int64_t n, int64_t R, int nkeys,
                                                                int target, void* ws,
@@ -747,33 +757,9 @@ __global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* _
     const int i = threadIdx.x + u * kResolveThreads;
     key[u] = i < nkeys ? src[i] : 0u;
   }
-  uint32_t prefix = 0, need = (uint32_t)target;
-  for (int level = 0; level < 2; ++level) {
-    const int shift = level == 0 ? 21 : 10;
-    const int bits = 11;
-    const int hi = shift + bits;   // bits at and above hi are fixed
-    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) {
-      const int i = threadIdx.x + u * kResolveThreads;
-      const bool in = i < nkeys && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
-      if (in) atomicAdd(&s_hist[(key[u] >> shift) & ((1u << bits) - 1u)], 1u);
-    }
-    __syncthreads();
-    constexpr int kPer = kBins / kResolveThreads;
-    uint32_t h[kPer];
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) {
-      const int bin = threadIdx.x * kPer + b;
-      h[b] = bin < (1 << bits) ? s_hist[bin] : 0u;
-    }
-    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    need = s_sel[1];
-    __syncthreads();
-  }
+  const uint32_t prefix = radix_cut(
+      key, [&](int u) { return (int)threadIdx.x + u * kResolveThreads < nkeys; },
+      (uint32_t)target, s_hist, s_tmp, s_sel);
   if (threadIdx.x == 0) {
     r.st[kS_TAU] = prefix;
     r.st[kS_OVER] = 0u;
