@@ -37,9 +37,6 @@ int64_t scan_max_workgroups(int64_t groups, int64_t n);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
 // Pieces of fathom_scan_topk's selection (workspace layout: topk::FusedWs).
-hipError_t launch_fused_guess(const uint32_t* sample, int64_t rows, int64_t n, int64_t R,
-                              int nkeys, int target, void* ws, uint32_t* gflag, int G,
-                              hipStream_t stream);
 hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                 int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
                                 hipStream_t stream);

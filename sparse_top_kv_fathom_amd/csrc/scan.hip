@@ -67,6 +67,7 @@
 
 #include "fathom_internal.h"
 #include "topk_layout.h"
+#include "topk_select.h"
 
 // Compile-time tuning: SCAN_U1 = depth-1 channels per pipelined set,
 // SCAN_ROUNDS = rounds per workgroup, SCAN_TOUCHES = L2 touches per 256-byte
@@ -284,6 +285,89 @@ constexpr int kTileKeys = kNB * kBlock;
 constexpr int64_t kFusedMinKeys = 65536;   // shorter rows: scan, then top-k
 constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stages
 constexpr int kRescanRounds = 8;           // rounds per workgroup of the gated second pass
+constexpr int kSampleRuns = 8;             // sampled runs of two wave tiles per group
+constexpr int kSampleKeys = 2 * kSampleRuns * kTileKeys;   // 8192 per row
+constexpr int kCutSpin = 1 << 14;          // polls of a cut that is not yet published
+
+// The cut of fathom_scan_topk.  The candidate scan's first workgroups (one
+// per row, ids [0, rows) of its grid, the count rounded up to a multiple of
+// the XCD count so that the scan's own ids keep their XCD) take tau from the
+// row's sample, as the target-th largest sampled order key with its low 10
+// bits cleared (two 11-bit radix digits), store it for the selection, and
+// publish tau | 1 in the row's ready word with an agent-scope atomic store.
+// The word carries the whole message, so no fence is needed (a device-scope
+// release would write back the L2).  Scan waves read the word (agent-scope
+// atomic loads) once their scores are nearly done and poll it, boundedly,
+// only if the cut is not out yet; a row whose cut is still missing after
+// kCutSpin polls emits nothing and is flagged, so its selection falls back
+// to the second pass.
+struct CutArgs {
+  const uint32_t* sample;   // [rows][kMaxSampleKeys] sampled order keys
+  int target;               // rank of tau among the row's kSampleKeys keys
+  int rows;                 // rows to cut; 0 outside the candidate scan
+};
+
+__host__ __device__ inline uint32_t cut_workgroups(int rows) {
+  return (uint32_t)((rows + kXcds - 1) / kXcds * kXcds);
+}
+
+template <int NT>
+__device__ void cut_row(const CutArgs& cut, int row, int64_t n, void* tws, uint32_t* smem) {
+  constexpr int kPieces = kSampleKeys / (4 * NT);
+  static_assert(kPieces * 4 * NT == kSampleKeys, "whole 16-byte pieces per thread");
+  const uint4* src =
+      reinterpret_cast<const uint4*>(cut.sample + (int64_t)row * topk::kMaxSampleKeys);
+  // The thread's keys are read again for each digit (they stay in L2), so
+  // that the cut holds no key registers: the kernel's register count is set
+  // by the scan.
+  const uint32_t tau = topk::radix_cut<NT>(
+      [&](auto&& f) {
+#pragma unroll 2
+        for (int u = 0; u < kPieces; ++u) {
+          const uint4 v = src[u * NT + threadIdx.x];
+          f(v.x);
+          f(v.y);
+          f(v.z);
+          f(v.w);
+        }
+      },
+      (uint32_t)cut.target, smem, smem + topk::kBins, smem + topk::kBins + NT / 64);
+  if (threadIdx.x == 0) {
+    uint32_t* st = topk::row_ws(tws, n, kTileKeys, row).st;
+    st[topk::kS_TAU] = tau;
+    __hip_atomic_store(st + topk::kS_READY, tau | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Lane h < G: the ready word of row (group, h).
+template <int G>
+__device__ __forceinline__ uint32_t cut_word(void* tws, int64_t n, int64_t grp) {
+  const int lane = lane_id();
+  if (lane >= G) return 1u;
+  uint32_t* p = topk::row_ws(tws, n, kTileKeys, grp * G + lane).st + topk::kS_READY;
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The G cuts as floats from the ready words (polled while one is missing);
+// a cut still missing gives NaN (no score is >= it) and flags its row.
+template <int G>
+__device__ __forceinline__ void cut_floats(void* tws, int64_t n, int64_t grp, uint32_t w,
+                                           float (&tf)[G]) {
+  for (int it = 0; it < kCutSpin && __ballot((w & 1u) == 0u) != 0ull; ++it) {
+    __builtin_amdgcn_s_sleep(8);
+    w = cut_word<G>(tws, n, grp);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)w, h);
+    if (v & 1u) {
+      tf[h] = topk::key_float(v & ~1u);
+    } else {
+      tf[h] = __builtin_nanf("");
+      if (lane_id() == 0) atomicOr(&topk::row_ws(tws, n, kTileKeys, grp * G + h).st[topk::kS_OVER], 1u);
+    }
+  }
+}
 
 template <int G>
 __device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float (&tf)[G],
@@ -540,27 +624,29 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t nrounds, int64_t n,
     int64_t wgs_per_group, float* __restrict__ scores, void* tws,
-    const uint32_t* __restrict__ gate) {
+    const uint32_t* __restrict__ gate, CutArgs cut) {
   static_assert(kNB * G <= 64, "one lane per (block, head) in the offset fold");
   static_assert(MODE != 1 || NR == 1, "candidate emission runs one round per workgroup");
+  static_assert(sizeof(MainShared<G>) >= (topk::kBins + kThreads / 64 + 2) * 4, "cut scratch");
   __shared__ MainShared<G> sh;
   __shared__ float s_o[kWaves][kNB * G];
 
-  // XCD-aware remap of the workgroup id (bijective on [0, gridDim.x)).
-  const uint32_t nwg = gridDim.x;
+  // MODE 1: the first workgroups take the rows' cuts.
+  const uint32_t ncut = MODE == 1 ? cut_workgroups(cut.rows) : 0u;
+  if (MODE == 1 && blockIdx.x < ncut) {   // uniform over the workgroup
+    if ((int)blockIdx.x < cut.rows)
+      cut_row<kThreads>(cut, (int)blockIdx.x, n, tws, reinterpret_cast<uint32_t*>(&sh));
+    return;
+  }
+  // XCD-aware remap of the scan's workgroup ids (bijective on [0, nwg)).
+  const uint32_t nwg = gridDim.x - ncut;
   const uint32_t per_xcd = nwg / kXcds;
-  uint32_t id = blockIdx.x;
+  uint32_t id = blockIdx.x - ncut;
   if (id < per_xcd * kXcds) id = (id % kXcds) * per_xcd + id / kXcds;
   const int64_t grp = id / wgs_per_group;
   if (gate != nullptr && gate[grp] == 0u) return;   // uniform over the workgroup
   const int64_t round0 = (id % wgs_per_group) * NR;
   const int nr = NR > 1 ? (int)min<int64_t>(NR, nrounds - round0) : 1;
-  float tf[G];   // MODE 1: the rows' cuts as floats
-  if (MODE == 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      tf[h] = topk::key_float(topk::row_ws(tws, n, kTileKeys, grp * G + h).st[topk::kS_TAU]);
-  }
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -675,11 +761,19 @@ __global__ __launch_bounds__(kThreads) void scan_main(
       asm volatile("" : "+v"(sink));
     }
     main_depth<2, G, true>(c, sh.tb, rc[0] + rc[1], rc[2], ChanIter{rm.lo[2], rm.hi[2]}, acc, o);
+    // MODE 1: the ready words of the group's cuts, read here so that they
+    // have arrived (and the cuts are out) by the time the tile is emitted.
+    uint32_t cw = 1u;
+    if (MODE == 1) cw = cut_word<G>(tws, n, grp);
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
     finish_tile<G>(acc, o, kNB - 1, n, scores_g != nullptr ? scores_g + blk0 * kBlock : nullptr,
                    s_o[wave]);
-    if (MODE == 1) emit_tile<G>(acc, tf, grp, blk0, n, tws);
+    if (MODE == 1) {
+      float tf[G];
+      cut_floats<G>(tws, n, grp, cw, tf);
+      emit_tile<G>(acc, tf, grp, blk0, n, tws);
+    }
 
     if (r + 1 < nr) {
       __syncthreads();   // every wave is done with this round's scales
@@ -837,11 +931,11 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
       hipExtLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, ev_start,
                             first < nblk ? nullptr : ev_stop, 0u, planes, scales, nb_store,
                             depths, q, nrounds, n, wgs, scores, (void*)nullptr,
-                            (const uint32_t*)nullptr);
+                            (const uint32_t*)nullptr, CutArgs{});
     else
       hipLaunchKernelGGL((scan_main<G, 0>), grid, block, 0, stream, planes, scales, nb_store,
                          depths, q, nrounds, n, wgs, scores, (void*)nullptr,
-                         (const uint32_t*)nullptr);
+                         (const uint32_t*)nullptr, CutArgs{});
   }
   if (first < nblk) {
     const dim3 grid((unsigned)((nblk - first + kNB - 1) / kNB), (unsigned)groups),
@@ -864,26 +958,26 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
 // particular order (only the cut tau is taken from them; the candidates are
 // then scored by the scan itself), written as order keys to
 // sample[group * G + h][i * kTileKeys + token] for sampled tile i.  One
-// workgroup per sampled tile: a first round of loads brings the depths, the
-// tile's block scales and the group's queries, a second the plane rows the
-// plan reads (row (j, p) with p < t_j, 64 bytes for the tile's 8 blocks), all
-// into LDS.  Then waves 2b and 2b + 1 score block b over the active channels
-// of [0, 64) and [64, 128) (one ballot mask per depth, so that each channel
-// reads its t_j planes and no more), and add their two partial sums.
-constexpr int kSampleRuns = 8;   // runs of two wave tiles per group (8192 keys)
+// workgroup per sampled tile: one round of loads brings the depths, the
+// tile's block scales, the group's queries and every plane row of the tile
+// (512 rows of 64 bytes for its 8 blocks, the rows past a channel's depth
+// included, so that no load waits for the plan), all into LDS.  Then waves
+// 2b and 2b + 1 score block b over the active channels of [0, 64) and
+// [64, 128) (one ballot mask per depth, so that each channel reads its t_j
+// planes and no more), and add their two partial sums.
 constexpr int kSampleThreads = 2 * kNB * 64;
-static_assert(2 * kSampleRuns * kTileKeys <= topk::kMaxSampleKeys, "sample buffer");
+static_assert(kSampleKeys <= topk::kMaxSampleKeys, "sample buffer");
 
 // The sample's channels of depth T (mask m over the wave's half of the
 // channels) for lane `bit` of half `hsel` of block `b`, four at a time: the
-// LDS reads (T plane words and the scale) and scalar reads (the G weights) of
-// the four are issued together, then their arithmetic.  A slot past the end
-// of the mask reads the half's first channel and adds 0.
+// LDS reads (T plane words, the scale and the G query entries) of the four
+// are issued together, then their arithmetic.  A slot past the end of the
+// mask reads the half's first channel and adds 0.
 template <int T, int G>
 __device__ __forceinline__ void sample_depth(const uint64_t (*s_w)[kNB],
-                                             const uint16_t (*s_sc)[kNB],
-                                             const float* __restrict__ qg, uint64_t m, int half,
-                                             int b, int hsel, int bit, float (&acc)[G]) {
+                                             const uint16_t (*s_sc)[kNB], const float (*s_q)[G],
+                                             uint64_t m, int half, int b, int hsel, int bit,
+                                             float (&acc)[G]) {
   while (m != 0ull) {
     int c[4];
     bool ok[4];
@@ -904,7 +998,7 @@ __device__ __forceinline__ void sample_depth(const uint64_t (*s_w)[kNB],
       for (int p = 0; p < T; ++p) w[u][p] = wp[p * 2 * kNB];
       a[u] = half_lo(s_sc[c[u]][b]);
 #pragma unroll
-      for (int h = 0; h < G; ++h) qv[u][h] = qg[h * kD + c[u]];   // uniform: scalar loads
+      for (int h = 0; h < G; ++h) qv[u][h] = s_q[c[u]][h];   // uniform address: broadcast
     }
     __builtin_amdgcn_sched_barrier(0);   // every read above is issued before the arithmetic
 #pragma unroll
@@ -925,25 +1019,26 @@ template <int G>
 __global__ __launch_bounds__(kSampleThreads) void fused_sample(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t run_stride,
-    uint32_t* __restrict__ sample) {
+    uint32_t* __restrict__ sample, void* tws, int64_t n, uint32_t* __restrict__ gflag) {
   constexpr int kT = kSampleThreads;                   // 1024 threads, two waves per block
   static_assert(kD * kPlanes * 4 == 2 * kT, "two 16-byte pieces per thread");
+  static_assert(G * kD <= kT, "one query entry per thread");
   __shared__ uint64_t s_w[kD * kPlanes][kNB];          // 32 KB: row (channel, plane), block
   __shared__ uint16_t s_sc[kD][kNB];
+  __shared__ float s_q[kD][G];
   __shared__ float s_part[kNB][G][kBlock];
   const int64_t grp = blockIdx.y, ti = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = wv >> 1, half = wv & 1;                // block, channel half
   const int64_t blk0 = ((ti >> 1) * run_stride + (ti & 1)) * kNB;
-  const uint8_t* dg = depths + grp * kD;
-  const float* qg = q + grp * G * kD;
-  // First round of loads: this lane's channel for the compute phase, the
-  // channels of the thread's two pieces (piece tid + 1024 i: row
-  // (tid + 1024 i) / 4, i.e. channel 64 i + tid / 16, plane (tid / 4) % 4),
-  // and the block scales.
-  const int tl = min((int)dg[64 * half + lane], kPlanes);
-  const int tp0 = dg[tid >> 4], tp1 = dg[64 + (tid >> 4)];
+  // One round of loads: this lane's channel depth for the compute phase, the
+  // block scales, one query entry per thread, and the thread's two 16-byte
+  // pieces of plane rows (piece tid + 1024 i: row (tid + 1024 i) / 4, i.e.
+  // channel 64 i + tid / 16, plane (tid / 4) % 4, blocks 2 (tid % 4) and
+  // 2 (tid % 4) + 1).
+  const int tl = min((int)depths[grp * kD + 64 * half + lane], kPlanes);
+  const float qv = tid < G * kD ? q[grp * G * kD + tid] : 0.0f;
   // 16-byte loads when the store's rows allow them, else 8- and 2-byte ones.
   const bool vec = (nb_store & 7) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
@@ -959,14 +1054,10 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
       sv = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
-  // Second round: the plane rows the plan reads.  A thread whose row is past
-  // its channel's depth loads the group's first row instead (a line every
-  // workgroup of the group reads anyway) and its LDS copy is never read.
   const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 + 2 * (tid & 3);
-  const int pl = (tid >> 2) & (kPlanes - 1);
   const int r0 = tid >> 2, r1 = (tid + kT) >> 2;
-  const uint64_t* a0 = pg + (pl < tp0 ? (int64_t)r0 * nb_store : 0);
-  const uint64_t* a1 = pg + (pl < tp1 ? (int64_t)r1 * nb_store : 0);
+  const uint64_t* a0 = pg + (int64_t)r0 * nb_store;
+  const uint64_t* a1 = pg + (int64_t)r1 * nb_store;
   uint4 v0, v1;
   if (vec) {
     v0 = *reinterpret_cast<const uint4*>(a0);
@@ -976,6 +1067,15 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
     v0 = make_uint4((uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)y0, (uint32_t)(y0 >> 32));
     v1 = make_uint4((uint32_t)x1, (uint32_t)(x1 >> 32), (uint32_t)y1, (uint32_t)(y1 >> 32));
   }
+  // The group's selection state starts clear: flags, published cuts.
+  if (ti == 0 && tid < G) {
+    uint32_t* st = topk::row_ws(tws, n, kTileKeys, grp * G + tid).st;
+    st[topk::kS_OVER] = 0u;
+    st[topk::kS_FAIL] = 0u;
+    st[topk::kS_READY] = 0u;
+  }
+  if (ti == 0 && tid == 0) gflag[grp] = 0u;
+  if (tid < G * kD) s_q[tid % kD][tid / kD] = qv;
   if (tid < kD) *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
   *reinterpret_cast<uint4*>(&s_w[r0][2 * (tid & 3)]) = v0;
   *reinterpret_cast<uint4*>(&s_w[r1][2 * (tid & 3)]) = v1;
@@ -984,10 +1084,10 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
   float acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-  sample_depth<4, G>(s_w, s_sc, qg, __ballot(tl == 4), half, b, hsel, bit, acc);
-  sample_depth<3, G>(s_w, s_sc, qg, __ballot(tl == 3), half, b, hsel, bit, acc);
-  sample_depth<2, G>(s_w, s_sc, qg, __ballot(tl == 2), half, b, hsel, bit, acc);
-  sample_depth<1, G>(s_w, s_sc, qg, __ballot(tl == 1), half, b, hsel, bit, acc);
+  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), half, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), half, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), half, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), half, b, hsel, bit, acc);
   if (half == 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
@@ -1030,24 +1130,22 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
   const int64_t ntiles = nblk / kNB, rstride = ntiles / kSampleRuns;   // >= 16 tiles
   hipLaunchKernelGGL((fused_sample<G>), dim3(2 * kSampleRuns, (unsigned)groups),
                      dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, rstride,
-                     fw.sample);
+                     fw.sample, fw.rows, n, fw.gflag);
   // The cut leaves about 1.6x the sample's share of k (plus 16 sampled keys)
   // at or above it, so that fewer than k candidates is rare.
-  const int nkeys = 2 * kSampleRuns * kTileKeys;
-  const double share = (double)k * (double)nkeys / (double)n;
-  const int target = (int)std::min<double>((double)nkeys, std::ceil(1.6 * share + 16.0));
-  hipError_t e = launch_fused_guess(fw.sample, rows, n, R, nkeys, target, fw.rows, fw.gflag, G,
-                                    stream);
-  if (e != hipSuccess) return e;
-  // The scan (MODE 1: with candidates; MODE 2, gated: the second pass).
+  const double share = (double)k * (double)kSampleKeys / (double)n;
+  const int target = (int)std::min<double>((double)kSampleKeys, std::ceil(1.6 * share + 16.0));
+  // The scan (MODE 1: with candidates, the cuts taken by its first
+  // workgroups; MODE 2, gated: the second pass).
   auto scan = [&](auto mode, float* out, const uint32_t* gate) {
     constexpr int M = decltype(mode)::value;
     constexpr int NR = M == 2 ? kRescanRounds : 1;
     void* tws = M == 1 ? fw.rows : nullptr;
+    const CutArgs cut = M == 1 ? CutArgs{fw.sample, target, (int)rows} : CutArgs{};
     const int64_t wgs = (nrounds + NR - 1) / NR;
-    hipLaunchKernelGGL((scan_main<G, M, NR>), dim3((unsigned)(wgs * groups)), dim3(kThreads), 0,
-                       stream, planes, scales, nb_store, depths, q, nrounds, n, wgs, out, tws,
-                       gate);
+    const unsigned grid = (unsigned)(wgs * groups) + (M == 1 ? cut_workgroups((int)rows) : 0u);
+    hipLaunchKernelGGL((scan_main<G, M, NR>), dim3(grid), dim3(kThreads), 0, stream, planes,
+                       scales, nb_store, depths, q, nrounds, n, wgs, out, tws, gate, cut);
     if (first < nblk)
       hipLaunchKernelGGL((scan_tail<G, M>), dim3((unsigned)((nblk - first + kNB - 1) / kNB),
                                                  (unsigned)groups),
@@ -1055,7 +1153,7 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
                          nblk, n, out, tws, gate);
   };
   scan(std::integral_constant<int, 1>(), scores, nullptr);
-  e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
+  hipError_t e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
   if (e != hipSuccess || scores != nullptr) return e;
   scan(std::integral_constant<int, 2>(), fw.scores, fw.gflag);
   return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, stream);

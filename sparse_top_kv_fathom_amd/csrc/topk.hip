@@ -30,6 +30,7 @@
 
 #include "fathom_internal.h"
 #include "topk_layout.h"
+#include "topk_select.h"
 
 namespace fathom {
 
@@ -106,41 +107,6 @@ __device__ __forceinline__ void load_vals(const float* __restrict__ src, int64_t
   }
 }
 
-// Inclusive prefix sum over the wave with DPP moves: shifts by 1, 2, 4 and 8
-// lanes inside each row of 16 (lanes shifted in from outside the row read 0),
-// then the last lane of row 0 added to row 1 and of row 2 to row 3
-// (row_bcast:15), then lane 31 added to rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  v = v + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return v;
-}
-
-// Exclusive prefix over the NT threads of a workgroup; the total through
-// `total`.
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* s_tmp,
-                                                        uint32_t& total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_sum(v);
-  if (lane == 63) s_tmp[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const uint32_t x = s_tmp[w];
-    before += (w < wave) ? x : 0u;
-    tot += x;
-  }
-  __syncthreads();
-  total = tot;
-  return before + inc - v;
-}
-
 // Exclusive prefix of cnt[0, m) in place, over the workgroup (m <= kGroups).
 template <int NT>
 __device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint32_t* s_tmp) {
@@ -155,67 +121,6 @@ __device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint3
     cnt[g] = run;
     run += v;
   }
-}
-
-// Find, over bins held kPer per thread (highest bin last), the bin that
-// holds the need-th largest key; thread-local h[] are the thread's bins.
-// Writes (bin, need within the bin) to sel[] from the one thread that owns it.
-template <int NT, int kPer>
-__device__ __forceinline__ void pick_bin(const uint32_t (&h)[kPer], uint32_t need, uint32_t* s_tmp,
-                                         uint32_t* sel) {
-  uint32_t mine = 0;
-#pragma unroll
-  for (int b = 0; b < kPer; ++b) mine += h[b];
-  uint32_t total;
-  const uint32_t before = block_exclusive_sum<NT>(mine, s_tmp, total);
-  const uint32_t above = total - before - mine;   // keys in higher bins
-  if (above < need && need <= above + mine) {
-    uint32_t acc = above;
-#pragma unroll
-    for (int b = kPer - 1; b >= 0; --b) {
-      if (acc + h[b] >= need) {
-        sel[0] = (uint32_t)(threadIdx.x * kPer + b);
-        sel[1] = need - acc;
-        break;
-      }
-      acc += h[b];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-
-// The need-th largest of the workgroup's keys (PER per thread; key u of a
-// thread counts when valid(u)) with its low 10 bits cleared: two radix
-// digits of 11 bits over an LDS histogram.  The result is at most 2^-13 of
-// the score below that key, never above it.
-template <int PER, class V>
-__device__ __forceinline__ uint32_t radix_cut(const uint32_t (&key)[PER], V&& valid,
-                                              uint32_t need, uint32_t* s_hist, uint32_t* s_tmp,
-                                              uint32_t* s_sel) {
-  uint32_t prefix = 0;
-  for (int level = 0; level < 2; ++level) {
-    const int shift = level == 0 ? 21 : 10;
-    const int hi = shift + 11;   // bits at and above hi are fixed
-    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const bool in = valid(u) && (hi >= 32 || (key[u] >> (hi & 31)) == (prefix >> (hi & 31)));
-      if (in) atomicAdd(&s_hist[(key[u] >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    constexpr int kPer = kBins / kResolveThreads;
-    uint32_t h[kPer];
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
-    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    need = s_sel[1];
-    __syncthreads();
-  }
-  return prefix;
 }
 
 // Per row: the cut tau from a sample of the row, in one workgroup: 16 runs of
@@ -272,9 +177,13 @@ __global__ __launch_bounds__(kResolveThreads) void topk_cut(const float* __restr
     need = (uint32_t)min<double>((double)nkeys, ceil(1.6 * share + 16.0));
   }
   // Only a whole-row sample has slots past the row's end to skip.
-  const uint32_t prefix = radix_cut(
-      key, [&](int u) { return !whole || tid + (int64_t)u * kResolveThreads < n; }, need, s_hist,
-      s_tmp, s_sel);
+  const uint32_t prefix = radix_cut<kResolveThreads>(
+      [&](auto&& f) {
+#pragma unroll
+        for (int u = 0; u < kCutPer; ++u)
+          if (!whole || tid + (int64_t)u * kResolveThreads < n) f(key[u]);
+      },
+      need, s_hist, s_tmp, s_sel);
   if (tid == 0) {
     r.st[kS_TAU] = prefix;
     r.st[kS_OVER] = 0u;
@@ -736,49 +645,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
 }
 
-// The cut of fathom_scan_topk, from its sample: tau = radix_cut of the row's
-// nkeys sampled order keys at the target-th largest, so that about
-// target * n / nkeys keys of the row are at or above it.  Also clears the
-// row's flags and its group's.
-__global__ __launch_bounds__(kResolveThreads) void fused_guess(const uint32_t* __restrict__ sample,
-                                                               int64_t n, int64_t R, int nkeys,
-                                                               int target, void* ws,
-                                                               uint32_t* gflag, int G) {
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_tmp[kResolveThreads / 64];
-  __shared__ uint32_t s_sel[2];
-  constexpr int kPerT = kMaxSampleKeys / kResolveThreads;
-  const int64_t row = blockIdx.x;
-  RowWs r = row_ws(ws, n, R, row);
-  const uint32_t* src = sample + row * (int64_t)kMaxSampleKeys;
-  uint32_t key[kPerT];
-#pragma unroll
-  for (int u = 0; u < kPerT; ++u) {
-    const int i = threadIdx.x + u * kResolveThreads;
-    key[u] = i < nkeys ? src[i] : 0u;
-  }
-  const uint32_t prefix = radix_cut(
-      key, [&](int u) { return (int)threadIdx.x + u * kResolveThreads < nkeys; },
-      (uint32_t)target, s_hist, s_tmp, s_sel);
-  if (threadIdx.x == 0) {
-    r.st[kS_TAU] = prefix;
-    r.st[kS_OVER] = 0u;
-    r.st[kS_FAIL] = 0u;
-    if (row % G == 0) gflag[row / G] = 0u;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_fused_guess(const uint32_t* sample, int64_t rows, int64_t n, int64_t R,
-                              int nkeys, int target, void* ws, uint32_t* gflag, int G,
-                              hipStream_t stream) {
-  if (nkeys < 1 || nkeys > kMaxSampleKeys || target < 1 || target > nkeys)
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(fused_guess, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, sample,
-                     n, R, nkeys, target, ws, gflag, G);
-  return hipGetLastError();
-}
 
 hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                 int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,

@@ -17,6 +17,7 @@ enum : int {
   kS_T,             // the k-th largest key (set by the resolve)
   kS_NEED,          // keys == T to take
   kS_FAIL,          // 1: fathom_scan_topk could not select from the candidates
+  kS_READY,         // fathom_scan_topk: tau | 1 once the cut is published, else 0
   kS_WORDS = 16
 };
 
