@@ -37,9 +37,11 @@ int64_t scan_max_workgroups(int64_t groups, int64_t n);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
 // Pieces of fathom_scan_topk's selection (workspace layout: topk::FusedWs).
+// Chunks [0, npacked) of a row come in runs of `pack` whose candidates are
+// packed from the run's first slot (1 and 0: every chunk on its own).
 hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                 int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
-                                hipStream_t stream);
+                                int pack, int64_t npacked, hipStream_t stream);
 size_t scan_topk_workspace_bytes(int64_t groups, int G, int64_t n, int k);
 hipError_t launch_scan_topk(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                             const uint8_t* depths, const float* q, int64_t groups, int G,

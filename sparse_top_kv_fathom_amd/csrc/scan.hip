@@ -275,12 +275,12 @@ __device__ __forceinline__ void finish_tile(float (&acc)[kNB][G], float o, int s
   }
 }
 
-// Candidate emission of fathom_scan_topk.  Every wave tile (kNB blocks =
-// kTileKeys keys of a row) is one region of the row's candidate buffer: the
-// wave writes each score >= tau of head h, as (order key, index) in index
-// order, to region `tile` of row (group, h), and the region's count to the
-// segment table; no other wave takes part, so there is no barrier.  A tile
-// with more candidates than its region holds flags the row.
+// Candidates of fathom_scan_topk.  Each wave tile (kNB blocks = kTileKeys
+// keys of a row) owns `region` slots of the row's candidate buffer, at slot
+// tile * region; the main kernel pools the slots of a round's kWaves tiles
+// (emit_round), the tail kernel fills each tile's own.  The segment table
+// holds, per tile, the first slot of its candidates and their count; every
+// score >= tau of head h goes there as (order key, index), in index order.
 constexpr int kTileKeys = kNB * kBlock;
 constexpr int64_t kFusedMinKeys = 65536;   // shorter rows: scan, then top-k
 constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stages
@@ -369,35 +369,62 @@ __device__ __forceinline__ void cut_floats(void* tws, int64_t n, int64_t grp, ui
   }
 }
 
+// Candidate emission of the main kernel.  The workgroup's kWaves wave tiles
+// (its round of kRoundBlocks blocks) share one region of kWaves * region
+// slots per row: every wave counts its scores >= tau per head, the counts are
+// prefixed over the waves in LDS, and each wave writes its candidates, as
+// (order key, index) in index order, right after those of the waves before
+// it, so that the round's candidates lie packed and in index order at the
+// front of the region (the selection then copies a round's candidates in one
+// piece).  The segment table gets each tile's first slot and count; a round
+// with more candidates than its region holds flags the row.
 template <int G>
-__device__ __forceinline__ void emit_tile(const float (&sc)[kNB][G], const float (&tf)[G],
-                                          int64_t grp, int64_t blk0, int64_t n, void* tws,
-                                          int last = kNB - 1) {
+__device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const float (&tf)[G],
+                                           int64_t grp, int64_t blk0, int wave, int64_t n,
+                                           void* tws, uint32_t (*s_ecnt)[G]) {
   const int lane = lane_id();
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  const int64_t tile = blk0 / kNB;
+  const int64_t tile = blk0 / kNB;   // round * kWaves + wave
+  const int64_t round = tile / kWaves;
+  uint32_t cnt[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) c += (uint32_t)__popcll(__ballot(sc[b][h] >= tf[h]));
+    cnt[h] = c;
+    if (lane == 0) s_ecnt[wave][h] = c;
+  }
+  __syncthreads();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const topk::RowWs rw = topk::row_ws(tws, n, kTileKeys, grp * G + h);
-    const uint32_t base = (uint32_t)tile * rw.region;
-    uint32_t cnt = 0;
+    const uint32_t cap = kWaves * rw.region;
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t x = s_ecnt[w][h];
+      before += w < wave ? x : 0u;
+      total += x;
+    }
+    const uint32_t start = (uint32_t)round * cap;
+    uint32_t at = before;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
-      if (b > last) break;   // past the row's end (a partial last tile)
       const bool cand = sc[b][h] >= tf[h];
       const uint64_t m = __ballot(cand);
       if (m != 0ull) {
-        const uint32_t sl = cnt + (uint32_t)__popcll(m & below);
-        if (cand && sl < rw.region)
-          reinterpret_cast<uint2*>(rw.cand)[base + sl] =
+        const uint32_t sl = at + (uint32_t)__popcll(m & below);
+        if (cand && sl < cap)
+          reinterpret_cast<uint2*>(rw.cand)[start + sl] =
               make_uint2(topk::order_key(sc[b][h]), (uint32_t)((blk0 + b) * kBlock + lane));
-        cnt += (uint32_t)__popcll(m);
+        at += (uint32_t)__popcll(m);
       }
     }
     if (lane == 0) {
-      rw.seg[2 * tile] = base;
-      rw.seg[2 * tile + 1] = cnt;
-      if (cnt > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
+      rw.seg[2 * tile] = start + before;
+      rw.seg[2 * tile + 1] = cnt[h];
+      if (wave == 0 && total > cap) atomicOr(&rw.st[topk::kS_OVER], 1u);
     }
   }
 }
@@ -630,6 +657,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   static_assert(sizeof(MainShared<G>) >= (topk::kBins + kThreads / 64 + 2) * 4, "cut scratch");
   __shared__ MainShared<G> sh;
   __shared__ float s_o[kWaves][kNB * G];
+  __shared__ uint32_t s_ecnt[MODE == 1 ? kWaves : 1][G];   // MODE 1: candidates per wave
 
   // MODE 1: the first workgroups take the rows' cuts.
   const uint32_t ncut = MODE == 1 ? cut_workgroups(cut.rows) : 0u;
@@ -772,7 +800,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     if (MODE == 1) {
       float tf[G];
       cut_floats<G>(tws, n, grp, cw, tf);
-      emit_tile<G>(acc, tf, grp, blk0, n, tws);
+      emit_round<G>(acc, tf, grp, blk0, wave, n, tws, s_ecnt);
     }
 
     if (r + 1 < nr) {
@@ -958,44 +986,48 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
 // particular order (only the cut tau is taken from them; the candidates are
 // then scored by the scan itself), written as order keys to
 // sample[group * G + h][i * kTileKeys + token] for sampled tile i.  One
-// workgroup per sampled tile: one round of loads brings the depths, the
-// tile's block scales, the group's queries and every plane row of the tile
-// (512 rows of 64 bytes for its 8 blocks, the rows past a channel's depth
-// included, so that no load waits for the plan), all into LDS.  Then waves
-// 2b and 2b + 1 score block b over the active channels of [0, 64) and
-// [64, 128) (one ballot mask per depth, so that each channel reads its t_j
-// planes and no more), and add their two partial sums.
-constexpr int kSampleThreads = 2 * kNB * 64;
+// workgroup per half tile (kSampleBlocks blocks), so that the sample covers
+// every CU: one round of loads brings the depths, the blocks' scales, the
+// group's queries and every plane row of the blocks (512 rows of 32 bytes,
+// the rows past a channel's depth included, so that no load waits for the
+// plan), all into LDS.  Then the four waves of block b score it over the
+// active channels of one quarter [32 k, 32 k + 32) each (one ballot mask per
+// depth, so that each channel reads its t_j planes and no more), and the
+// first adds the other three's partial sums.
+constexpr int kSampleBlocks = kNB / 2;                   // blocks per workgroup
+constexpr int kSampleQuarters = 4;                       // waves per block
+constexpr int kSampleThreads = kSampleBlocks * kSampleQuarters * 64;
 static_assert(kSampleKeys <= topk::kMaxSampleKeys, "sample buffer");
+static_assert(kD == 32 * kSampleQuarters, "32 channels per wave");
 
-// The sample's channels of depth T (mask m over the wave's half of the
-// channels) for lane `bit` of half `hsel` of block `b`, four at a time: the
-// LDS reads (T plane words, the scale and the G query entries) of the four
-// are issued together, then their arithmetic.  A slot past the end of the
-// mask reads the half's first channel and adds 0.
+// The sample's channels of depth T (mask m over the wave's quarter of the
+// channels, lanes 0-31) for lane `bit` of half `hsel` of block `b`, four at a
+// time: the LDS reads of the four (the lane's T plane words in one read, the
+// scale, the G query entries in one read) are issued together, then their
+// arithmetic.  A slot past the end of the mask reads the quarter's first
+// channel and adds 0.
 template <int T, int G>
-__device__ __forceinline__ void sample_depth(const uint64_t (*s_w)[kNB],
-                                             const uint16_t (*s_sc)[kNB], const float (*s_q)[G],
-                                             uint64_t m, int half, int b, int hsel, int bit,
-                                             float (&acc)[G]) {
+__device__ __forceinline__ void sample_depth(const uint4 (*s_w)[kSampleBlocks][2],
+                                             const uint16_t (*s_sc)[kSampleBlocks],
+                                             const float (*s_q)[G], uint64_t m, int c0, int b,
+                                             int hsel, int bit, float (&acc)[G]) {
   while (m != 0ull) {
     int c[4];
     bool ok[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ok[u] = m != 0ull;
-      c[u] = 64 * half + (ok[u] ? __builtin_ctzll(m) : 0);
+      c[u] = c0 + (ok[u] ? __builtin_ctzll(m) : 0);
       m &= m - 1;   // stays 0 once empty
     }
     uint32_t w[4][T];
     float a[4], qv[4][G];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      // Plane p of channel c is row 4c + p; the lane's word is word hsel of
-      // the row's block b.
-      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[c[u] * kPlanes][b]) + hsel;
+      // Word hsel of planes 0-3 of channel c, block b.
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[c[u]][b][hsel]);
 #pragma unroll
-      for (int p = 0; p < T; ++p) w[u][p] = wp[p * 2 * kNB];
+      for (int p = 0; p < T; ++p) w[u][p] = wp[p];
       a[u] = half_lo(s_sc[c[u]][b]);
 #pragma unroll
       for (int h = 0; h < G; ++h) qv[u][h] = s_q[c[u]][h];   // uniform address: broadcast
@@ -1020,84 +1052,91 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
     const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
     const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t run_stride,
     uint32_t* __restrict__ sample, void* tws, int64_t n, uint32_t* __restrict__ gflag) {
-  constexpr int kT = kSampleThreads;                   // 1024 threads, two waves per block
-  static_assert(kD * kPlanes * 4 == 2 * kT, "two 16-byte pieces per thread");
+  constexpr int kT = kSampleThreads;                   // 1024 threads, four waves per block
+  constexpr int kSB = kSampleBlocks;
+  static_assert(kD * kPlanes * 2 == kT, "one 16-byte piece (two blocks of a row) per thread");
   static_assert(G * kD <= kT, "one query entry per thread");
-  __shared__ uint64_t s_w[kD * kPlanes][kNB];          // 32 KB: row (channel, plane), block
-  __shared__ uint16_t s_sc[kD][kNB];
-  __shared__ float s_q[kD][G];
-  __shared__ float s_part[kNB][G][kBlock];
-  const int64_t grp = blockIdx.y, ti = blockIdx.x;
+  // 16 KB: for channel c, block b and 32-token half hs, the four plane words
+  // (planes 0-3) side by side, so that a lane reads its channel's planes at once.
+  __shared__ uint4 s_w[kD][kSB][2];
+  __shared__ uint16_t s_sc[kD][kSB];
+  __shared__ alignas(16) float s_q[kD][G];   // a channel's G entries in one read
+  __shared__ float s_part[kSB][kSampleQuarters - 1][G][kBlock];
+  const int64_t grp = blockIdx.y, hi = blockIdx.x;     // half tile hi: tile hi / 2
+  const int64_t ti = hi >> 1;
   const int tid = threadIdx.x, lane = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = wv >> 1, half = wv & 1;                // block, channel half
-  const int64_t blk0 = ((ti >> 1) * run_stride + (ti & 1)) * kNB;
-  // One round of loads: this lane's channel depth for the compute phase, the
-  // block scales, one query entry per thread, and the thread's two 16-byte
-  // pieces of plane rows (piece tid + 1024 i: row (tid + 1024 i) / 4, i.e.
-  // channel 64 i + tid / 16, plane (tid / 4) % 4, blocks 2 (tid % 4) and
-  // 2 (tid % 4) + 1).
-  const int tl = min((int)depths[grp * kD + 64 * half + lane], kPlanes);
+  const int b = wv / kSampleQuarters, qtr = wv % kSampleQuarters;   // block, channel quarter
+  const int64_t blk0 = ((ti >> 1) * run_stride + (ti & 1)) * kNB + (hi & 1) * kSB;
+  // One round of loads: this lane's channel depth for the compute phase
+  // (lanes 0-31: channel 32 qtr + lane), the block scales, one query entry
+  // per thread, and the thread's 16-byte piece of plane row tid / 2 (blocks
+  // 2 (tid % 2) and 2 (tid % 2) + 1).
+  const int tl = lane < 32 ? min((int)depths[grp * kD + 32 * qtr + lane], kPlanes) : 0;
   const float qv = tid < G * kD ? q[grp * G * kD + tid] : 0.0f;
   // 16-byte loads when the store's rows allow them, else 8- and 2-byte ones.
   const bool vec = (nb_store & 7) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
-  uint4 sv = make_uint4(0u, 0u, 0u, 0u);
+  uint2 sv = make_uint2(0u, 0u);
   if (tid < kD) {
     const uint16_t* sp = scales + (grp * kD + tid) * nb_store + blk0;
     if (vec) {
-      sv = *reinterpret_cast<const uint4*>(sp);
+      sv = *reinterpret_cast<const uint2*>(sp);
     } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = sp[2 * u] | ((uint32_t)sp[2 * u + 1] << 16);
-      sv = make_uint4(w[0], w[1], w[2], w[3]);
+      sv = make_uint2(sp[0] | ((uint32_t)sp[1] << 16), sp[2] | ((uint32_t)sp[3] << 16));
     }
   }
-  const uint64_t* pg = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 + 2 * (tid & 3);
-  const int r0 = tid >> 2, r1 = (tid + kT) >> 2;
-  const uint64_t* a0 = pg + (int64_t)r0 * nb_store;
-  const uint64_t* a1 = pg + (int64_t)r1 * nb_store;
-  uint4 v0, v1;
+  const int r = tid >> 1;
+  const uint64_t* a0 = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 +
+                       (int64_t)r * nb_store + 2 * (tid & 1);
+  uint4 v0;
   if (vec) {
     v0 = *reinterpret_cast<const uint4*>(a0);
-    v1 = *reinterpret_cast<const uint4*>(a1);
   } else {
-    const uint64_t x0 = a0[0], y0 = a0[1], x1 = a1[0], y1 = a1[1];
+    const uint64_t x0 = a0[0], y0 = a0[1];
     v0 = make_uint4((uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)y0, (uint32_t)(y0 >> 32));
-    v1 = make_uint4((uint32_t)x1, (uint32_t)(x1 >> 32), (uint32_t)y1, (uint32_t)(y1 >> 32));
   }
   // The group's selection state starts clear: flags, published cuts.
-  if (ti == 0 && tid < G) {
+  if (hi == 0 && tid < G) {
     uint32_t* st = topk::row_ws(tws, n, kTileKeys, grp * G + tid).st;
     st[topk::kS_OVER] = 0u;
     st[topk::kS_FAIL] = 0u;
     st[topk::kS_READY] = 0u;
   }
-  if (ti == 0 && tid == 0) gflag[grp] = 0u;
+  if (hi == 0 && tid == 0) gflag[grp] = 0u;
   if (tid < G * kD) s_q[tid % kD][tid / kD] = qv;
-  if (tid < kD) *reinterpret_cast<uint4*>(&s_sc[tid][0]) = sv;
-  *reinterpret_cast<uint4*>(&s_w[r0][2 * (tid & 3)]) = v0;
-  *reinterpret_cast<uint4*>(&s_w[r1][2 * (tid & 3)]) = v1;
+  if (tid < kD) *reinterpret_cast<uint2*>(&s_sc[tid][0]) = sv;
+  {
+    // Row r = (channel r / 4, plane r % 4), blocks 2 (tid % 2) and 2 (tid % 2) + 1.
+    uint32_t* w = reinterpret_cast<uint32_t*>(s_w[r >> 2][2 * (tid & 1)]) + (r & 3);
+    w[0] = v0.x;    // block 2 (tid % 2), half 0
+    w[4] = v0.y;    //                    half 1
+    w[8] = v0.z;    // next block, half 0
+    w[12] = v0.w;   //             half 1
+  }
   __syncthreads();
-  const int hsel = lane >> 5, bit = lane & 31;
+  const int hsel = lane >> 5, bit = lane & 31, c0 = 32 * qtr;
   float acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), half, b, hsel, bit, acc);
-  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), half, b, hsel, bit, acc);
-  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), half, b, hsel, bit, acc);
-  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), half, b, hsel, bit, acc);
-  if (half == 1) {
+  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), c0, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), c0, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), c0, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), c0, b, hsel, bit, acc);
+  if (qtr > 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
+    for (int h = 0; h < G; ++h) s_part[b][qtr - 1][h][lane] = acc[h];
   }
   __syncthreads();
-  if (half == 0) {
+  if (qtr == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      sample[(grp * G + h) * (int64_t)topk::kMaxSampleKeys + ti * kTileKeys + b * kBlock + lane] =
-          topk::order_key(acc[h] + s_part[b][h][lane]);
+    for (int h = 0; h < G; ++h) {
+      float v = acc[h];
+#pragma unroll
+      for (int k = 0; k < kSampleQuarters - 1; ++k) v += s_part[b][k][h][lane];
+      sample[(grp * G + h) * (int64_t)topk::kMaxSampleKeys + ti * kTileKeys +
+             ((hi & 1) * kSB + b) * kBlock + lane] = topk::order_key(v);
+    }
   }
 }
 
@@ -1128,7 +1167,7 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
     return launch_topk(sc, rows, n, k, indices, ws, stream);
   }
   const int64_t ntiles = nblk / kNB, rstride = ntiles / kSampleRuns;   // >= 16 tiles
-  hipLaunchKernelGGL((fused_sample<G>), dim3(2 * kSampleRuns, (unsigned)groups),
+  hipLaunchKernelGGL((fused_sample<G>), dim3(2 * 2 * kSampleRuns, (unsigned)groups),
                      dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, rstride,
                      fw.sample, fw.rows, n, fw.gflag);
   // The cut leaves about 1.6x the sample's share of k (plus 16 sampled keys)
@@ -1153,10 +1192,14 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
                          nblk, n, out, tws, gate);
   };
   scan(std::integral_constant<int, 1>(), scores, nullptr);
-  hipError_t e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G, stream);
+  // The main kernel packs each round's kWaves tiles (emit_round).
+  const int64_t npacked = kWaves * nrounds;
+  hipError_t e = launch_fused_resolve(scores, rows, n, R, k, indices, fw.rows, 0, fw.gflag, G,
+                                      kWaves, npacked, stream);
   if (e != hipSuccess || scores != nullptr) return e;
   scan(std::integral_constant<int, 2>(), fw.scores, fw.gflag);
-  return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, stream);
+  return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, kWaves,
+                              npacked, stream);
 }
 
 int64_t scan_max_workgroups(int64_t groups, int64_t n) {

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict
 // The keys the one-workgroup path selects among: the candidate regions, or
 // (direct mode) the row itself.
 struct ResolveSrc {
-  const uint2* cand;      // (key, index) pairs, region per chunk
+  const uint2* cand;      // (key, index) pairs; chunk c's at seg[2c], seg[2c + 1] of them
   const uint32_t* seg;
   const float* scores;
   int64_t n, nc, R;       // keys, regions and keys per region of the row
@@ -283,20 +283,21 @@ template <class F>
 __device__ __forceinline__ void for_each_key(const ResolveSrc s, F&& f) {
   constexpr int kU = 4;
   if (!s.direct) {
-    const int64_t slots = s.nc * s.region;
-    for (int64_t i0 = threadIdx.x; i0 < slots; i0 += kU * kResolveThreads) {
-      uint2 e[kU];
-      bool v[kU];
+    // Wave w takes chunks w, w + 16, ..., 64 candidates at a time.
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    for (int64_t c = wave; c < s.nc; c += kResolveThreads / 64) {
+      const uint32_t b = s.seg[2 * c], cnt = s.seg[2 * c + 1];
+      for (uint32_t o0 = lane; o0 < cnt; o0 += kU * 64) {
+        uint2 e[kU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int64_t i = i0 + u * kResolveThreads;
-        const int64_t c = i / s.region;
-        v[u] = i < slots && (uint32_t)(i - c * s.region) < s.seg[2 * c + 1];
-        e[u] = v[u] ? s.cand[i] : make_uint2(0u, 0u);
+        for (int u = 0; u < kU; ++u) {
+          const uint32_t o = o0 + u * 64;
+          e[u] = o < cnt ? s.cand[b + o] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+          if (o0 + u * 64 < cnt) f(e[u].x, e[u].y);
       }
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        if (v[u]) f(e[u].x, e[u].y);
     }
   } else {
     for (int64_t i0 = threadIdx.x; i0 < s.n; i0 += kU * kResolveThreads) {
@@ -348,12 +349,15 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
 // the scores, or, when there are none (fathom_scan_topk without a score
 // buffer), is flagged (kS_FAIL, and its group in gflag) for a second pass.
 // mode 1: the flagged rows only, from the scores.
+// pack > 1 (fathom_scan_topk): chunks [0, npacked) come in runs of `pack`
+// whose candidates lie packed in index order from the run's first slot (the
+// main scan kernel's rounds); the others each at their own first slot.
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
                                                                 int64_t n, int64_t R, int k,
                                                                 void* ws,
                                                                 int32_t* __restrict__ out,
                                                                 int mode, uint32_t* gflag,
-                                                                int G) {
+                                                                int G, int pack, int64_t npacked) {
   __shared__ uint32_t s_hist[2 * kBins];
   __shared__ uint32_t s_gt[kGroups];
   // Staged candidates: keys and indices.  The path that does not stage them
@@ -361,6 +365,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   __shared__ uint32_t s_key[kLdsCand], s_idx[kLdsCand];
   static_assert(kGroups <= kLdsCand, "s_eq aliases s_idx");
   uint32_t* const s_eq = s_idx;
+  // While staging: the first candidate slot of every chunk (s_hist is free).
+  static_assert(kGroups <= 2 * kBins, "s_base aliases s_hist");
+  uint32_t* const s_base = s_hist;
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
   const int64_t row = blockIdx.x;
@@ -384,9 +391,16 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   // candidate slots of the wave's chunks (w, w + 16, ...) are loaded at the
   // same time as the counts and the overflow flag, before either is known,
   // so staging them costs no second round trip to memory; slots past a
-  // chunk's count are never used.
+  // chunk's count are never used.  With packed runs (pack > 1) the same holds
+  // for the first 32 slots of each run among the wave's first kPreRuns runs
+  // (w, w + 16, ...: four runs of 16 lanes per load).
   const bool small = nc <= kGroups;
-  const bool pre = nc <= kW * kU;
+  const bool pre = pack == 1 && nc <= kW * kU;
+  const bool ppre = pack > 1;
+  constexpr int kPreRuns = 4 * kU;
+  const int64_t nrun = npacked / pack;
+  const uint32_t cap = (uint32_t)pack * src.region;   // slots of a run
+  auto pre_run = [&](int i) { return wave + (int64_t)kW * (4 * i + (lane >> 4)); };
   uint32_t ncand = 0;
   const int64_t per = (nc + kResolveThreads - 1) / kResolveThreads;
   const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
@@ -404,12 +418,33 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
                                              : make_uint2(0u, 0u);
       }
     }
+  } else if (ppre) {
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int64_t run = pre_run(i);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t o = (lane & 15) + 16 * h;
+        e[i][h] = (run < nrun && o < cap) ? src.cand[(uint32_t)run * cap + o] : make_uint2(0u, 0u);
+      }
+    }
   }
+  // Chunks past the packed runs (the scan's tail tiles, each at its own
+  // slots chunk * region): wave w < their number prefetches the first 64 of
+  // chunk npacked + w.
+  const int64_t ntail = nc - npacked;
+  const bool tpre = ppre && ntail <= kW;
+  uint2 et = make_uint2(0u, 0u);
+  if (tpre && wave < ntail && (uint32_t)lane < src.region)
+    et = src.cand[(uint32_t)(npacked + wave) * src.region + lane];
   {
     uint32_t mine = 0;
     for (int64_t c = c0; c < c1; ++c) {
       const uint32_t t = c == c0 ? first_count : r.seg[2 * c + 1];
-      if (small) s_gt[c] = t;
+      if (small) {
+        s_gt[c] = t;
+        s_base[c] = r.seg[2 * c];
+      }
       mine += t;
     }
     uint32_t tot;
@@ -433,6 +468,43 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;
   __syncthreads();
 
+  // Candidates of packed run `run`: first LDS slot and count.
+  auto run_span = [&](int64_t run, uint32_t& d) {
+    const int64_t ca = run * pack, cb = ca + pack;
+    d = s_gt[ca];
+    return (cb < nc ? s_gt[cb] : ncand) - d;
+  };
+  if (lds && ppre) {
+#pragma unroll
+    for (int i = 0; i < kU; ++i) {
+      const int64_t run = pre_run(i);
+      if (run < nrun) {
+        uint32_t d;
+        const uint32_t cnt = run_span(run, d);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t o = (lane & 15) + 16 * h;
+          if (o < cnt) {
+            s_key[d + o] = e[i][h].x;
+            s_idx[d + o] = e[i][h].y;
+          }
+        }
+      }
+    }
+  }
+  if (lds && tpre && wave < ntail) {
+    const int64_t c = npacked + wave;
+    const uint32_t d = s_gt[c], cnt = (c + 1 < nc ? s_gt[c + 1] : ncand) - d;
+    if ((uint32_t)lane < cnt) {
+      s_key[d + lane] = et.x;
+      s_idx[d + lane] = et.y;
+    }
+    for (uint32_t o = 64 + lane; o < cnt; o += 64) {
+      const uint2 x = src.cand[(uint32_t)c * src.region + o];
+      s_key[d + o] = x.x;
+      s_idx[d + o] = x.y;
+    }
+  }
   if (lds && pre) {
     auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
 #pragma unroll
@@ -453,9 +525,8 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     // Stage the candidates, chunk after chunk in index order: chunk c at
     // [s_gt[c], s_gt[c] + count(c)).  With at most 128 chunks the first 128
     // candidates of every chunk were loaded above; any rest follows, wave w
-    // taking chunks w, w + 16, ...  With more chunks, candidate i (in index
-    // order) belongs to the last chunk c with s_gt[c] <= i, found by binary
-    // search, and every thread keeps kU independent loads in flight.
+    // taking chunks w, w + 16, ...  Otherwise the staging goes by units of
+    // chunks whose candidates are contiguous (below).
     auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
     if (pre) {
       for (int64_t c = wave; c < nc; c += kW)
@@ -465,28 +536,68 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
           s_idx[s_gt[c] + o] = e.y;
         }
     } else {
-      for (uint32_t i0 = threadIdx.x; i0 < ncand; i0 += kU * kResolveThreads) {
-        uint2 ev[kU];
+      // Runs prefetched above: the candidates past their first 32.
+      const int64_t ufirst = ppre ? min<int64_t>(nrun, (int64_t)kW * kPreRuns) : 0;
+      if (ppre) {
+        // Lane j < kPreRuns checks run w + 16 j; only runs with more than 32
+        // candidates (rare) are visited.
+        static_assert(kPreRuns <= 64, "one lane per prefetched run");
+        const int64_t myrun = wave + (int64_t)kW * lane;
+        uint32_t myd = 0, mycnt = 0;
+        if (lane < kPreRuns && myrun < nrun) mycnt = run_span(myrun, myd);
+        uint64_t big = __ballot(mycnt > 32u);
+        while (big != 0ull) {
+          const int j = __builtin_ctzll(big);
+          big &= big - 1;
+          const int64_t run = wave + (int64_t)kW * j;
+          const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)myd, j);
+          const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)mycnt, j);
+          for (uint32_t o = 32 + lane; o < cnt; o += 64) {
+            const uint2 e = src.cand[(uint32_t)run * cap + o];
+            s_key[d + o] = e.x;
+            s_idx[d + o] = e.y;
+          }
+        }
+      }
+      // The other staging units: below npacked a run of `pack` chunks (its
+      // candidates packed from the run's first slot, in index order), above it
+      // single chunks.  Wave w copies units ufirst + w, ufirst + w + 16, ...,
+      // kUU of them at a time, each in one piece of up to 128 candidates (the
+      // rest of a larger unit follows).
+      const int64_t nunits = tpre ? nrun : nrun + (nc - npacked);   // tail chunks done above
+      constexpr int kUU = 8;
+      for (int64_t u0 = ufirst + wave; u0 < nunits; u0 += kW * kUU) {
+        uint32_t d[kUU], cnt[kUU], b[kUU];
+        uint2 ev[kUU][2];
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const uint32_t i = i0 + u * kResolveThreads;
-          ev[u] = make_uint2(0u, 0u);
-          if (i < ncand) {
-            int lo = 0, hi = (int)nc - 1;
-            while (lo < hi) {
-              const int mid = (lo + hi + 1) >> 1;
-              if (s_gt[mid] <= i) lo = mid;
-              else hi = mid - 1;
-            }
-            ev[u] = src.cand[(uint32_t)lo * src.region + (i - s_gt[lo])];
+        for (int x = 0; x < kUU; ++x) {
+          const int64_t u = u0 + x * kW;
+          const int64_t ca = u < nrun ? u * pack : npacked + (u - nrun);
+          const int64_t cb = u < nrun ? ca + pack : ca + 1;
+          const bool v = u < nunits;
+          d[x] = v ? s_gt[ca] : 0u;
+          cnt[x] = v ? (cb < nc ? s_gt[cb] : ncand) - d[x] : 0u;
+          b[x] = v ? s_base[ca] : 0u;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t o = lane + 64 * h;
+            ev[x][h] = o < cnt[x] ? src.cand[b[x] + o] : make_uint2(0u, 0u);
           }
         }
 #pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const uint32_t i = i0 + u * kResolveThreads;
-          if (i < ncand) {
-            s_key[i] = ev[u].x;
-            s_idx[i] = ev[u].y;
+        for (int x = 0; x < kUU; ++x) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t o = lane + 64 * h;
+            if (o < cnt[x]) {
+              s_key[d[x] + o] = ev[x][h].x;
+              s_idx[d[x] + o] = ev[x][h].y;
+            }
+          }
+          for (uint32_t o = 128 + lane; o < cnt[x]; o += 64) {
+            const uint2 e = src.cand[b[x] + o];
+            s_key[d[x] + o] = e.x;
+            s_idx[d[x] + o] = e.y;
           }
         }
       }
@@ -649,9 +760,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
 
 hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                 int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
-                                hipStream_t stream) {
+                                int pack, int64_t npacked, hipStream_t stream) {
   hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
-                     n, R, k, ws, indices, mode, gflag, G);
+                     n, R, k, ws, indices, mode, gflag, G, pack, npacked);
   return hipGetLastError();
 }
 
@@ -668,7 +779,7 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int3
   hipLaunchKernelGGL(topk_cut, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
   hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
-                     ws, indices, 0, (uint32_t*)nullptr, 1);
+                     ws, indices, 0, (uint32_t*)nullptr, 1, 1, (int64_t)0);
   return hipGetLastError();
 }
 
