@@ -305,6 +305,7 @@ struct CutArgs {
   const uint32_t* sample;   // [rows][kMaxSampleKeys] sampled order keys
   int target;               // rank of tau among the row's kSampleKeys keys
   int rows;                 // rows to cut; 0 outside the candidate scan
+  topk::RowGeom geom;       // the rows' selection state (R = kTileKeys)
 };
 
 __host__ __device__ inline uint32_t cut_workgroups(int rows) {
@@ -333,7 +334,7 @@ __device__ void cut_row(const CutArgs& cut, int row, int64_t n, void* tws, uint3
       },
       (uint32_t)cut.target, smem, smem + topk::kBins, smem + topk::kBins + NT / 64);
   if (threadIdx.x == 0) {
-    uint32_t* st = topk::row_ws(tws, n, kTileKeys, row).st;
+    uint32_t* st = topk::row_at(tws, cut.geom, row).st;
     st[topk::kS_TAU] = tau;
     __hip_atomic_store(st + topk::kS_READY, tau | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -341,21 +342,21 @@ __device__ void cut_row(const CutArgs& cut, int row, int64_t n, void* tws, uint3
 
 // Lane h < G: the ready word of row (group, h).
 template <int G>
-__device__ __forceinline__ uint32_t cut_word(void* tws, int64_t n, int64_t grp) {
+__device__ __forceinline__ uint32_t cut_word(void* tws, const topk::RowGeom& geom, int64_t grp) {
   const int lane = lane_id();
   if (lane >= G) return 1u;
-  uint32_t* p = topk::row_ws(tws, n, kTileKeys, grp * G + lane).st + topk::kS_READY;
+  uint32_t* p = topk::row_at(tws, geom, grp * G + lane).st + topk::kS_READY;
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The G cuts as floats from the ready words (polled while one is missing);
 // a cut still missing gives NaN (no score is >= it) and flags its row.
 template <int G>
-__device__ __forceinline__ void cut_floats(void* tws, int64_t n, int64_t grp, uint32_t w,
-                                           float (&tf)[G]) {
+__device__ __forceinline__ void cut_floats(void* tws, const topk::RowGeom& geom, int64_t grp,
+                                           uint32_t w, float (&tf)[G]) {
   for (int it = 0; it < kCutSpin && __ballot((w & 1u) == 0u) != 0ull; ++it) {
     __builtin_amdgcn_s_sleep(8);
-    w = cut_word<G>(tws, n, grp);
+    w = cut_word<G>(tws, geom, grp);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -364,7 +365,7 @@ __device__ __forceinline__ void cut_floats(void* tws, int64_t n, int64_t grp, ui
       tf[h] = topk::key_float(v & ~1u);
     } else {
       tf[h] = __builtin_nanf("");
-      if (lane_id() == 0) atomicOr(&topk::row_ws(tws, n, kTileKeys, grp * G + h).st[topk::kS_OVER], 1u);
+      if (lane_id() == 0) atomicOr(&topk::row_at(tws, geom, grp * G + h).st[topk::kS_OVER], 1u);
     }
   }
 }
@@ -380,10 +381,10 @@ __device__ __forceinline__ void cut_floats(void* tws, int64_t n, int64_t grp, ui
 // with more candidates than its region holds flags the row.
 template <int G>
 __device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const float (&tf)[G],
-                                           int64_t grp, int64_t blk0, int wave, int64_t n,
-                                           void* tws, uint32_t (*s_ecnt)[G]) {
+                                           int64_t grp, int64_t blk0, int wave,
+                                           const topk::RowGeom& geom, void* tws,
+                                           uint32_t (*s_ecnt)[G]) {
   const int lane = lane_id();
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int64_t tile = blk0 / kNB;   // round * kWaves + wave
   const int64_t round = tile / kWaves;
   uint32_t cnt[G];
@@ -396,9 +397,10 @@ __device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const floa
     if (lane == 0) s_ecnt[wave][h] = c;
   }
   __syncthreads();
+  const uint32_t idx0 = (uint32_t)(blk0 * kBlock) + (uint32_t)lane;   // this lane's key in block 0
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const topk::RowWs rw = topk::row_ws(tws, n, kTileKeys, grp * G + h);
+    const topk::RowWs rw = topk::row_at(tws, geom, grp * G + h);
     const uint32_t cap = kWaves * rw.region;
     uint32_t before = 0, total = 0;
 #pragma unroll
@@ -407,22 +409,28 @@ __device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const floa
       before += w < wave ? x : 0u;
       total += x;
     }
-    const uint32_t start = (uint32_t)round * cap;
+    uint2* dst = reinterpret_cast<uint2*>(rw.cand) + (uint32_t)round * cap;
+    const bool fits = before + cnt[h] <= cap;   // uniform: no slot check needed
     uint32_t at = before;
 #pragma unroll
     for (int b = 0; b < kNB; ++b) {
       const bool cand = sc[b][h] >= tf[h];
-      const uint64_t m = __ballot(cand);
-      if (m != 0ull) {
-        const uint32_t sl = at + (uint32_t)__popcll(m & below);
-        if (cand && sl < cap)
-          reinterpret_cast<uint2*>(rw.cand)[start + sl] =
-              make_uint2(topk::order_key(sc[b][h]), (uint32_t)((blk0 + b) * kBlock + lane));
-        at += (uint32_t)__popcll(m);
+      const uint64_t mb = __ballot(cand);
+      if (mb != 0ull) {
+        if (cand) {
+          const uint32_t sl = at + __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u));
+          // Order key without the -0 case: these scores are never -0 (both
+          // folds start at +0, and a sum that is exactly 0 rounds to +0).
+          const uint32_t u = __float_as_uint(sc[b][h]);
+          const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+          if (fits || sl < cap) dst[sl] = make_uint2(key, idx0 + (uint32_t)(b * kBlock));
+        }
+        at += (uint32_t)__popcll(mb);
       }
     }
     if (lane == 0) {
-      rw.seg[2 * tile] = start + before;
+      rw.seg[2 * tile] = (uint32_t)round * cap + before;
       rw.seg[2 * tile + 1] = cnt[h];
       if (wave == 0 && total > cap) atomicOr(&rw.st[topk::kS_OVER], 1u);
     }
@@ -792,15 +800,15 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     // MODE 1: the ready words of the group's cuts, read here so that they
     // have arrived (and the cuts are out) by the time the tile is emitted.
     uint32_t cw = 1u;
-    if (MODE == 1) cw = cut_word<G>(tws, n, grp);
+    if (MODE == 1) cw = cut_word<G>(tws, cut.geom, grp);
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
     finish_tile<G>(acc, o, kNB - 1, n, scores_g != nullptr ? scores_g + blk0 * kBlock : nullptr,
                    s_o[wave]);
     if (MODE == 1) {
       float tf[G];
-      cut_floats<G>(tws, n, grp, cw, tf);
-      emit_round<G>(acc, tf, grp, blk0, wave, n, tws, s_ecnt);
+      cut_floats<G>(tws, cut.geom, grp, cw, tf);
+      emit_round<G>(acc, tf, grp, blk0, wave, cut.geom, tws, s_ecnt);
     }
 
     if (r + 1 < nr) {
@@ -1180,7 +1188,8 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
     constexpr int M = decltype(mode)::value;
     constexpr int NR = M == 2 ? kRescanRounds : 1;
     void* tws = M == 1 ? fw.rows : nullptr;
-    const CutArgs cut = M == 1 ? CutArgs{fw.sample, target, (int)rows} : CutArgs{};
+    const CutArgs cut =
+        M == 1 ? CutArgs{fw.sample, target, (int)rows, topk::row_geom(n, R)} : CutArgs{};
     const int64_t wgs = (nrounds + NR - 1) / NR;
     const unsigned grid = (unsigned)(wgs * groups) + (M == 1 ? cut_workgroups((int)rows) : 0u);
     hipLaunchKernelGGL((scan_main<G, M, NR>), dim3(grid), dim3(kThreads), 0, stream, planes,

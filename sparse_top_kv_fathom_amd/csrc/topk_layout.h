@@ -59,6 +59,33 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   return r;
 }
 
+// The same layout from precomputed offsets (no division on the device): for
+// kernels that address many rows.
+struct RowGeom {
+  uint64_t words;      // row_words(n, R)
+  uint32_t region;     // region(n, R)
+  uint32_t seg_off;    // first word of the segment table
+  uint32_t ord_off;    // first word of the order table
+};
+__host__ __device__ inline RowGeom row_geom(int64_t n, int64_t R) {
+  RowGeom g;
+  g.words = row_words(n, R);
+  g.region = region(n, R);
+  g.seg_off = (uint32_t)(kS_WORDS + 2 * cand_cap(n));
+  g.ord_off = g.seg_off + 2 * (uint32_t)n_chunks(n, R);
+  return g;
+}
+__device__ __forceinline__ RowWs row_at(void* ws, const RowGeom& g, int64_t row) {
+  uint32_t* p = reinterpret_cast<uint32_t*>(ws) + g.words * (uint64_t)row;
+  RowWs r;
+  r.region = g.region;
+  r.st = p;
+  r.cand = p + kS_WORDS;
+  r.seg = p + g.seg_off;
+  r.ord = p + g.ord_off;
+  return r;
+}
+
 // Workspace of fathom_scan_topk: per-row selection state with one candidate
 // region per scan wave tile (R = 512 keys), the sample's order keys, a flag
 // per group (a row of the group must be selected again from its scores), and
