@@ -258,13 +258,15 @@ int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
  * writes them (when `scores` is non-null), indices as fathom_topk selects
  * them (§2 order, ascending).  When 65536 <= n <= 2^21 (and the group's
  * plane array is under 4 GiB): 8 runs of 1024 keys spread evenly over each
- * row are scored first, a cut tau per row is taken from that sample, and the
- * scan then writes every score >= tau, per 512-key tile (the last one
- * possibly partial), to the row's candidate buffer, from which the selection
- * is made.  A row whose candidates cannot
- * give the selection (fewer than k of them, or a tile with more than its
- * region holds: heavy ties) is selected from its scores: from `scores`, or,
- * when `scores` is null, from a second scan of its group into the workspace.
+ * row are scored first, a cut tau per row is taken from that sample (inside
+ * the scan's launch), and the scan then writes every score >= tau, in index
+ * order, to the row's candidate buffer (pooled per 2048-key round, the
+ * blocks after the last whole round per 512-key tile, the last one possibly
+ * partial), from which the selection is made.  A row whose candidates
+ * cannot give the selection (fewer than k of them, or a round with more
+ * than its region holds: heavy ties) is selected from its scores: from
+ * `scores`, or, when `scores` is null, from a second scan of its group into
+ * the workspace.
  * Otherwise the two calls run as they are (into the workspace when `scores`
  * is null).
  *
