@@ -50,9 +50,9 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 7   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
+#define FATHOM_ABI_VERSION 8   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
                                   5: fathom_klt_*; 6: fathom_scan_timed;
-                                  7: fathom_topk_noalloc */
+                                  7: fathom_topk_noalloc; 8: fathom_test_cut_hooks */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -354,6 +354,19 @@ int fathom_klt_rotate_queries(const float* q, const float* basis, int64_t groups
 
 /* Static, NUL-terminated name of a status code. */
 const char* fathom_status_string(int status);
+/*
+ * fathom_test_cut_hooks — for tests of fathom_scan_topk's fallback only.
+ * In the fused path the scan's first workgroups publish each row's cut and
+ * the scan waves poll for it a bounded number of times; a row whose cut is
+ * still missing then is flagged and selected by the fallback.  publish = 0
+ * makes those workgroups store the cut without publishing it, so that every
+ * wave reaches its poll limit; spin_limit (1 to 16384 polls of about
+ * 0.2 us) sets the limit.  (1, 16384) are the defaults.  Host-side settings
+ * of the calling process, read by later calls; FATHOM_ERR_BAD_RANGE for a
+ * publish other than 0 or 1 or a limit outside the range.
+ */
+int fathom_test_cut_hooks(int32_t publish, int32_t spin_limit);
+
 /* FATHOM_ABI_VERSION of the loaded library. */
 int fathom_abi_version(void);
 

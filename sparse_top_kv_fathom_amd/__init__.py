@@ -10,6 +10,7 @@ it has not been built.
 """
 _EXPORTS = ("encode", "plan", "plan_fixed", "PLAN_MODES", "scan", "scan_topk", "scan_topk_workspace", "gather", "klt_fit", "klt_fit_workspace",
             "klt_rotate_keys", "klt_rotate_queries", "topk", "topk_noalloc", "topk_workspace_bytes", "topk_workspace",
+            "test_cut_hooks",
             "empty_store", "store_shapes", "FathomError", "lib", "STATUS", "EXPORTED")
 
 __all__ = list(_EXPORTS)

@@ -41,7 +41,7 @@ EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
             "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
             "fathom_klt_rotate_queries",
             "fathom_topk_workspace_bytes", "fathom_topk_noalloc", "fathom_topk_noalloc_max_bytes",
-            "fathom_status_string", "fathom_abi_version")
+            "fathom_test_cut_hooks", "fathom_status_string", "fathom_abi_version")
 
 
 class FathomError(RuntimeError):
@@ -238,6 +238,12 @@ def gather(host_planes: torch.Tensor, host_scales: torch.Tensor, depths: torch.T
         _stream(stream))
     _check(st, "fathom_gather")
     return planes, scales
+
+
+def test_cut_hooks(publish: bool = True, spin_limit: int = 16384) -> None:
+    """fathom_test_cut_hooks (tests of fathom_scan_topk's fallback only)."""
+    _check(lib().fathom_test_cut_hooks(int(bool(publish)), int(spin_limit)),
+           "fathom_test_cut_hooks")
 
 
 def scan_topk_workspace(groups: int, G: int, n: int, k: int, device="cuda") -> torch.Tensor:

@@ -32,6 +32,13 @@ bool valid_tokens(int64_t n) { return n >= fathom::kBlock && n % fathom::kBlock 
 
 extern "C" {
 
+int fathom_test_cut_hooks(int32_t publish, int32_t spin_limit) {
+  if ((publish != 0 && publish != 1) || spin_limit < 1 || spin_limit > 16384)
+    return FATHOM_ERR_BAD_RANGE;
+  fathom::set_cut_hooks(publish, spin_limit);
+  return FATHOM_OK;
+}
+
 int fathom_abi_version(void) { return FATHOM_ABI_VERSION; }
 
 const char* fathom_status_string(int status) {

@@ -62,6 +62,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -306,6 +307,8 @@ struct CutArgs {
   int target;               // rank of tau among the row's kSampleKeys keys
   int rows;                 // rows to cut; 0 outside the candidate scan
   topk::RowGeom geom;       // the rows' selection state (R = kTileKeys)
+  int publish;              // 1; 0 only under fathom_test_cut_hooks
+  int spin;                 // the waves' poll limit (kCutSpin)
 };
 
 __host__ __device__ inline uint32_t cut_workgroups(int rows) {
@@ -336,7 +339,9 @@ __device__ void cut_row(const CutArgs& cut, int row, int64_t n, void* tws, uint3
   if (threadIdx.x == 0) {
     uint32_t* st = topk::row_at(tws, cut.geom, row).st;
     st[topk::kS_TAU] = tau;
-    __hip_atomic_store(st + topk::kS_READY, tau | 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (cut.publish)
+      __hip_atomic_store(st + topk::kS_READY, tau | 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -353,8 +358,8 @@ __device__ __forceinline__ uint32_t cut_word(void* tws, const topk::RowGeom& geo
 // a cut still missing gives NaN (no score is >= it) and flags its row.
 template <int G>
 __device__ __forceinline__ void cut_floats(void* tws, const topk::RowGeom& geom, int64_t grp,
-                                           uint32_t w, float (&tf)[G]) {
-  for (int it = 0; it < kCutSpin && __ballot((w & 1u) == 0u) != 0ull; ++it) {
+                                           int spin, uint32_t w, float (&tf)[G]) {
+  for (int it = 0; it < spin && __ballot((w & 1u) == 0u) != 0ull; ++it) {
     __builtin_amdgcn_s_sleep(8);
     w = cut_word<G>(tws, geom, grp);
   }
@@ -807,7 +812,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
                    s_o[wave]);
     if (MODE == 1) {
       float tf[G];
-      cut_floats<G>(tws, cut.geom, grp, cw, tf);
+      cut_floats<G>(tws, cut.geom, grp, cut.spin, cw, tf);
       emit_round<G>(acc, tf, grp, blk0, wave, cut.geom, tws, s_ecnt);
     }
 
@@ -1159,6 +1164,9 @@ __global__ __launch_bounds__(kSampleThreads) void fused_sample(
 // (fewer than k, or a region overflowed) are flagged: their groups are
 // scanned again into the workspace's score area and selected from there; the
 // other groups' work ends at once.  Otherwise the two calls run as they are.
+// fathom_test_cut_hooks' settings.
+static std::atomic<int> g_cut_publish{1}, g_cut_spin{kCutSpin};
+
 template <int G>
 hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_store,
                               const uint8_t* depths, const float* q, int64_t groups, int64_t n,
@@ -1188,8 +1196,9 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
     constexpr int M = decltype(mode)::value;
     constexpr int NR = M == 2 ? kRescanRounds : 1;
     void* tws = M == 1 ? fw.rows : nullptr;
-    const CutArgs cut =
-        M == 1 ? CutArgs{fw.sample, target, (int)rows, topk::row_geom(n, R)} : CutArgs{};
+    const CutArgs cut = M == 1 ? CutArgs{fw.sample, target, (int)rows, topk::row_geom(n, R),
+                                         g_cut_publish.load(), g_cut_spin.load()}
+                               : CutArgs{};
     const int64_t wgs = (nrounds + NR - 1) / NR;
     const unsigned grid = (unsigned)(wgs * groups) + (M == 1 ? cut_workgroups((int)rows) : 0u);
     hipLaunchKernelGGL((scan_main<G, M, NR>), dim3(grid), dim3(kThreads), 0, stream, planes,
@@ -1209,6 +1218,11 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
   scan(std::integral_constant<int, 2>(), fw.scores, fw.gflag);
   return launch_fused_resolve(fw.scores, rows, n, R, k, indices, fw.rows, 1, fw.gflag, G, kWaves,
                               npacked, stream);
+}
+
+void set_cut_hooks(int publish, int spin_limit) {
+  g_cut_publish.store(publish);
+  g_cut_spin.store(spin_limit);
 }
 
 int64_t scan_max_workgroups(int64_t groups, int64_t n) {

@@ -47,7 +47,7 @@ def test_header_declares_the_calls():
               "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
               "fathom_klt_rotate_queries",
               "fathom_topk_workspace_bytes", "fathom_topk_noalloc", "fathom_topk_noalloc_max_bytes",
-              "fathom_status_string", "fathom_abi_version"):
+              "fathom_test_cut_hooks", "fathom_status_string", "fathom_abi_version"):
         assert f in names
 
 
@@ -61,7 +61,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 7
+    assert L.fathom_abi_version() == 8
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8, -9):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
@@ -322,3 +322,10 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(ImportError):
         b.lib()
     importlib.reload(b)
+
+
+def test_cut_hooks_reject_bad_arguments(L):
+    """fathom_test_cut_hooks checks its arguments on the host (no GPU call)."""
+    for publish, spin in ((2, 16), (-1, 16), (1, 0), (1, 16385), (0, -3)):
+        assert L.fathom_test_cut_hooks(publish, spin) == BAD_RANGE
+    assert L.fathom_test_cut_hooks(1, 16384) == OK
