@@ -361,7 +361,7 @@ const char* fathom_status_string(int status);
  * still missing then is flagged and selected by the fallback.  publish = 0
  * makes those workgroups store the cut without publishing it, so that every
  * wave reaches its poll limit; spin_limit (1 to 16384 polls of about
- * 0.2 us) sets the limit.  (1, 16384) are the defaults.  Host-side settings
+ * 0.2 us) sets the limit.  (1, 2048) are the defaults.  Host-side settings
  * of the calling process, read by later calls; FATHOM_ERR_BAD_RANGE for a
  * publish other than 0 or 1 or a limit outside the range.
  */

@@ -240,7 +240,7 @@ def gather(host_planes: torch.Tensor, host_scales: torch.Tensor, depths: torch.T
     return planes, scales
 
 
-def test_cut_hooks(publish: bool = True, spin_limit: int = 16384) -> None:
+def test_cut_hooks(publish: bool = True, spin_limit: int = 2048) -> None:
     """fathom_test_cut_hooks (tests of fathom_scan_topk's fallback only)."""
     _check(lib().fathom_test_cut_hooks(int(bool(publish)), int(spin_limit)),
            "fathom_test_cut_hooks")

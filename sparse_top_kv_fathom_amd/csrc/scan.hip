@@ -288,89 +288,260 @@ constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stag
 constexpr int kRescanRounds = 8;           // rounds per workgroup of the gated second pass
 constexpr int kSampleRuns = 8;             // sampled runs of two wave tiles per group
 constexpr int kSampleKeys = 2 * kSampleRuns * kTileKeys;   // 8192 per row
-constexpr int kCutSpin = 1 << 14;          // polls of a cut that is not yet published
+constexpr int kSampleWgs = 2 * kSampleRuns * kNB / 2;      // sample workgroups per group (64)
+constexpr int kCutSpin = 2048;             // polls (about 0.2 us each) of a cut not yet out
 
-// The cut of fathom_scan_topk.  The candidate scan's first workgroups (one
-// per row, ids [0, rows) of its grid, the count rounded up to a multiple of
-// the XCD count so that the scan's own ids keep their XCD) take tau from the
-// row's sample, as the target-th largest sampled order key with its low 10
-// bits cleared (two 11-bit radix digits), store it for the selection, and
-// publish tau | 1 in the row's ready word with an agent-scope atomic store.
-// The word carries the whole message, so no fence is needed (a device-scope
-// release would write back the L2).  Scan waves read the word (agent-scope
-// atomic loads) once their scores are nearly done and poll it, boundedly,
-// only if the cut is not out yet; a row whose cut is still missing after
-// kCutSpin polls emits nothing and is flagged, so its selection falls back
-// to the second pass.
+// The sample and the cut of fathom_scan_topk, taken inside the candidate
+// scan's launch.  Its first groups * kSampleWgs workgroups (a multiple of the
+// XCD count, so the scan's own ids keep their XCD) each score two blocks of
+// the group's sample: 8 runs of two adjacent wave tiles spread evenly over
+// the row.  Their order keys go to the sample buffer with agent-scope stores,
+// and each workgroup then sets its own flag to the call's epoch.  Sample
+// workgroups 0 to G - 1 of a group wait until all the group's flags carry
+// this call's epoch and take one row's cut each: tau = the target-th largest of the
+// row's kSampleKeys sampled keys with its low 10 bits cleared (two 11-bit
+// radix digits, the keys read with agent-scope loads), stored for the
+// selection and published in the row's ready word as tau | epoch << 1 | 1
+// with an agent-scope atomic store.  Every message is a single word or is
+// complete before the word that announces it is written (s_waitcnt), so no
+// fence is needed (a device-scope release would write back the L2).
+// Scan waves read the ready word with agent-scope loads before their depth-1
+// channels and poll it (boundedly) only if this call's cut is not out yet; a
+// cut still missing after `spin` polls flags the row, and every emitting tile
+// stamps the cut it used, which the selection checks, so that no timing or
+// stale word can change a result: it can only send a row to the fallback.
 struct CutArgs {
-  const uint32_t* sample;   // [rows][kMaxSampleKeys] sampled order keys
+  uint32_t* sample;         // [rows][kMaxSampleKeys] sampled order keys
   int target;               // rank of tau among the row's kSampleKeys keys
-  int rows;                 // rows to cut; 0 outside the candidate scan
+  int groups;               // groups sampled; 0 outside the candidate scan
   topk::RowGeom geom;       // the rows' selection state (R = kTileKeys)
   int publish;              // 1; 0 only under fathom_test_cut_hooks
   int spin;                 // the waves' poll limit (kCutSpin)
+  int64_t rstride;          // wave tiles between two sampled runs
+  uint32_t* gflag;          // [groups] second-pass flags (cleared by the cut)
+  uint32_t* sflag;          // [groups][kSampleFlags] epochs of the sample parts that are out
+  uint32_t epoch;           // the call's epoch (its low 9 bits are used)
 };
 
-__host__ __device__ inline uint32_t cut_workgroups(int rows) {
-  return (uint32_t)((rows + kXcds - 1) / kXcds * kXcds);
+__host__ __device__ inline uint32_t sample_workgroups(int groups) {
+  static_assert((kSampleWgs % kXcds) == 0, "whole XCD rounds");
+  static_assert(kSampleWgs == topk::kSampleFlags, "one flag per sample workgroup, one per lane");
+  return (uint32_t)groups * kSampleWgs;
+}
+// The low 10 bits of a published ready word.
+__device__ __forceinline__ uint32_t ready_bits(uint32_t epoch) { return ((epoch & 0x1FFu) << 1) | 1u; }
+
+// The sample's channels of depth T (mask m over the wave's half of the
+// channels) for lane `bit` of half `hsel` of block `b`, four at a time: the
+// LDS reads of the four (the lane's T plane words in one read, the scale,
+// the G query entries in one read) are issued together, then their
+// arithmetic.  A slot past the end of the mask reads the half's first
+// channel and adds 0.
+template <int T, int G>
+__device__ __forceinline__ void sample_depth(const uint4 (*s_w)[2][2], const uint16_t (*s_sc)[2],
+                                             const float (*s_q)[G], uint64_t m, int c0, int b,
+                                             int hsel, int bit, float (&acc)[G]) {
+  while (m != 0ull) {
+    int c[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ok[u] = m != 0ull;
+      c[u] = c0 + (ok[u] ? __builtin_ctzll(m) : 0);
+      m &= m - 1;   // stays 0 once empty
+    }
+    uint32_t w[4][T];
+    float a[4], qv[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // Word hsel of planes 0-3 of channel c, block b.
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[c[u]][b][hsel]);
+#pragma unroll
+      for (int p = 0; p < T; ++p) w[u][p] = wp[p];
+      a[u] = half_lo(s_sc[c[u]][b]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) qv[u][h] = s_q[c[u]][h];   // uniform address: broadcast
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every read above is issued before the arithmetic
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t cp = 0u;
+#pragma unroll
+      for (int p = 0; p < T; ++p) cp = 2 * cp + ((w[u][p] >> bit) & 1u);
+      // (c' + 1/2 - 2^(T-1)) * a / 2^(T-1)
+      float kh = __builtin_ldexpf(((float)cp + (0.5f - (float)(1 << (T - 1)))) * a[u], 1 - T);
+      kh = ok[u] ? kh : 0.0f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qv[u][h], kh, acc[h]);
+    }
+  }
 }
 
-template <int NT>
-__device__ void cut_row(const CutArgs& cut, int row, int64_t n, void* tws, uint32_t* smem) {
-  constexpr int kPieces = kSampleKeys / (4 * NT);
-  static_assert(kPieces * 4 * NT == kSampleKeys, "whole 16-byte pieces per thread");
-  const uint4* src =
-      reinterpret_cast<const uint4*>(cut.sample + (int64_t)row * topk::kMaxSampleKeys);
-  // The thread's keys are read again for each digit (they stay in L2), so
-  // that the cut holds no key registers: the kernel's register count is set
-  // by the scan.
-  const uint32_t tau = topk::radix_cut<NT>(
+// One sample workgroup of the candidate scan (workgroup id `wg` below
+// sample_workgroups): blocks 2 pr and 2 pr + 1 of sampled tile ti, in fp32
+// but in no particular order (only the cut is taken from the sample).  One
+// round of loads brings the depths, the two blocks' scales, the group's
+// queries and every plane row of the two blocks (512 rows of 16 bytes, the
+// rows past a channel's depth too, so no load waits for the plan) into LDS,
+// laid out so that a lane reads its channel's plane words, and a channel's
+// query entries, in one LDS read each; waves 2b and 2b + 1 score block b
+// over the channels [0, 64) and [64, 128), and the first adds the second's
+// partial sums.  Then its flag and, in sample workgroups 0 to G - 1, a cut.
+template <int G>
+__device__ void sample_wg(const CutArgs& cut, uint32_t wg, const uint64_t* __restrict__ planes,
+                          const uint16_t* __restrict__ scales, int64_t nb_store,
+                          const uint8_t* __restrict__ depths, const float* __restrict__ q,
+                          void* tws, char* smem) {
+  constexpr int kQOff = kD * 2 * 2 * 16 + kD * 2 * 2;       // after s_w and s_sc
+  constexpr int kPartOff = kQOff + kD * G * 4;
+  constexpr int kArrOff = kPartOff + 2 * G * kBlock * 4;
+  static_assert(kQOff % 16 == 0, "s_q in whole 16-byte rows");
+  uint4 (*s_w)[2][2] = reinterpret_cast<uint4 (*)[2][2]>(smem);            // [kD][2][2]
+  uint16_t (*s_sc)[2] = reinterpret_cast<uint16_t (*)[2]>(smem + kD * 2 * 2 * 16);
+  float (*s_q)[G] = reinterpret_cast<float (*)[G]>(smem + kQOff);
+  float (*s_part)[G][kBlock] = reinterpret_cast<float (*)[G][kBlock]>(smem + kPartOff);
+  uint32_t* s_arr = reinterpret_cast<uint32_t*>(smem + kArrOff);
+  const int64_t grp = wg / kSampleWgs;
+  const int sb = (int)(wg % kSampleWgs), ti = sb >> 2, pr = sb & 3;
+  const int64_t blk0 = ((ti >> 1) * cut.rstride + (ti & 1)) * kNB + 2 * pr;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = wv >> 1, half = wv & 1;   // block of the pair, channel half
+  const int tl = min((int)depths[grp * kD + 64 * half + lane], kPlanes);
+  for (int i = tid; i < G * kD; i += kThreads) s_q[i % kD][i / kD] = q[grp * G * kD + i];
+  if (tid < kD) {
+    const uint16_t* sp = scales + (grp * kD + tid) * nb_store + blk0;
+    s_sc[tid][0] = sp[0];
+    s_sc[tid][1] = sp[1];
+  }
+  // Plane rows r = tid and tid + 256: (channel r / 4, plane r % 4), both blocks.
+  const bool vec = (nb_store & 1) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = tid + kThreads * i;
+    const uint64_t* a0 = planes + (grp * kD * kPlanes + r) * nb_store + blk0;
+    uint64_t x0, x1;
+    if (vec) {
+      const uint4 v = *reinterpret_cast<const uint4*>(a0);
+      x0 = v.x | ((uint64_t)v.y << 32);
+      x1 = v.z | ((uint64_t)v.w << 32);
+    } else {
+      x0 = a0[0];
+      x1 = a0[1];
+    }
+    uint32_t* w = reinterpret_cast<uint32_t*>(s_w[r >> 2][0]) + (r & 3);
+    w[0] = (uint32_t)x0;           // block 0, tokens 0-31
+    w[4] = (uint32_t)(x0 >> 32);   //          tokens 32-63
+    w[8] = (uint32_t)x1;           // block 1
+    w[12] = (uint32_t)(x1 >> 32);
+  }
+  __syncthreads();
+  const int hsel = lane >> 5, bit = lane & 31, c0 = 64 * half;
+  float acc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), c0, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), c0, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), c0, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), c0, b, hsel, bit, acc);
+  if (half == 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
+  }
+  __syncthreads();
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      __hip_atomic_store(cut.sample + (grp * G + h) * (int64_t)topk::kMaxSampleKeys +
+                             ti * kTileKeys + (2 * pr + b) * kBlock + lane,
+                         topk::order_key(acc[h] + s_part[b][h][lane]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the keys are out before the flag
+  }
+  __syncthreads();
+  uint32_t* flags = cut.sflag + grp * topk::kSampleFlags;
+  if (tid == 0) __hip_atomic_store(flags + sb, cut.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (sb >= G) return;   // uniform over the workgroup
+  const int h = sb;
+  // Wave 0 reads the group's flags, one per lane, until all are this call's.
+  if (tid < 64) {
+    bool all = false;
+    for (int it = 0; it < kCutSpin && !all; ++it) {
+      const uint32_t f =
+          __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      all = __ballot(f != cut.epoch) == 0ull;
+      if (!all) __builtin_amdgcn_s_sleep(4);
+    }
+    if (tid == 0) s_arr[1] = all ? 1u : 0u;
+  }
+  __syncthreads();
+  if (s_arr[1] == 0u) return;   // the row's waves time out and flag it
+  const int64_t row = grp * G + h;
+  uint32_t* st = topk::row_at(tws, cut.geom, row).st;
+  if (tid == 0) {
+    __hip_atomic_store(st + topk::kS_OVER, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (h == 0) __hip_atomic_store(cut.gflag + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // The row's keys, read again for each digit with agent-scope loads, in two
+  // batches of 16 per thread whose loads are all issued before any is used
+  // (the kernel's register count stays the scan's).
+  constexpr int kPer = kSampleKeys / kThreads, kBatch = kPer / 2;
+  const uint32_t* src = cut.sample + row * (int64_t)topk::kMaxSampleKeys;
+  uint32_t* h32 = reinterpret_cast<uint32_t*>(smem);   // the sample's LDS is free now
+  const uint32_t tau = topk::radix_cut<kThreads>(
       [&](auto&& f) {
-#pragma unroll 2
-        for (int u = 0; u < kPieces; ++u) {
-          const uint4 v = src[u * NT + threadIdx.x];
-          f(v.x);
-          f(v.y);
-          f(v.z);
-          f(v.w);
+        for (int half = 0; half < 2; ++half) {
+          uint32_t key[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            key[u] = __hip_atomic_load(src + (half * kBatch + u) * kThreads + tid,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) f(key[u]);
         }
       },
-      (uint32_t)cut.target, smem, smem + topk::kBins, smem + topk::kBins + NT / 64);
-  if (threadIdx.x == 0) {
-    uint32_t* st = topk::row_at(tws, cut.geom, row).st;
+      (uint32_t)cut.target, h32, h32 + topk::kBins, h32 + topk::kBins + kThreads / 64);
+  if (tid == 0) {
     st[topk::kS_TAU] = tau;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the flag clears are out first
     if (cut.publish)
-      __hip_atomic_store(st + topk::kS_READY, tau | 1u, __ATOMIC_RELAXED,
+      __hip_atomic_store(st + topk::kS_READY, tau | ready_bits(cut.epoch), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Lane h < G: the ready word of row (group, h).
+// Lane h < G: the ready word of row (group, h); other lanes read as ready.
 template <int G>
-__device__ __forceinline__ uint32_t cut_word(void* tws, const topk::RowGeom& geom, int64_t grp) {
+__device__ __forceinline__ uint32_t cut_word(void* tws, const CutArgs& cut, int64_t grp) {
   const int lane = lane_id();
-  if (lane >= G) return 1u;
-  uint32_t* p = topk::row_at(tws, geom, grp * G + lane).st + topk::kS_READY;
+  if (lane >= G) return ready_bits(cut.epoch);
+  uint32_t* p = topk::row_at(tws, cut.geom, grp * G + lane).st + topk::kS_READY;
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The G cuts as floats from the ready words (polled while one is missing);
-// a cut still missing gives NaN (no score is >= it) and flags its row.
+// The G cuts (as keys and as floats) from the ready words, polled while one
+// of this call's is missing; a cut still missing gives NaN (no score is >=
+// it) and a key no cut has, and flags its row.
 template <int G>
-__device__ __forceinline__ void cut_floats(void* tws, const topk::RowGeom& geom, int64_t grp,
-                                           int spin, uint32_t w, float (&tf)[G]) {
-  for (int it = 0; it < spin && __ballot((w & 1u) == 0u) != 0ull; ++it) {
+__device__ __forceinline__ void cut_floats(void* tws, const CutArgs& cut, int64_t grp, uint32_t w,
+                                           uint32_t (&tk)[G], float (&tf)[G]) {
+  const uint32_t rb = ready_bits(cut.epoch);
+  for (int it = 0; it < cut.spin && __ballot((w & 0x3FFu) != rb) != 0ull; ++it) {
     __builtin_amdgcn_s_sleep(8);
-    w = cut_word<G>(tws, geom, grp);
+    w = cut_word<G>(tws, cut, grp);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)w, h);
-    if (v & 1u) {
-      tf[h] = topk::key_float(v & ~1u);
+    if ((v & 0x3FFu) == rb) {
+      tk[h] = v & ~0x3FFu;
+      tf[h] = topk::key_float(tk[h]);
     } else {
+      tk[h] = 0xFFFFFFFFu;   // low bits set: never a cut
       tf[h] = __builtin_nanf("");
-      if (lane_id() == 0) atomicOr(&topk::row_at(tws, geom, grp * G + h).st[topk::kS_OVER], 1u);
+      if (lane_id() == 0)
+        atomicOr(&topk::row_at(tws, cut.geom, grp * G + h).st[topk::kS_OVER], 1u);
     }
   }
 }
@@ -382,11 +553,12 @@ __device__ __forceinline__ void cut_floats(void* tws, const topk::RowGeom& geom,
 // (order key, index) in index order, right after those of the waves before
 // it, so that the round's candidates lie packed and in index order at the
 // front of the region (the selection then copies a round's candidates in one
-// piece).  The segment table gets each tile's first slot and count; a round
-// with more candidates than its region holds flags the row.
+// piece).  The segment table gets each tile's first slot and count, the
+// stamp table the cut the tile used; a round with more candidates than its
+// region holds flags the row.
 template <int G>
-__device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const float (&tf)[G],
-                                           int64_t grp, int64_t blk0, int wave,
+__device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const uint32_t (&tk)[G],
+                                           const float (&tf)[G], int64_t grp, int64_t blk0, int wave,
                                            const topk::RowGeom& geom, void* tws,
                                            uint32_t (*s_ecnt)[G]) {
   const int lane = lane_id();
@@ -437,6 +609,7 @@ __device__ __forceinline__ void emit_round(const float (&sc)[kNB][G], const floa
     if (lane == 0) {
       rw.seg[2 * tile] = (uint32_t)round * cap + before;
       rw.seg[2 * tile + 1] = cnt[h];
+      rw.stamp[2 * tile] = tk[h];
       if (wave == 0 && total > cap) atomicOr(&rw.st[topk::kS_OVER], 1u);
     }
   }
@@ -667,16 +840,20 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     const uint32_t* __restrict__ gate, CutArgs cut) {
   static_assert(kNB * G <= 64, "one lane per (block, head) in the offset fold");
   static_assert(MODE != 1 || NR == 1, "candidate emission runs one round per workgroup");
+  // The sample workgroups' LDS (sample_wg) lives in sh.
+  static_assert(sizeof(MainShared<G>) >=
+                    kD * 2 * 2 * 16 + kD * 2 * 2 + kD * G * 4 + 2 * G * kBlock * 4 + 8,
+                "sample scratch");
   static_assert(sizeof(MainShared<G>) >= (topk::kBins + kThreads / 64 + 2) * 4, "cut scratch");
   __shared__ MainShared<G> sh;
   __shared__ float s_o[kWaves][kNB * G];
   __shared__ uint32_t s_ecnt[MODE == 1 ? kWaves : 1][G];   // MODE 1: candidates per wave
 
-  // MODE 1: the first workgroups take the rows' cuts.
-  const uint32_t ncut = MODE == 1 ? cut_workgroups(cut.rows) : 0u;
+  // MODE 1: the first workgroups take the sample and the cuts.
+  const uint32_t ncut = MODE == 1 ? sample_workgroups(cut.groups) : 0u;
   if (MODE == 1 && blockIdx.x < ncut) {   // uniform over the workgroup
-    if ((int)blockIdx.x < cut.rows)
-      cut_row<kThreads>(cut, (int)blockIdx.x, n, tws, reinterpret_cast<uint32_t*>(&sh));
+    sample_wg<G>(cut, blockIdx.x, planes, scales, nb_store, depths, q, tws,
+                 reinterpret_cast<char*>(&sh));
     return;
   }
   // XCD-aware remap of the scan's workgroup ids (bijective on [0, nwg)).
@@ -805,15 +982,16 @@ __global__ __launch_bounds__(kThreads) void scan_main(
     // MODE 1: the ready words of the group's cuts, read here so that they
     // have arrived (and the cuts are out) by the time the tile is emitted.
     uint32_t cw = 1u;
-    if (MODE == 1) cw = cut_word<G>(tws, cut.geom, grp);
+    if (MODE == 1) cw = cut_word<G>(tws, cut, grp);
     main_depth<1, G, true, SCAN_U1>(c, sh.tb, rc[0] + rc[1] + rc[2], rc[3],
                                     ChanIter{rm.lo[3], rm.hi[3]}, acc, o);
     finish_tile<G>(acc, o, kNB - 1, n, scores_g != nullptr ? scores_g + blk0 * kBlock : nullptr,
                    s_o[wave]);
     if (MODE == 1) {
+      uint32_t tk[G];
       float tf[G];
-      cut_floats<G>(tws, cut.geom, grp, cut.spin, cw, tf);
-      emit_round<G>(acc, tf, grp, blk0, wave, cut.geom, tws, s_ecnt);
+      cut_floats<G>(tws, cut, grp, cw, tk, tf);
+      emit_round<G>(acc, tk, tf, grp, blk0, wave, cut.geom, tws, s_ecnt);
     }
 
     if (r + 1 < nr) {
@@ -946,6 +1124,7 @@ __global__ __launch_bounds__(kTailThreads) void scan_tail(
       if (tid == 0) {
         rw.seg[2 * tile] = base;
         rw.seg[2 * tile + 1] = total;
+        rw.stamp[2 * tile] = rw.st[topk::kS_TAU];
         if (total > rw.region) atomicOr(&rw.st[topk::kS_OVER], 1u);
       }
     }
@@ -993,166 +1172,6 @@ void launch_scan_g(const uint64_t* planes, const uint16_t* scales, int64_t nb_st
   }
 }
 
-// The sample of fathom_scan_topk: the scores of 2 * kSampleRuns wave tiles
-// per group, runs of two adjacent tiles (each plane row of a run is one
-// 128-byte line) spread evenly over the group's row, in fp32 but in no
-// particular order (only the cut tau is taken from them; the candidates are
-// then scored by the scan itself), written as order keys to
-// sample[group * G + h][i * kTileKeys + token] for sampled tile i.  One
-// workgroup per half tile (kSampleBlocks blocks), so that the sample covers
-// every CU: one round of loads brings the depths, the blocks' scales, the
-// group's queries and every plane row of the blocks (512 rows of 32 bytes,
-// the rows past a channel's depth included, so that no load waits for the
-// plan), all into LDS.  Then the four waves of block b score it over the
-// active channels of one quarter [32 k, 32 k + 32) each (one ballot mask per
-// depth, so that each channel reads its t_j planes and no more), and the
-// first adds the other three's partial sums.
-constexpr int kSampleBlocks = kNB / 2;                   // blocks per workgroup
-constexpr int kSampleQuarters = 4;                       // waves per block
-constexpr int kSampleThreads = kSampleBlocks * kSampleQuarters * 64;
-static_assert(kSampleKeys <= topk::kMaxSampleKeys, "sample buffer");
-static_assert(kD == 32 * kSampleQuarters, "32 channels per wave");
-
-// The sample's channels of depth T (mask m over the wave's quarter of the
-// channels, lanes 0-31) for lane `bit` of half `hsel` of block `b`, four at a
-// time: the LDS reads of the four (the lane's T plane words in one read, the
-// scale, the G query entries in one read) are issued together, then their
-// arithmetic.  A slot past the end of the mask reads the quarter's first
-// channel and adds 0.
-template <int T, int G>
-__device__ __forceinline__ void sample_depth(const uint4 (*s_w)[kSampleBlocks][2],
-                                             const uint16_t (*s_sc)[kSampleBlocks],
-                                             const float (*s_q)[G], uint64_t m, int c0, int b,
-                                             int hsel, int bit, float (&acc)[G]) {
-  while (m != 0ull) {
-    int c[4];
-    bool ok[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ok[u] = m != 0ull;
-      c[u] = c0 + (ok[u] ? __builtin_ctzll(m) : 0);
-      m &= m - 1;   // stays 0 once empty
-    }
-    uint32_t w[4][T];
-    float a[4], qv[4][G];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // Word hsel of planes 0-3 of channel c, block b.
-      const uint32_t* wp = reinterpret_cast<const uint32_t*>(&s_w[c[u]][b][hsel]);
-#pragma unroll
-      for (int p = 0; p < T; ++p) w[u][p] = wp[p];
-      a[u] = half_lo(s_sc[c[u]][b]);
-#pragma unroll
-      for (int h = 0; h < G; ++h) qv[u][h] = s_q[c[u]][h];   // uniform address: broadcast
-    }
-    __builtin_amdgcn_sched_barrier(0);   // every read above is issued before the arithmetic
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t cp = 0u;
-#pragma unroll
-      for (int p = 0; p < T; ++p) cp = 2 * cp + ((w[u][p] >> bit) & 1u);
-      // (c' + 1/2 - 2^(T-1)) * a / 2^(T-1)
-      float kh = __builtin_ldexpf(((float)cp + (0.5f - (float)(1 << (T - 1)))) * a[u], 1 - T);
-      kh = ok[u] ? kh : 0.0f;
-#pragma unroll
-      for (int h = 0; h < G; ++h) acc[h] = __builtin_fmaf(qv[u][h], kh, acc[h]);
-    }
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kSampleThreads) void fused_sample(
-    const uint64_t* __restrict__ planes, const uint16_t* __restrict__ scales, int64_t nb_store,
-    const uint8_t* __restrict__ depths, const float* __restrict__ q, int64_t run_stride,
-    uint32_t* __restrict__ sample, void* tws, int64_t n, uint32_t* __restrict__ gflag) {
-  constexpr int kT = kSampleThreads;                   // 1024 threads, four waves per block
-  constexpr int kSB = kSampleBlocks;
-  static_assert(kD * kPlanes * 2 == kT, "one 16-byte piece (two blocks of a row) per thread");
-  static_assert(G * kD <= kT, "one query entry per thread");
-  // 16 KB: for channel c, block b and 32-token half hs, the four plane words
-  // (planes 0-3) side by side, so that a lane reads its channel's planes at once.
-  __shared__ uint4 s_w[kD][kSB][2];
-  __shared__ uint16_t s_sc[kD][kSB];
-  __shared__ alignas(16) float s_q[kD][G];   // a channel's G entries in one read
-  __shared__ float s_part[kSB][kSampleQuarters - 1][G][kBlock];
-  const int64_t grp = blockIdx.y, hi = blockIdx.x;     // half tile hi: tile hi / 2
-  const int64_t ti = hi >> 1;
-  const int tid = threadIdx.x, lane = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = wv / kSampleQuarters, qtr = wv % kSampleQuarters;   // block, channel quarter
-  const int64_t blk0 = ((ti >> 1) * run_stride + (ti & 1)) * kNB + (hi & 1) * kSB;
-  // One round of loads: this lane's channel depth for the compute phase
-  // (lanes 0-31: channel 32 qtr + lane), the block scales, one query entry
-  // per thread, and the thread's 16-byte piece of plane row tid / 2 (blocks
-  // 2 (tid % 2) and 2 (tid % 2) + 1).
-  const int tl = lane < 32 ? min((int)depths[grp * kD + 32 * qtr + lane], kPlanes) : 0;
-  const float qv = tid < G * kD ? q[grp * G * kD + tid] : 0.0f;
-  // 16-byte loads when the store's rows allow them, else 8- and 2-byte ones.
-  const bool vec = (nb_store & 7) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(scales) & 15) == 0;
-  uint2 sv = make_uint2(0u, 0u);
-  if (tid < kD) {
-    const uint16_t* sp = scales + (grp * kD + tid) * nb_store + blk0;
-    if (vec) {
-      sv = *reinterpret_cast<const uint2*>(sp);
-    } else {
-      sv = make_uint2(sp[0] | ((uint32_t)sp[1] << 16), sp[2] | ((uint32_t)sp[3] << 16));
-    }
-  }
-  const int r = tid >> 1;
-  const uint64_t* a0 = planes + grp * kD * (int64_t)kPlanes * nb_store + blk0 +
-                       (int64_t)r * nb_store + 2 * (tid & 1);
-  uint4 v0;
-  if (vec) {
-    v0 = *reinterpret_cast<const uint4*>(a0);
-  } else {
-    const uint64_t x0 = a0[0], y0 = a0[1];
-    v0 = make_uint4((uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)y0, (uint32_t)(y0 >> 32));
-  }
-  // The group's selection state starts clear: flags, published cuts.
-  if (hi == 0 && tid < G) {
-    uint32_t* st = topk::row_ws(tws, n, kTileKeys, grp * G + tid).st;
-    st[topk::kS_OVER] = 0u;
-    st[topk::kS_FAIL] = 0u;
-    st[topk::kS_READY] = 0u;
-  }
-  if (hi == 0 && tid == 0) gflag[grp] = 0u;
-  if (tid < G * kD) s_q[tid % kD][tid / kD] = qv;
-  if (tid < kD) *reinterpret_cast<uint2*>(&s_sc[tid][0]) = sv;
-  {
-    // Row r = (channel r / 4, plane r % 4), blocks 2 (tid % 2) and 2 (tid % 2) + 1.
-    uint32_t* w = reinterpret_cast<uint32_t*>(s_w[r >> 2][2 * (tid & 1)]) + (r & 3);
-    w[0] = v0.x;    // block 2 (tid % 2), half 0
-    w[4] = v0.y;    //                    half 1
-    w[8] = v0.z;    // next block, half 0
-    w[12] = v0.w;   //             half 1
-  }
-  __syncthreads();
-  const int hsel = lane >> 5, bit = lane & 31, c0 = 32 * qtr;
-  float acc[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), c0, b, hsel, bit, acc);
-  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), c0, b, hsel, bit, acc);
-  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), c0, b, hsel, bit, acc);
-  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), c0, b, hsel, bit, acc);
-  if (qtr > 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) s_part[b][qtr - 1][h][lane] = acc[h];
-  }
-  __syncthreads();
-  if (qtr == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float v = acc[h];
-#pragma unroll
-      for (int k = 0; k < kSampleQuarters - 1; ++k) v += s_part[b][k][h][lane];
-      sample[(grp * G + h) * (int64_t)topk::kMaxSampleKeys + ti * kTileKeys +
-             ((hi & 1) * kSB + b) * kBlock + lane] = topk::order_key(v);
-    }
-  }
-}
-
 }  // namespace
 
 // fathom_scan_topk.  Fused path (64k to 2M keys, 32-bit offsets into a
@@ -1183,24 +1202,28 @@ hipError_t launch_scan_topk_g(const uint64_t* planes, const uint16_t* scales, in
     return launch_topk(sc, rows, n, k, indices, ws, stream);
   }
   const int64_t ntiles = nblk / kNB, rstride = ntiles / kSampleRuns;   // >= 16 tiles
-  hipLaunchKernelGGL((fused_sample<G>), dim3(2 * 2 * kSampleRuns, (unsigned)groups),
-                     dim3(kSampleThreads), 0, stream, planes, scales, nb_store, depths, q, rstride,
-                     fw.sample, fw.rows, n, fw.gflag);
+  // The call's epoch tells its sample flags and published cuts from those of
+  // earlier calls.
+  static std::atomic<uint32_t> epochs{0};
+  uint32_t epoch = ++epochs;
+  if (epoch == 0u) epoch = ++epochs;   // 0: zeroed memory is never taken for this call
   // The cut leaves about 1.6x the sample's share of k (plus 16 sampled keys)
   // at or above it, so that fewer than k candidates is rare.
   const double share = (double)k * (double)kSampleKeys / (double)n;
   const int target = (int)std::min<double>((double)kSampleKeys, std::ceil(1.6 * share + 16.0));
-  // The scan (MODE 1: with candidates, the cuts taken by its first
-  // workgroups; MODE 2, gated: the second pass).
+  // The scan (MODE 1: with candidates, the sample and the cuts taken by its
+  // first workgroups; MODE 2, gated: the second pass).
   auto scan = [&](auto mode, float* out, const uint32_t* gate) {
     constexpr int M = decltype(mode)::value;
     constexpr int NR = M == 2 ? kRescanRounds : 1;
     void* tws = M == 1 ? fw.rows : nullptr;
-    const CutArgs cut = M == 1 ? CutArgs{fw.sample, target, (int)rows, topk::row_geom(n, R),
-                                         g_cut_publish.load(), g_cut_spin.load()}
+    const CutArgs cut = M == 1 ? CutArgs{fw.sample, target, (int)groups, topk::row_geom(n, R),
+                                         g_cut_publish.load(), g_cut_spin.load(), rstride,
+                                         fw.gflag, fw.sflag, epoch}
                                : CutArgs{};
     const int64_t wgs = (nrounds + NR - 1) / NR;
-    const unsigned grid = (unsigned)(wgs * groups) + (M == 1 ? cut_workgroups((int)rows) : 0u);
+    const unsigned grid =
+        (unsigned)(wgs * groups) + (M == 1 ? sample_workgroups((int)groups) : 0u);
     hipLaunchKernelGGL((scan_main<G, M, NR>), dim3(grid), dim3(kThreads), 0, stream, planes,
                        scales, nb_store, depths, q, nrounds, n, wgs, out, tws, gate, cut);
     if (first < nblk)

@@ -53,7 +53,7 @@ static_assert(kChunk == kCompactChunk, "compaction regions are whole chunks");
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
-constexpr int kLdsCand = 16368;                      // candidates staged in LDS at most
+constexpr int kLdsCand = 16320;                      // candidates staged in LDS at most
 
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
@@ -406,6 +406,9 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
   const uint32_t first_count = c0 < c1 ? r.seg[2 * c0 + 1] : 0u;
   const uint32_t over = r.st[kS_OVER];
+  // fathom_scan_topk (pack > 1): every tile stamps the cut it was emitted
+  // with; a stamp other than the row's cut sends the row to the slow path.
+  const uint32_t tau_row = r.st[kS_TAU];
   uint2 e[kU][2];
   if (pre) {
 #pragma unroll
@@ -437,16 +440,19 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   uint2 et = make_uint2(0u, 0u);
   if (tpre && wave < ntail && (uint32_t)lane < src.region)
     et = src.cand[(uint32_t)(npacked + wave) * src.region + lane];
+  int stale = 0;
   {
     uint32_t mine = 0;
     for (int64_t c = c0; c < c1; ++c) {
       const uint32_t t = c == c0 ? first_count : r.seg[2 * c + 1];
+      if (pack > 1) stale |= r.stamp[2 * c] != tau_row;
       if (small) {
         s_gt[c] = t;
         s_base[c] = r.seg[2 * c];
       }
       mine += t;
     }
+    stale = __syncthreads_or(stale);
     uint32_t tot;
     uint32_t run = block_exclusive_sum<kResolveThreads>(mine, s_tmp, tot);
     ncand = tot;
@@ -457,12 +463,12 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         run += t;
       }
   }
-  src.direct = ncand < (uint32_t)k || over != 0u || mode == 1;   // the cut failed
-  if (src.direct && scores == nullptr) {   // no scores to fall back on: flag the row
-    if (threadIdx.x == 0) {
-      r.st[kS_FAIL] = 1u;
-      gflag[row / G] = 1u;
-    }
+  src.direct = ncand < (uint32_t)k || over != 0u || stale || mode == 1;   // the cut failed
+  // Mode 0 records for every row whether the second pass must select it.
+  const bool fail = src.direct && scores == nullptr;
+  if (mode == 0 && threadIdx.x == 0 && gflag != nullptr) r.st[kS_FAIL] = fail ? 1u : 0u;
+  if (fail) {   // no scores to fall back on: flag the row
+    if (threadIdx.x == 0) gflag[row / G] = 1u;
     return;
   }
   const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;

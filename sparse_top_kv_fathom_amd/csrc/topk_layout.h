@@ -43,8 +43,8 @@ __host__ __device__ inline size_t row_words(int64_t n, int64_t R) {
 struct RowWs {
   uint32_t* st;      // [kS_WORDS]
   uint32_t* cand;    // [nchunks][region][2]: key, index
-  uint32_t* seg;     // [nchunks][2]: first slot of the chunk's region, its candidates
-  uint32_t* ord;     // [nchunks][2]: keys > T and == T in the chunks before this one
+  uint32_t* seg;     // [nchunks][2]: first slot of the chunk's candidates, their count
+  uint32_t* stamp;   // [nchunks][2]: fathom_scan_topk: the cut chunk c was emitted with, at [2c]
   uint32_t region;
 };
 
@@ -55,7 +55,7 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   r.st = p;
   r.cand = r.st + kS_WORDS;
   r.seg = r.cand + 2 * (size_t)cand_cap(n);
-  r.ord = r.seg + 2 * (size_t)n_chunks(n, R);
+  r.stamp = r.seg + 2 * (size_t)n_chunks(n, R);
   return r;
 }
 
@@ -65,14 +65,14 @@ struct RowGeom {
   uint64_t words;      // row_words(n, R)
   uint32_t region;     // region(n, R)
   uint32_t seg_off;    // first word of the segment table
-  uint32_t ord_off;    // first word of the order table
+  uint32_t stamp_off;  // first word of the stamp table
 };
 __host__ __device__ inline RowGeom row_geom(int64_t n, int64_t R) {
   RowGeom g;
   g.words = row_words(n, R);
   g.region = region(n, R);
   g.seg_off = (uint32_t)(kS_WORDS + 2 * cand_cap(n));
-  g.ord_off = g.seg_off + 2 * (uint32_t)n_chunks(n, R);
+  g.stamp_off = g.seg_off + 2 * (uint32_t)n_chunks(n, R);
   return g;
 }
 __device__ __forceinline__ RowWs row_at(void* ws, const RowGeom& g, int64_t row) {
@@ -82,7 +82,7 @@ __device__ __forceinline__ RowWs row_at(void* ws, const RowGeom& g, int64_t row)
   r.st = p;
   r.cand = p + kS_WORDS;
   r.seg = p + g.seg_off;
-  r.ord = p + g.ord_off;
+  r.stamp = p + g.stamp_off;
   return r;
 }
 
@@ -93,10 +93,12 @@ __device__ __forceinline__ RowWs row_at(void* ws, const RowGeom& g, int64_t row)
 // buffer and a row's selection fails, or when the call cannot take the fused
 // path).
 constexpr int kMaxSampleKeys = 16384;   // sampled keys per row at most
+constexpr int kSampleFlags = 64;        // sample workgroups per group at most
 struct FusedWs {
   void* rows;        // [rows] RowWs with R = the scan's tile
   uint32_t* sample;  // [rows][kMaxSampleKeys] order keys of the sampled scores
   uint32_t* gflag;   // [groups]
+  uint32_t* sflag;   // [groups][kSampleFlags] epoch of the call whose sample part is out
   float* scores;     // [rows][n]
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -105,7 +107,8 @@ __host__ __device__ inline size_t fused_front_bytes(int64_t rows, int64_t groups
   // The fused layout, or fathom_topk's (used when the call is not fused),
   // whichever is larger; the score area follows.
   const size_t fused = align256((size_t)rows * row_words(n, R) * 4) +
-                       align256((size_t)rows * kMaxSampleKeys * 4) + align256((size_t)groups * 4);
+                       align256((size_t)rows * kMaxSampleKeys * 4) +
+                       align256((size_t)groups * (1 + kSampleFlags) * 4);
   const size_t plain = align256((size_t)rows * row_words(n, kCompactChunk) * 4);
   return fused > plain ? fused : plain;
 }
@@ -117,6 +120,7 @@ __host__ __device__ inline FusedWs fused_ws(void* ws, int64_t rows, int64_t grou
   f.sample = reinterpret_cast<uint32_t*>(p + align256((size_t)rows * row_words(n, R) * 4));
   f.gflag = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(f.sample) +
                                         align256((size_t)rows * kMaxSampleKeys * 4));
+  f.sflag = f.gflag + groups;
   f.scores = reinterpret_cast<float*>(p + fused_front_bytes(rows, groups, n, R));
   return f;
 }

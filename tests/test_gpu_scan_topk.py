@@ -448,5 +448,5 @@ def test_scan_topk_cut_never_published_falls_back(fk, write_scores):
     try:
         _scan_topk_case(fk, 2, n, k, 92, seed=101, write_scores=write_scores)
     finally:
-        fk.test_cut_hooks(publish=True, spin_limit=16384)
+        fk.test_cut_hooks(publish=True, spin_limit=2048)
     _scan_topk_case(fk, 2, n, k, 92, seed=102, write_scores=write_scores)
