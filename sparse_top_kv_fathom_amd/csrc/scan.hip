@@ -288,12 +288,13 @@ constexpr int64_t kFusedMaxTiles = 4096;   // regions per row the selection stag
 constexpr int kRescanRounds = 8;           // rounds per workgroup of the gated second pass
 constexpr int kSampleRuns = 8;             // sampled runs of two wave tiles per group
 constexpr int kSampleKeys = 2 * kSampleRuns * kTileKeys;   // 8192 per row
-constexpr int kSampleWgs = 2 * kSampleRuns * kNB / 2;      // sample workgroups per group (64)
+constexpr int kSampleWgBlocks = 4;                         // blocks per sample workgroup
+constexpr int kSampleWgs = 2 * kSampleRuns * kNB / kSampleWgBlocks;   // per group (32)
 constexpr int kCutSpin = 2048;             // polls (about 0.2 us each) of a cut not yet out
 
 // The sample and the cut of fathom_scan_topk, taken inside the candidate
 // scan's launch.  Its first groups * kSampleWgs workgroups (a multiple of the
-// XCD count, so the scan's own ids keep their XCD) each score two blocks of
+// XCD count, so the scan's own ids keep their XCD) each score four blocks of
 // the group's sample: 8 runs of two adjacent wave tiles spread evenly over
 // the row.  Their order keys go to the sample buffer with agent-scope stores,
 // and each workgroup then sets its own flag to the call's epoch.  Sample
@@ -325,20 +326,20 @@ struct CutArgs {
 
 __host__ __device__ inline uint32_t sample_workgroups(int groups) {
   static_assert((kSampleWgs % kXcds) == 0, "whole XCD rounds");
-  static_assert(kSampleWgs == topk::kSampleFlags, "one flag per sample workgroup, one per lane");
+  static_assert(kSampleWgs <= topk::kSampleFlags, "one flag per sample workgroup, one per lane");
   return (uint32_t)groups * kSampleWgs;
 }
 // The low 10 bits of a published ready word.
 __device__ __forceinline__ uint32_t ready_bits(uint32_t epoch) { return ((epoch & 0x1FFu) << 1) | 1u; }
 
-// The sample's channels of depth T (mask m over the wave's half of the
-// channels) for lane `bit` of half `hsel` of block `b`, four at a time: the
+// The sample's channels of depth T (mask m over 64 channels from c0) for
+// lane `bit` of half `hsel` of block `b`, four at a time: the
 // LDS reads of the four (the lane's T plane words in one read, the scale,
 // the G query entries in one read) are issued together, then their
-// arithmetic.  A slot past the end of the mask reads the half's first
-// channel and adds 0.
+// arithmetic.  A slot past the end of the mask reads channel c0 and adds 0.
 template <int T, int G>
-__device__ __forceinline__ void sample_depth(const uint4 (*s_w)[2][2], const uint16_t (*s_sc)[2],
+__device__ __forceinline__ void sample_depth(const uint4 (*s_w)[kSampleWgBlocks][2],
+                                             const uint16_t (*s_sc)[kSampleWgBlocks],
                                              const float (*s_q)[G], uint64_t m, int c0, int b,
                                              int hsel, int bit, float (&acc)[G]) {
   while (m != 0ull) {
@@ -378,86 +379,89 @@ __device__ __forceinline__ void sample_depth(const uint4 (*s_w)[2][2], const uin
 }
 
 // One sample workgroup of the candidate scan (workgroup id `wg` below
-// sample_workgroups): blocks 2 pr and 2 pr + 1 of sampled tile ti, in fp32
+// sample_workgroups): blocks 4 pr to 4 pr + 3 of sampled tile ti, in fp32
 // but in no particular order (only the cut is taken from the sample).  One
-// round of loads brings the depths, the two blocks' scales, the group's
-// queries and every plane row of the two blocks (512 rows of 16 bytes, the
-// rows past a channel's depth too, so no load waits for the plan) into LDS,
-// laid out so that a lane reads its channel's plane words, and a channel's
-// query entries, in one LDS read each; waves 2b and 2b + 1 score block b
-// over the channels [0, 64) and [64, 128), and the first adds the second's
-// partial sums.  Then its flag and, in sample workgroups 0 to G - 1, a cut.
+// round of loads brings the depths, the blocks' scales, the group's queries
+// and every plane row of the blocks (512 rows of 32 bytes, the rows past a
+// channel's depth too, so no load waits for the plan) into LDS, laid out so
+// that a lane reads its channel's plane words, and a channel's query
+// entries, in one LDS read each; wave b scores block b over every active
+// channel.  Then its flag and, in sample workgroups 0 to G - 1, a cut.
 template <int G>
 __device__ void sample_wg(const CutArgs& cut, uint32_t wg, const uint64_t* __restrict__ planes,
                           const uint16_t* __restrict__ scales, int64_t nb_store,
                           const uint8_t* __restrict__ depths, const float* __restrict__ q,
                           void* tws, char* smem) {
-  constexpr int kQOff = kD * 2 * 2 * 16 + kD * 2 * 2;       // after s_w and s_sc
-  constexpr int kPartOff = kQOff + kD * G * 4;
-  constexpr int kArrOff = kPartOff + 2 * G * kBlock * 4;
+  constexpr int SB = kSampleWgBlocks;
+  static_assert(SB == kWaves, "one wave per block");
+  constexpr int kScOff = kD * SB * 2 * 16;
+  constexpr int kQOff = kScOff + kD * SB * 2;                // after s_w and s_sc
+  constexpr int kArrOff = kQOff + kD * G * 4;
   static_assert(kQOff % 16 == 0, "s_q in whole 16-byte rows");
-  uint4 (*s_w)[2][2] = reinterpret_cast<uint4 (*)[2][2]>(smem);            // [kD][2][2]
-  uint16_t (*s_sc)[2] = reinterpret_cast<uint16_t (*)[2]>(smem + kD * 2 * 2 * 16);
+  uint4 (*s_w)[SB][2] = reinterpret_cast<uint4 (*)[SB][2]>(smem);             // [kD][SB][2]
+  uint16_t (*s_sc)[SB] = reinterpret_cast<uint16_t (*)[SB]>(smem + kScOff);
   float (*s_q)[G] = reinterpret_cast<float (*)[G]>(smem + kQOff);
-  float (*s_part)[G][kBlock] = reinterpret_cast<float (*)[G][kBlock]>(smem + kPartOff);
   uint32_t* s_arr = reinterpret_cast<uint32_t*>(smem + kArrOff);
   const int64_t grp = wg / kSampleWgs;
-  const int sb = (int)(wg % kSampleWgs), ti = sb >> 2, pr = sb & 3;
-  const int64_t blk0 = ((ti >> 1) * cut.rstride + (ti & 1)) * kNB + 2 * pr;
+  const int sb = (int)(wg % kSampleWgs);
+  constexpr int kPerTile = kNB / SB;                          // sample workgroups per tile
+  const int ti = sb / kPerTile, pr = sb % kPerTile;
+  const int64_t blk0 = ((ti >> 1) * cut.rstride + (ti & 1)) * kNB + SB * pr;
   const int tid = threadIdx.x, lane = lane_id();
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = wv >> 1, half = wv & 1;   // block of the pair, channel half
-  const int tl = min((int)depths[grp * kD + 64 * half + lane], kPlanes);
+  const int b = __builtin_amdgcn_readfirstlane(tid >> 6);   // this wave's block
+  const int tlo = min((int)depths[grp * kD + lane], kPlanes);
+  const int thi = min((int)depths[grp * kD + 64 + lane], kPlanes);
   for (int i = tid; i < G * kD; i += kThreads) s_q[i % kD][i / kD] = q[grp * G * kD + i];
   if (tid < kD) {
     const uint16_t* sp = scales + (grp * kD + tid) * nb_store + blk0;
-    s_sc[tid][0] = sp[0];
-    s_sc[tid][1] = sp[1];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) s_sc[tid][u] = sp[u];
   }
-  // Plane rows r = tid and tid + 256: (channel r / 4, plane r % 4), both blocks.
+  // Plane rows r = tid and tid + 256: (channel r / 4, plane r % 4), the
+  // workgroup's SB blocks.
   const bool vec = (nb_store & 1) == 0 && (reinterpret_cast<uintptr_t>(planes) & 15) == 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = tid + kThreads * i;
     const uint64_t* a0 = planes + (grp * kD * kPlanes + r) * nb_store + blk0;
-    uint64_t x0, x1;
+    uint64_t x[SB];
     if (vec) {
-      const uint4 v = *reinterpret_cast<const uint4*>(a0);
-      x0 = v.x | ((uint64_t)v.y << 32);
-      x1 = v.z | ((uint64_t)v.w << 32);
+#pragma unroll
+      for (int u = 0; u < SB / 2; ++u) {
+        const uint4 v = reinterpret_cast<const uint4*>(a0)[u];
+        x[2 * u] = v.x | ((uint64_t)v.y << 32);
+        x[2 * u + 1] = v.z | ((uint64_t)v.w << 32);
+      }
     } else {
-      x0 = a0[0];
-      x1 = a0[1];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) x[u] = a0[u];
     }
     uint32_t* w = reinterpret_cast<uint32_t*>(s_w[r >> 2][0]) + (r & 3);
-    w[0] = (uint32_t)x0;           // block 0, tokens 0-31
-    w[4] = (uint32_t)(x0 >> 32);   //          tokens 32-63
-    w[8] = (uint32_t)x1;           // block 1
-    w[12] = (uint32_t)(x1 >> 32);
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      w[8 * u] = (uint32_t)x[u];               // block u, tokens 0-31
+      w[8 * u + 4] = (uint32_t)(x[u] >> 32);   //          tokens 32-63
+    }
   }
   __syncthreads();
-  const int hsel = lane >> 5, bit = lane & 31, c0 = 64 * half;
+  const int hsel = lane >> 5, bit = lane & 31;
   float acc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h] = 0.0f;
-  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tl == 4), c0, b, hsel, bit, acc);
-  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tl == 3), c0, b, hsel, bit, acc);
-  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tl == 2), c0, b, hsel, bit, acc);
-  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tl == 1), c0, b, hsel, bit, acc);
-  if (half == 1) {
+  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(tlo == 4), 0, b, hsel, bit, acc);
+  sample_depth<4, G>(s_w, s_sc, s_q, __ballot(thi == 4), 64, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(tlo == 3), 0, b, hsel, bit, acc);
+  sample_depth<3, G>(s_w, s_sc, s_q, __ballot(thi == 3), 64, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(tlo == 2), 0, b, hsel, bit, acc);
+  sample_depth<2, G>(s_w, s_sc, s_q, __ballot(thi == 2), 64, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(tlo == 1), 0, b, hsel, bit, acc);
+  sample_depth<1, G>(s_w, s_sc, s_q, __ballot(thi == 1), 64, b, hsel, bit, acc);
 #pragma unroll
-    for (int h = 0; h < G; ++h) s_part[b][h][lane] = acc[h];
-  }
-  __syncthreads();
-  if (half == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      __hip_atomic_store(cut.sample + (grp * G + h) * (int64_t)topk::kMaxSampleKeys +
-                             ti * kTileKeys + (2 * pr + b) * kBlock + lane,
-                         topk::order_key(acc[h] + s_part[b][h][lane]), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the keys are out before the flag
-  }
+  for (int h = 0; h < G; ++h)
+    __hip_atomic_store(cut.sample + (grp * G + h) * (int64_t)topk::kMaxSampleKeys +
+                           ti * kTileKeys + (SB * pr + b) * kBlock + lane,
+                       topk::order_key(acc[h]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the keys are out before the flag
   __syncthreads();
   uint32_t* flags = cut.sflag + grp * topk::kSampleFlags;
   if (tid == 0) __hip_atomic_store(flags + sb, cut.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -468,7 +472,9 @@ __device__ void sample_wg(const CutArgs& cut, uint32_t wg, const uint64_t* __res
     bool all = false;
     for (int it = 0; it < kCutSpin && !all; ++it) {
       const uint32_t f =
-          __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          lane < kSampleWgs
+              ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+              : cut.epoch;
       all = __ballot(f != cut.epoch) == 0ull;
       if (!all) __builtin_amdgcn_s_sleep(4);
     }
@@ -649,9 +655,13 @@ struct MainCtx {
 
 template <int T, int G>
 __device__ __forceinline__ void main_load_plane(const MainCtx& c, int j, int p, ChanLoad<T, G>& L) {
+  // Read through the constant address space (the store is read-only while
+  // the scan runs): the uniform plane words are then always scalar loads,
+  // whatever else the kernel writes.
+  typedef const __attribute__((address_space(4))) uint64_t cu64;
   const char* rp = c.planes + (uint32_t)j * (kPlanes * c.pstride) + p * c.pstride;
 #pragma unroll
-  for (int b = 0; b < kNB; ++b) L.pw[p][b] = *reinterpret_cast<const uint64_t*>(rp + b * 8);
+  for (int b = 0; b < kNB; ++b) L.pw[p][b] = *(cu64*)(rp + b * 8);
 }
 
 template <int T, int G>
@@ -842,7 +852,7 @@ __global__ __launch_bounds__(kThreads) void scan_main(
   static_assert(MODE != 1 || NR == 1, "candidate emission runs one round per workgroup");
   // The sample workgroups' LDS (sample_wg) lives in sh.
   static_assert(sizeof(MainShared<G>) >=
-                    kD * 2 * 2 * 16 + kD * 2 * 2 + kD * G * 4 + 2 * G * kBlock * 4 + 8,
+                    kD * kSampleWgBlocks * 2 * 16 + kD * kSampleWgBlocks * 2 + kD * G * 4 + 8,
                 "sample scratch");
   static_assert(sizeof(MainShared<G>) >= (topk::kBins + kThreads / 64 + 2) * 4, "cut scratch");
   __shared__ MainShared<G> sh;
