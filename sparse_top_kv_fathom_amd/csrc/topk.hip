@@ -15,17 +15,17 @@
 //   compact — one pass over the row writes every key >= tau (key, index) of
 //             a chunk, in index order, to that chunk's own region of the
 //             row's candidate buffer, and its count;
-//   resolve — one workgroup per row: stages the candidates (key, index) in
-//             LDS, finds the k-th largest key T with two radix digits counted
-//             from tau and the keys == T still needed, counts per chunk the
-//             keys > T and == T, prefixes the counts and writes every chunk's
-//             selected indices (every key > T, the earliest keys == T) at its
-//             prefix position, so the row comes out in index order without a
-//             sort.
-// If the cut fails (fewer than k keys >= tau, or a chunk with more than
-// its region holds: heavy ties or adversarial rows), or the candidates do not
-// fit in LDS, the resolve workgroup does all of it alone, from the scores or
-// the regions: same result, many more passes.
+//   resolve — one workgroup per row: prefixes the chunk counts, loads the
+//             candidates into registers (each wave a contiguous segment of
+//             them in index order), finds the k-th largest key T with two
+//             radix digits counted from tau and the keys == T still needed,
+//             and writes every selected index (every key > T, the earliest
+//             keys == T) at its place, so the row comes out in index order
+//             without a sort.
+// If the cut fails (fewer than k keys >= tau, or a chunk with more than its
+// region holds: heavy ties or adversarial rows), or there are more candidates
+// than the registers hold, the resolve workgroup does all of it alone, from
+// the scores or the regions: same result, many more passes.
 #include <mutex>
 
 #include "fathom_internal.h"
@@ -53,7 +53,6 @@ static_assert(kChunk == kCompactChunk, "compaction regions are whole chunks");
 constexpr int kWaveKeys = 64 * kPerThread;           // 2048 contiguous keys per wave
 constexpr int kResolveThreads = 1024;
 constexpr int kGroups = 4096;                        // chunk groups of the one-workgroup write
-constexpr int kLdsCand = 16320;                      // candidates staged in LDS at most
 
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = lane_id();
@@ -341,35 +340,51 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
 }
 
 // Per row: T (the k-th largest key), the keys == T still needed, and the
-// ordered write.  Rows whose candidates fit in LDS (the usual case) stage
-// (key, index) there and do everything from LDS; other rows (the cut
-// failed, or too many candidates or chunks) are resolved and written from the
-// candidate regions or the scores, by the same workgroup.
+// ordered write.  The row's candidates come in units whose candidates lie
+// packed in index order from the unit's first slot: below npacked, runs of
+// `pack` chunks (the main scan kernel's rounds; pack = 1: every chunk of a
+// compaction from scores), then single chunks (the scan's tail tiles).
+//   counts — chunk counts and stamps read coalesced (thread c takes chunk c,
+//            c + 1024, ...), summed per unit across the unit's lanes, then
+//            prefixed over the units in index order;
+//   load   — with at most kRegCand candidates the row's candidates, in index
+//            order, are split into one contiguous segment per wave and loaded
+//            64 at a time into registers (lane l of step j: candidate
+//            s0 + 64 j + l of the wave's segment [s0, s1)), the unit of each
+//            found from the unit of its 64-candidate block;
+//   select — two radix digits counted from the cut into LDS give T and the
+//            keys == T still needed; the keys > T and == T of every wave's
+//            segment, prefixed over the waves, place every selected index
+//            (every key > T, the earliest keys == T) at its position in index
+//            order.
+// A row whose cut failed (fewer than k candidates, a unit with more than its
+// slots hold, a chunk stamped with another cut) is selected from the scores;
+// a row with more candidates than the registers hold, from the candidate
+// regions; both by the same workgroup with more passes.
 // mode 0: every row; a row whose candidates cannot give the selection goes to
 // the scores, or, when there are none (fathom_scan_topk without a score
 // buffer), is flagged (kS_FAIL, and its group in gflag) for a second pass.
 // mode 1: the flagged rows only, from the scores.
-// pack > 1 (fathom_scan_topk): chunks [0, npacked) come in runs of `pack`
-// whose candidates lie packed in index order from the run's first slot (the
-// main scan kernel's rounds); the others each at their own first slot.
+// flags: kResolveStamps — every chunk's stamp must equal the row's cut;
+// kResolveOver — the row's overflow word is checked.
+// pack is a power of two at most 64 and npacked a multiple of it, so a run's
+// chunks c are consecutive lanes of one wave.
+constexpr int kResolveStamps = 1, kResolveOver = 2;
+constexpr int kRegSteps = 16;                              // loads of 64 candidates per wave
+constexpr int kRegCand = kRegSteps * kResolveThreads;      // 16384 candidates at most
 __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __restrict__ scores,
                                                                 int64_t n, int64_t R, int k,
                                                                 void* ws,
                                                                 int32_t* __restrict__ out,
                                                                 int mode, uint32_t* gflag,
-                                                                int G, int pack, int64_t npacked) {
+                                                                int G, int pack, int64_t npacked,
+                                                                int flags) {
   __shared__ uint32_t s_hist[2 * kBins];
-  __shared__ uint32_t s_gt[kGroups];
-  // Staged candidates: keys and indices.  The path that does not stage them
-  // uses s_idx as its per-group count of keys == T (kGroups <= kLdsCand).
-  __shared__ uint32_t s_key[kLdsCand], s_idx[kLdsCand];
-  static_assert(kGroups <= kLdsCand, "s_eq aliases s_idx");
-  uint32_t* const s_eq = s_idx;
-  // While staging: the first candidate slot of every chunk (s_hist is free).
-  static_assert(kGroups <= 2 * kBins, "s_base aliases s_hist");
-  uint32_t* const s_base = s_hist;
+  __shared__ uint32_t s_gt[kGroups];   // units' first candidates; groups' keys > T
+  __shared__ uint32_t s_eq[kGroups];   // the unit of each 64-candidate block; groups' keys == T
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
+  static_assert(kRegCand / 64 <= kGroups, "one word per 64-candidate block");
   const int64_t row = blockIdx.x;
   RowWs r = row_ws(ws, n, R, row);
   if (mode == 1 && r.st[kS_FAIL] == 0u) return;   // uniform over the workgroup
@@ -383,85 +398,76 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   src.region = r.region;
   const int64_t nc = src.nc;
   int32_t* dst = out + row * (int64_t)k;
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  constexpr int kW = kResolveThreads / 64, kU = 8;
+  // The wave index, known to the compiler as uniform.
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = lane_id();
+  constexpr int kW = kResolveThreads / 64;
+  const uint64_t below = lanes_below();
 
-  // Candidates of the row: the chunk counts, summed (and, when they fit,
-  // prefixed into s_gt for staging).  With at most 128 chunks, the first 128
-  // candidate slots of the wave's chunks (w, w + 16, ...) are loaded at the
-  // same time as the counts and the overflow flag, before either is known,
-  // so staging them costs no second round trip to memory; slots past a
-  // chunk's count are never used.  With packed runs (pack > 1) the same holds
-  // for the first 32 slots of each run among the wave's first kPreRuns runs
-  // (w, w + 16, ...: four runs of 16 lanes per load).
-  const bool small = nc <= kGroups;
-  const bool pre = pack == 1 && nc <= kW * kU;
-  const bool ppre = pack > 1;
-  constexpr int kPreRuns = 4 * kU;
   const int64_t nrun = npacked / pack;
+  const int64_t nunits = nrun + (nc - npacked);
+  const int lp = __builtin_ctz((unsigned)pack);
   const uint32_t cap = (uint32_t)pack * src.region;   // slots of a run
-  auto pre_run = [&](int i) { return wave + (int64_t)kW * (4 * i + (lane >> 4)); };
+  auto unit_base = [&](int64_t u) {
+    return u < nrun ? (uint32_t)u * cap : (uint32_t)(npacked + (u - nrun)) * src.region;
+  };
+  const uint32_t over = (flags & kResolveOver) ? r.st[kS_OVER] : 0u;
+  const uint32_t tau = r.st[kS_TAU];
+
+  // Counts.  Candidates per unit (s_gt[u] while they fit), the unit's limit
+  // checked; then their prefix in s_gt and the total.
+  const bool small = nunits <= kGroups;
   uint32_t ncand = 0;
-  const int64_t per = (nc + kResolveThreads - 1) / kResolveThreads;
-  const int64_t c0 = min<int64_t>(nc, threadIdx.x * per), c1 = min<int64_t>(nc, c0 + per);
-  const uint32_t first_count = c0 < c1 ? r.seg[2 * c0 + 1] : 0u;
-  const uint32_t over = r.st[kS_OVER];
-  // fathom_scan_topk (pack > 1): every tile stamps the cut it was emitted
-  // with; a stamp other than the row's cut sends the row to the slow path.
-  const uint32_t tau_row = r.st[kS_TAU];
-  uint2 e[kU][2];
-  if (pre) {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t c = wave + u * kW;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t o = lane + 64 * h;
-        e[u][h] = (c < nc && o < src.region) ? src.cand[(uint32_t)c * src.region + o]
-                                             : make_uint2(0u, 0u);
-      }
-    }
-  } else if (ppre) {
-#pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int64_t run = pre_run(i);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t o = (lane & 15) + 16 * h;
-        e[i][h] = (run < nrun && o < cap) ? src.cand[(uint32_t)run * cap + o] : make_uint2(0u, 0u);
-      }
-    }
-  }
-  // Chunks past the packed runs (the scan's tail tiles, each at its own
-  // slots chunk * region): wave w < their number prefetches the first 64 of
-  // chunk npacked + w.
-  const int64_t ntail = nc - npacked;
-  const bool tpre = ppre && ntail <= kW;
-  uint2 et = make_uint2(0u, 0u);
-  if (tpre && wave < ntail && (uint32_t)lane < src.region)
-    et = src.cand[(uint32_t)(npacked + wave) * src.region + lane];
   int stale = 0;
   {
     uint32_t mine = 0;
-    for (int64_t c = c0; c < c1; ++c) {
-      const uint32_t t = c == c0 ? first_count : r.seg[2 * c + 1];
-      if (pack > 1) stale |= r.stamp[2 * c] != tau_row;
-      if (small) {
-        s_gt[c] = t;
-        s_base[c] = r.seg[2 * c];
+    // The loop bound is uniform: every lane takes part in the shuffles.
+    for (int64_t c0 = 0; c0 < nc; c0 += 4 * kResolveThreads) {
+      // Slices x of 1024 chunks that hold a chunk (uniform).
+      const int nx = (int)min<int64_t>(4, (nc - c0 + kResolveThreads - 1) / kResolveThreads);
+      uint32_t cnt[4] = {0u, 0u, 0u, 0u}, stp[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        if (x < nx) {
+          const int64_t c = min<int64_t>(c0 + threadIdx.x + x * kResolveThreads, nc - 1);
+          cnt[x] = r.seg[2 * c + 1];
+          stp[x] = r.stamp[2 * c];
+        }
       }
-      mine += t;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int64_t c = c0 + threadIdx.x + x * kResolveThreads;
+        const bool v = c < nc;
+        const uint32_t t = v ? cnt[x] : 0u;
+        if (v && (flags & kResolveStamps)) stale |= stp[x] != tau;
+        uint32_t tr = t;   // the run's sum over its `pack` lanes
+        for (int m = 1; m < pack; m <<= 1) tr += (uint32_t)__shfl_xor((int)tr, m);
+        const bool packed = c < npacked;
+        const int64_t u = packed ? (c >> lp) : nrun + (c - npacked);
+        if (v && (!packed || (c & (pack - 1)) == 0)) {
+          const uint32_t tot = packed ? tr : t;
+          stale |= tot > (packed ? cap : src.region);   // more than the unit holds
+          if (small) s_gt[u] = tot;
+          mine += tot;
+        }
+      }
     }
     stale = __syncthreads_or(stale);
     uint32_t tot;
-    uint32_t run = block_exclusive_sum<kResolveThreads>(mine, s_tmp, tot);
-    ncand = tot;
-    if (small)
-      for (int64_t c = c0; c < c1; ++c) {
-        const uint32_t t = s_gt[c];
-        s_gt[c] = run;   // first LDS slot of chunk c
+    if (small) {
+      const int64_t per = (nunits + kResolveThreads - 1) / kResolveThreads;
+      const int64_t u0 = min<int64_t>(nunits, threadIdx.x * per), u1 = min<int64_t>(nunits, u0 + per);
+      uint32_t sum = 0;
+      for (int64_t u = u0; u < u1; ++u) sum += s_gt[u];
+      uint32_t run = block_exclusive_sum<kResolveThreads>(sum, s_tmp, tot);
+      for (int64_t u = u0; u < u1; ++u) {
+        const uint32_t t = s_gt[u];
+        s_gt[u] = run;
         run += t;
       }
+    } else {
+      (void)block_exclusive_sum<kResolveThreads>(mine, s_tmp, tot);
+    }
+    ncand = tot;
   }
   src.direct = ncand < (uint32_t)k || over != 0u || stale || mode == 1;   // the cut failed
   // Mode 0 records for every row whether the second pass must select it.
@@ -471,279 +477,174 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     if (threadIdx.x == 0) gflag[row / G] = 1u;
     return;
   }
-  const bool lds = !src.direct && small && ncand <= (uint32_t)kLdsCand;
-  __syncthreads();
+  const bool regs = !src.direct && small && ncand <= (uint32_t)kRegCand;
 
-  // Candidates of packed run `run`: first LDS slot and count.
-  auto run_span = [&](int64_t run, uint32_t& d) {
-    const int64_t ca = run * pack, cb = ca + pack;
-    d = s_gt[ca];
-    return (cb < nc ? s_gt[cb] : ncand) - d;
-  };
-  if (lds && ppre) {
+  // T (the k-th largest of the keys visit(f) passes to f, once per digit) and
+  // the keys == T to take.  from_tau: every key is >= tau and the cut sits
+  // just below the k-th key, so bins of 4096 keys above tau (the last one
+  // open-ended), then the 4096 keys of the chosen bin; otherwise, or when the
+  // k-th key lies in the open-ended bin, three radix digits (11, 11, 10 bits)
+  // from the top.
+  auto kth = [&](auto&& visit, bool from_tau, uint32_t& T, uint32_t& need) {
+    need = (uint32_t)k;
+    uint32_t prefix = 0;
+    bool done = false;
+    if (from_tau) {
+      for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+      __syncthreads();
+      visit([&](uint32_t key) { atomicAdd(&s_hist[min((key - tau) >> 12, (uint32_t)kBins - 1u)], 1u); });
+      __syncthreads();
+      {
+        constexpr int kPer = kBins / kResolveThreads;
+        uint32_t h[kPer];
 #pragma unroll
-    for (int i = 0; i < kU; ++i) {
-      const int64_t run = pre_run(i);
-      if (run < nrun) {
-        uint32_t d;
-        const uint32_t cnt = run_span(run, d);
+        for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+        pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
+      }
+      __syncthreads();
+      const uint32_t binA = s_sel[0], needA = s_sel[1];
+      __syncthreads();
+      if (binA < (uint32_t)kBins - 1u) {
+        for (int i = threadIdx.x; i < 2 * kBins; i += kResolveThreads) s_hist[i] = 0u;
+        __syncthreads();
+        visit([&](uint32_t key) {
+          const uint32_t d = key - tau;
+          if ((d >> 12) == binA) atomicAdd(&s_hist[d & 4095u], 1u);
+        });
+        __syncthreads();
+        constexpr int kPer = 2 * kBins / kResolveThreads;
+        uint32_t h[kPer];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t o = (lane & 15) + 16 * h;
-          if (o < cnt) {
-            s_key[d + o] = e[i][h].x;
-            s_idx[d + o] = e[i][h].y;
-          }
-        }
+        for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+        pick_bin<kResolveThreads, kPer>(h, needA, s_tmp, s_sel);
+        __syncthreads();
+        prefix = tau + (binA << 12) + s_sel[0];
+        need = s_sel[1];
+        done = true;
+        __syncthreads();
       }
     }
-  }
-  if (lds && tpre && wave < ntail) {
-    const int64_t c = npacked + wave;
-    const uint32_t d = s_gt[c], cnt = (c + 1 < nc ? s_gt[c + 1] : ncand) - d;
-    if ((uint32_t)lane < cnt) {
-      s_key[d + lane] = et.x;
-      s_idx[d + lane] = et.y;
-    }
-    for (uint32_t o = 64 + lane; o < cnt; o += 64) {
-      const uint2 x = src.cand[(uint32_t)c * src.region + o];
-      s_key[d + o] = x.x;
-      s_idx[d + o] = x.y;
-    }
-  }
-  if (lds && pre) {
-    auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t c = wave + u * kW;
-      const uint32_t cnt = c < nc ? count(c) : 0u;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t o = lane + 64 * h;
-        if (o < cnt) {
-          s_key[s_gt[c] + o] = e[u][h].x;
-          s_idx[s_gt[c] + o] = e[u][h].y;
-        }
-      }
-    }
-  }
-  if (lds) {
-    // Stage the candidates, chunk after chunk in index order: chunk c at
-    // [s_gt[c], s_gt[c] + count(c)).  With at most 128 chunks the first 128
-    // candidates of every chunk were loaded above; any rest follows, wave w
-    // taking chunks w, w + 16, ...  Otherwise the staging goes by units of
-    // chunks whose candidates are contiguous (below).
-    auto count = [&](int64_t c) { return (c + 1 < nc ? s_gt[c + 1] : ncand) - s_gt[c]; };
-    if (pre) {
-      for (int64_t c = wave; c < nc; c += kW)
-        for (uint32_t o = 128 + lane; o < count(c); o += 64) {
-          const uint2 e = src.cand[(uint32_t)c * src.region + o];
-          s_key[s_gt[c] + o] = e.x;
-          s_idx[s_gt[c] + o] = e.y;
-        }
-    } else {
-      // Runs prefetched above: the candidates past their first 32.
-      const int64_t ufirst = ppre ? min<int64_t>(nrun, (int64_t)kW * kPreRuns) : 0;
-      if (ppre) {
-        // Lane j < kPreRuns checks run w + 16 j; only runs with more than 32
-        // candidates (rare) are visited.
-        static_assert(kPreRuns <= 64, "one lane per prefetched run");
-        const int64_t myrun = wave + (int64_t)kW * lane;
-        uint32_t myd = 0, mycnt = 0;
-        if (lane < kPreRuns && myrun < nrun) mycnt = run_span(myrun, myd);
-        uint64_t big = __ballot(mycnt > 32u);
-        while (big != 0ull) {
-          const int j = __builtin_ctzll(big);
-          big &= big - 1;
-          const int64_t run = wave + (int64_t)kW * j;
-          const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)myd, j);
-          const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)mycnt, j);
-          for (uint32_t o = 32 + lane; o < cnt; o += 64) {
-            const uint2 e = src.cand[(uint32_t)run * cap + o];
-            s_key[d + o] = e.x;
-            s_idx[d + o] = e.y;
-          }
-        }
-      }
-      // The other staging units: below npacked a run of `pack` chunks (its
-      // candidates packed from the run's first slot, in index order), above it
-      // single chunks.  Wave w copies units ufirst + w, ufirst + w + 16, ...,
-      // kUU of them at a time, each in one piece of up to 128 candidates (the
-      // rest of a larger unit follows).
-      const int64_t nunits = tpre ? nrun : nrun + (nc - npacked);   // tail chunks done above
-      constexpr int kUU = 8;
-      for (int64_t u0 = ufirst + wave; u0 < nunits; u0 += kW * kUU) {
-        uint32_t d[kUU], cnt[kUU], b[kUU];
-        uint2 ev[kUU][2];
-#pragma unroll
-        for (int x = 0; x < kUU; ++x) {
-          const int64_t u = u0 + x * kW;
-          const int64_t ca = u < nrun ? u * pack : npacked + (u - nrun);
-          const int64_t cb = u < nrun ? ca + pack : ca + 1;
-          const bool v = u < nunits;
-          d[x] = v ? s_gt[ca] : 0u;
-          cnt[x] = v ? (cb < nc ? s_gt[cb] : ncand) - d[x] : 0u;
-          b[x] = v ? s_base[ca] : 0u;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t o = lane + 64 * h;
-            ev[x][h] = o < cnt[x] ? src.cand[b[x] + o] : make_uint2(0u, 0u);
-          }
-        }
-#pragma unroll
-        for (int x = 0; x < kUU; ++x) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t o = lane + 64 * h;
-            if (o < cnt[x]) {
-              s_key[d[x] + o] = ev[x][h].x;
-              s_idx[d[x] + o] = ev[x][h].y;
-            }
-          }
-          for (uint32_t o = 128 + lane; o < cnt[x]; o += 64) {
-            const uint2 e = src.cand[b[x] + o];
-            s_key[d[x] + o] = e.x;
-            s_idx[d[x] + o] = e.y;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  uint32_t need = (uint32_t)k;
-  uint32_t prefix = 0;
-  bool done = false;
-  if (lds) {
-    // Candidates are keys >= tau and the cut sits just below the k-th key:
-    // bins of 4096 keys above tau (the last one open-ended), then the 4096
-    // keys of the chosen bin.
-    const uint32_t tau = r.st[kS_TAU];
-    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads)
-      atomicAdd(&s_hist[min((s_key[i] - tau) >> 12, (uint32_t)kBins - 1u)], 1u);
-    __syncthreads();
-    {
-      constexpr int kPer = kBins / kResolveThreads;
+    for (int level = 0; level < 3 && !done; ++level) {
+      const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
+      const int bits = level == 2 ? 10 : 11;
+      const int hi = shift + bits;   // bits at and above hi are fixed
+      for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
+      __syncthreads();
+      visit([&](uint32_t key) {
+        const bool in = hi >= 32 || (key >> (hi & 31)) == (prefix >> (hi & 31));
+        if (in) atomicAdd(&s_hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
+      });
+      __syncthreads();
+      constexpr int kPer = kBins / kResolveThreads;   // 2
       uint32_t h[kPer];
 #pragma unroll
-      for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
+      for (int b = 0; b < kPer; ++b) {
+        const int bin = threadIdx.x * kPer + b;
+        h[b] = bin < (1 << bits) ? s_hist[bin] : 0u;
+      }
       pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
-    }
-    __syncthreads();
-    const uint32_t binA = s_sel[0], needA = s_sel[1];
-    __syncthreads();
-    if (binA < (uint32_t)kBins - 1u) {
-      for (int i = threadIdx.x; i < 2 * kBins; i += kResolveThreads) s_hist[i] = 0u;
       __syncthreads();
-      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) {
-        const uint32_t d = s_key[i] - tau;
-        if ((d >> 12) == binA) atomicAdd(&s_hist[d & 4095u], 1u);
-      }
-      __syncthreads();
-      constexpr int kPer = 2 * kBins / kResolveThreads;
-      uint32_t h[kPer];
-#pragma unroll
-      for (int b = 0; b < kPer; ++b) h[b] = s_hist[threadIdx.x * kPer + b];
-      pick_bin<kResolveThreads, kPer>(h, needA, s_tmp, s_sel);
-      __syncthreads();
-      prefix = tau + (binA << 12) + s_sel[0];
+      prefix |= s_sel[0] << shift;
       need = s_sel[1];
-      done = true;
       __syncthreads();
     }
-  }
-  // f(key, index) over every key the row selects among (LDS: the index is
-  // not needed, 0 is passed).
-  auto keys = [&](auto&& f) {
-    if (lds) {
-      for (uint32_t i = threadIdx.x; i < ncand; i += kResolveThreads) f(s_key[i], 0u);
-    } else {
-      for_each_key(src, f);
-    }
+    T = prefix;   // take every key > T and the first `need` keys == T
   };
-  // Three radix digits (11, 11, 10 bits), from the top.
-  for (int level = 0; level < 3 && !done; ++level) {
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int bits = level == 2 ? 10 : 11;
-    const int hi = shift + bits;   // bits at and above hi are fixed
-    for (int i = threadIdx.x; i < kBins; i += kResolveThreads) s_hist[i] = 0u;
-    __syncthreads();
-    keys([&](uint32_t key, uint32_t) {
-      const bool in = hi >= 32 || (key >> (hi & 31)) == (prefix >> (hi & 31));
-      if (in) atomicAdd(&s_hist[(key >> shift) & ((1u << bits) - 1u)], 1u);
-    });
-    __syncthreads();
-    constexpr int kPer = kBins / kResolveThreads;   // 2
-    uint32_t h[kPer];
-#pragma unroll
-    for (int b = 0; b < kPer; ++b) {
-      const int bin = threadIdx.x * kPer + b;
-      h[b] = bin < (1 << bits) ? s_hist[bin] : 0u;
-    }
-    pick_bin<kResolveThreads, kPer>(h, need, s_tmp, s_sel);
-    __syncthreads();
-    prefix |= s_sel[0] << shift;
-    need = s_sel[1];
-    __syncthreads();
-  }
-  const uint32_t T = prefix;   // take every key > T and the first `need` keys == T
 
-  // The row's chunks in at most kGroups groups of consecutive chunks: the keys
-  // > T and == T of every group, prefixed over the groups.
-  const int64_t per_group = (nc + kGroups - 1) / kGroups;
-  const int ngroups = (int)((nc + per_group - 1) / per_group);
-  if (lds) {
-    // The staged candidates are in index order, so the selection is written
-    // from one flat pass: wave w takes a contiguous segment of them, 64 at a
-    // time; its counts of keys > T and == T (packed as gt | eq << 16, both
-    // at most kLdsCand < 2^16) are prefixed over the waves, and a key's
-    // output position is (keys > T before it) + min(keys == T before it,
-    // need).
+  if (regs) {
+    // Load.  s_eq[b]: the unit holding candidate 64 b.
+    uint32_t* const s_blk = s_eq;
+    {
+      const int64_t per = (nunits + kResolveThreads - 1) / kResolveThreads;
+      const int64_t u0 = min<int64_t>(nunits, threadIdx.x * per), u1 = min<int64_t>(nunits, u0 + per);
+      for (int64_t u = u0; u < u1; ++u) {
+        const uint32_t a = s_gt[u], e = u + 1 < nunits ? s_gt[u + 1] : ncand;
+        for (uint32_t b = (a + 63) >> 6; (b << 6) < e; ++b) s_blk[b] = (uint32_t)u;
+      }
+    }
+    __syncthreads();
     const uint32_t seg = ((ncand + kW * 64 - 1) / (kW * 64)) * 64;
     const uint32_t s0 = min(ncand, (uint32_t)wave * seg), s1 = min(ncand, s0 + seg);
+    const int steps = (int)((s1 - s0 + 63) / 64);   // uniform, at most kRegSteps
+    uint2 e[kRegSteps];
+    uint32_t vmask = 0;   // bit j: step j holds a candidate
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {
+      e[j] = make_uint2(0u, 0u);
+      if (j < steps) {
+        const uint32_t f = s0 + 64u * j + (uint32_t)lane;
+        const bool v = f < s1;
+        uint32_t addr = 0;
+        if (v) {
+          int64_t u = s_blk[f >> 6];
+          while (u + 1 < nunits && s_gt[u + 1] <= f) ++u;
+          addr = unit_base(u) + (f - s_gt[u]);
+          vmask |= 1u << j;
+        }
+        e[j] = src.cand[addr];
+      }
+    }
+    uint32_t T, need;
+    kth(
+        [&](auto&& f) {
+#pragma unroll
+          for (int j = 0; j < kRegSteps; ++j)
+            if (j < steps && ((vmask >> j) & 1u)) f(e[j].x);
+        },
+        true, T, need);
+    // Keys > T and == T of each wave's segment (packed as gt | eq << 16, both
+    // at most kRegCand < 2^16), prefixed over the waves; a key's output
+    // position is (keys > T before it) + min(keys == T before it, need).
     uint32_t gt = 0, eq = 0;
-    for (uint32_t o = s0; o < s1; o += 64) {
-      const bool v = o + lane < s1;
-      const uint32_t key = v ? s_key[o + lane] : 0u;
-      gt += (uint32_t)__popcll(__ballot(v && key > T));
-      eq += (uint32_t)__popcll(__ballot(v && key == T));
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {
+      if (j < steps) {   // uniform
+        const bool v = (vmask >> j) & 1u;
+        gt += (uint32_t)__popcll(__ballot(v && e[j].x > T));
+        eq += (uint32_t)__popcll(__ballot(v && e[j].x == T));
+      }
     }
     if (lane == 0) s_hist[wave] = gt | (eq << 16);
     __syncthreads();
     uint32_t before = 0;
     for (int w = 0; w < wave; ++w) before += s_hist[w];
-    const uint64_t below = lanes_below();
     uint32_t eq_seen = before >> 16;
     uint32_t pos = (before & 0xffffu) + min(eq_seen, need);
-    for (uint32_t o = s0; o < s1; o += 64) {
-      const bool v = o + lane < s1;
-      const uint2 e = v ? make_uint2(s_key[o + lane], s_idx[o + lane]) : make_uint2(0u, 0u);
-      const bool g = v && e.x > T, q = v && e.x == T;
-      const uint64_t eqm = __ballot(q);
-      const bool take = g || (q && eq_seen + (uint32_t)__popcll(eqm & below) < need);
-      const uint64_t tm = __ballot(take);
-      const uint32_t p = pos + (uint32_t)__popcll(tm & below);
-      if (take && p < (uint32_t)k) dst[p] = (int32_t)e.y;   // p < k by construction
-      pos += (uint32_t)__popcll(tm);
-      eq_seen += (uint32_t)__popcll(eqm);
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {
+      if (j < steps) {   // uniform
+        const bool v = (vmask >> j) & 1u;
+        const bool g = v && e[j].x > T, q = v && e[j].x == T;
+        const uint64_t eqm = __ballot(q);
+        const bool take = g || (q && eq_seen + (uint32_t)__popcll(eqm & below) < need);
+        const uint64_t tm = __ballot(take);
+        const uint32_t p = pos + (uint32_t)__popcll(tm & below);
+        if (take && p < (uint32_t)k) dst[p] = (int32_t)e[j].y;   // p < k by construction
+        pos += (uint32_t)__popcll(tm);
+        eq_seen += (uint32_t)__popcll(eqm);
+      }
     }
     return;
-  } else {
-    for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
-    __syncthreads();
-    for_each_key(src, [&](uint32_t key, uint32_t idx) {
-      const int g = (int)((int64_t)(idx / R) / per_group);
-      if (key > T) atomicAdd(&s_gt[g], 1u);
-      if (key == T) atomicAdd(&s_eq[g], 1u);
-    });
   }
+
+  uint32_t T, need;
+  kth([&](auto&& f) { for_each_key(src, [&](uint32_t key, uint32_t) { f(key); }); }, false, T,
+      need);
+  // The row's chunks in at most kGroups groups of consecutive chunks: the keys
+  // > T and == T of every group, prefixed over the groups.
+  const int64_t per_group = (nc + kGroups - 1) / kGroups;
+  const int ngroups = (int)((nc + per_group - 1) / per_group);
+  for (int g = threadIdx.x; g < ngroups; g += kResolveThreads) s_gt[g] = s_eq[g] = 0u;
+  __syncthreads();
+  for_each_key(src, [&](uint32_t key, uint32_t idx) {
+    const int g = (int)((int64_t)(idx / R) / per_group);
+    if (key > T) atomicAdd(&s_gt[g], 1u);
+    if (key == T) atomicAdd(&s_eq[g], 1u);
+  });
   __syncthreads();
   block_prefix_inplace<kResolveThreads>(s_gt, ngroups, s_tmp);
   block_prefix_inplace<kResolveThreads>(s_eq, ngroups, s_tmp);
   __syncthreads();
-  const uint64_t below = lanes_below();
   // One wave per group writes its selected indices in index order.
   for (int g = wave; g < ngroups; g += kResolveThreads / 64) {
     uint32_t eq_seen = s_eq[g];
@@ -762,14 +663,23 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
 }
 
+hipError_t launch_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
+                          int32_t* indices, void* ws, int mode, uint32_t* gflag, int G, int pack,
+                          int64_t npacked, int flags, hipStream_t stream) {
+  if (pack < 1 || pack > 64 || (pack & (pack - 1)) != 0 || npacked % pack != 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
+                     n, R, k, ws, indices, mode, gflag, G, pack, npacked, flags);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fused_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
                                 int32_t* indices, void* ws, int mode, uint32_t* gflag, int G,
                                 int pack, int64_t npacked, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_resolve, dim3((unsigned)rows), dim3(kResolveThreads), 0, stream, scores,
-                     n, R, k, ws, indices, mode, gflag, G, pack, npacked);
-  return hipGetLastError();
+  return launch_resolve(scores, rows, n, R, k, indices, ws, mode, gflag, G, pack, npacked,
+                        kResolveStamps | kResolveOver, stream);
 }
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
@@ -784,9 +694,10 @@ hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int3
   const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
   hipLaunchKernelGGL(topk_cut, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k, ws);
   hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
-  hipLaunchKernelGGL(topk_resolve, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k,
-                     ws, indices, 0, (uint32_t*)nullptr, 1, 1, (int64_t)0);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_resolve(scores, rows, n, R, k, indices, ws, 0, nullptr, 1, 1, nc, kResolveOver,
+                        stream);
 }
 
 namespace {

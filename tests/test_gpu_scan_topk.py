@@ -227,6 +227,20 @@ def test_topk_full_rows(fk, kind):
     assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
 
 
+@pytest.mark.parametrize("n", [1 << 21, 3 * (1 << 20) + 4099])
+def test_topk_long_rows(fk, n):
+    """Rows of 2M keys (256 chunks: the selection from registers with 64
+    slots per chunk) and of 3M + 4099 keys (385 chunks, more than the
+    registers cover: the candidates staged in LDS, 8 chunks per wave at a
+    time, the last chunk partial), k = 4096."""
+    rows, k = 2, 4096
+    scores = fathom_inputs.random_scores(rows, n, seed=81, kind="normal")
+    say("topk long rows rows=%d n=%d k=%d" % (rows, n, k))
+    gpu = _topk(fk, scores, k)
+    ref = oracle.topk(scores, k)
+    assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+
+
 def test_topk_crowded_chunks(fk):
     """Rows of 1M scores with 300 and 200 large scores planted in two chunks
     of 8192 keys that the cut's sample does not read (chunks 3 and 77): those
@@ -370,7 +384,7 @@ def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=Tr
 @pytest.mark.parametrize("write_scores", [True, False])
 @pytest.mark.parametrize("groups,n,k", [(2, 1 << 17, 512), (3, 1 << 16, 64), (1, 1 << 18, 4096),
                                         (2, 3 * 4096, 100), (1, 65536 + 2048, 300),
-                                        (2, 65536 + 64 * 37, 500)])
+                                        (2, 65536 + 64 * 37, 500), (1, 1 << 21, 4096)])
 def test_scan_topk_matches_scan_then_topk(fk, groups, n, k, write_scores):
     """Fused (64k <= n <= 2M: whole rounds in the main kernel, the rest, down
     to a partial last tile, in the tail kernel) and unfused (shorter rows)
