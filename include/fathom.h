@@ -23,7 +23,10 @@
  *     host store of fathom_gather (pinned host memory).  The library
  *     allocates nothing, keeps no pointer after a call returns and holds no
  *     state between calls, apart from the fixed per-GPU scratch of
- *     fathom_topk_noalloc (and its looked-up device address).
+ *     fathom_topk_noalloc (and its looked-up device address), the host-side
+ *     call counters that tag the messages between workgroups of one launch
+ *     (fathom_topk, fathom_scan_topk) and the settings of
+ *     fathom_test_cut_hooks.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it; no call synchronises the host
  *     with the device.  Calls are reentrant; calls on different streams are
@@ -355,13 +358,16 @@ int fathom_klt_rotate_queries(const float* q, const float* basis, int64_t groups
 /* Static, NUL-terminated name of a status code. */
 const char* fathom_status_string(int status);
 /*
- * fathom_test_cut_hooks — for tests of fathom_scan_topk's fallback only.
- * In the fused path the scan's first workgroups publish each row's cut and
- * the scan waves poll for it a bounded number of times; a row whose cut is
- * still missing then is flagged and selected by the fallback.  publish = 0
- * makes those workgroups store the cut without publishing it, so that every
- * wave reaches its poll limit; spin_limit (1 to 16384 polls of about
- * 0.2 us) sets the limit.  (1, 2048) are the defaults.  Host-side settings
+ * fathom_test_cut_hooks — for tests of the fallbacks of fathom_scan_topk
+ * and fathom_topk only.  In fathom_scan_topk's fused path the scan's first
+ * workgroups publish each row's cut and the scan waves poll for it a
+ * bounded number of times; a row whose cut is still missing then is flagged
+ * and selected by the fallback.  In fathom_topk the first workgroups of the
+ * compaction publish the cuts in the same way, and a chunk whose cut does
+ * not come in time sends its row to the selection from the scores.
+ * publish = 0 makes those workgroups store the cut without publishing it,
+ * so that every waiting wave reaches its poll limit; spin_limit (1 to 16384
+ * polls of about 0.2 us) sets the limit.  (1, 2048) are the defaults.  Host-side settings
  * of the calling process, read by later calls; FATHOM_ERR_BAD_RANGE for a
  * publish other than 0 or 1 or a limit outside the range.
  */

@@ -36,6 +36,7 @@ int fathom_test_cut_hooks(int32_t publish, int32_t spin_limit) {
   if ((publish != 0 && publish != 1) || spin_limit < 1 || spin_limit > 16384)
     return FATHOM_ERR_BAD_RANGE;
   fathom::set_cut_hooks(publish, spin_limit);
+  fathom::set_topk_cut_hooks(publish, spin_limit);
   return FATHOM_OK;
 }
 

@@ -37,9 +37,11 @@ int64_t scan_max_workgroups(int64_t groups, int64_t n);
 
 size_t topk_workspace_bytes(int64_t rows, int64_t n, int k);
 // Pieces of fathom_scan_topk's selection (workspace layout: topk::FusedWs).
-// fathom_test_cut_hooks: whether the candidate scan publishes its cuts, and
-// the waves' poll limit (defaults 1 and 2048).
+// fathom_test_cut_hooks: whether the candidate scan (set_cut_hooks) and
+// fathom_topk's cut workgroups (set_topk_cut_hooks) publish their cuts, and
+// the poll limit of the waves that wait for them (defaults 1 and 2048).
 void set_cut_hooks(int publish, int spin_limit);
+void set_topk_cut_hooks(int publish, int spin_limit);
 
 // Chunks [0, npacked) of a row come in runs of `pack` whose candidates are
 // packed from the run's first slot (1 and 0: every chunk on its own).

@@ -26,6 +26,8 @@
 // region holds: heavy ties or adversarial rows), or there are more candidates
 // than the registers hold, the resolve workgroup does all of it alone, from
 // the scores or the regions: same result, many more passes.
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "fathom_internal.h"
@@ -66,42 +68,46 @@ struct ChunkVals {
   float v[kPerThread / 4][4];
 };
 
-__device__ __forceinline__ int64_t key_index(int64_t c0, int i, int c) {
+// Offset of the key (i, c) of this thread from the chunk's first key.
+// Offsets and indices within a row fit in 32 bits (rows have fewer than 2^31
+// keys), so a load takes the chunk's (uniform) first key plus one 32-bit
+// offset.
+__device__ __forceinline__ uint32_t key_off(int i, int c) {
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  return c0 + (int64_t)wave * kWaveKeys + (int64_t)(i * 64 + lane) * 4 + c;
-}
-
-// FULL: the chunk lies inside the row and the row start is 16-byte aligned,
-// so every key is valid and the loads are 16-byte vectors.
-template <bool FULL>
-__device__ __forceinline__ bool valid(int64_t c0, int i, int c, int64_t n) {
-  return FULL || key_index(c0, i, c) < n;
+  return (uint32_t)(wave * kWaveKeys + (i * 64 + lane) * 4 + c);
 }
 
 __device__ __forceinline__ bool chunk_full(const float* src, int64_t n, int64_t c0) {
   return (reinterpret_cast<uintptr_t>(src) & 15) == 0 && c0 + kChunk <= n;
 }
 
-// Padding of a partial chunk reads -inf (never a candidate: see compact).
+// FULL: the chunk lies inside the row and the row start is 16-byte aligned,
+// so every key is valid and the loads are 16-byte vectors.
+// Padding of a partial chunk reads NaN, never >= a cut: no key past the row
+// is a candidate.
 template <bool FULL>
 __device__ __forceinline__ void load_vals(const float* __restrict__ src, int64_t n, int64_t c0,
                                           ChunkVals& V) {
+  const float* __restrict__ base = src + c0;
   if (FULL) {
     typedef float f4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int i = 0; i < kPerThread / 4; ++i) {
-      const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + key_index(c0, i, 0)));
+      const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(base + key_off(i, 0)));
       V.v[i][0] = x.x;
       V.v[i][1] = x.y;
       V.v[i][2] = x.z;
       V.v[i][3] = x.w;
     }
   } else {
+    const uint32_t lim = (uint32_t)min<int64_t>(n - c0, kChunk);   // keys of the chunk in the row
 #pragma unroll
     for (int i = 0; i < kPerThread / 4; ++i) {
-      const int64_t e = key_index(c0, i, 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) V.v[i][c] = (e + c < n) ? src[e + c] : -__builtin_inff();
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t o = key_off(i, c);
+        V.v[i][c] = o < lim ? base[o] : __builtin_nanf("");
+      }
     }
   }
 }
@@ -122,39 +128,57 @@ __device__ __forceinline__ void block_prefix_inplace(uint32_t* cnt, int m, uint3
   }
 }
 
-// Per row: the cut tau from a sample of the row, in one workgroup: 16 runs of
-// 1024 keys spread evenly over the row (the whole row when it has at most
-// 16384 keys), held 16 per thread; tau = radix_cut of them at the target-th
-// largest, target = the sample's share of k raised by 60% plus 16 keys (k
-// itself for a whole row, where the cut then lies at or just below the k-th
-// key).  Clears the row's overflow flag.
-constexpr int kCutRuns = 16, kCutRun = 1024, kCutPer = kCutRuns * kCutRun / kResolveThreads;
-static_assert(kCutPer == 16, "16 sampled keys per thread");
+// The cut and the compaction in one launch.  Its first `rows` workgroups
+// take one row's cut each from a sample of the row: 8 runs of 1024 keys
+// spread evenly over the row (the whole row when it has at most 8192 keys),
+// 32 per thread; tau = radix_cut of them at the target-th largest, target =
+// the sample's share of k raised by 60% plus 16 keys (k itself for a whole
+// row, where the cut then lies at or just below the k-th key).  tau goes to
+// the row's state for the selection and is published in the row's ready word
+// as tau | epoch << 1 | 1 (tau's low 10 bits are clear) with an agent-scope
+// atomic store.  The other workgroups each compact chunks (see compact_chunk):
+// they load their chunk, then read the ready word (agent-scope loads) until
+// it carries this call's epoch, polling a bounded number of times.  A chunk
+// whose cut never came writes no candidates and stamps an impossible cut, and
+// the selection checks every chunk's stamp against the row's cut, so no
+// timing or stale word can change a result: it can only send a row to the
+// selection from its scores.
+constexpr int kCutRuns = 8, kCutRun = 1024, kCutKeys = kCutRuns * kCutRun;
+constexpr int kCutPer = kCutKeys / kThreads;
+static_assert(kCutPer == 32, "32 sampled keys per thread");
+constexpr size_t kCutHistBytes = kBins * sizeof(uint32_t);
+constexpr int kTopkCutSpin = 2048;              // polls (about 0.2 us each) of a cut not yet out
+constexpr int64_t kMaxCompactWgs = 1 << 22;     // compaction workgroups at most (then they loop)
+constexpr uint32_t kNoCut = 0xFFFFFFFFu;        // a stamp no cut equals (a cut's low bits are 0)
 
-__global__ __launch_bounds__(kResolveThreads) void topk_cut(const float* __restrict__ scores,
-                                                            int64_t n, int64_t R, int k,
-                                                            void* ws) {
-  __shared__ uint32_t s_hist[kBins];
-  __shared__ uint32_t s_tmp[kResolveThreads / 64];
-  __shared__ uint32_t s_sel[2];
-  const int64_t row = blockIdx.x;
-  RowWs r = row_ws(ws, n, R, row);
-  const float* src = scores + row * n;
+__device__ __forceinline__ uint32_t cut_ready_bits(uint32_t epoch) {
+  return ((epoch & 0x1FFu) << 1) | 1u;
+}
+
+struct TopkCut {
+  uint32_t epoch;   // the call's epoch (its low 9 bits are used)
+  int publish;      // 1; 0 only under fathom_test_cut_hooks
+  int spin;         // the poll limit
+};
+
+__device__ __forceinline__ void cut_row(const float* __restrict__ src, int64_t n, int k,
+                                        const RowWs& r, const TopkCut& cut, uint32_t* s_hist,
+                                        uint32_t* s_tmp, uint32_t* s_sel) {
   const int tid = threadIdx.x;
-  const bool whole = n <= (int64_t)kCutRuns * kCutRun;
-  const int nkeys = whole ? (int)n : kCutRuns * kCutRun;
+  const bool whole = n <= (int64_t)kCutKeys;
+  const int nkeys = whole ? (int)n : kCutKeys;
   uint32_t key[kCutPer];
   if (whole) {
 #pragma unroll
     for (int u = 0; u < kCutPer; ++u) {
-      const int64_t i = tid + (int64_t)u * kResolveThreads;
+      const int64_t i = tid + (int64_t)u * kThreads;
       key[u] = i < n ? order_key(src[i]) : 0u;
     }
   } else {
-    // Run c = tid / 64 starts at c * (n - 1024) / 15 (rounded down to 4
-    // keys); lane l takes its keys [16 l, 16 l + 16).
-    const int64_t start = ((tid >> 6) * ((n - kCutRun) / (kCutRuns - 1))) & ~(int64_t)3;
-    const float* p = src + start + (tid & 63) * kCutPer;
+    // Run c = tid / 32 starts at c * (n - 1024) / 7 (rounded down to 4 keys);
+    // thread t takes its keys [32 (t mod 32), 32 (t mod 32) + 32).
+    const int64_t start = ((tid >> 5) * ((n - kCutRun) / (kCutRuns - 1))) & ~(int64_t)3;
+    const float* p = src + start + (tid & 31) * kCutPer;
     if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
       typedef float f4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -176,48 +200,70 @@ __global__ __launch_bounds__(kResolveThreads) void topk_cut(const float* __restr
     need = (uint32_t)min<double>((double)nkeys, ceil(1.6 * share + 16.0));
   }
   // Only a whole-row sample has slots past the row's end to skip.
-  const uint32_t prefix = radix_cut<kResolveThreads>(
+  const uint32_t tau = radix_cut<kThreads>(
       [&](auto&& f) {
 #pragma unroll
         for (int u = 0; u < kCutPer; ++u)
-          if (!whole || tid + (int64_t)u * kResolveThreads < n) f(key[u]);
+          if (!whole || tid + (int64_t)u * kThreads < n) f(key[u]);
       },
       need, s_hist, s_tmp, s_sel);
   if (tid == 0) {
-    r.st[kS_TAU] = prefix;
-    r.st[kS_OVER] = 0u;
+    r.st[kS_TAU] = tau;
+    if (cut.publish)
+      __hip_atomic_store(&r.st[kS_READY], tau | cut_ready_bits(cut.epoch), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Every key >= tau of one chunk written in index order to the chunk's region
-// of the candidate buffer; the count goes to the segment table (a count above
-// the region flags the row).  The test is a float compare against the cut
-// (padding reads -inf: never >= a finite cut, and a cut of -inf's key only
-// comes with whole-row sampling, where the cut is the low edge of a bin with
-// keys); order keys are formed for candidates only.
+// Every key >= tau of chunk `chunk` (keys [c0, c0 + kChunk) of the row)
+// written in index order to the chunk's region of the candidate buffer; the
+// count and the cut used go to the segment and stamp tables (a count above
+// the region sends the row to the slow path).  The test is a float compare
+// against the cut (a NaN, the padding included, is never a candidate); order
+// keys are formed for candidates only.
 template <bool F>
 __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int64_t n, int64_t c0,
-                                              const RowWs& r, uint32_t* s_cnt) {
-  const float tauf = key_float(r.st[kS_TAU]);
+                                              int64_t chunk, const RowWs& r, const TopkCut& cut,
+                                              uint32_t* s_cnt, uint32_t* s_cut) {
   const int wave = threadIdx.x >> 6;
   ChunkVals V;
   load_vals<F>(src, n, c0, V);
+  if (threadIdx.x == 0) {
+    const uint32_t rb = cut_ready_bits(cut.epoch);
+    uint32_t w = __hip_atomic_load(&r.st[kS_READY], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; it < cut.spin && (w & 0x3FFu) != rb; ++it) {
+      __builtin_amdgcn_s_sleep(8);
+      w = __hip_atomic_load(&r.st[kS_READY], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *s_cut = (w & 0x3FFu) == rb ? (w & ~0x3FFu) : kNoCut;
+  }
+  __syncthreads();
+  const uint32_t tau = *s_cut;
+  const uint32_t base = (uint32_t)chunk * r.region;
+  if (tau == kNoCut) {   // uniform: the cut never came
+    if (threadIdx.x == 0) {
+      r.seg[2 * chunk] = base;
+      r.seg[2 * chunk + 1] = 0u;
+      r.stamp[2 * chunk] = kNoCut;
+    }
+    return;
+  }
+  const float tauf = key_float(tau);
   uint32_t ncand = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread / 4; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      ncand += (uint32_t)__popcll(__ballot(V.v[i][c] >= tauf && valid<F>(c0, i, c, n)));
+      ncand += (uint32_t)__popcll(__ballot(V.v[i][c] >= tauf));
   if (lane_id() == 0) s_cnt[wave] = ncand;
   __syncthreads();
-  const uint32_t base = (uint32_t)blockIdx.x * r.region;
   if (threadIdx.x == 0) {
     uint32_t t = 0;
 #pragma unroll
     for (int w = 0; w < kWavesPerWg; ++w) t += s_cnt[w];
-    r.seg[2 * blockIdx.x] = base;
-    r.seg[2 * blockIdx.x + 1] = t;
-    if (t > r.region) atomicOr(&r.st[kS_OVER], 1u);
+    r.seg[2 * chunk] = base;
+    r.seg[2 * chunk + 1] = t;
+    r.stamp[2 * chunk] = tau;
   }
   if (ncand != 0u) {
     // Slots follow index order: the keys of step i are (lane, c) with index
@@ -231,7 +277,7 @@ __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int
       uint64_t m[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        cand[c] = V.v[i][c] >= tauf && valid<F>(c0, i, c, n);
+        cand[c] = V.v[i][c] >= tauf;
         m[c] = __ballot(cand[c]);
       }
       if ((m[0] | m[1] | m[2] | m[3]) == 0ull) continue;
@@ -246,7 +292,7 @@ __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int
         if (cand[c]) {
           if (sl < r.region)
             reinterpret_cast<uint2*>(r.cand)[base + sl] =
-                make_uint2(order_key(V.v[i][c]), (uint32_t)key_index(c0, i, c));
+                make_uint2(order_key(V.v[i][c]), (uint32_t)c0 + key_off(i, c));
           ++sl;
         }
       }
@@ -254,15 +300,36 @@ __device__ __forceinline__ void compact_chunk(const float* __restrict__ src, int
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict__ scores,
-                                                         int64_t n, void* ws) {
+// Workgroups [0, rows): the rows' cuts; the others: chunks w, w + nwg, ...
+// of the rows' chunks in row-major order (nwg compaction workgroups).
+__global__ __launch_bounds__(kThreads) void topk_cut_compact(const float* __restrict__ scores,
+                                                             int64_t rows, int64_t n, int k,
+                                                             void* ws, int64_t nwg,
+                                                             TopkCut cut) {
+  // The cut's counts in dynamic LDS (kCutHistBytes at launch): a static
+  // array would make the compiler size the compaction's registers for the
+  // occupancy that array allows, which is lower than the registers allow.
+  extern __shared__ uint32_t s_hist[];
+  __shared__ uint32_t s_tmp[kWavesPerWg];
+  __shared__ uint32_t s_sel[2];
   __shared__ uint32_t s_cnt[kWavesPerWg];
-  const int64_t row = blockIdx.y;
-  const RowWs r = row_ws(ws, n, kChunk, row);
-  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
-  const float* src = scores + row * n;
-  if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, r, s_cnt);
-  else compact_chunk<false>(src, n, c0, r, s_cnt);
+  __shared__ uint32_t s_cut;
+  const int64_t id = blockIdx.x;
+  if (id < rows) {
+    const RowWs r = row_ws(ws, n, kChunk, id);
+    cut_row(scores + id * n, n, k, r, cut, s_hist, s_tmp, s_sel);
+    return;
+  }
+  const int64_t nc = n_chunks(n, kChunk);
+  for (int64_t g = id - rows; g < rows * nc; g += nwg) {
+    if (g != id - rows) __syncthreads();   // s_cnt and s_cut of the last chunk are read
+    const int64_t row = g / nc, chunk = g - row * nc;
+    const RowWs r = row_ws(ws, n, kChunk, row);
+    const int64_t c0 = chunk * kChunk;
+    const float* src = scores + row * n;
+    if (chunk_full(src, n, c0)) compact_chunk<true>(src, n, c0, chunk, r, cut, s_cnt, &s_cut);
+    else compact_chunk<false>(src, n, c0, chunk, r, cut, s_cnt, &s_cut);
+  }
 }
 
 // The keys the one-workgroup path selects among: the candidate regions, or
@@ -688,15 +755,27 @@ size_t topk_workspace_bytes(int64_t rows, int64_t n, int k) {
   return (bytes + 255) & ~(size_t)255;
 }
 
+namespace {
+std::atomic<uint32_t> g_topk_epoch{0};
+std::atomic<int> g_topk_publish{1}, g_topk_spin{kTopkCutSpin};
+}  // namespace
+
+void set_topk_cut_hooks(int publish, int spin_limit) {
+  g_topk_publish.store(publish);
+  g_topk_spin.store(spin_limit);
+}
+
 hipError_t launch_topk(const float* scores, int64_t rows, int64_t n, int k, int32_t* indices,
                        void* ws, hipStream_t stream) {
   const int64_t R = kChunk, nc = n_chunks(n, R);
-  const dim3 grid_rows((unsigned)rows), grid_chunks((unsigned)nc, (unsigned)rows);
-  hipLaunchKernelGGL(topk_cut, grid_rows, dim3(kResolveThreads), 0, stream, scores, n, R, k, ws);
-  hipLaunchKernelGGL(topk_compact, grid_chunks, dim3(kThreads), 0, stream, scores, n, ws);
+  const int64_t nwg = std::min<int64_t>(rows * nc, kMaxCompactWgs);
+  const TopkCut cut{g_topk_epoch.fetch_add(1u) + 1u, g_topk_publish.load(), g_topk_spin.load()};
+  hipLaunchKernelGGL(topk_cut_compact, dim3((unsigned)(rows + nwg)), dim3(kThreads), kCutHistBytes,
+                     stream,
+                     scores, rows, n, k, ws, nwg, cut);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_resolve(scores, rows, n, R, k, indices, ws, 0, nullptr, 1, 1, nc, kResolveOver,
+  return launch_resolve(scores, rows, n, R, k, indices, ws, 0, nullptr, 1, 1, nc, kResolveStamps,
                         stream);
 }
 
@@ -740,9 +819,9 @@ hipError_t launch_topk_noalloc(const float* scores, int64_t rows, int64_t n, int
   if (e != hipSuccess) return e;
   void* ws = nullptr;
   if ((e = scratch_ptr(dev, &ws)) != hipSuccess) return e;
-  // Every kernel of the selection writes what it later reads (the cut and
-  // the overflow flag set by the cut kernel, every chunk's count by the
-  // compaction), so nothing of the previous call's contents needs clearing.
+  // Every kernel of the selection writes what it later reads (the cut, and
+  // every chunk's count and stamp), and the ready word carries the call's
+  // epoch, so nothing of the previous call's contents needs clearing.
   return launch_topk(scores, rows, n, k, indices, ws, stream);
 }
 

@@ -241,6 +241,26 @@ def test_topk_long_rows(fk, n):
     assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
 
 
+def test_topk_cut_never_published_falls_back(fk):
+    """fathom_topk's cut workgroups store the cuts without publishing them
+    (fathom_test_cut_hooks) and the compaction gives up after 4 polls: every
+    chunk stamps a cut no row has, so every row is selected from its scores,
+    with the same result.  The hooks are restored and a second call checks
+    the candidate path again."""
+    rows, n, k = 3, (1 << 17) + 4099, 700
+    scores = fathom_inputs.random_scores(rows, n, seed=83, kind="normal")
+    ref = oracle.topk(scores, k)
+    say("topk cut never published rows=%d n=%d k=%d" % (rows, n, k))
+    fk.test_cut_hooks(publish=False, spin_limit=4)
+    try:
+        gpu = _topk(fk, scores, k)
+    finally:
+        fk.test_cut_hooks(publish=True, spin_limit=2048)
+    assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+    gpu = _topk(fk, scores, k)
+    assert np.array_equal(gpu, ref), first_mismatch(gpu, ref)
+
+
 def test_topk_crowded_chunks(fk):
     """Rows of 1M scores with 300 and 200 large scores planted in two chunks
     of 8192 keys that the cut's sample does not read (chunks 3 and 77): those
