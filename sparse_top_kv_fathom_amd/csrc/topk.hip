@@ -417,8 +417,8 @@ __device__ __forceinline__ void walk_chunks(const ResolveSrc s, int64_t cb, int6
 //   load   — with at most kRegCand candidates the row's candidates, in index
 //            order, are split into one contiguous segment per wave and loaded
 //            64 at a time into registers (lane l of step j: candidate
-//            s0 + 64 j + l of the wave's segment [s0, s1)), the unit of each
-//            found from the unit of its 64-candidate block;
+//            s0 + 64 j + l of the wave's segment [s0, s1)), each candidate's
+//            slot read from an LDS table the units' threads fill;
 //   select — two radix digits counted from the cut into LDS give T and the
 //            keys == T still needed; the keys > T and == T of every wave's
 //            segment, prefixed over the waves, place every selected index
@@ -448,10 +448,10 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
                                                                 int flags) {
   __shared__ uint32_t s_hist[2 * kBins];
   __shared__ uint32_t s_gt[kGroups];   // units' first candidates; groups' keys > T
-  __shared__ uint32_t s_eq[kGroups];   // the unit of each 64-candidate block; groups' keys == T
+  __shared__ uint32_t s_eq[kGroups];   // groups' keys == T
+  __shared__ uint32_t s_addr[kRegCand];   // candidate f's slot in the candidate buffer
   __shared__ uint32_t s_tmp[kResolveThreads / 64];
   __shared__ uint32_t s_sel[2];
-  static_assert(kRegCand / 64 <= kGroups, "one word per 64-candidate block");
   const int64_t row = blockIdx.x;
   RowWs r = row_ws(ws, n, R, row);
   if (mode == 1 && r.st[kS_FAIL] == 0u) return;   // uniform over the workgroup
@@ -531,6 +531,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         s_gt[u] = run;
         run += t;
       }
+      __syncthreads();   // every unit's prefix is read by other threads below
     } else {
       (void)block_exclusive_sum<kResolveThreads>(mine, s_tmp, tot);
     }
@@ -619,14 +620,25 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   };
 
   if (regs) {
-    // Load.  s_eq[b]: the unit holding candidate 64 b.
-    uint32_t* const s_blk = s_eq;
-    {
-      const int64_t per = (nunits + kResolveThreads - 1) / kResolveThreads;
-      const int64_t u0 = min<int64_t>(nunits, threadIdx.x * per), u1 = min<int64_t>(nunits, u0 + per);
-      for (int64_t u = u0; u < u1; ++u) {
-        const uint32_t a = s_gt[u], e = u + 1 < nunits ? s_gt[u + 1] : ncand;
-        for (uint32_t b = (a + 63) >> 6; (b << 6) < e; ++b) s_blk[b] = (uint32_t)u;
+    // Load.  s_addr[f]: the candidate buffer slot of candidate f (in index
+    // order), written by the thread that owns f's unit, so that the loads'
+    // addresses are one independent LDS read each.
+    // Wave w fills units w, w + 16, ...: lane i reads the bounds of the
+    // wave's i-th unit of a batch of 64, then the wave writes each unit's
+    // entries 64 at a time.
+    for (int64_t ub = 0; ub < nunits; ub += (int64_t)kW * 64) {
+      const int64_t my = ub + wave + (int64_t)kW * lane;
+      const bool ok = my < nunits;
+      const uint32_t ma = ok ? s_gt[my] : 0u;
+      const uint32_t me = ok ? (my + 1 < nunits ? s_gt[my + 1] : ncand) : 0u;
+      const uint32_t mb = ok ? unit_base(my) : 0u;
+      const int64_t left = nunits - ub - wave;   // this wave's units in the batch: ceil(left / 16)
+      const int nb = left > 0 ? (int)min<int64_t>(64, (left + kW - 1) / kW) : 0;
+      for (int i = 0; i < nb; ++i) {
+        const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)ma, i);
+        const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)me, i);
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)mb, i);
+        for (uint32_t f = a + (uint32_t)lane; f < e; f += 64) s_addr[f] = b + (f - a);
       }
     }
     __syncthreads();
@@ -635,21 +647,18 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     const int steps = (int)((s1 - s0 + 63) / 64);   // uniform, at most kRegSteps
     uint2 e[kRegSteps];
     uint32_t vmask = 0;   // bit j: step j holds a candidate
+    uint32_t addr[kRegSteps];
+#pragma unroll
+    for (int j = 0; j < kRegSteps; ++j) {   // every slot read first: one wait
+      const uint32_t f = s0 + 64u * j + (uint32_t)lane;
+      const bool v = f < s1;
+      if (v) vmask |= 1u << j;
+      addr[j] = s_addr[v ? f : 0u];
+    }
 #pragma unroll
     for (int j = 0; j < kRegSteps; ++j) {
       e[j] = make_uint2(0u, 0u);
-      if (j < steps) {
-        const uint32_t f = s0 + 64u * j + (uint32_t)lane;
-        const bool v = f < s1;
-        uint32_t addr = 0;
-        if (v) {
-          int64_t u = s_blk[f >> 6];
-          while (u + 1 < nunits && s_gt[u + 1] <= f) ++u;
-          addr = unit_base(u) + (f - s_gt[u]);
-          vmask |= 1u << j;
-        }
-        e[j] = src.cand[addr];
-      }
+      if (j < steps) e[j] = src.cand[addr[j]];   // uniform
     }
     uint32_t T, need;
     kth(

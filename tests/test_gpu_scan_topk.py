@@ -404,7 +404,8 @@ def _scan_topk_case(fk, groups, n, k, budget, seed, depths=None, write_scores=Tr
 @pytest.mark.parametrize("write_scores", [True, False])
 @pytest.mark.parametrize("groups,n,k", [(2, 1 << 17, 512), (3, 1 << 16, 64), (1, 1 << 18, 4096),
                                         (2, 3 * 4096, 100), (1, 65536 + 2048, 300),
-                                        (2, 65536 + 64 * 37, 500), (1, 1 << 21, 4096)])
+                                        (2, 65536 + 64 * 37, 500), (1, 1 << 21, 4096),
+                                        (1, (1 << 21) - 64, 4096)])
 def test_scan_topk_matches_scan_then_topk(fk, groups, n, k, write_scores):
     """Fused (64k <= n <= 2M: whole rounds in the main kernel, the rest, down
     to a partial last tile, in the tail kernel) and unfused (shorter rows)
