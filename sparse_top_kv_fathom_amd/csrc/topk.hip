@@ -539,9 +539,12 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
   }
   src.direct = ncand < (uint32_t)k || over != 0u || stale || mode == 1;   // the cut failed
   // Mode 0 records for every row whether the second pass must select it.
+  // A row it need not select is recorded at the end: a barrier waits for
+  // every global store in flight, so the store goes after the last one.
   const bool fail = src.direct && scores == nullptr;
-  if (mode == 0 && threadIdx.x == 0 && gflag != nullptr) r.st[kS_FAIL] = fail ? 1u : 0u;
+  const bool record = mode == 0 && threadIdx.x == 0 && gflag != nullptr;
   if (fail) {   // no scores to fall back on: flag the row
+    if (record) r.st[kS_FAIL] = 1u;
     if (threadIdx.x == 0) gflag[row / G] = 1u;
     return;
   }
@@ -700,6 +703,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
         eq_seen += (uint32_t)__popcll(eqm);
       }
     }
+    if (record) r.st[kS_FAIL] = 0u;
     return;
   }
 
@@ -737,6 +741,7 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
                   eq_seen += (uint32_t)__popcll(eqm);
                 });
   }
+  if (record) r.st[kS_FAIL] = 0u;
 }
 
 hipError_t launch_resolve(const float* scores, int64_t rows, int64_t n, int64_t R, int k,
