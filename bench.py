@@ -126,8 +126,8 @@ class TimingEvent:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q1m")
     ap.add_argument("--budget", type=int, default=92)
     ap.add_argument("--copies", type=int, default=4, help="store copies the steps rotate through")
@@ -468,7 +468,7 @@ def run_configs(fk, args, main_ctx):
 
     import fathom_inputs
     out = []
-    reps = max(10, args.steps)
+    reps = max(10, min(args.steps, 30))
     dev = torch.device("cuda:0")
     todo = [("q256k", (68, 92, 136)), ("q1m", (68, 136)), ("s16", (92,))]
     for name, budgets in todo:
@@ -533,7 +533,7 @@ def run_layouts(fk, args, ctx):
     stores, q_d, var_d, n, k, B = (ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["k"],
                                    ctx["B"])
     dev = q_d.device
-    reps = max(10, args.steps)
+    reps = max(10, min(args.steps, 30))
     H, G = q_d.shape[1], q_d.shape[2]
     nb = n // 64
     p0, s0 = stores[0]
@@ -589,7 +589,7 @@ def run_compare(fk, args, ctx, ins):
     stores, q_d, var_d, n, k = ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["k"]
     H, G = q_d.shape[1], q_d.shape[2]
     nq = q_d.shape[0]
-    reps = max(10, args.steps)
+    reps = max(10, min(args.steps, 30))
     dev = q_d.device
     scores = torch.empty((H, G, n), dtype=torch.float32, device=dev)
     idx = torch.empty((H * G, k), dtype=torch.int32, device=dev)
