@@ -637,11 +637,28 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
       const uint32_t mb = ok ? unit_base(my) : 0u;
       const int64_t left = nunits - ub - wave;   // this wave's units in the batch: ceil(left / 16)
       const int nb = left > 0 ? (int)min<int64_t>(64, (left + kW - 1) / kW) : 0;
-      for (int i = 0; i < nb; ++i) {
-        const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)ma, i);
-        const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)me, i);
-        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)mb, i);
-        for (uint32_t f = a + (uint32_t)lane; f < e; f += 64) s_addr[f] = b + (f - a);
+      // The bounds are in registers before the loop: without this wait the
+      // loop would wait at every unit for the LDS writes of the one before.
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      // Four units at a time (the last one repeated past nb: the same
+      // writes again); a unit's first 64 entries in one write, the rest of
+      // a larger unit after.
+      for (int i0 = 0; i0 < nb; i0 += 4) {
+        uint32_t ua[4], ue[4], uw[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = min(i0 + x, nb - 1);
+          ua[x] = (uint32_t)__builtin_amdgcn_readlane((int)ma, i);
+          ue[x] = (uint32_t)__builtin_amdgcn_readlane((int)me, i);
+          uw[x] = (uint32_t)__builtin_amdgcn_readlane((int)mb, i);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (ua[x] + (uint32_t)lane < ue[x]) s_addr[ua[x] + lane] = uw[x] + (uint32_t)lane;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          for (uint32_t f = ua[x] + 64u + (uint32_t)lane; f < ue[x]; f += 64)
+            s_addr[f] = uw[x] + (f - ua[x]);
       }
     }
     __syncthreads();
