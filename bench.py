@@ -829,21 +829,22 @@ def main():
     torch.cuda.synchronize()
 
     def step(s, ev=None, scan_ev=None, mode="separate"):
-        """One decode step: append the newest block, plan, scan, select.
+        """One decode step: append the newest block and plan (fathom_append_plan;
+        fathom_encode and fathom_plan in the stage pass), scan, select.
         mode "fused": the scan and the selection as fathom_scan_topk without a
         score buffer; "separate": fathom_scan then fathom_topk.
         ev: five events between the stages (separate mode); scan_ev: two
         events that fathom_scan_timed records from the scan kernels' own
         timestamps."""
         planes, scales = stores[s % len(stores)]
-        if ev is not None:
-            ev[0].record()
-        fk.encode(newest, planes, scales, block_offset=nb - 1)
-        if ev is not None:
-            ev[1].record()
         q = query(s)
-        fk.plan(q, var_d, B, depths=depths)
-        if ev is not None:
+        if ev is None:   # the append and the plan as one call (one launch)
+            fk.append_plan(newest, planes, scales, nb - 1, q, var_d, B, depths=depths)
+        else:            # the stage pass times them apart
+            ev[0].record()
+            fk.encode(newest, planes, scales, block_offset=nb - 1)
+            ev[1].record()
+            fk.plan(q, var_d, B, depths=depths)
             ev[2].record()
         if mode == "fused":
             fk.scan_topk(planes, scales, depths, q, n, k, indices=idx, workspace=fws,

@@ -53,9 +53,10 @@
 extern "C" {
 #endif
 
-#define FATHOM_ABI_VERSION 8   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
+#define FATHOM_ABI_VERSION 9   /* 2: fathom_plan_fixed; 3: fathom_scan_topk; 4: fathom_gather;
                                   5: fathom_klt_*; 6: fathom_scan_timed;
-                                  7: fathom_topk_noalloc; 8: fathom_test_cut_hooks */
+                                  7: fathom_topk_noalloc; 8: fathom_test_cut_hooks;
+                                  9: fathom_append_plan */
 
 enum fathom_status {
   FATHOM_OK = 0,
@@ -126,6 +127,24 @@ int fathom_encode(const uint16_t* k, int64_t groups, int64_t n, int32_t d,
 int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G,
                 int32_t d, int32_t budget_bits, uint8_t* depths, double* theta,
                 int32_t* bits_used, void* stream);
+
+/*
+ * fathom_append_plan — a decode step's store append (§3.2) and plan (§3.3,
+ * Eq. 4) in one call: exactly fathom_encode(k, groups, n, d, nb_store,
+ * block_offset, planes, scales, nonfinite_flag) and then fathom_plan(q, var,
+ * groups, G, d, budget_bits, depths, theta, bits_used), the same outputs bit
+ * for bit.  The two read and write disjoint data, so when the append is at
+ * most 64 blocks per group (n <= 4096, the decode-time append) they run as
+ * one launch, the plan's groups first; longer appends run as the two
+ * launches.  Arguments, layouts and errors are those of the two calls (a
+ * failed check of either returns before anything is enqueued); q, var and
+ * depths must not overlap k, planes or scales.
+ */
+int fathom_append_plan(const uint16_t* k, int64_t groups, int64_t n, int32_t d,
+                       int64_t nb_store, int64_t block_offset, uint64_t* planes,
+                       uint16_t* scales, uint32_t* nonfinite_flag, const float* q,
+                       const float* var, int32_t G, int32_t budget_bits, uint8_t* depths,
+                       double* theta, int32_t* bits_used, void* stream);
 
 /*
  * fathom_plan_fixed — fixed-depth plans, the pages' comparison points read

@@ -8,7 +8,7 @@ libfathom.so (include/fathom.h); this package is a thin ctypes binding that
 takes torch device tensors.  Importing a call loads the library and raises if
 it has not been built.
 """
-_EXPORTS = ("encode", "plan", "plan_fixed", "PLAN_MODES", "scan", "scan_topk", "scan_topk_workspace", "gather", "klt_fit", "klt_fit_workspace",
+_EXPORTS = ("encode", "plan", "append_plan", "plan_fixed", "PLAN_MODES", "scan", "scan_topk", "scan_topk_workspace", "gather", "klt_fit", "klt_fit_workspace",
             "klt_rotate_keys", "klt_rotate_queries", "topk", "topk_noalloc", "topk_workspace_bytes", "topk_workspace",
             "test_cut_hooks",
             "empty_store", "store_shapes", "FathomError", "lib", "STATUS", "EXPORTED")

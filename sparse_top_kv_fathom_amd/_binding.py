@@ -35,7 +35,7 @@ STATUS = {
     -9: "FATHOM_ERR_TOO_LARGE",
 }
 
-EXPORTED = ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+EXPORTED = ("fathom_encode", "fathom_plan", "fathom_append_plan", "fathom_plan_fixed", "fathom_scan",
             "fathom_scan_timed", "fathom_topk",
             "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
             "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
@@ -64,6 +64,8 @@ def lib():
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.fathom_encode.argtypes = [P, I64, I64, I32, I64, I64, P, P, P, P]
         L.fathom_plan.argtypes = [P, P, I64, I32, I32, I32, P, P, P, P]
+        L.fathom_append_plan.argtypes = [P, I64, I64, I32, I64, I64, P, P, P, P, P, I32, I32, P,
+                                         P, P, P]
         L.fathom_plan_fixed.argtypes = [P, P, I64, I32, I32, I32, I32, P, P]
         L.fathom_scan.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P]
         L.fathom_scan_timed.argtypes = [P, P, I64, P, P, I64, I32, I32, I64, P, P, P, P]
@@ -162,6 +164,32 @@ def plan(q: torch.Tensor, var: torch.Tensor, budget_bits: int, depths: torch.Ten
         _opt(theta, "theta", torch.float64, (groups,)),
         _opt(bits_used, "bits_used", torch.int32, (groups,)), _stream(stream))
     _check(st, "fathom_plan")
+    return depths
+
+
+def append_plan(k: torch.Tensor, planes: torch.Tensor, scales: torch.Tensor, block_offset: int,
+                q: torch.Tensor, var: torch.Tensor, budget_bits: int,
+                depths: torch.Tensor | None = None, theta: torch.Tensor | None = None,
+                bits_used: torch.Tensor | None = None, nonfinite_flag: torch.Tensor | None = None,
+                stream=None):
+    """fathom_append_plan: encode(k, planes, scales, block_offset) and
+    plan(q, var, budget_bits) in one call (one launch for an append of at
+    most 64 blocks per group) -> depths uint8 [groups][d]."""
+    groups, n, d = k.shape
+    G = q.shape[1]
+    nb_store = planes.shape[-1]
+    ps, ss = store_shapes(groups, nb_store, d)
+    if depths is None:
+        depths = torch.empty((groups, d), dtype=torch.uint8, device=q.device)
+    st = lib().fathom_append_plan(
+        _dev(k, "k", torch.float16), groups, n, d, nb_store, block_offset,
+        _dev(planes, "planes", torch.uint64, ps), _dev(scales, "scales", torch.uint16, ss),
+        _opt(nonfinite_flag, "nonfinite_flag", torch.int32, (1,)),
+        _dev(q, "q", torch.float32, (groups, G, d)), _dev(var, "var", torch.float32, (groups, d)),
+        G, int(budget_bits), _dev(depths, "depths", torch.uint8, (groups, d)),
+        _opt(theta, "theta", torch.float64, (groups,)),
+        _opt(bits_used, "bits_used", torch.int32, (groups,)), _stream(stream))
+    _check(st, "fathom_append_plan")
     return depths
 
 

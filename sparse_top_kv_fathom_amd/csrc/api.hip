@@ -89,6 +89,30 @@ int fathom_plan(const float* q, const float* var, int64_t groups, int32_t G, int
                                        static_cast<hipStream_t>(stream)));
 }
 
+int fathom_append_plan(const uint16_t* k, int64_t groups, int64_t n, int32_t d,
+                       int64_t nb_store, int64_t block_offset, uint64_t* planes,
+                       uint16_t* scales, uint32_t* nonfinite_flag, const float* q,
+                       const float* var, int32_t G, int32_t budget_bits, uint8_t* depths,
+                       double* theta, int32_t* bits_used, void* stream) {
+  if (!k || !planes || !scales || !q || !var || !depths) return FATHOM_ERR_NULL_ARG;
+  if (d != fathom::kD || G < 1 || G > 8 || groups < 1 || groups > kMaxGroups ||
+      !valid_tokens(n))
+    return FATHOM_ERR_BAD_SHAPE;
+  if (nb_store < 1 || nb_store >= kMaxTokens / fathom::kBlock || block_offset < 0 ||
+      block_offset + n / fathom::kBlock > nb_store)
+    return FATHOM_ERR_BAD_SHAPE;
+  if (budget_bits < 0 || budget_bits > fathom::kPlanes * d) return FATHOM_ERR_BAD_RANGE;
+  if (!aligned(k, 16) || !aligned(planes, 8) || !aligned(scales, 2) ||
+      !aligned(nonfinite_flag, 4) || !aligned(q, 4) || !aligned(var, 4) || !aligned(theta, 8) ||
+      !aligned(bits_used, 4))
+    return FATHOM_ERR_ALIGNMENT;
+  if (int s = device_ready()) return s;
+  return to_status(fathom::launch_append_plan(k, groups, n, nb_store, block_offset, planes,
+                                              scales, nonfinite_flag, q, var, G, budget_bits,
+                                              depths, theta, bits_used,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int fathom_plan_fixed(const float* q, const float* stat, int64_t groups, int32_t G, int32_t d,
                       int32_t mode, int32_t param, uint8_t* depths, void* stream) {
   if (!depths) return FATHOM_ERR_NULL_ARG;

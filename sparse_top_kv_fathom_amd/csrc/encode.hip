@@ -21,6 +21,7 @@
 // (channel, plane).  Calls with few blocks use a column-split kernel instead
 // (below), which spreads a block's channels over waves with lane = token.
 #include "fathom_internal.h"
+#include "plan_core.h"
 
 namespace fathom {
 namespace {
@@ -233,13 +234,12 @@ __global__ __launch_bounds__(kStoreWaves * 64) void encode_kernel(
 // of a block is not one wave's serial loop.  Grid: (blocks, groups, 4); the
 // 4 waves of a workgroup take columns 4z .. 4z+3.  Words and scales are
 // written directly, one 32-bit half of a word per lane.
-__global__ __launch_bounds__(256) void encode_cols_kernel(
+__device__ __forceinline__ void encode_cols_block(
     const uint16_t* __restrict__ k, int64_t n, int64_t nb_store, int64_t block_offset,
-    uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag) {
+    uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag,
+    int64_t g, int64_t blk, int z) {
   const int lane = lane_id();
-  const int col = blockIdx.z * kWavesPerWg + (threadIdx.x >> 6);   // 0..15
-  const int64_t g = blockIdx.y;
-  const int64_t blk = blockIdx.x;
+  const int col = z * kWavesPerWg + (threadIdx.x >> 6);   // 0..15
   const uint4 v = *reinterpret_cast<const uint4*>(k + ((g * n) + blk * kBlock + lane) * kD + col * 8);
   bool bad = false;
   uint32_t words = 0u, sc = 0u;
@@ -252,10 +252,84 @@ __global__ __launch_bounds__(256) void encode_cols_kernel(
   if (flag != nullptr && bad && lane == 0) atomicOr(flag, 1u);
 }
 
+__global__ __launch_bounds__(256) void encode_cols_kernel(
+    const uint16_t* __restrict__ k, int64_t n, int64_t nb_store, int64_t block_offset,
+    uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag) {
+  encode_cols_block(k, n, nb_store, block_offset, planes, scales, flag, blockIdx.y, blockIdx.x,
+                    blockIdx.z);
+}
+
+// fathom_append_plan: a decode step's append and plan in one launch (they
+// read and write disjoint data).  Workgroups [0, groups) plan one group each
+// (wave 0: plan_core::plan_group; they come first, as the plan is the longer
+// chain); the others encode the appended blocks as encode_cols_kernel does,
+// workgroup groups + (g * nblk + blk) * 4 + z taking block blk of group g,
+// columns 4z .. 4z+3.
+template <int G>
+__global__ __launch_bounds__(256) void append_plan_kernel(
+    const uint16_t* __restrict__ k, int64_t n, int64_t nb_store, int64_t block_offset,
+    uint64_t* __restrict__ planes, uint16_t* __restrict__ scales, uint32_t* __restrict__ flag,
+    int64_t groups, const float* __restrict__ q, const float* __restrict__ var, int budget,
+    uint8_t* __restrict__ depths, double* __restrict__ theta, int32_t* __restrict__ bits) {
+  const int64_t id = blockIdx.x;
+  if (id < groups) {
+    if (threadIdx.x < 64) plan_core::plan_group<G>(q, var, budget, depths, theta, bits, id);
+    return;
+  }
+  const int64_t nblk = n / kBlock;
+  const int64_t e = id - groups;
+  const int z = (int)(e % (kD / 8 / kWavesPerWg));
+  const int64_t gb = e / (kD / 8 / kWavesPerWg);
+  encode_cols_block(k, n, nb_store, block_offset, planes, scales, flag, gb / nblk, gb % nblk, z);
+}
+
+template <int G>
+void launch_append_plan_g(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
+                          int64_t block_offset, uint64_t* planes, uint16_t* scales,
+                          uint32_t* flag, const float* q, const float* var, int budget,
+                          uint8_t* depths, double* theta, int32_t* bits, hipStream_t stream) {
+  const int64_t wgs = groups + groups * (n / kBlock) * (kD / 8 / kWavesPerWg);
+  hipLaunchKernelGGL(append_plan_kernel<G>, dim3((unsigned)wgs), dim3(64 * kWavesPerWg), 0,
+                     stream, k, n, nb_store, block_offset, planes, scales, flag, groups, q, var,
+                     budget, depths, theta, bits);
+}
+
 }  // namespace
 
 // Below this many blocks per group the column-split kernel is used.
 constexpr int64_t kColsKernelMaxBlocks = 64;
+
+hipError_t launch_append_plan(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
+                              int64_t block_offset, uint64_t* planes, uint16_t* scales,
+                              uint32_t* nonfinite_flag, const float* q, const float* var, int G,
+                              int budget_bits, uint8_t* depths, double* theta,
+                              int32_t* bits_used, hipStream_t stream) {
+  if (n / kBlock > kColsKernelMaxBlocks) {   // not an append: the two launches
+    hipError_t e = launch_encode(k, groups, n, nb_store, block_offset, planes, scales,
+                                 nonfinite_flag, stream);
+    if (e != hipSuccess) return e;
+    return launch_plan(q, var, groups, G, budget_bits, depths, theta, bits_used, stream);
+  }
+  switch (G) {
+#define FATHOM_APPEND_PLAN_CASE(GG)                                                          \
+  case GG:                                                                                  \
+    launch_append_plan_g<GG>(k, groups, n, nb_store, block_offset, planes, scales,          \
+                             nonfinite_flag, q, var, budget_bits, depths, theta, bits_used, \
+                             stream);                                                       \
+    break;
+    FATHOM_APPEND_PLAN_CASE(1)
+    FATHOM_APPEND_PLAN_CASE(2)
+    FATHOM_APPEND_PLAN_CASE(3)
+    FATHOM_APPEND_PLAN_CASE(4)
+    FATHOM_APPEND_PLAN_CASE(5)
+    FATHOM_APPEND_PLAN_CASE(6)
+    FATHOM_APPEND_PLAN_CASE(7)
+    FATHOM_APPEND_PLAN_CASE(8)
+#undef FATHOM_APPEND_PLAN_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_encode(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
                          int64_t block_offset, uint64_t* planes, uint16_t* scales,

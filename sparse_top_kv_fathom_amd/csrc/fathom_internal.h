@@ -19,6 +19,13 @@ hipError_t launch_encode(const uint16_t* k, int64_t groups, int64_t n, int64_t n
                          int64_t block_offset, uint64_t* planes, uint16_t* scales,
                          uint32_t* nonfinite_flag, hipStream_t stream);
 
+// fathom_append_plan: launch_encode and launch_plan in one launch when the
+// append is at most 64 blocks per group (else the two launches).
+hipError_t launch_append_plan(const uint16_t* k, int64_t groups, int64_t n, int64_t nb_store,
+                              int64_t block_offset, uint64_t* planes, uint16_t* scales,
+                              uint32_t* nonfinite_flag, const float* q, const float* var, int G,
+                              int budget_bits, uint8_t* depths, double* theta,
+                              int32_t* bits_used, hipStream_t stream);
 hipError_t launch_plan(const float* q, const float* var, int64_t groups, int G,
                        int budget_bits, uint8_t* depths, double* theta, int32_t* bits_used,
                        hipStream_t stream);

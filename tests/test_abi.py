@@ -41,7 +41,7 @@ def _gpu_visible():
 
 def test_header_declares_the_calls():
     names = declared()
-    for f in ("fathom_encode", "fathom_plan", "fathom_plan_fixed", "fathom_scan",
+    for f in ("fathom_encode", "fathom_plan", "fathom_append_plan", "fathom_plan_fixed", "fathom_scan",
               "fathom_scan_timed", "fathom_topk",
               "fathom_scan_topk", "fathom_scan_topk_workspace_bytes", "fathom_gather",
               "fathom_klt_fit", "fathom_klt_fit_workspace_bytes", "fathom_klt_rotate_keys",
@@ -61,7 +61,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fathom_abi_version() == 8
+    assert L.fathom_abi_version() == 9
     for code in (OK, NULL_ARG, BAD_SHAPE, BAD_RANGE, WORKSPACE, HIP, NO_DEVICE, ALIGN, -8, -9):
         s = L.fathom_status_string(code).decode()
         assert s.startswith("FATHOM_")
@@ -97,6 +97,36 @@ def test_plan_validation(L):
     assert p(FAKE, FAKE, 1, 4, 128, -1, FAKE, None, None, None) == BAD_RANGE
     assert p(FAKE, FAKE, 1, 4, 128, 513, FAKE, None, None, None) == BAD_RANGE
     assert p(FAKE, FAKE, 1, 4, 128, 92, FAKE, P(4), None, None) == ALIGN         # theta 8 B
+
+
+def test_append_plan_validation(L):
+    """fathom_append_plan checks both calls' arguments: each failure of
+    fathom_encode's or fathom_plan's checks, and the same codes."""
+    a = L.fathom_append_plan
+    enc = (FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, None)
+    pl = (FAKE, FAKE, 4, 92, FAKE, None, None, None)
+
+    def call(e=enc, p=pl):
+        return a(*e, *p)
+    assert call() != NULL_ARG
+    assert call(e=(None,) + enc[1:]) == NULL_ARG                                # k
+    assert call(e=enc[:6] + (None,) + enc[7:]) == NULL_ARG                      # planes
+    assert call(e=enc[:7] + (None,) + enc[8:]) == NULL_ARG                      # scales
+    assert call(p=(None,) + pl[1:]) == NULL_ARG                                 # q
+    assert call(p=pl[:1] + (None,) + pl[2:]) == NULL_ARG                        # var
+    assert call(p=pl[:4] + (None,) + pl[5:]) == NULL_ARG                        # depths
+    assert call(e=enc[:3] + (64,) + enc[4:]) == BAD_SHAPE                       # d != 128
+    assert call(e=(FAKE, 0) + enc[2:]) == BAD_SHAPE                             # groups
+    assert call(e=(FAKE, 1, 4000) + enc[3:]) == BAD_SHAPE                       # n % 64
+    assert call(e=enc[:4] + (63,) + enc[5:]) == BAD_SHAPE                       # capacity
+    assert call(e=enc[:4] + (70, 7) + enc[6:]) == BAD_SHAPE                     # offset + nb
+    assert call(p=(FAKE, FAKE, 0) + pl[3:]) == BAD_SHAPE                        # G
+    assert call(p=(FAKE, FAKE, 9) + pl[3:]) == BAD_SHAPE
+    assert call(p=(FAKE, FAKE, 4, -1) + pl[4:]) == BAD_RANGE                    # budget
+    assert call(p=(FAKE, FAKE, 4, 513) + pl[4:]) == BAD_RANGE
+    assert call(e=(P(8),) + enc[1:]) == ALIGN                                   # k 16 B
+    assert call(e=enc[:8] + (P(2),)) == ALIGN                                   # flag 4 B
+    assert call(p=pl[:5] + (P(4), None, None)) == ALIGN                         # theta 8 B
 
 
 def test_plan_fixed_validation(L):
@@ -311,6 +341,8 @@ def test_valid_calls_report_no_device(L):
     assert L.fathom_topk_noalloc(FAKE, 4, 1000, 10, FAKE, None) == NO_DEVICE
     assert L.fathom_plan(FAKE, FAKE, 1, 4, 128, 92, FAKE, None, None, None) == NO_DEVICE
     assert L.fathom_encode(FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, None, None) == NO_DEVICE
+    assert L.fathom_append_plan(FAKE, 1, 4096, 128, 64, 0, FAKE, FAKE, None, FAKE, FAKE, 4, 92,
+                                FAKE, None, None, None) == NO_DEVICE
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

@@ -189,3 +189,40 @@ def test_plan_fixed_matches_oracle(fk, G):
         got = to_host(fk.plan_fixed("topstat", r, stat=to_dev(stat), G=G))
         ref = oracle.plan_fixed("topstat", r, stat=stat)
         assert np.array_equal(got, ref), (r, first_mismatch(got, ref))
+
+
+# --------------------------------------------------------------------------
+# The decode step's append and plan as one call
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,nblk_new,offset", [(1, 1, 69), (4, 3, 10), (8, 1, 0), (4, 65, 2)])
+def test_append_plan_matches_two_calls(fk, G, nblk_new, offset):
+    """fathom_append_plan against fathom_encode then fathom_plan on copies of
+    the same store, bit for bit: every plane word and scale of the store, the
+    depths, water lines and bit counts.  One launch for appends of 1 and 3
+    blocks; 65 blocks (more than 64) takes the two launches."""
+    import torch
+    groups, nb_store, B = 3, 70 + 64, 92
+    ins = fathom_inputs.make_inputs(groups, G, 64 * nb_store, seed=300 + G)
+    base = torch.from_numpy(ins.k[:, :64 * nb_store].copy()).cuda()
+    p0, s0 = fk.encode(base)                               # a full store to append into
+    new = torch.from_numpy(ins.k[:, ::-1][:, :64 * nblk_new].copy()).cuda()
+    q, var = to_dev(ins.q), to_dev(ins.var)
+    say("append_plan G=%d blocks=%d offset=%d" % (G, nblk_new, offset))
+    pa, sa = p0.clone(), s0.clone()
+    pb, sb = p0.clone(), s0.clone()
+    da = torch.empty((groups, 128), dtype=torch.uint8, device="cuda")
+    ta = torch.empty(groups, dtype=torch.float64, device="cuda")
+    ba = torch.empty(groups, dtype=torch.int32, device="cuda")
+    fk.append_plan(new, pa, sa, offset, q, var, B, depths=da, theta=ta, bits_used=ba)
+    tb = torch.empty(groups, dtype=torch.float64, device="cuda")
+    bb = torch.empty(groups, dtype=torch.int32, device="cuda")
+    fk.encode(new, pb, sb, block_offset=offset)
+    db = fk.plan(q, var, B, theta=tb, bits_used=bb)
+    torch.cuda.synchronize()
+    assert torch.equal(pa, pb) and torch.equal(sa, sb)
+    assert not torch.equal(pa, p0)                         # the append wrote the store
+    assert torch.equal(da, db) and torch.equal(ba, bb)
+    assert np.array_equal(to_host(ta).view(np.uint64), to_host(tb).view(np.uint64))
+    od, ot, ob = oracle.plan(ins.q, ins.var, B)
+    assert np.array_equal(to_host(da), od)
