@@ -626,17 +626,19 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     // Load.  s_addr[f]: the candidate buffer slot of candidate f (in index
     // order), written by the thread that owns f's unit, so that the loads'
     // addresses are one independent LDS read each.
-    // Wave w fills units w, w + 16, ...: lane i reads the bounds of the
-    // wave's i-th unit of a batch of 64, then the wave writes each unit's
-    // entries 64 at a time.
-    for (int64_t ub = 0; ub < nunits; ub += (int64_t)kW * 64) {
-      const int64_t my = ub + wave + (int64_t)kW * lane;
-      const bool ok = my < nunits;
+    // Wave w fills its own run of consecutive units [w * upw, w * upw +
+    // upw), 64 at a time: lane i reads the bounds of the i-th (consecutive
+    // words: no LDS bank conflicts), then the wave writes each unit's entries
+    // 64 at a time.
+    const int64_t upw = (nunits + kW - 1) / kW;
+    const int64_t wend = min<int64_t>(nunits, (int64_t)(wave + 1) * upw);
+    for (int64_t ub = (int64_t)wave * upw; ub < wend; ub += 64) {
+      const int64_t my = ub + lane;
+      const bool ok = my < wend;
       const uint32_t ma = ok ? s_gt[my] : 0u;
       const uint32_t me = ok ? (my + 1 < nunits ? s_gt[my + 1] : ncand) : 0u;
       const uint32_t mb = ok ? unit_base(my) : 0u;
-      const int64_t left = nunits - ub - wave;   // this wave's units in the batch: ceil(left / 16)
-      const int nb = left > 0 ? (int)min<int64_t>(64, (left + kW - 1) / kW) : 0;
+      const int nb = (int)min<int64_t>(64, wend - ub);   // >= 1
       // The bounds are in registers before the loop: without this wait the
       // loop would wait at every unit for the LDS writes of the one before.
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
