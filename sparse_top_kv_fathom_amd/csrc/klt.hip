@@ -449,25 +449,35 @@ __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __rest
   const int to = tid & 15, jo = tid >> 4;
   const int lt = tid >> 1, lc = (tid & 1) * 64;      // staging: token, first channel
   const int64_t ntile = (n + kRotTok - 1) / kRotTok;
-  for (int64_t tile = (int64_t)blockIdx.x * kRotTiles;
-       tile < min<int64_t>(ntile, ((int64_t)blockIdx.x + 1) * kRotTiles); ++tile) {
+  const int64_t t_begin = (int64_t)blockIdx.x * kRotTiles;
+  const int64_t t_end = min<int64_t>(ntile, t_begin + kRotTiles);
+  // The next tile's keys are loaded into registers while the current tile
+  // is folded (the workgroup has the CU to itself: nothing else hides the
+  // load); tokens past the row's end read the last token, and their
+  // columns are folded and never written.
+  uint4 pre[8];
+  auto load_tile = [&](int64_t tile) {
+    const int64_t tok = min<int64_t>(tile * kRotTok + lt, n - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok) * kD + lc);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) pre[v] = src[v];
+  };
+  if (t_begin < t_end) load_tile(t_begin);
+  for (int64_t tile = t_begin; tile < t_end; ++tile) {
     const int64_t tok0 = tile * kRotTok;
-    __syncthreads();
-    if (tok0 + lt < n) {
-      const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok0 + lt) * kD + lc);
+    __syncthreads();   // the last tile's folds are done with s_x (s_mu is written)
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const uint4 w = src[v];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    for (int v = 0; v < 8; ++v) {
+      const uint32_t ws[4] = {pre[v].x, pre[v].y, pre[v].z, pre[v].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = lc + 8 * v + 2 * e;
-          s_x[c][lt] = f16_to_f32((uint16_t)(ws[e] & 0xffffu)) - s_mu[c];
-          s_x[c + 1][lt] = f16_to_f32((uint16_t)(ws[e] >> 16)) - s_mu[c + 1];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int c = lc + 8 * v + 2 * e;
+        s_x[c][lt] = f16_to_f32((uint16_t)(ws[e] & 0xffffu)) - s_mu[c];
+        s_x[c + 1][lt] = f16_to_f32((uint16_t)(ws[e] >> 16)) - s_mu[c + 1];
       }
     }
     __syncthreads();
+    if (tile + 1 < t_end) load_tile(tile + 1);
     float acc[8][8];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
