@@ -44,7 +44,7 @@ constexpr int kPacked = kD * (kD + 1) / 2;
 constexpr int kMaxSweeps = 24;
 constexpr int kRotThreads = 256;
 constexpr int kRotTok = 128;         // tokens per rotation tile
-constexpr int kRotTiles = 8;         // tiles per rotation workgroup
+constexpr int kRotTiles = 32;        // tiles per rotation workgroup
 constexpr int kXPitch = kRotTok + 4; // floats per channel row of the staged tile
 
 __device__ __forceinline__ double f16_to_f64(uint16_t h) {
