@@ -42,7 +42,7 @@ constexpr int kEigThreads = 1024;
 constexpr int kPairs = kD / 2;       // disjoint rotations per Jacobi step
 constexpr int kPacked = kD * (kD + 1) / 2;
 constexpr int kMaxSweeps = 24;
-constexpr int kRotThreads = 256;
+constexpr int kRotThreads = 512;
 constexpr int kRotTok = 128;         // tokens per rotation tile
 constexpr int kRotTiles = 32;        // tiles per rotation workgroup
 constexpr int kXPitch = kRotTok + 4; // floats per channel row of the staged tile
@@ -430,8 +430,9 @@ __global__ __launch_bounds__(kEigThreads) void klt_eig(int64_t n, int64_t P, con
 }
 
 // Rotated keys of kRotTiles 128-token tiles of group blockIdx.y.  Thread t
-// owns tokens 8 (t % 16) .. +7 and outputs 8 (t / 16) .. +7 of a tile; per
-// channel c it reads 8 centred values and 8 basis entries from LDS for 64
+// (of 512: two waves per SIMD, the one workgroup its LDS lets a CU hold)
+// owns tokens 8 (t % 16) .. +7 and outputs 4 (t / 16) .. +3 of a tile; per
+// channel c it reads 8 centred values and 4 basis entries from LDS for 32
 // fused multiply-adds.
 __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __restrict__ k,
                                                           const float* __restrict__ mu,
@@ -446,8 +447,8 @@ __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __rest
   for (int e = tid; e < kD * kD / 4; e += kRotThreads)
     reinterpret_cast<float4*>(&s_v[0][0])[e] = vsrc[e];
   if (tid < kD) s_mu[tid] = mu[g * kD + tid];
-  const int to = tid & 15, jo = tid >> 4;
-  const int lt = tid >> 1, lc = (tid & 1) * 64;      // staging: token, first channel
+  const int to = tid & 15, jo = tid >> 4;            // tokens 8 to .. +7, outputs 4 jo .. +3
+  const int lt = tid >> 2, lc = (tid & 3) * 32;      // staging: token, first channel
   const int64_t ntile = (n + kRotTok - 1) / kRotTok;
   const int64_t t_begin = (int64_t)blockIdx.x * kRotTiles;
   const int64_t t_end = min<int64_t>(ntile, t_begin + kRotTiles);
@@ -455,19 +456,19 @@ __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __rest
   // is folded (the workgroup has the CU to itself: nothing else hides the
   // load); tokens past the row's end read the last token, and their
   // columns are folded and never written.
-  uint4 pre[8];
+  uint4 pre[4];
   auto load_tile = [&](int64_t tile) {
     const int64_t tok = min<int64_t>(tile * kRotTok + lt, n - 1);
     const uint4* src = reinterpret_cast<const uint4*>(k + (g * n + tok) * kD + lc);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) pre[v] = src[v];
+    for (int v = 0; v < 4; ++v) pre[v] = src[v];
   };
   if (t_begin < t_end) load_tile(t_begin);
   for (int64_t tile = t_begin; tile < t_end; ++tile) {
     const int64_t tok0 = tile * kRotTok;
     __syncthreads();   // the last tile's folds are done with s_x (s_mu is written)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
+    for (int v = 0; v < 4; ++v) {
       const uint32_t ws[4] = {pre[v].x, pre[v].y, pre[v].z, pre[v].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -478,35 +479,32 @@ __global__ __launch_bounds__(kRotThreads) void klt_rotate(const uint16_t* __rest
     }
     __syncthreads();
     if (tile + 1 < t_end) load_tile(tile + 1);
-    float acc[8][8];
+    float acc[8][4];
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = 0.0f;
+      for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
 #pragma unroll 4
     for (int c = 0; c < kD; ++c) {
       const float4 x0 = *reinterpret_cast<const float4*>(&s_x[c][8 * to]);
       const float4 x1 = *reinterpret_cast<const float4*>(&s_x[c][8 * to + 4]);
-      const float4 v0 = *reinterpret_cast<const float4*>(&s_v[c][8 * jo]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&s_v[c][8 * jo + 4]);
+      const float4 v0 = *reinterpret_cast<const float4*>(&s_v[c][4 * jo]);
       const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      const float vs[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const float vs[4] = {v0.x, v0.y, v0.z, v0.w};
 #pragma unroll
       for (int a = 0; a < 8; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = __builtin_fmaf(xs[a], vs[b], acc[a][b]);
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_fmaf(xs[a], vs[b], acc[a][b]);
     }
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const int64_t tok = tok0 + 8 * to + a;
       if (tok >= n) break;
-      uint32_t h[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        h[b] = (uint32_t)f32_to_f16_rne(acc[a][2 * b]) |
-               ((uint32_t)f32_to_f16_rne(acc[a][2 * b + 1]) << 16);
-      *reinterpret_cast<uint4*>(out + (g * n + tok) * kD + 8 * jo) =
-          make_uint4(h[0], h[1], h[2], h[3]);
+      const uint32_t h0 = (uint32_t)f32_to_f16_rne(acc[a][0]) |
+                          ((uint32_t)f32_to_f16_rne(acc[a][1]) << 16);
+      const uint32_t h1 = (uint32_t)f32_to_f16_rne(acc[a][2]) |
+                          ((uint32_t)f32_to_f16_rne(acc[a][3]) << 16);
+      *reinterpret_cast<uint2*>(out + (g * n + tok) * kD + 4 * jo) = make_uint2(h0, h1);
     }
   }
 }
