@@ -469,19 +469,20 @@ def test_scan_topk_unrepresentative_sample_falls_back(fk, write_scores):
     _scan_topk_case(fk, groups, n, k, 92, seed=0, write_scores=write_scores, ins=ins)
 
 
-@pytest.mark.parametrize("write_scores", [True, False])
-def test_scan_topk_cut_never_published_falls_back(fk, write_scores):
+@pytest.mark.parametrize("groups,n,k,write_scores", [(2, (1 << 17) + 64 * 5, 700, True),
+                                                     (2, (1 << 17) + 64 * 5, 700, False),
+                                                     (1, 1 << 21, 4096, False)])
+def test_scan_topk_cut_never_published_falls_back(fk, groups, n, k, write_scores):
     """The scan's cut workgroups store the cuts but do not publish them
     (fathom_test_cut_hooks), and the waves give up after 4 polls: every row
     is flagged by the scan and selected from its scores (the caller's, or a
-    second scan into the workspace), with the same result.  The hooks are
-    restored afterwards, and a second call checks that the fused path is
-    back."""
-    n, k = (1 << 17) + 64 * 5, 700
-    say("scan_topk cut never published write_scores=%s" % write_scores)
+    second scan into the workspace: at 2^21 keys the largest fused row), with
+    the same result.  The hooks are restored afterwards, and a second call
+    checks that the fused path is back."""
+    say("scan_topk cut never published groups=%d n=%d write_scores=%s" % (groups, n, write_scores))
     fk.test_cut_hooks(publish=False, spin_limit=4)
     try:
-        _scan_topk_case(fk, 2, n, k, 92, seed=101, write_scores=write_scores)
+        _scan_topk_case(fk, groups, n, k, 92, seed=101, write_scores=write_scores)
     finally:
         fk.test_cut_hooks(publish=True, spin_limit=2048)
-    _scan_topk_case(fk, 2, n, k, 92, seed=102, write_scores=write_scores)
+    _scan_topk_case(fk, groups, n, k, 92, seed=102, write_scores=write_scores)
