@@ -523,12 +523,13 @@ def run_configs(fk, args, main_ctx):
     return out
 
 
-def run_layouts(fk, args, ctx):
+def run_layouts(fk, args, ctx, ins):
     """Store layouts and row lengths off the main kernel's 16-byte path: the
     scan on a copy of the store with capacity n/64 + 3 blocks (scale rows not
-    16-byte aligned) beside the store itself, and fathom_scan_topk on a ragged
-    row length (whole rounds plus a tail) beside scan then top-k.  Event
-    medians in ms."""
+    16-byte aligned) beside the store itself, fathom_scan_topk on a ragged
+    row length (whole rounds plus a tail) beside scan then top-k, and
+    fathom_scan_topk on a store whose top keys crowd into one round beside
+    the plain store.  Event medians in ms."""
     import torch
     stores, q_d, var_d, n, k, B = (ctx["stores"], ctx["q_d"], ctx["var_d"], ctx["n"], ctx["k"],
                                    ctx["B"])
@@ -575,7 +576,37 @@ def run_layouts(fk, args, ctx):
         "separate_scan_topk_ms": timed(lambda: (fk.scan(p0, s0, depths, q_d[0], nr, scores=sr),
                                                 fk.topk(sr, k, indices=idx, workspace=tws))),
     }
-    del p3, s3, scores, fws, tws, sr
+    del p3, s3, fws, tws, sr
+    # Top keys crowded into one stretch of each row: 420 keys aligned with
+    # the group's queries inside the last 2048-key round (the sample reads
+    # none of it), the round re-encoded into a copy of the store.
+    width, r0 = 420, n - 2048
+    kr = ins.k[:, r0:, :].copy()
+    q0 = ctx["qs"][0]
+    rng = np.random.default_rng(7)
+    for g in range(H):
+        qn = q0[g].astype(np.float64).sum(axis=0)
+        qn /= np.abs(qn).max()
+        top = 4.0 * float(np.abs(ins.k[g]).max())
+        mag = top * rng.uniform(0.5, 1.0, width)
+        kr[g, 512:512 + width] = (mag[:, None] * qn[None, :]).astype(np.float16)
+    pc, sc = p0.clone(), s0.clone()
+    fk.encode(torch.from_numpy(kr).to(dev), planes=pc, scales=sc, block_offset=r0 // 64)
+    fws = fk.scan_topk_workspace(H, G, n, k, dev)
+    tws = fk.topk_workspace(H * G, n, k, dev)
+    idx2 = torch.empty((H * G, k), dtype=torch.int32, device=dev)
+    fused_c = timed(lambda: fk.scan_topk(pc, sc, depths, q_d[0], n, k, indices=idx,
+                                         workspace=fws, write_scores=False))
+    fused_p = timed(lambda: fk.scan_topk(p0, s0, depths, q_d[0], n, k, indices=idx2,
+                                         workspace=fws, write_scores=False))
+    fk.scan(pc, sc, depths, q_d[0], n, scores=scores)
+    fk.topk(scores, k, indices=idx2, workspace=tws)
+    fk.scan_topk(pc, sc, depths, q_d[0], n, k, indices=idx, workspace=fws, write_scores=False)
+    torch.cuda.synchronize()
+    out["clustered"] = {"window_keys": width, "round_first_key": r0,
+                        "fused_scan_topk_ms": fused_c, "fused_scan_topk_ms_plain_store": fused_p,
+                        "indices_equal_scan_then_topk": bool(torch.equal(idx, idx2))}
+    del pc, sc, fws, tws, scores, idx2
     torch.cuda.empty_cache()
     return out
 
@@ -1021,7 +1052,7 @@ def main():
     ctx = {"name": w.name, "stores": stores, "q_d": q_d, "qs": qs, "var_d": var_d, "n": n,
            "k": k, "B": B}
     if not args.no_compare and args.store == "raw":
-        out["layouts"] = run_layouts(fk, args, ctx)
+        out["layouts"] = run_layouts(fk, args, ctx, ins)
         print("[bench] layouts done", file=sys.stderr, flush=True)
         out["compare_plans"] = run_compare(fk, args, ctx, ins)
         print("[bench] fixed-plan comparison done", file=sys.stderr, flush=True)

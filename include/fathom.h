@@ -282,11 +282,12 @@ int fathom_topk_noalloc(const float* scores, int64_t rows, int64_t n, int32_t k,
  * plane array is under 4 GiB): 8 runs of 1024 keys spread evenly over each
  * row are scored first, a cut tau per row is taken from that sample (inside
  * the scan's launch), and the scan then writes every score >= tau, in index
- * order, to the row's candidate buffer (pooled per 2048-key round, the
- * blocks after the last whole round per 512-key tile, the last one possibly
- * partial), from which the selection is made.  A row whose candidates
- * cannot give the selection (fewer than k of them, or a round with more
- * than its region holds: heavy ties) is selected from its scores: from
+ * order, to the row's candidate buffer (pooled per 2048-key round, which
+ * holds 512 of them; the blocks after the last whole round per 512-key
+ * tile, 128 each, the last tile possibly partial), from which the selection
+ * is made.  A row whose candidates cannot give the selection (fewer than k
+ * of them, or a round with more than its region holds: heavy ties, or top
+ * keys crowded past a quarter of a round) is selected from its scores: from
  * `scores`, or, when `scores` is null, from a second scan of its group into
  * the workspace.
  * Otherwise the two calls run as they are (into the workspace when `scores`

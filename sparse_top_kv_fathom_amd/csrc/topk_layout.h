@@ -26,18 +26,24 @@ enum : int {
 // scan emits them.
 __host__ __device__ inline int64_t n_chunks(int64_t n, int64_t R) { return (n + R - 1) / R; }
 
-// Candidate buffer capacity: n / 8, between 8192 and 65536 keys, shared
-// equally by the chunks (512 per chunk at n = 2^20).
-__host__ __device__ inline int64_t cand_cap(int64_t n) {
+// Candidate buffer capacity of a row, shared equally by its chunks.
+// Compaction from scores (R = kCompactChunk): n / 8, between 8192 and 65536
+// keys (512 per 8192-key chunk at n = 2^20).  The scan's own candidates (R =
+// its 512-key wave tile): n / 4, at least 8192 (128 per tile, 512 per
+// 2048-key round), so that top keys crowded into one stretch of the row, up
+// to a quarter of a round, still fit; only the candidates written cost time,
+// not the capacity.
+__host__ __device__ inline int64_t cand_cap(int64_t n, int64_t R) {
+  if (R != kCompactChunk) return n / 4 < 8192 ? 8192 : n / 4;
   const int64_t c = n / 8;
   return c < 8192 ? 8192 : (c > 65536 ? 65536 : c);
 }
 __host__ __device__ inline uint32_t region(int64_t n, int64_t R) {
-  return (uint32_t)(cand_cap(n) / n_chunks(n, R));
+  return (uint32_t)(cand_cap(n, R) / n_chunks(n, R));
 }
 
 __host__ __device__ inline size_t row_words(int64_t n, int64_t R) {
-  return kS_WORDS + 2 * (size_t)cand_cap(n) + 4 * (size_t)n_chunks(n, R);
+  return kS_WORDS + 2 * (size_t)cand_cap(n, R) + 4 * (size_t)n_chunks(n, R);
 }
 
 struct RowWs {
@@ -54,7 +60,7 @@ __device__ __forceinline__ RowWs row_ws(void* ws, int64_t n, int64_t R, int64_t 
   r.region = region(n, R);
   r.st = p;
   r.cand = r.st + kS_WORDS;
-  r.seg = r.cand + 2 * (size_t)cand_cap(n);
+  r.seg = r.cand + 2 * (size_t)cand_cap(n, R);
   r.stamp = r.seg + 2 * (size_t)n_chunks(n, R);
   return r;
 }
@@ -71,7 +77,7 @@ __host__ __device__ inline RowGeom row_geom(int64_t n, int64_t R) {
   RowGeom g;
   g.words = row_words(n, R);
   g.region = region(n, R);
-  g.seg_off = (uint32_t)(kS_WORDS + 2 * cand_cap(n));
+  g.seg_off = (uint32_t)(kS_WORDS + 2 * cand_cap(n, R));
   g.stamp_off = g.seg_off + 2 * (uint32_t)n_chunks(n, R);
   return g;
 }

@@ -469,6 +469,30 @@ def test_scan_topk_unrepresentative_sample_falls_back(fk, write_scores):
     _scan_topk_case(fk, groups, n, k, 92, seed=0, write_scores=write_scores, ins=ins)
 
 
+@pytest.mark.parametrize("write_scores", [True, False])
+@pytest.mark.parametrize("width", [300, 420])
+def test_scan_topk_clustered_window(fk, width, write_scores):
+    """Top keys crowded into one stretch of the row, away from the sampled
+    runs: `width` keys aligned with the group's queries inside the 2048-key
+    round at keys 4096..6143 (the sample reads keys 0..1023, 16384..17407,
+    ...).  With the round's other candidates (about 50 at this k) they fit
+    the round's 512 slots, so these rows are selected from the candidates,
+    through a round far fuller than the others; the result is the same as
+    scan then top-k."""
+    groups, G, n, k = 2, 4, 1 << 17, 2000
+    ins = fathom_inputs.make_inputs(groups, G, n, seed=121)
+    rng = np.random.default_rng(122)
+    s0 = 4096 + 300
+    for g in range(groups):
+        qn = ins.q[g].astype(np.float64).sum(axis=0)
+        qn /= np.abs(qn).max()
+        top = 4.0 * float(np.abs(ins.k[g]).max())
+        mag = top * rng.uniform(0.5, 1.0, width)
+        ins.k[g, s0:s0 + width] = (mag[:, None] * qn[None, :]).astype(np.float16)
+    say("scan_topk clustered window width=%d write_scores=%s" % (width, write_scores))
+    _scan_topk_case(fk, groups, n, k, 92, seed=0, write_scores=write_scores, ins=ins)
+
+
 @pytest.mark.parametrize("groups,n,k,write_scores", [(2, (1 << 17) + 64 * 5, 700, True),
                                                      (2, (1 << 17) + 64 * 5, 700, False),
                                                      (1, 1 << 21, 4096, False)])
