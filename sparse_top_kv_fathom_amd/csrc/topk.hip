@@ -628,8 +628,11 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
     // addresses are one independent LDS read each.
     // Wave w fills its own run of consecutive units [w * upw, w * upw +
     // upw), 64 at a time: lane i reads the bounds of the i-th (consecutive
-    // words: no LDS bank conflicts), then the wave writes each unit's entries
-    // 64 at a time.
+    // words: no LDS bank conflicts).  When none of the 64 holds more than 64
+    // candidates (the fused call's rounds: about 17 each at q1m), lane i
+    // writes its unit's entries itself, entry j of every unit in step j;
+    // otherwise (fathom_topk's chunks: about 68 each) the wave writes each
+    // unit's entries 64 at a time.
     const int64_t upw = (nunits + kW - 1) / kW;
     const int64_t wend = min<int64_t>(nunits, (int64_t)(wave + 1) * upw);
     for (int64_t ub = (int64_t)wave * upw; ub < wend; ub += 64) {
@@ -642,6 +645,14 @@ __global__ __launch_bounds__(kResolveThreads) void topk_resolve(const float* __r
       // The bounds are in registers before the loop: without this wait the
       // loop would wait at every unit for the LDS writes of the one before.
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      const uint32_t cnt = me - ma;   // 0 past wend
+      uint32_t mx = cnt;
+      for (int o = 1; o < 64; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+      if (mx <= 64u) {   // uniform
+        for (uint32_t j = 0; j < mx; ++j)
+          if (j < cnt) s_addr[ma + j] = mb + j;
+        continue;
+      }
       // Four units at a time (the last one repeated past nb: the same
       // writes again); a unit's first 64 entries in one write, the rest of
       // a larger unit after.
